@@ -1,0 +1,244 @@
+"""Seeded synthetic inputs for split-KV decode, shaped like the pages' workloads.
+
+This module only draws random numbers and builds index lists: it holds none of the attention,
+planner or merge arithmetic, so both the GPU path and the CPU oracle can be fed from it.
+
+Shapes follow the workloads the pages describe:
+
+* absorbed MLA decode (moonmath-amd README, "MLA decode"): bf16 ``q_lat [B*q_len, H, 512]`` and
+  ``q_pe [B*q_len, H, 64]`` drawn N(0,1); one fused fp8 e4m3 row of 576 bytes per token, stored as
+  N(0,1) / kv_scale with kv_scale = 1/32; page_size 1, so ``kv_indices`` is a flat slot list (a
+  seeded permutation: any permutation is legal); softmax scale 576^-0.5;
+* sparse top-k MLA decode (AITER issue on pa_decode_sparse, "Measurements"): 64 heads, rows of
+  512 fp8 bytes (448 NoPE + 64 RoPE) in a 262144-token cache, 2048 indices per query drawn
+  without replacement;
+* grouped-query decode over bf16 pages (moonmath-amd README, gfx950 "forward_paged"): caches
+  ``[pages, 16, kv_heads, 128]``, ``kv_indptr`` counting pages per sequence and
+  ``kv_page_indices`` a random placement of pages in the pool.
+
+Seeds: workload k uses base seed 1000*k; tensor offsets +1 q_lat (or q), +2 q_pe, +3 KV,
++4 indices, +5 lengths, +6 page placement.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Optional, Sequence
+
+import torch
+
+KV_SCALE = 1.0 / 32.0
+
+
+def _gen(device, seed):
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
+    return g
+
+
+def _randn(shape, seed, device, dtype=torch.float32):
+    return torch.randn(shape, generator=_gen(device, seed), device=device, dtype=dtype)
+
+
+def fp8_e4m3fn_bytes(x: torch.Tensor) -> torch.Tensor:
+    """Encode with torch's float8_e4m3fn cast and return the raw bytes (uint8)."""
+    b = x.to(torch.float8_e4m3fn).view(torch.uint8)
+    nan = (b & 0x7F) == 0x7F
+    if bool(nan.any()):
+        raise ValueError("fp8 encode produced NaN bytes (value above the e4m3fn range)")
+    return b
+
+
+def _fp8_pool(rows, width, seed, device, chunk_rows=1 << 20):
+    """[rows, width] fp8 bytes of N(0,1)/KV_SCALE, drawn in chunks to bound temporaries."""
+    out = torch.empty((rows, width), dtype=torch.uint8, device=device)
+    g = _gen(device, seed)
+    for r0 in range(0, rows, chunk_rows):
+        r1 = min(rows, r0 + chunk_rows)
+        x = torch.randn((r1 - r0, width), generator=g, device=device, dtype=torch.float32)
+        out[r0:r1] = fp8_e4m3fn_bytes(x / KV_SCALE)
+    return out
+
+
+@dataclasses.dataclass
+class MlaInputs:
+    B: int
+    q_len: int
+    H: int
+    d_qk: int
+    d_rope: int
+    d_v: int
+    q_lat: torch.Tensor        # bf16 [B*q_len, H, d_qk - d_rope] (may be a strided view)
+    q_pe: torch.Tensor         # bf16 [B*q_len, H, d_rope] (may be a strided view)
+    pool: torch.Tensor         # uint8 [N, d_qk] fp8 e4m3fn bytes
+    kv_indices: torch.Tensor   # int32 [sum of keys]
+    kv_indptr: torch.Tensor    # int32 [B+1]
+    seq_lens: torch.Tensor     # int32 [B]
+    max_num_keys: int
+    scale: float
+    kv_scale: float = KV_SCALE
+    name: str = ""
+
+    @property
+    def rows(self) -> int:
+        return self.B * self.q_len * self.H
+
+    @property
+    def kv_bytes(self) -> int:
+        """KV payload bytes one decode reads: every key of every request once (576 or 512 B)."""
+        return int(self.seq_lens.sum().item()) * self.d_qk
+
+
+@dataclasses.dataclass
+class GqaInputs:
+    B: int
+    q_len: int
+    Hq: int
+    Hkv: int
+    D: int
+    page_size: int
+    q: torch.Tensor            # bf16 [B*q_len, Hq, D]
+    k_cache: torch.Tensor      # bf16 [num_pages, page_size, Hkv, D]
+    v_cache: torch.Tensor
+    kv_page_indices: torch.Tensor  # int32
+    kv_indptr: torch.Tensor    # int32 [B+1] (pages)
+    seq_lens: torch.Tensor     # int32 [B] (tokens)
+    max_num_keys: int
+    scale: float
+    name: str = ""
+
+    @property
+    def rows(self) -> int:
+        return self.B * self.q_len * self.Hq
+
+    @property
+    def kv_bytes(self) -> int:
+        """K and V bytes one decode reads: per token, per kv head, D bf16 values of each."""
+        return int(self.seq_lens.sum().item()) * self.Hkv * self.D * 2 * 2
+
+
+def mla_inputs(*, B: int, q_len: int, H: int, seq_lens: Sequence[int], pool_rows: Optional[int] = None,
+               d_qk: int = 576, d_rope: int = 64, d_v: int = 512, seed: int = 0,
+               device="cpu", shuffle: bool = True, fused_q: bool = False, name: str = "") -> MlaInputs:
+    """Absorbed-MLA decode inputs; request b owns keys kv_indices[kv_indptr[b]:kv_indptr[b+1]].
+
+    fused_q=True draws one q [B*q_len, H, d_qk] and exposes q_lat / q_pe as views of it (the
+    sparse top-k workload's single 512-wide query)."""
+    lens = [int(x) for x in seq_lens]
+    assert len(lens) == B
+    total = sum(lens)
+    N = pool_rows if pool_rows is not None else max(total, 1)
+    d_lat = d_qk - d_rope
+    if fused_q:
+        q = _randn((B * q_len, H, d_qk), seed + 1, device, torch.bfloat16)
+        q_lat, q_pe = q[..., :d_lat], q[..., d_lat:]
+    else:
+        q_lat = _randn((B * q_len, H, d_lat), seed + 1, device, torch.bfloat16)
+        q_pe = _randn((B * q_len, H, d_rope), seed + 2, device, torch.bfloat16)
+    pool = _fp8_pool(N, d_qk, seed + 3, device)
+    if shuffle:
+        if total <= N:
+            idx = torch.randperm(N, generator=_gen(device, seed + 4), device=device)[:total]
+        else:
+            idx = torch.randint(0, N, (total,), generator=_gen(device, seed + 4), device=device)
+    else:
+        idx = torch.arange(total, device=device) % N
+    kv_indices = idx.to(torch.int32)
+    indptr = [0]
+    for L in lens:
+        indptr.append(indptr[-1] + L)
+    kv_indptr = torch.tensor(indptr, dtype=torch.int32, device=device)
+    sl = torch.tensor(lens, dtype=torch.int32, device=device)
+    return MlaInputs(B=B, q_len=q_len, H=H, d_qk=d_qk, d_rope=d_rope, d_v=d_v, q_lat=q_lat,
+                     q_pe=q_pe, pool=pool, kv_indices=kv_indices, kv_indptr=kv_indptr,
+                     seq_lens=sl, max_num_keys=max(lens) if lens else 0,
+                     scale=float(d_qk) ** -0.5, name=name)
+
+
+def sparse_mla_inputs(*, num_queries: int, topk: int = 2048, cache_rows: int = 262144, H: int = 64,
+                      seed: int = 4000, device="cpu", name: str = "") -> MlaInputs:
+    """Sparse top-k MLA decode: each query is its own request whose keys are `topk` cache rows
+    drawn without replacement; rows are 512 fp8 bytes (448 NoPE + 64 RoPE), value = NoPE part."""
+    nq = num_queries
+    q = _randn((nq, H, 512), seed + 1, device, torch.bfloat16)
+    pool = _fp8_pool(cache_rows, 512, seed + 3, device)
+    g = _gen(device, seed + 4)
+    rows = []
+    for _ in range(nq):
+        rows.append(torch.randperm(cache_rows, generator=g, device=device)[:topk])
+    kv_indices = torch.cat(rows).to(torch.int32) if nq else torch.empty(0, dtype=torch.int32, device=device)
+    kv_indptr = (torch.arange(nq + 1, device=device, dtype=torch.int32) * topk)
+    sl = torch.full((nq,), topk, dtype=torch.int32, device=device)
+    return MlaInputs(B=nq, q_len=1, H=H, d_qk=512, d_rope=64, d_v=448, q_lat=q[..., :448],
+                     q_pe=q[..., 448:], pool=pool, kv_indices=kv_indices, kv_indptr=kv_indptr,
+                     seq_lens=sl, max_num_keys=topk, scale=512.0 ** -0.5, name=name)
+
+
+def gqa_inputs(*, B: int, Hq: int, Hkv: int, D: int = 128, page_size: int = 16,
+               seq_lens: Sequence[int], num_pages: int, q_len: int = 1, seed: int = 3000,
+               device="cpu", name: str = "") -> GqaInputs:
+    lens = [int(x) for x in seq_lens]
+    assert len(lens) == B
+    pages_per = [(L + page_size - 1) // page_size for L in lens]
+    total_pages = sum(pages_per)
+    assert total_pages <= num_pages, (total_pages, num_pages)
+    q = _randn((B * q_len, Hq, D), seed + 1, device, torch.bfloat16)
+    k_cache = _randn((num_pages, page_size, Hkv, D), seed + 3, device, torch.bfloat16)
+    v_cache = _randn((num_pages, page_size, Hkv, D), seed + 7, device, torch.bfloat16)
+    placement = torch.randperm(num_pages, generator=_gen(device, seed + 6), device=device)[:total_pages]
+    indptr = [0]
+    for n in pages_per:
+        indptr.append(indptr[-1] + n)
+    return GqaInputs(B=B, q_len=q_len, Hq=Hq, Hkv=Hkv, D=D, page_size=page_size, q=q,
+                     k_cache=k_cache, v_cache=v_cache,
+                     kv_page_indices=placement.to(torch.int32),
+                     kv_indptr=torch.tensor(indptr, dtype=torch.int32, device=device),
+                     seq_lens=torch.tensor(lens, dtype=torch.int32, device=device),
+                     max_num_keys=max(lens) if lens else 0, scale=float(D) ** -0.5, name=name)
+
+
+def uniform_lengths(B: int, lo: int, hi: int, seed: int) -> list:
+    """B lengths uniform on the integers [lo, hi] (seeded, CPU generator so the draw is the same
+    on every device)."""
+    g = _gen("cpu", seed)
+    return [int(x) for x in torch.randint(lo, hi + 1, (B,), generator=g)]
+
+
+# --------------------------------------------------------------------------------------------
+# The five workloads, at full size
+# --------------------------------------------------------------------------------------------
+
+def mla_tiny(device="cpu"):
+    """B=1, q_len=1, H=16, 4096 shuffled keys (run with np in {1, 4, 16})."""
+    return mla_inputs(B=1, q_len=1, H=16, seq_lens=[4096], pool_rows=4096, seed=0,
+                      device=device, name="mla_tiny_b1_h16_s4096")
+
+
+def mla_b2_s65536(device="cpu"):
+    """H=64, B=2, 65536 keys each, shuffled slots in a 131072-row pool."""
+    return mla_inputs(B=2, q_len=1, H=64, seq_lens=[65536] * 2, pool_rows=131072, seed=1000,
+                      device=device, name="mla_h64_b2_s65536")
+
+
+def mla_long(B: int, q_len: int = 1, device="cpu"):
+    """H=64, B in {8, 16}, 131072 keys each; q_len=4 is the speculative-verify window."""
+    return mla_inputs(B=B, q_len=q_len, H=64, seq_lens=[131072] * B, pool_rows=B * 131072,
+                      seed=2000, device=device, name="mla_h64_b%d_s131072_q%d" % (B, q_len))
+
+
+GQA_LEN_SEED = 3000 + 5
+
+
+def gqa_paged(device="cpu"):
+    """B=32, 64 query heads over 8 kv heads, D=128, page 16, lengths U[1024, 32768], pages
+    placed at random in a pool of 2^21 tokens (131072 pages)."""
+    lens = uniform_lengths(32, 1024, 32768, GQA_LEN_SEED)
+    return gqa_inputs(B=32, Hq=64, Hkv=8, D=128, page_size=16, seq_lens=lens, num_pages=131072,
+                      seed=3000, device=device, name="gqa_b32_hq64_hkv8_d128_p16")
+
+
+SPARSE_QUERY_COUNTS = (24, 32, 34, 64, 128, 256)
+
+
+def sparse_topk(num_queries: int, device="cpu"):
+    return sparse_mla_inputs(num_queries=num_queries, seed=4000, device=device,
+                             name="sparse_mla_h64_topk2048_nq%d" % num_queries)
