@@ -1,0 +1,281 @@
+#!/usr/bin/env python3
+"""Benchmark of split-KV decode on one MI355X.
+
+One step = one decode() call through the C ABI: plan (partition count + tile size, host),
+split kernel, LSE-merge reducer, on one stream, inputs already resident in HBM.
+
+Prints ONE JSON line (rank 0): the headline workload's KV-read GB/s (KV payload bytes of the
+call / wall time per call), the split kernel's roofline against the 8 TB/s HBM peak (HIP events
+on the launch stream), a per-workload table (us/call, GB/s, % of peak for every workload), and
+the CPU oracle timed on a bounded sample of the headline workload (with the sampled parity
+errors of the GPU result against it).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+LOG2E = 1.4426950408889634
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="mla_h64_b16_s131072_q1")
+    ap.add_argument("--headline-only", action="store_true",
+                    help="time only the headline workload (no per-workload table)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target CPU time of the oracle sample")
+    ap.add_argument("--table-steps", type=int, default=20)
+    return ap.parse_args()
+
+
+def make_workloads():
+    import workloads as w
+    items = [
+        ("mla_tiny_b1_h16_s4096_np1", lambda d: w.mla_tiny(d), 1),
+        ("mla_tiny_b1_h16_s4096_np4", lambda d: w.mla_tiny(d), 4),
+        ("mla_tiny_b1_h16_s4096_np16", lambda d: w.mla_tiny(d), 16),
+        ("mla_h64_b2_s65536", lambda d: w.mla_b2_s65536(d), 0),
+        ("mla_h64_b8_s131072_q1", lambda d: w.mla_long(8, 1, d), 0),
+        ("mla_h64_b16_s131072_q1", lambda d: w.mla_long(16, 1, d), 0),
+        ("mla_h64_b8_s131072_q4", lambda d: w.mla_long(8, 4, d), 0),
+        ("mla_h64_b16_s131072_q4", lambda d: w.mla_long(16, 4, d), 0),
+        ("gqa_b32_hq64_hkv8_d128_p16", lambda d: w.gqa_paged(d), 0),
+    ]
+    for nq in w.SPARSE_QUERY_COUNTS:
+        items.append(("sparse_mla_h64_topk2048_nq%d" % nq, (lambda n: lambda d: w.sparse_topk(n, d))(nq), 0))
+    return items
+
+
+class Case:
+    """One workload bound to the C ABI: problem, output and workspace buffers."""
+
+    def __init__(self, inp, np_fixed, stream):
+        import torch
+        import gqa_plan_splits_amd as g
+        self.g = g
+        self.inp = inp
+        self.is_mla = hasattr(inp, "pool")
+        if self.is_mla:
+            self.p = g.mla_problem(inp.q_lat, inp.q_pe, inp.pool, inp.kv_indices, inp.kv_indptr,
+                                   inp.seq_lens, batch=inp.B, q_len=inp.q_len, num_heads=inp.H,
+                                   max_num_keys=inp.max_num_keys, scale=inp.scale,
+                                   kv_scale=inp.kv_scale, d_v=inp.d_v)
+            self.d_v = inp.d_v
+        else:
+            self.p = g.gqa_problem(inp.q, inp.k_cache, inp.v_cache, inp.kv_page_indices,
+                                   inp.kv_indptr, inp.seq_lens, batch=inp.B, q_len=inp.q_len,
+                                   max_num_keys=inp.max_num_keys, scale=inp.scale)
+            self.d_v = inp.D
+        self.np_arg = np_fixed
+        self.np, self.bk = g.decode_plan(self.p, np_fixed, 0)
+        rows = self.p.rows
+        dev = torch.device("cuda")
+        self.out = torch.empty((rows, self.d_v), dtype=torch.bfloat16, device=dev)
+        self.lse = torch.empty((rows,), dtype=torch.float32, device=dev)
+        ws = g.decode_workspace_bytes(self.p, self.np)
+        self.ws = torch.empty((max(ws, 256) // 4 + 64,), dtype=torch.float32, device=dev)
+        self.po = torch.empty((rows, self.np, self.d_v), dtype=torch.float32, device=dev)
+        self.pl = torch.empty((rows, self.np), dtype=torch.float32, device=dev)
+        self.stream = stream
+        self.rows = rows
+
+    def step(self):
+        # the whole hot path: plan (np=0 / block_k=0 -> planner and tile rule) + split + reduce
+        self.g.decode(self.p, self.out, self.lse, np=self.np_arg, block_k=0, workspace=self.ws,
+                      stream=self.stream)
+
+    def split_only(self):
+        self.g.decode_split(self.p, self.np, self.bk, self.po, self.pl, stream=self.stream)
+
+    def reduce_only(self):
+        self.g.splitk_reduce(self.rows, self.np, self.d_v, self.po, self.pl, self.out, self.lse,
+                             stream=self.stream)
+
+    def kv_bytes(self):
+        return self.inp.kv_bytes
+
+    def split_algorithmic_bytes(self):
+        """Compulsory HBM bytes of one split launch: each key's payload and index once, Q once,
+        the fp32 partial outputs and LSEs written once (np == 1 writes bf16 output directly)."""
+        inp = self.inp
+        keys = int(inp.seq_lens.sum().item())
+        if self.is_mla:
+            q_bytes = self.rows * inp.d_qk * 2
+            idx = keys * 4
+        else:
+            q_bytes = self.rows * inp.D * 2
+            idx = sum((int(x) + inp.page_size - 1) // inp.page_size for x in inp.seq_lens.tolist()) * 4
+        if self.np == 1:
+            writes = self.rows * (self.d_v * 2 + 4)
+        else:
+            writes = self.rows * self.np * (self.d_v + 1) * 4
+        return self.kv_bytes() + idx + q_bytes + writes
+
+
+def time_events(fn, n, stream):
+    """Average ms per call of fn over n calls, HIP events recorded on `stream`."""
+    import torch
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(n):
+        fn()
+    end.record(stream)
+    end.synchronize()
+    return start.elapsed_time(end) / n
+
+
+def cpu_baseline(case, target_s):
+    """The oracle as it stands, on a bounded sample of rows of the headline workload, with the
+    sampled parity of the GPU output against it."""
+    import numpy as np
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    import oracle
+    from gpu_util import compare, oracle_gqa, oracle_mla, sample_rows
+
+    inp = case.inp
+    H = inp.H if case.is_mla else inp.Hq
+    total_rows = case.rows
+    cores = oracle.default_threads()
+    n = max(cores, 8)
+    t_used = 0.0
+    while True:
+        rows = sample_rows(inp.B, inp.q_len, H, n, seed=n)
+        t0 = time.perf_counter()
+        ref_o, ref_l = (oracle_mla if case.is_mla else oracle_gqa)(inp, rows, n_threads=cores)
+        dt = time.perf_counter() - t0
+        t_used += dt
+        if dt * 2.2 > target_s or n * 2 > total_rows or t_used > 2 * target_s:
+            break
+        n *= 2
+    max_abs, rel, lse_err = compare(case.out[rows], case.lse[rows], ref_o, ref_l, "bench parity")
+    full_s = dt * total_rows / len(rows)
+    return {
+        "value": round(case.kv_bytes() / full_s / 1e9, 4),
+        "unit": "GB/s",
+        "cores": cores,
+        "kind": "oracle",
+        "sample": "%d of %d output rows of %s (fp64 unsplit attention, %d threads, %.2f s); "
+                  "value = KV bytes / (sample time x rows / sampled rows)"
+                  % (len(rows), total_rows, inp.name, cores, dt),
+        "cpu_model": platform.processor() or platform.machine(),
+        "parity": {"max_abs": max_abs, "rel": rel, "lse2_rel": lse_err, "rows": len(rows)},
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import gqa_plan_splits_amd as g
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    torch.cuda.set_device(0)
+    stream = torch.cuda.Stream()
+    sm = g.device_sm_count()
+
+    table = {}
+    headline = None
+    for name, make, np_fixed in make_workloads():
+        if args.headline_only and name != args.workload:
+            continue
+        with torch.cuda.stream(stream):
+            inp = make("cuda")
+        torch.cuda.synchronize()
+        case = Case(inp, np_fixed, stream)
+        is_head = name == args.workload
+        steps = args.steps if is_head else args.table_steps
+        warm = args.warmup if is_head else max(3, args.warmup // 2)
+        for _ in range(warm):
+            case.step()
+        torch.cuda.synchronize()
+        ms = time_events(case.step, steps, stream)
+        ms_split = time_events(case.split_only, steps, stream)
+        ms_red = time_events(case.reduce_only, steps, stream) if case.np > 1 else 0.0
+        case.step()
+        torch.cuda.synchronize()
+        entry = {
+            "us_per_call": round(ms * 1e3, 2),
+            "kv_gbs": round(case.kv_bytes() / (ms * 1e-3) / 1e9, 1),
+            "pct_hbm_peak": round(100 * case.kv_bytes() / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 1),
+            "split_us": round(ms_split * 1e3, 2),
+            "reduce_us": round(ms_red * 1e3, 2),
+            "np": case.np, "block_k": case.bk, "kv_bytes": case.kv_bytes(),
+        }
+        table[name] = entry
+        print("# %-36s %s" % (name, json.dumps(entry)), file=sys.stderr, flush=True)
+        if is_head:
+            headline = (case, ms, ms_split, steps)
+        else:
+            del case, inp
+            torch.cuda.empty_cache()
+
+    if headline is None:
+        print("unknown workload %s" % args.workload, file=sys.stderr)
+        sys.exit(2)
+    case, ms, ms_split, steps = headline
+    alg = case.split_algorithmic_bytes()
+    achieved = alg / (ms_split * 1e-3) / 1e9
+    inp = case.inp
+    result = {
+        "metric": "split-KV decode KV-read GB/s (% of HBM peak) and us/call per config",
+        "value": round(case.kv_bytes() / (ms * 1e-3) / 1e9, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16 queries, fp8 e4m3fn KV = N(0,1)*32, shuffled slots)",
+        "config": {
+            "workload": args.workload,
+            "batch": inp.B, "q_len": inp.q_len,
+            "heads": inp.H if case.is_mla else inp.Hq,
+            "seq_len": int(inp.max_num_keys),
+            "kv_dtype": "fp8_e4m3fn" if case.is_mla else "bf16",
+            "np": case.np, "block_k": case.bk, "sm_count": sm,
+            "us_per_call": round(ms * 1e3, 2),
+            "pct_hbm_peak": round(100 * case.kv_bytes() / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
+            "parallelism": "single GPU",
+        },
+        "roofline": {
+            "kernel": "mla_split_kernel" if case.is_mla else "gqa_split_kernel",
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "algorithmic_bytes": alg,
+            "avg_launch_us": round(ms_split * 1e3, 2),
+        },
+        "per_config": table,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,31 @@
+"""Split-KV attention decode for MI355X (gfx950): Python binding of the C ABI.
+
+Every entry point of ``include/gqa_splits.h`` has a function of the same name here; this module
+only marshals arguments (device pointers, sizes, the current HIP stream) and raises
+:class:`GqaError` on a non-zero status.  All arithmetic runs in the HIP kernels of
+``libgqa_splits.so``; if that library has not been built, importing the binding raises.
+"""
+from __future__ import annotations
+
+from ._lib import (  # noqa: F401
+    DecodeProblem,
+    GqaError,
+    KIND_GQA_PAGED,
+    KIND_MLA_FUSED,
+    FP8_E4M3FN,
+    FP8_E4M3FNUZ,
+    block_k_for,
+    decode,
+    decode_plan,
+    decode_split,
+    decode_workspace_bytes,
+    device_sm_count,
+    exported_symbols,
+    fp8_e4m3_to_bf16,
+    gqa_problem,
+    library_path,
+    mla_problem,
+    plan_splits,
+    splitk_reduce,
+    status_string,
+)

@@ -1,0 +1,282 @@
+// api.cpp -- the C ABI declared in include/gqa_splits.h: argument checks, planning glue and
+// kernel dispatch.  Every check runs on the host before anything is enqueued.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "../../include/gqa_splits.h"
+#include "kernels.hpp"
+
+namespace {
+
+constexpr int kMaxPartitions = 256;
+constexpr int kMlaRowsPerCta = 32;
+constexpr int kGqaHeadDim = 128;
+constexpr int kGqaMaxRowsPerCta = 16;
+constexpr float kLog2e = 1.4426950408889634f;
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
+int ilog2(int64_t x) {
+    int r = 0;
+    while ((int64_t(1) << r) < x) ++r;
+    return r;
+}
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+struct Derived {
+    int64_t rows;           // B * q_len * H
+    int64_t rows_per_req;   // q_len * H
+    int64_t cta_rows;       // MLA: 32-row blocks per request; GQA: kv heads
+    int64_t hpg;            // heads_per_group the planner sees
+    bool is_mla;
+};
+
+int check_problem(const gqa_decode_problem *p, Derived *d) {
+    if (!p) return GQA_ERR_INVALID_ARGUMENT;
+    if (p->batch < 1 || p->q_len < 1 || p->num_heads < 1 || p->max_num_keys < 0)
+        return GQA_ERR_INVALID_ARGUMENT;
+    if (!p->q || !p->kv_indices || !p->kv_indptr || !p->seq_lens) return GQA_ERR_INVALID_ARGUMENT;
+    if (!(p->scale > 0.f) || !std::isfinite(p->scale)) return GQA_ERR_INVALID_ARGUMENT;
+    if (p->num_heads > 128) return GQA_ERR_UNSUPPORTED;
+    const int64_t rows_per_req = p->q_len * p->num_heads;
+    const int64_t rows = p->batch * rows_per_req;
+    if (rows_per_req > (int64_t(1) << 20) || rows > (int64_t(1) << 30)) return GQA_ERR_UNSUPPORTED;
+    if (p->q_stride_tok % 8 || p->q_stride_head % 8 || !aligned16(p->q)) return GQA_ERR_UNSUPPORTED;
+
+    if (p->kind == GQA_KIND_MLA_FUSED) {
+        if (p->fp8_format != GQA_FP8_E4M3FN && p->fp8_format != GQA_FP8_E4M3FNUZ)
+            return GQA_ERR_INVALID_ARGUMENT;
+        if (!p->kv || !p->q_pe || p->num_kv_heads != 1) return GQA_ERR_INVALID_ARGUMENT;
+        if (!(p->kv_scale > 0.f) || !std::isfinite(p->kv_scale)) return GQA_ERR_INVALID_ARGUMENT;
+        // gfx950 converts OCP e4m3fn natively; the fnuz encoding has no kernel in this build.
+        if (p->fp8_format == GQA_FP8_E4M3FNUZ) return GQA_ERR_UNSUPPORTED;
+        const bool wide = p->d_qk == 576 && p->d_rope == 64 && p->d_v == 512;
+        const bool sparse = p->d_qk == 512 && p->d_rope == 64 && p->d_v == 448;
+        if (!wide && !sparse) return GQA_ERR_UNSUPPORTED;
+        if (p->page_size != 1) return GQA_ERR_UNSUPPORTED;
+        if (p->kv_stride_row < p->d_qk || p->kv_stride_row % 16 || !aligned16(p->kv))
+            return GQA_ERR_UNSUPPORTED;
+        if (p->q_pe_stride_tok % 8 || p->q_pe_stride_head % 8 || !aligned16(p->q_pe))
+            return GQA_ERR_UNSUPPORTED;
+        d->is_mla = true;
+        d->cta_rows = (rows_per_req + kMlaRowsPerCta - 1) / kMlaRowsPerCta;
+        d->hpg = rows_per_req;
+    } else if (p->kind == GQA_KIND_GQA_PAGED) {
+        if (!p->k_cache || !p->v_cache || p->num_kv_heads < 1) return GQA_ERR_INVALID_ARGUMENT;
+        if (p->num_heads % p->num_kv_heads) return GQA_ERR_INVALID_ARGUMENT;
+        if (p->d_qk != kGqaHeadDim || p->d_v != kGqaHeadDim || p->d_rope != 0)
+            return GQA_ERR_UNSUPPORTED;
+        if (!pow2(p->page_size) || p->page_size < 8 || p->page_size > (int64_t(1) << 20))
+            return GQA_ERR_UNSUPPORTED;
+        if (p->q_len * (p->num_heads / p->num_kv_heads) > kGqaMaxRowsPerCta) return GQA_ERR_UNSUPPORTED;
+        if (!aligned16(p->k_cache) || !aligned16(p->v_cache)) return GQA_ERR_UNSUPPORTED;
+        d->is_mla = false;
+        d->cta_rows = p->num_kv_heads;
+        d->hpg = p->num_kv_heads;
+    } else {
+        return GQA_ERR_INVALID_ARGUMENT;
+    }
+    d->rows = rows;
+    d->rows_per_req = rows_per_req;
+    return GQA_OK;
+}
+
+int resolve_plan(const gqa_decode_problem *p, const Derived &d, int64_t np_or_0, int bk_or_0,
+                 int64_t sm, int64_t *np_out, int *bk_out) {
+    if (np_or_0 < 0 || np_or_0 > kMaxPartitions) return GQA_ERR_UNSUPPORTED;
+    if (bk_or_0 != 0 && bk_or_0 != 32 && bk_or_0 != 64) return GQA_ERR_UNSUPPORTED;
+    if ((np_or_0 == 0 || bk_or_0 == 0) && sm <= 0) {
+        const int rc = device_sm_count(&sm);
+        if (rc != GQA_OK) return rc;
+    }
+    int64_t np = np_or_0;
+    if (np == 0) {
+        const int rc = plan_splits(p->batch, p->max_num_keys, d.hpg, sm, d.is_mla ? 1 : 0, &np);
+        if (rc != GQA_OK) return rc;
+    }
+    int bk = bk_or_0;
+    if (bk == 0) {
+        bk = block_k_for(p->batch * np * d.cta_rows, sm);
+        if (bk < 0) return bk;
+    }
+    *np_out = np;
+    *bk_out = bk;
+    return GQA_OK;
+}
+
+int launch_split(const gqa_decode_problem *p, const Derived &d, int64_t np, int bk,
+                 float *part_o, float *part_lse2, void *out, float *lse2_out, hipStream_t s) {
+    const int64_t total = p->batch * np * d.cta_rows;
+    if (total > (int64_t(1) << 30)) return GQA_ERR_UNSUPPORTED;
+    const bool direct = out != nullptr;
+    hipError_t err;
+    if (d.is_mla) {
+        gqa::MlaSplitArgs a;
+        a.q = static_cast<const uint16_t *>(p->q);
+        a.q_st_tok = p->q_stride_tok;
+        a.q_st_head = p->q_stride_head;
+        a.q_pe = static_cast<const uint16_t *>(p->q_pe);
+        a.qpe_st_tok = p->q_pe_stride_tok;
+        a.qpe_st_head = p->q_pe_stride_head;
+        a.kv = static_cast<const uint8_t *>(p->kv);
+        a.kv_stride = p->kv_stride_row;
+        a.kv_indices = p->kv_indices;
+        a.kv_indptr = p->kv_indptr;
+        a.seq_lens = p->seq_lens;
+        a.q_len = int32_t(p->q_len);
+        a.H = int32_t(p->num_heads);
+        a.np = int32_t(np);
+        a.rows_per_req = int32_t(d.rows_per_req);
+        a.row_blocks = int32_t(d.cta_rows);
+        a.total_ctas = int32_t(total);
+        a.score_scale = p->scale * p->kv_scale * kLog2e;
+        a.out_scale = p->kv_scale;
+        a.part_o = part_o;
+        a.part_lse2 = part_lse2;
+        a.out = static_cast<uint16_t *>(out);
+        a.lse2_out = lse2_out;
+        err = gqa::launch_mla_split(a, bk, int(p->d_qk), int(p->d_v), direct, s);
+    } else {
+        gqa::GqaSplitArgs a;
+        a.q = static_cast<const uint16_t *>(p->q);
+        a.q_st_tok = p->q_stride_tok;
+        a.q_st_head = p->q_stride_head;
+        a.k_cache = static_cast<const uint16_t *>(p->k_cache);
+        a.v_cache = static_cast<const uint16_t *>(p->v_cache);
+        a.page_indices = p->kv_indices;
+        a.kv_indptr = p->kv_indptr;
+        a.seq_lens = p->seq_lens;
+        a.q_len = int32_t(p->q_len);
+        a.Hq = int32_t(p->num_heads);
+        a.Hkv = int32_t(p->num_kv_heads);
+        a.group = int32_t(p->num_heads / p->num_kv_heads);
+        a.page_shift = ilog2(p->page_size);
+        a.np = int32_t(np);
+        a.total_ctas = int32_t(total);
+        a.score_scale = p->scale * kLog2e;
+        a.part_o = part_o;
+        a.part_lse2 = part_lse2;
+        a.out = static_cast<uint16_t *>(out);
+        a.lse2_out = lse2_out;
+        err = gqa::launch_gqa_split(a, bk, int(p->q_len * a.group), direct, s);
+    }
+    return err == hipSuccess ? GQA_OK : GQA_ERR_LAUNCH_FAILED;
+}
+
+int partial_bytes(const Derived &d, int64_t np, int64_t dv, size_t *o_bytes, size_t *l_bytes) {
+    *o_bytes = align256(size_t(d.rows) * size_t(np) * size_t(dv) * sizeof(float));
+    *l_bytes = align256(size_t(d.rows) * size_t(np) * sizeof(float));
+    return GQA_OK;
+}
+
+}  // namespace
+
+extern "C" int decode_plan(const gqa_decode_problem *p, int64_t np_or_0, int block_k_or_0,
+                           int64_t sm_count, int64_t *np_out, int *block_k_out) {
+    if (!np_out || !block_k_out) return GQA_ERR_INVALID_ARGUMENT;
+    Derived d;
+    int rc = check_problem(p, &d);
+    if (rc != GQA_OK) return rc;
+    return resolve_plan(p, d, np_or_0, block_k_or_0, sm_count, np_out, block_k_out);
+}
+
+extern "C" int decode_split(const gqa_decode_problem *p, int64_t np, int block_k,
+                            float *partial_o, float *partial_lse2, gqa_stream_t s) {
+    Derived d;
+    int rc = check_problem(p, &d);
+    if (rc != GQA_OK) return rc;
+    if (!partial_o || !partial_lse2) return GQA_ERR_INVALID_ARGUMENT;
+    if (np < 1 || np > kMaxPartitions || (block_k != 32 && block_k != 64)) return GQA_ERR_UNSUPPORTED;
+    return launch_split(p, d, np, block_k, partial_o, partial_lse2, nullptr, nullptr,
+                        reinterpret_cast<hipStream_t>(s));
+}
+
+extern "C" int splitk_reduce(int64_t rows, int64_t np, int64_t d_v, const float *partial_o,
+                             const float *partial_lse2, void *out, float *lse2_out,
+                             gqa_stream_t s) {
+    if (rows < 0 || !partial_o || !partial_lse2 || !out) return GQA_ERR_INVALID_ARGUMENT;
+    if (np < 1 || np > kMaxPartitions || d_v < 4 || d_v > 1024 || d_v % 4) return GQA_ERR_UNSUPPORTED;
+    if (rows > (int64_t(1) << 30)) return GQA_ERR_UNSUPPORTED;
+    if (rows == 0) return GQA_OK;
+    gqa::ReduceArgs a;
+    a.part_o = partial_o;
+    a.part_lse2 = partial_lse2;
+    a.out = static_cast<uint16_t *>(out);
+    a.lse2_out = lse2_out;
+    a.rows = rows;
+    a.np = int32_t(np);
+    a.dv = int32_t(d_v);
+    return gqa::launch_splitk_reduce(a, reinterpret_cast<hipStream_t>(s)) == hipSuccess
+               ? GQA_OK
+               : GQA_ERR_LAUNCH_FAILED;
+}
+
+extern "C" int decode_workspace_bytes(const gqa_decode_problem *p, int64_t np, size_t *bytes) {
+    if (!bytes) return GQA_ERR_INVALID_ARGUMENT;
+    Derived d;
+    int rc = check_problem(p, &d);
+    if (rc != GQA_OK) return rc;
+    if (np == 0) {
+        int bk;
+        rc = resolve_plan(p, d, 0, 64, 0, &np, &bk);
+        if (rc != GQA_OK) return rc;
+    }
+    if (np < 1 || np > kMaxPartitions) return GQA_ERR_UNSUPPORTED;
+    if (np == 1) {
+        *bytes = 0;
+        return GQA_OK;
+    }
+    size_t ob, lb;
+    partial_bytes(d, np, p->d_v, &ob, &lb);
+    *bytes = ob + lb;
+    return GQA_OK;
+}
+
+extern "C" int decode(const gqa_decode_problem *p, int64_t np_or_0, int block_k_or_0,
+                      void *workspace, size_t ws_bytes, void *out, float *lse2_out,
+                      gqa_stream_t s) {
+    Derived d;
+    int rc = check_problem(p, &d);
+    if (rc != GQA_OK) return rc;
+    if (!out) return GQA_ERR_INVALID_ARGUMENT;
+    int64_t np;
+    int bk;
+    rc = resolve_plan(p, d, np_or_0, block_k_or_0, 0, &np, &bk);
+    if (rc != GQA_OK) return rc;
+    const hipStream_t st = reinterpret_cast<hipStream_t>(s);
+    if (np == 1) return launch_split(p, d, 1, bk, nullptr, nullptr, out, lse2_out, st);
+    size_t ob, lb;
+    partial_bytes(d, np, p->d_v, &ob, &lb);
+    if (!workspace) return GQA_ERR_INVALID_ARGUMENT;
+    if (ws_bytes < ob + lb) return GQA_ERR_WORKSPACE_TOO_SMALL;
+    if (reinterpret_cast<uintptr_t>(workspace) & 255u) return GQA_ERR_INVALID_ARGUMENT;
+    float *part_o = static_cast<float *>(workspace);
+    float *part_l = reinterpret_cast<float *>(static_cast<char *>(workspace) + ob);
+    rc = launch_split(p, d, np, bk, part_o, part_l, nullptr, nullptr, st);
+    if (rc != GQA_OK) return rc;
+    return splitk_reduce(d.rows, np, p->d_v, part_o, part_l, out, lse2_out, s);
+}
+
+extern "C" int fp8_e4m3_to_bf16(const void *in, int64_t n, void *out, gqa_stream_t s) {
+    if (!in || !out || n < 0) return GQA_ERR_INVALID_ARGUMENT;
+    if (!aligned16(in) || !aligned16(out)) return GQA_ERR_UNSUPPORTED;
+    if (n == 0) return GQA_OK;
+    return gqa::launch_fp8_to_bf16(static_cast<const uint8_t *>(in), n, static_cast<uint16_t *>(out),
+                                   reinterpret_cast<hipStream_t>(s)) == hipSuccess
+               ? GQA_OK
+               : GQA_ERR_LAUNCH_FAILED;
+}
+
+extern "C" const char *status_string(int status) {
+    switch (status) {
+        case GQA_OK: return "ok";
+        case GQA_ERR_INVALID_ARGUMENT: return "invalid argument";
+        case GQA_ERR_UNSUPPORTED: return "unsupported problem for this build";
+        case GQA_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+        case GQA_ERR_LAUNCH_FAILED: return "kernel launch failed";
+        case GQA_ERR_DEVICE: return "no usable HIP device";
+        default: return "unknown status";
+    }
+}

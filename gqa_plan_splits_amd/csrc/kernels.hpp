@@ -1,0 +1,58 @@
+// kernels.hpp -- internal interface between the C-ABI host code and the gfx950 kernels.
+// Not installed; the public interface is include/gqa_splits.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace gqa {
+
+// Absorbed-MLA split kernel (fused fp8 rows: K = the whole row, V = its first DV bytes).
+struct MlaSplitArgs {
+    const uint16_t *q;            // bf16 [tokens, H, DQK - 64], element strides below
+    int64_t q_st_tok, q_st_head;
+    const uint16_t *q_pe;         // bf16 [tokens, H, 64]
+    int64_t qpe_st_tok, qpe_st_head;
+    const uint8_t *kv;            // fp8 rows
+    int64_t kv_stride;            // bytes between rows
+    const int32_t *kv_indices, *kv_indptr, *seq_lens;
+    int32_t q_len, H, np, rows_per_req, row_blocks, total_ctas;
+    float score_scale;            // scale * kv_scale * log2(e): scores in base-2 units
+    float out_scale;              // kv_scale: the raw fp8 values are accumulated unscaled
+    float *part_o;                // [rows, np, DV]
+    float *part_lse2;             // [rows, np]
+    uint16_t *out;                // bf16 [rows, DV] when np == 1 (direct mode)
+    float *lse2_out;              // [rows] in direct mode (may be null)
+};
+
+// Grouped-query split kernel over bf16 K/V pages (head dim 128).
+struct GqaSplitArgs {
+    const uint16_t *q;            // bf16 [tokens, Hq, 128]
+    int64_t q_st_tok, q_st_head;
+    const uint16_t *k_cache, *v_cache;  // bf16 [pages, page_size, Hkv, 128]
+    const int32_t *page_indices, *kv_indptr, *seq_lens;
+    int32_t q_len, Hq, Hkv, group, page_shift, np, total_ctas;
+    float score_scale;            // scale * log2(e)
+    float *part_o, *part_lse2;
+    uint16_t *out;
+    float *lse2_out;
+};
+
+struct ReduceArgs {
+    const float *part_o, *part_lse2;
+    uint16_t *out;
+    float *lse2_out;
+    int64_t rows;
+    int32_t np, dv;
+};
+
+// Launchers: return hipSuccess or the launch error.  All enqueue on `s` only.
+hipError_t launch_mla_split(const MlaSplitArgs &a, int block_k, int d_qk, int d_v, bool direct,
+                            hipStream_t s);
+hipError_t launch_gqa_split(const GqaSplitArgs &a, int block_k, int rows_per_cta, bool direct,
+                            hipStream_t s);
+hipError_t launch_splitk_reduce(const ReduceArgs &a, hipStream_t s);
+hipError_t launch_fp8_to_bf16(const uint8_t *in, int64_t n, uint16_t *out, hipStream_t s);
+
+}  // namespace gqa

@@ -1,0 +1,204 @@
+/*
+ * gqa_splits.h -- C ABI of the gfx950 split-KV ("flash-decoding") attention decode library.
+ *
+ * The library computes attention decode over a paged KV cache in three steps:
+ *
+ *   1. plan     -- a wave-aligned partition count (plan_splits) and a tile size (block_k_for);
+ *   2. split    -- one partial output and one base-2 log-sum-exp per (row, partition)
+ *                  (decode_split);
+ *   3. reduce   -- the fp32 base-2 LSE merge of up to 256 partitions (splitk_reduce).
+ *
+ * decode() runs the three in order on one stream.
+ *
+ * Sources (pages cited by title and section):
+ *   [MAX]   Modular MAX API page "hip_mha_decoding_num_partitions": the planner (regime bullets,
+ *           EXCEPTION paragraph, Phase 0 sweep, AMD reducer constraint, Tunables, Args).
+ *   [AITER] AITER issue "[Perf] pa_decode_sparse: BLOCK_K=64 is suboptimal above the CU count":
+ *           the CTA-keyed tile rule ("Why it is not monotonic in num_queries") and the sparse
+ *           top-k workload ("Measurements").
+ *   [MM]    moonmath-amd README: absorbed MLA decode ("MLA decode" usage and constraints: fused
+ *           fp8 rows that are both K and V, one per-tensor kv_scale, page_size 1 slot lists,
+ *           kv_indptr / seq_lens, the end-aligned draft window, in-place outputs on the caller's
+ *           stream, the base-2 LSE), paged K/V for head dim 128 (gfx950 "forward_paged":
+ *           caches [pages, page_size, kv_heads, D], kv_indptr counting pages, kv_page_indices),
+ *           gfx950 bf16 output rounding (RTNE), a row that sees no key is 0.
+ *
+ * Conventions (all entry points):
+ *   - Row numbering: row r = (b * q_len + t) * H + h for request b, draft position t, query
+ *     head h.  Row (b, t, h) attends keys 0 .. seq_lens[b] - q_len + t of request b [MM].
+ *   - Ownership: the caller owns every buffer.  The library never allocates device memory;
+ *     decode() takes its scratch space as a caller-provided workspace.  Outputs are written in
+ *     place.  The only state is the CU count of each device, cached on first query.
+ *   - Streams: every kernel is enqueued on the caller's stream `s` (a hipStream_t; NULL is the
+ *     null stream).  No entry point synchronises the host with the device, so every call can be
+ *     captured into a HIP graph.
+ *   - Errors: functions return GQA_OK (0) or a negative gqa_status.  Arguments are checked on
+ *     the host before anything is enqueued; nothing is enqueued on error.  GQA_ERR_LAUNCH_FAILED
+ *     reports a launch error from the HIP runtime.  No C++ exception crosses this interface.
+ *   - Device data is not checked (that would need a device sync).  The caller guarantees:
+ *     every index is in range; seq_lens[b] <= keys addressable from kv_indptr (tokens for MLA,
+ *     pages * page_size for paged GQA); inputs hold no NaN or Inf.
+ */
+#ifndef GQA_SPLITS_H
+#define GQA_SPLITS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Same type as hipStream_t. */
+typedef struct ihipStream_t *gqa_stream_t;
+
+typedef enum gqa_status {
+    GQA_OK = 0,
+    GQA_ERR_INVALID_ARGUMENT = -1,   /* null pointer, non-positive size, inconsistent sizes */
+    GQA_ERR_UNSUPPORTED = -2,        /* a valid problem this build has no kernel for */
+    GQA_ERR_WORKSPACE_TOO_SMALL = -3,
+    GQA_ERR_LAUNCH_FAILED = -4,      /* the HIP runtime refused a launch */
+    GQA_ERR_DEVICE = -5              /* no usable HIP device / device query failed */
+} gqa_status;
+
+typedef enum gqa_kind {
+    /* Absorbed MLA [MM]: one fused fp8 row per token, K = the whole row, V = its first d_v
+     * bytes; page_size 1.  Sparse top-k decode [AITER] is this kind with one request per query
+     * whose kv_indices row holds that query's top-k slots. */
+    GQA_KIND_MLA_FUSED = 0,
+    /* Grouped-query / multi-head decode over bf16 K and V pages [MM, forward_paged]. */
+    GQA_KIND_GQA_PAGED = 1
+} gqa_kind;
+
+typedef enum gqa_fp8_format {
+    GQA_FP8_E4M3FN = 0,    /* OCP e4m3fn: gfx950's native fp8 */
+    GQA_FP8_E4M3FNUZ = 1   /* e4m3fnuz (the gfx942 encoding used by [MM]) */
+} gqa_fp8_format;
+
+typedef struct gqa_decode_problem {
+    int32_t kind;          /* gqa_kind */
+    int32_t fp8_format;    /* gqa_fp8_format (MLA only) */
+
+    int64_t batch;         /* B: requests, >= 1 */
+    int64_t q_len;         /* queries per request, >= 1 (1: decode; > 1: draft window) */
+    int64_t num_heads;     /* H: query heads, 1..128 */
+    int64_t num_kv_heads;  /* GQA: kv heads (num_heads % num_kv_heads == 0); MLA: 1 */
+    int64_t d_qk;          /* MLA: 576 (512 latent + 64 rope) or 512 (448 + 64); GQA: 128 */
+    int64_t d_rope;        /* MLA: 64; GQA: 0 */
+    int64_t d_v;           /* MLA: 512 (for d_qk 576) or 448 (for d_qk 512); GQA: 128 */
+    int64_t page_size;     /* MLA: 1; GQA: a power of two >= 8 */
+    int64_t max_num_keys;  /* host-known max(seq_lens): the planner's num_keys [MAX, Args] */
+
+    /* Queries, bf16.  q: [B*q_len, H, d_qk - d_rope]; q_pe: [B*q_len, H, d_rope] (NULL when
+     * d_rope == 0).  Strides are in elements; the last dimension is contiguous.  Pointers
+     * 16-byte aligned, strides multiples of 8. */
+    const void *q;
+    int64_t q_stride_tok, q_stride_head;
+    const void *q_pe;
+    int64_t q_pe_stride_tok, q_pe_stride_head;
+
+    /* MLA pool: fp8 bytes [N, d_qk]; row stride kv_stride_row bytes (a multiple of 16,
+     * >= d_qk; pointer 16-byte aligned). */
+    const void *kv;
+    int64_t kv_stride_row;
+
+    /* GQA caches: bf16 [num_pages, page_size, num_kv_heads, d_qk], contiguous. */
+    const void *k_cache;
+    const void *v_cache;
+
+    /* MLA: kv_indices[kv_indptr[b] + j] is the pool row of key j of request b.
+     * GQA: kv_indices[kv_indptr[b] + j / page_size] is the page of token j of request b.
+     * kv_indptr: int32 [B + 1]; seq_lens: int32 [B] keys (tokens) per request. */
+    const int32_t *kv_indices;
+    const int32_t *kv_indptr;
+    const int32_t *seq_lens;
+
+    float scale;           /* softmax scale applied to q . k */
+    float kv_scale;        /* MLA: per-tensor dequantization scale of the fp8 pool; GQA: 1 */
+} gqa_decode_problem;
+
+/* ---------------------------------------------------------------------------------------- */
+/* Planning [MAX], [AITER]                                                                  */
+/* ---------------------------------------------------------------------------------------- */
+
+/* Partition count of the wave-aligned planner [MAX]:
+ *   batch_size      requests in the batch (>= 1)
+ *   num_keys        keys to scan (>= 0)
+ *   heads_per_group not a group size: the kv-head count for MHA-style callers, the number of
+ *                   query rows packed per request for MLA callers (>= 1)
+ *   sm_count        CUs used to size the waves; <= 0 queries the current HIP device (cached)
+ *   is_mla          non-zero for the MLA caller
+ * Writes the count (1..256) to *np_out.  Pure host integer arithmetic when sm_count > 0.
+ * Errors: INVALID_ARGUMENT (np_out NULL, batch_size/heads_per_group < 1, num_keys < 0),
+ * DEVICE (sm_count <= 0 and no device). */
+int plan_splits(int64_t batch_size, int64_t num_keys, int64_t heads_per_group, int64_t sm_count,
+                int is_mla, int64_t *np_out);
+
+/* Tile size in keys [AITER]: 32 when the launch has more CTAs than the device has CUs,
+ * else 64.  Returns 32 or 64, or GQA_ERR_INVALID_ARGUMENT when ctas < 1 or sm_count < 1. */
+int block_k_for(int64_t ctas, int64_t sm_count);
+
+/* CU count of the current HIP device, cached per device after the first query. */
+int device_sm_count(int64_t *sm_out);
+
+/* What decode() would launch: the partition count (np_or_0, or the planner's choice when 0)
+ * and the tile size (block_k_or_0, or the tile rule's choice when 0), for the device with
+ * sm_count CUs (<= 0: the current device).  The planner sees heads_per_group = q_len * H for
+ * MLA (the query rows packed per request) and num_kv_heads for GQA; the tile rule sees the
+ * split kernel's CTA count, B * np * ceil(q_len * H / 32) for MLA and B * np * num_kv_heads
+ * for GQA. */
+int decode_plan(const gqa_decode_problem *p, int64_t np_or_0, int block_k_or_0, int64_t sm_count,
+                int64_t *np_out, int *block_k_out);
+
+/* ---------------------------------------------------------------------------------------- */
+/* Split, reduce, decode                                                                    */
+/* ---------------------------------------------------------------------------------------- */
+
+/* Split kernel: request b's keys are cut into np contiguous partitions of
+ * ceil(seq_lens[b] / np) keys rounded up to block_k (trailing partitions may be empty).  For
+ * every row r and partition i it writes
+ *   partial_o   [rows, np, d_v] fp32: softmax-weighted mean of the partition's values,
+ *   partial_lse2[rows, np]      fp32: log2 of the sum of e^score over the partition's keys,
+ * with (0, -inf) for a partition the row sees no key of.  np in 1..256, block_k 32 or 64.
+ * Errors: INVALID_ARGUMENT, UNSUPPORTED (shapes outside the table at the top of the problem
+ * struct, fnuz fp8, group or q_len * group above 16 for GQA), LAUNCH_FAILED. */
+int decode_split(const gqa_decode_problem *p, int64_t np, int block_k, float *partial_o,
+                 float *partial_lse2, gqa_stream_t s);
+
+/* Reducer: for every row, lse2 = log2(sum_i 2^lse2_i) and o = sum_i 2^(lse2_i - lse2) * o_i,
+ * summed in partition order 0..np-1 in fp32 (deterministic); partitions with lse2_i = -inf
+ * carry no weight and a row with none gets o = 0, lse2 = -inf [MAX, AMD reducer constraint].
+ *   partial_o [rows, np, d_v] fp32, partial_lse2 [rows, np] fp32 (inputs)
+ *   out       [rows, d_v] bf16, rounded to nearest even (output)
+ *   lse2_out  [rows] fp32 (output; may be NULL)
+ * np in 1..256, d_v a multiple of 4 up to 1024. */
+int splitk_reduce(int64_t rows, int64_t np, int64_t d_v, const float *partial_o,
+                  const float *partial_lse2, void *out, float *lse2_out, gqa_stream_t s);
+
+/* Workspace decode() needs for np partitions (np = 0: the planner's choice on the current
+ * device): the fp32 partials, 256-byte aligned; 0 when np == 1 (the split kernel then writes
+ * the final output itself). */
+int decode_workspace_bytes(const gqa_decode_problem *p, int64_t np, size_t *bytes);
+
+/* Whole decode: plan (np_or_0 == 0 / block_k_or_0 == 0 use the planner / tile rule on the
+ * current device), split, and reduce.
+ *   out      [B*q_len, H, d_v] bf16, contiguous (output)
+ *   lse2_out [B*q_len, H] fp32 (output; may be NULL)
+ * Errors: as decode_split, plus WORKSPACE_TOO_SMALL when ws_bytes is below
+ * decode_workspace_bytes. */
+int decode(const gqa_decode_problem *p, int64_t np_or_0, int block_k_or_0, void *workspace,
+           size_t ws_bytes, void *out, float *lse2_out, gqa_stream_t s);
+
+/* Utility: decode n OCP e4m3fn bytes to bf16 with the same conversion the MLA split kernel
+ * applies to the pool (exact; unit scale).  in, out 16-byte aligned device buffers; out holds
+ * n bf16 values.  Lets callers and tests check the device's fp8 decoding byte by byte. */
+int fp8_e4m3_to_bf16(const void *in, int64_t n, void *out, gqa_stream_t s);
+
+/* Static description of a status code. */
+const char *status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GQA_SPLITS_H */

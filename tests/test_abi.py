@@ -1,0 +1,192 @@
+"""The C-ABI library on the host (no GPU): exports, planner parity with the oracle, and the
+argument checks that run before anything is enqueued."""
+import ctypes
+import itertools
+import os
+import re
+import subprocess
+
+import pytest
+
+import gqa_plan_splits_amd as g
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 0x10000  # a 16-byte-aligned non-null address; never dereferenced by the host checks
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "gqa_splits.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return set(re.findall(r"^(?:int|const char \*)\s*\*?(\w+)\(", text, flags=re.M))
+
+
+def test_header_declares_the_boundary():
+    names = header_functions()
+    for required in ("plan_splits", "block_k_for", "decode_split", "splitk_reduce",
+                     "decode_workspace_bytes", "decode", "status_string"):
+        assert required in names
+
+
+def test_library_exports_every_declared_symbol():
+    names = header_functions()
+    out = subprocess.run(["nm", "-D", "--defined-only", g.library_path()], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    missing = names - exported
+    assert not missing, missing
+    assert set(g.exported_symbols()) == names
+
+
+def test_status_strings():
+    for code in (0, -1, -2, -3, -4, -5):
+        assert g.status_string(code) != "unknown status"
+    assert g.status_string(-99) == "unknown status"
+
+
+@pytest.mark.parametrize("is_mla", [False, True])
+def test_planner_matches_oracle_dense_sweep(is_mla):
+    bss = [1, 2, 3, 4, 5, 7, 8, 9, 16, 17, 24, 32, 34, 64, 100, 128, 256, 512]
+    nks = [0, 1, 127, 128, 255, 256, 257, 1000, 1280, 1281, 2048, 4096, 8191, 32768, 65280,
+           65281, 65536, 81920, 131072, 150000, 262144, 1 << 20]
+    hpgs = [1, 2, 4, 8, 12, 16, 24, 32, 48, 64, 96, 128, 256]
+    sms = [1, 32, 80, 256, 260, 304]
+    for bs, nk, hpg, sm in itertools.product(bss, nks, hpgs, sms):
+        assert g.plan_splits(bs, nk, hpg, sm, is_mla) == oracle.plan_splits(bs, nk, hpg, sm, is_mla), \
+            (bs, nk, hpg, sm, is_mla)
+
+
+def test_block_k_matches_oracle():
+    for ctas, sm in itertools.product([1, 2, 100, 255, 256, 257, 512, 8192], [1, 80, 256, 304]):
+        assert g.block_k_for(ctas, sm) == oracle.block_k(ctas, sm)
+
+
+def test_planner_rejections():
+    for args in [(0, 1, 1, 256), (1, -1, 1, 256), (1, 1, 0, 256)]:
+        with pytest.raises(g.GqaError) as e:
+            g.plan_splits(*args, is_mla=True)
+        assert e.value.status == -1
+    with pytest.raises(g.GqaError):
+        g.block_k_for(0, 256)
+    with pytest.raises(g.GqaError):
+        g.block_k_for(10, 0)
+
+
+def mla_fake(B=2, q_len=1, H=64, d_qk=576, d_v=512, max_keys=65536):
+    p = g.DecodeProblem()
+    p.kind, p.fp8_format = g.KIND_MLA_FUSED, g.FP8_E4M3FN
+    p.batch, p.q_len, p.num_heads, p.num_kv_heads = B, q_len, H, 1
+    p.d_qk, p.d_rope, p.d_v, p.page_size, p.max_num_keys = d_qk, 64, d_v, 1, max_keys
+    p.q, p.q_stride_tok, p.q_stride_head = FAKE, H * (d_qk - 64), d_qk - 64
+    p.q_pe, p.q_pe_stride_tok, p.q_pe_stride_head = FAKE, H * 64, 64
+    p.kv, p.kv_stride_row = FAKE, d_qk
+    p.kv_indices = p.kv_indptr = p.seq_lens = FAKE
+    p.scale, p.kv_scale = d_qk ** -0.5, 1 / 32
+    return p
+
+
+def gqa_fake(B=32, Hq=64, Hkv=8, page=16, q_len=1, max_keys=32768):
+    p = g.DecodeProblem()
+    p.kind = g.KIND_GQA_PAGED
+    p.batch, p.q_len, p.num_heads, p.num_kv_heads = B, q_len, Hq, Hkv
+    p.d_qk, p.d_rope, p.d_v, p.page_size, p.max_num_keys = 128, 0, 128, page, max_keys
+    p.q, p.q_stride_tok, p.q_stride_head = FAKE, Hq * 128, 128
+    p.k_cache = p.v_cache = FAKE
+    p.kv_indices = p.kv_indptr = p.seq_lens = FAKE
+    p.scale, p.kv_scale = 128 ** -0.5, 1.0
+    return p
+
+
+@pytest.mark.parametrize("B,q_len,H,keys", [(1, 1, 16, 4096), (2, 1, 64, 65536), (8, 1, 64, 131072),
+                                            (16, 1, 64, 131072), (8, 4, 64, 131072),
+                                            (16, 4, 64, 131072), (24, 1, 64, 2048),
+                                            (34, 1, 64, 2048), (256, 1, 64, 2048)])
+def test_decode_plan_mla_matches_oracle(B, q_len, H, keys):
+    p = mla_fake(B=B, q_len=q_len, H=H, max_keys=keys)
+    np_, bk = g.decode_plan(p, 0, 0, 256)
+    # the planner sees the query rows packed per request; the tile rule sees the split CTAs
+    want_np = oracle.plan_splits(B, keys, q_len * H, 256, True)
+    assert np_ == want_np
+    assert bk == oracle.block_k(B * want_np * -(-(q_len * H) // 32), 256)
+
+
+def test_decode_plan_gqa_matches_oracle():
+    p = gqa_fake()
+    np_, bk = g.decode_plan(p, 0, 0, 256)
+    assert np_ == oracle.plan_splits(32, 32768, 8, 256, False)
+    assert bk == oracle.block_k(32 * np_ * 8, 256)
+    assert (np_, bk) == (32, 32)
+
+
+def test_decode_plan_explicit_overrides():
+    p = mla_fake()
+    assert g.decode_plan(p, 4, 32, 256) == (4, 32)
+    assert g.decode_plan(p, 1, 64, 256) == (1, 64)
+
+
+def expect_status(fn, status):
+    with pytest.raises(g.GqaError) as e:
+        fn()
+    assert e.value.status == status, (e.value.status, status)
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("batch", 0, -1), ("q_len", 0, -1), ("num_heads", 0, -1), ("max_num_keys", -1, -1),
+    ("num_heads", 129, -2), ("q", 0, -1), ("kv", 0, -1), ("q_pe", 0, -1), ("kv_indices", 0, -1),
+    ("kv_indptr", 0, -1), ("seq_lens", 0, -1), ("num_kv_heads", 2, -1), ("kind", 7, -1),
+    ("fp8_format", 1, -2), ("fp8_format", 5, -1), ("d_qk", 128, -2), ("d_v", 256, -2),
+    ("page_size", 16, -2), ("kv_stride_row", 500, -2), ("q", FAKE + 8, -2),
+    ("q_stride_head", 4, -2), ("scale", 0.0, -1), ("kv_scale", 0.0, -1),
+])
+def test_mla_rejections(field, value, status):
+    p = mla_fake()
+    setattr(p, field, value)
+    expect_status(lambda: g.decode_plan(p, 4, 32, 256), status)
+    expect_status(lambda: g.decode_split(p, 4, 32, FAKE, FAKE), status)
+    expect_status(lambda: g.decode(p, FAKE, np=4, block_k=32, workspace=None), status)
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("num_kv_heads", 0, -1), ("num_kv_heads", 7, -1), ("k_cache", 0, -1), ("v_cache", 0, -1),
+    ("d_qk", 64, -2), ("d_rope", 64, -2), ("page_size", 12, -2), ("page_size", 4, -2),
+    ("num_kv_heads", 2, -2),  # 32 query rows per kv head: above the 16-row tile
+])
+def test_gqa_rejections(field, value, status):
+    p = gqa_fake()
+    setattr(p, field, value)
+    expect_status(lambda: g.decode_plan(p, 4, 32, 256), status)
+    expect_status(lambda: g.decode_split(p, 4, 32, FAKE, FAKE), status)
+
+
+def test_split_argument_rejections():
+    p = mla_fake()
+    expect_status(lambda: g.decode_split(p, 0, 32, FAKE, FAKE), -2)
+    expect_status(lambda: g.decode_split(p, 257, 32, FAKE, FAKE), -2)
+    expect_status(lambda: g.decode_split(p, 4, 48, FAKE, FAKE), -2)
+    expect_status(lambda: g.decode_split(p, 4, 32, 0, FAKE), -1)
+    expect_status(lambda: g.decode_split(p, 4, 32, FAKE, 0), -1)
+
+
+def test_reduce_argument_rejections():
+    expect_status(lambda: g.splitk_reduce(-1, 4, 512, FAKE, FAKE, FAKE), -1)
+    expect_status(lambda: g.splitk_reduce(8, 0, 512, FAKE, FAKE, FAKE), -2)
+    expect_status(lambda: g.splitk_reduce(8, 257, 512, FAKE, FAKE, FAKE), -2)
+    expect_status(lambda: g.splitk_reduce(8, 4, 510, FAKE, FAKE, FAKE), -2)
+    expect_status(lambda: g.splitk_reduce(8, 4, 512, 0, FAKE, FAKE), -1)
+    expect_status(lambda: g.splitk_reduce(8, 4, 512, FAKE, FAKE, 0), -1)
+    g.splitk_reduce(0, 4, 512, FAKE, FAKE, FAKE)   # no rows: nothing to enqueue
+
+
+def test_workspace_contract():
+    p = mla_fake(B=2, H=64)
+    need = g.decode_workspace_bytes(p, 64)
+    rows = 2 * 64
+    assert need >= rows * 64 * 512 * 4 + rows * 64 * 4
+    assert need % 256 == 0
+    assert g.decode_workspace_bytes(p, 1) == 0
+    lib = g._lib._load()
+    rc = lib.decode(ctypes.byref(p), 64, 64, ctypes.c_void_p(FAKE), need - 256,
+                    ctypes.c_void_p(FAKE), None, None)
+    assert rc == -3
+    rc = lib.decode(ctypes.byref(p), 64, 64, None, need, ctypes.c_void_p(FAKE), None, None)
+    assert rc == -1

@@ -1,0 +1,265 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 CPU oracle, element by element.
+
+Small shapes compare every output (several tiles, ragged tails, empty rows); the full-size
+workloads compare sampled rows in exactly the launch configuration the benchmark times
+(planner np, tile rule BLOCK_K)."""
+import numpy as np
+import pytest
+import torch
+
+import gqa_plan_splits_amd as g
+import oracle
+import workloads
+from gpu_util import (compare, gqa_problem, log, mla_problem, oracle_gqa, oracle_mla, run_decode,
+                      sample_rows)
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+DEV = "cuda"
+
+
+# ---------------------------------------------------------------------------------------------
+# fp8 conversion and reducer
+# ---------------------------------------------------------------------------------------------
+
+def test_fp8_conversion_matches_definition():
+    table = oracle.e4m3_table(False)
+    src = torch.arange(256, dtype=torch.uint8, device=DEV).repeat(4)
+    out = torch.empty(1024, dtype=torch.bfloat16, device=DEV)
+    g.fp8_e4m3_to_bf16(src, 1024, out)
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy().astype(np.float64)[:256]
+    ok = ~np.isnan(table)
+    assert np.array_equal(got[ok], table[ok])
+    assert np.all(np.isnan(got[~ok]))
+
+
+@pytest.mark.parametrize("rows,np_,dv", [(1, 1, 512), (7, 2, 512), (33, 5, 448), (64, 64, 512),
+                                         (10, 256, 128), (5, 37, 128), (300, 16, 512)])
+def test_reduce_matches_oracle_merge(rows, np_, dv):
+    gen = torch.Generator(device="cpu").manual_seed(rows * 1000 + np_)
+    po = torch.randn((rows, np_, dv), generator=gen) * 0.3
+    pl = torch.randn((rows, np_), generator=gen) * 4 + 12
+    drop = torch.rand((rows, np_), generator=gen) < 0.3
+    pl[drop] = -float("inf")
+    po[drop] = 0
+    pl[0, :] = -float("inf")          # a row no partition saw
+    po[0, :] = 0
+    ref_o, ref_l = oracle.lse_merge(po.double().numpy(), pl.double().numpy())
+    out = torch.empty((rows, dv), dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty((rows,), dtype=torch.float32, device=DEV)
+    g.splitk_reduce(rows, np_, dv, po.to(DEV), pl.to(DEV), out, lse)
+    torch.cuda.synchronize()
+    compare(out, lse, ref_o, ref_l, "reduce rows=%d np=%d dv=%d" % (rows, np_, dv))
+    # bf16 output of an fp32 merge: within one bf16 rounding of the fp64 merge
+    o = out.float().cpu().double().numpy()
+    assert np.all(np.abs(o - ref_o) <= np.abs(ref_o) * 2 ** -8 + 1e-6)
+
+
+def test_reduce_is_deterministic():
+    po = torch.randn((64, 200, 512), device=DEV)
+    pl = torch.randn((64, 200), device=DEV) * 3
+    outs = []
+    for _ in range(3):
+        out = torch.empty((64, 512), dtype=torch.bfloat16, device=DEV)
+        lse = torch.empty((64,), dtype=torch.float32, device=DEV)
+        g.splitk_reduce(64, 200, 512, po, pl, out, lse)
+        outs.append((out.clone(), lse.clone()))
+    torch.cuda.synchronize()
+    for o, l in outs[1:]:
+        assert torch.equal(o, outs[0][0]) and torch.equal(l, outs[0][1])
+
+
+# ---------------------------------------------------------------------------------------------
+# Absorbed MLA
+# ---------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("np_", [1, 4, 16, 0])
+@pytest.mark.parametrize("bk", [32, 64])
+def test_mla_tiny_all_rows(np_, bk):
+    inp = workloads.mla_tiny(DEV)
+    log("mla tiny np=%d bk=%d" % (np_, bk))
+    out, lse = run_decode(mla_problem(inp), 512, np_, bk)
+    torch.cuda.synchronize()
+    ref_o, ref_l = oracle_mla(inp)
+    compare(out, lse, ref_o, ref_l, "mla tiny np=%d bk=%d" % (np_, bk))
+
+
+@pytest.mark.parametrize("d_qk,d_v", [(576, 512), (512, 448)])
+@pytest.mark.parametrize("q_len", [1, 4])
+@pytest.mark.parametrize("np_", [1, 3, 8])
+@pytest.mark.parametrize("bk", [32, 64])
+def test_mla_ragged_all_rows(d_qk, d_v, q_len, np_, bk):
+    # several tiles per partition, ragged tails, a request shorter than the draft window (rows
+    # that see no key), an empty request, and 40 heads (a partial second 32-row block)
+    lens = [1000, 37, 2, 0, 2049]
+    inp = workloads.mla_inputs(B=5, q_len=q_len, H=40, seq_lens=lens, pool_rows=4000, d_qk=d_qk,
+                               d_v=d_v, seed=77, device=DEV, fused_q=(d_qk == 512))
+    log("mla ragged d_qk=%d q_len=%d np=%d bk=%d" % (d_qk, q_len, np_, bk))
+    out, lse = run_decode(mla_problem(inp), d_v, np_, bk)
+    torch.cuda.synchronize()
+    ref_o, ref_l = oracle_mla(inp)
+    compare(out, lse, ref_o, ref_l, "mla ragged")
+
+
+def test_mla_split_partials_match_oracle_on_key_ranges():
+    # decode_split alone: each partial equals the oracle over that partition's key range
+    inp = workloads.mla_inputs(B=2, q_len=1, H=32, seq_lens=[300, 129], pool_rows=512, seed=5,
+                               device=DEV)
+    np_, bk = 3, 32
+    p = mla_problem(inp)
+    rows = inp.rows
+    po = torch.empty((rows, np_, 512), dtype=torch.float32, device=DEV)
+    pl = torch.empty((rows, np_), dtype=torch.float32, device=DEV)
+    g.decode_split(p, np_, bk, po, pl)
+    torch.cuda.synchronize()
+    for b, S in enumerate([300, 129]):
+        chunk = -(-(-(-S // np_)) // bk) * bk
+        for part in range(np_):
+            a, e = min(S, part * chunk), min(S, (part + 1) * chunk)
+            sub = workloads.mla_inputs(B=1, q_len=1, H=32, seq_lens=[1], pool_rows=1, seed=5)
+            sub.q_lat = inp.q_lat[b:b + 1].cpu()
+            sub.q_pe = inp.q_pe[b:b + 1].cpu()
+            sub.pool = inp.pool.cpu()
+            base = int(inp.kv_indptr[b])
+            sub.kv_indices = inp.kv_indices[base + a:base + max(e, a + 1)].cpu()
+            sub.kv_indptr = torch.tensor([0, max(e - a, 1)], dtype=torch.int32)
+            sub.seq_lens = torch.tensor([e - a], dtype=torch.int32)
+            sub.B = 1
+            ro, rl = oracle_mla(sub)
+            got_o = po[b * 32:(b + 1) * 32, part].cpu().double().numpy()
+            got_l = pl[b * 32:(b + 1) * 32, part].cpu().double().numpy()
+            if e <= a:
+                assert np.all(got_l == -np.inf) and np.all(got_o == 0)
+                continue
+            assert np.abs(got_o - ro).max() <= 1e-3 * max(1.0, np.abs(ro).max())
+            assert np.all(np.abs(got_l - rl) <= 1e-4 * np.maximum(1, np.abs(rl)))
+
+
+def test_mla_split_invariance_and_determinism():
+    inp = workloads.mla_inputs(B=2, q_len=1, H=64, seq_lens=[5000, 3333], pool_rows=9000, seed=9,
+                               device=DEV)
+    p = mla_problem(inp)
+    base_o, base_l = run_decode(p, 512, 1, 64)
+    for np_, bk in [(4, 32), (16, 64), (0, 0), (256, 32)]:
+        o, l = run_decode(p, 512, np_, bk)
+        torch.cuda.synchronize()
+        assert (o.float() - base_o.float()).abs().max().item() <= 4e-3
+        assert ((l - base_l).abs() / base_l.abs().clamp(min=1)).max().item() <= 1e-5
+    o1, l1 = run_decode(p, 512, 16, 32)
+    o2, l2 = run_decode(p, 512, 16, 32)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_mla_graph_replay_matches_eager():
+    inp = workloads.mla_inputs(B=2, q_len=2, H=64, seq_lens=[4000, 2500], pool_rows=7000, seed=3,
+                               device=DEV)
+    p = mla_problem(inp)
+    rows = inp.rows
+    ws = torch.empty((g.decode_workspace_bytes(p, 8) // 4 + 64,), dtype=torch.float32, device=DEV)
+    out = torch.empty((rows, 512), dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty((rows,), dtype=torch.float32, device=DEV)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        g.decode(p, out, lse, np=8, block_k=32, workspace=ws, stream=s)
+    torch.cuda.synchronize()
+    eager_o, eager_l = out.clone(), lse.clone()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=s):
+        g.decode(p, out, lse, np=8, block_k=32, workspace=ws, stream=s)
+    for _ in range(4):
+        out.zero_()
+        lse.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager_o) and torch.equal(lse, eager_l)
+
+
+FULL_MLA = [("b2_s65536", lambda: workloads.mla_b2_s65536(DEV)),
+            ("b8_s131072_q1", lambda: workloads.mla_long(8, 1, DEV)),
+            ("b16_s131072_q1", lambda: workloads.mla_long(16, 1, DEV)),
+            ("b8_s131072_q4", lambda: workloads.mla_long(8, 4, DEV)),
+            ("b16_s131072_q4", lambda: workloads.mla_long(16, 4, DEV))]
+
+
+@pytest.mark.parametrize("name,make", FULL_MLA, ids=[n for n, _ in FULL_MLA])
+def test_mla_full_size_sampled(name, make):
+    inp = make()
+    p = mla_problem(inp)
+    np_, bk = g.decode_plan(p)
+    log("mla %s planner np=%d bk=%d" % (name, np_, bk))
+    out, lse = run_decode(p, 512)
+    torch.cuda.synchronize()
+    rows = sample_rows(inp.B, inp.q_len, inp.H, 24, seed=hash(name) % 1000)
+    ref_o, ref_l = oracle_mla(inp, rows)
+    compare(out[rows], lse[rows], ref_o, ref_l, "mla " + name)
+    del inp, out, lse
+    torch.cuda.empty_cache()
+
+
+# ---------------------------------------------------------------------------------------------
+# Sparse top-k MLA
+# ---------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("nq", list(workloads.SPARSE_QUERY_COUNTS))
+def test_sparse_full_size_both_tiles(nq):
+    inp = workloads.sparse_topk(nq, DEV)
+    p = mla_problem(inp)
+    np_, bk = g.decode_plan(p)
+    log("sparse nq=%d planner np=%d bk=%d" % (nq, np_, bk))
+    rows = sample_rows(inp.B, 1, inp.H, 32, seed=nq)
+    ref_o, ref_l = oracle_mla(inp, rows)
+    results = {}
+    for tile in (32, 64):   # the rule's choice and the other one: same numerics either way
+        out, lse = run_decode(p, 448, np_, tile)
+        torch.cuda.synchronize()
+        compare(out[rows], lse[rows], ref_o, ref_l, "sparse nq=%d bk=%d" % (nq, tile))
+        results[tile] = (out, lse)
+    d = (results[32][0].float() - results[64][0].float()).abs().max().item()
+    assert d <= 4e-3
+
+
+# ---------------------------------------------------------------------------------------------
+# Paged GQA
+# ---------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("Hq,Hkv,q_len", [(16, 2, 1), (32, 4, 2), (8, 8, 1), (12, 3, 4), (16, 1, 1)])
+@pytest.mark.parametrize("np_", [1, 3, 32])
+@pytest.mark.parametrize("bk", [32, 64])
+def test_gqa_ragged_all_rows(Hq, Hkv, q_len, np_, bk):
+    lens = [700, 33, 1, 0, 1600, 16]
+    inp = workloads.gqa_inputs(B=6, Hq=Hq, Hkv=Hkv, D=128, page_size=16, seq_lens=lens,
+                               num_pages=300, q_len=q_len, seed=31, device=DEV)
+    log("gqa ragged Hq=%d Hkv=%d q_len=%d np=%d bk=%d" % (Hq, Hkv, q_len, np_, bk))
+    out, lse = run_decode(gqa_problem(inp), 128, np_, bk)
+    torch.cuda.synchronize()
+    ref_o, ref_l = oracle_gqa(inp)
+    compare(out, lse, ref_o, ref_l, "gqa ragged")
+
+
+@pytest.mark.parametrize("page_size", [8, 32, 64])
+def test_gqa_page_sizes(page_size):
+    inp = workloads.gqa_inputs(B=3, Hq=16, Hkv=2, D=128, page_size=page_size, seq_lens=[333, 64, 1000],
+                               num_pages=100, seed=41, device=DEV)
+    out, lse = run_decode(gqa_problem(inp), 128, 4, 32)
+    torch.cuda.synchronize()
+    ref_o, ref_l = oracle_gqa(inp)
+    compare(out, lse, ref_o, ref_l, "gqa page %d" % page_size)
+
+
+def test_gqa_full_size_sampled():
+    inp = workloads.gqa_paged(DEV)
+    p = gqa_problem(inp)
+    np_, bk = g.decode_plan(p)
+    log("gqa full planner np=%d bk=%d" % (np_, bk))
+    out, lse = run_decode(p, 128)
+    torch.cuda.synchronize()
+    rows = sample_rows(inp.B, 1, inp.Hq, 48, seed=123)
+    ref_o, ref_l = oracle_gqa(inp, rows)
+    compare(out[rows], lse[rows], ref_o, ref_l, "gqa full")
+    o2, l2 = run_decode(p, 128)
+    torch.cuda.synchronize()
+    assert torch.equal(out, o2) and torch.equal(lse, l2)
