@@ -38,6 +38,11 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle sample")
     ap.add_argument("--table-steps", type=int, default=20)
+    ap.add_argument("--block-k", type=int, default=0,
+                    help="force the split kernel's key tile (0: the CTA-keyed tile rule)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (5 times): the reference kernel "
+                         "that scales rocprofv3 FETCH_SIZE / WRITE_SIZE readings to bytes")
     return ap.parse_args()
 
 
@@ -62,7 +67,7 @@ def make_workloads():
 class Case:
     """One workload bound to the C ABI: problem, output and workspace buffers."""
 
-    def __init__(self, inp, np_fixed, stream):
+    def __init__(self, inp, np_fixed, stream, block_k=0):
         import torch
         import gqa_plan_splits_amd as g
         self.g = g
@@ -80,7 +85,8 @@ class Case:
                                    max_num_keys=inp.max_num_keys, scale=inp.scale)
             self.d_v = inp.D
         self.np_arg = np_fixed
-        self.np, self.bk = g.decode_plan(self.p, np_fixed, 0)
+        self.bk_arg = block_k
+        self.np, self.bk = g.decode_plan(self.p, np_fixed, block_k)
         rows = self.p.rows
         dev = torch.device("cuda")
         self.out = torch.empty((rows, self.d_v), dtype=torch.bfloat16, device=dev)
@@ -94,8 +100,8 @@ class Case:
 
     def step(self):
         # the whole hot path: plan (np=0 / block_k=0 -> planner and tile rule) + split + reduce
-        self.g.decode(self.p, self.out, self.lse, np=self.np_arg, block_k=0, workspace=self.ws,
-                      stream=self.stream)
+        self.g.decode(self.p, self.out, self.lse, np=self.np_arg, block_k=self.bk_arg,
+                      workspace=self.ws, stream=self.stream)
 
     def split_only(self):
         self.g.decode_split(self.p, self.np, self.bk, self.po, self.pl, stream=self.stream)
@@ -189,6 +195,15 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     torch.cuda.set_device(0)
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "launches": 5}))
+        return
     stream = torch.cuda.Stream()
     sm = g.device_sm_count()
 
@@ -200,7 +215,7 @@ def main():
         with torch.cuda.stream(stream):
             inp = make("cuda")
         torch.cuda.synchronize()
-        case = Case(inp, np_fixed, stream)
+        case = Case(inp, np_fixed, stream, args.block_k)
         is_head = name == args.workload
         steps = args.steps if is_head else args.table_steps
         warm = args.warmup if is_head else max(3, args.warmup // 2)

@@ -23,6 +23,7 @@ from ._lib import (  # noqa: F401
     exported_symbols,
     fp8_e4m3_to_bf16,
     gqa_problem,
+    last_error_detail,
     library_path,
     mla_problem,
     plan_splits,

@@ -15,13 +15,15 @@ FP8_E4M3FNUZ = 1
 # Every function include/gqa_splits.h declares.
 _SYMBOLS = ("plan_splits", "block_k_for", "device_sm_count", "decode_plan", "decode_split",
             "splitk_reduce", "decode_workspace_bytes", "decode", "fp8_e4m3_to_bf16",
-            "status_string")
+            "status_string", "last_error_detail")
 
 
 class GqaError(RuntimeError):
     def __init__(self, status: int, where: str):
         self.status = status
-        super().__init__("%s failed: %s (status %d)" % (where, status_string(status), status))
+        detail = last_error_detail() if status == -4 else ""
+        super().__init__("%s failed: %s (status %d)%s" % (where, status_string(status), status,
+                                                          (": " + detail) if detail else ""))
 
 
 class DecodeProblem(ctypes.Structure):
@@ -77,6 +79,12 @@ def _load():
     if not os.path.exists(_LIB_PATH):
         raise ImportError("libgqa_splits.so is not built (run `python gqa_plan_splits_amd/build.py`); "
                           "there is no fallback path")
+    try:
+        # load torch's HIP runtime first: the library then binds to that same runtime instance
+        # (same soname), so streams and memory from torch are valid in its calls
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     lib = ctypes.CDLL(_LIB_PATH)
     i64, i32, vp = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p
     pp = ctypes.POINTER(DecodeProblem)
@@ -91,8 +99,10 @@ def _load():
     lib.fp8_e4m3_to_bf16.argtypes = [vp, i64, vp, vp]
     lib.status_string.argtypes = [i32]
     lib.status_string.restype = ctypes.c_char_p
+    lib.last_error_detail.argtypes = []
+    lib.last_error_detail.restype = ctypes.c_char_p
     for name in _SYMBOLS:
-        if name != "status_string":
+        if name not in ("status_string", "last_error_detail"):
             getattr(lib, name).restype = i32
     _lib = lib
     return lib
@@ -109,6 +119,10 @@ def exported_symbols():
 
 def status_string(status: int) -> str:
     return _load().status_string(int(status)).decode()
+
+
+def last_error_detail() -> str:
+    return _load().last_error_detail().decode()
 
 
 def _check(rc: int, where: str):

@@ -20,6 +20,8 @@ ARCH = "gfx950"
 # -packed-fp32-ops: hipcc must not emit packed fp32 arithmetic (v_pk_*_f32) on its own.
 HIPCC_FLAGS = [
     "-O3", "-std=c++17", "-fPIC", "-shared", "--offload-arch=" + ARCH,
+    # code object v5: loadable by the HIP runtime torch ships (ROCm 7.0) as well as ROCm 7.2's
+    "-mcode-object-version=5",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-ffp-contract=fast", "-Wall", "-Wno-unused-function",
 ]

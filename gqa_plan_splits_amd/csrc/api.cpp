@@ -4,6 +4,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <cstdio>
 
 #include "../../include/gqa_splits.h"
 #include "kernels.hpp"
@@ -24,6 +25,14 @@ int ilog2(int64_t x) {
     return r;
 }
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+thread_local char g_last_error[160] = "";
+
+int launch_status(hipError_t err, const char *what) {
+    if (err == hipSuccess) return GQA_OK;
+    snprintf(g_last_error, sizeof g_last_error, "%s: %s (%d)", what, hipGetErrorString(err), int(err));
+    return GQA_ERR_LAUNCH_FAILED;
+}
 
 struct Derived {
     int64_t rows;           // B * q_len * H
@@ -111,7 +120,6 @@ int launch_split(const gqa_decode_problem *p, const Derived &d, int64_t np, int 
     const int64_t total = p->batch * np * d.cta_rows;
     if (total > (int64_t(1) << 30)) return GQA_ERR_UNSUPPORTED;
     const bool direct = out != nullptr;
-    hipError_t err;
     if (d.is_mla) {
         gqa::MlaSplitArgs a;
         a.q = static_cast<const uint16_t *>(p->q);
@@ -137,7 +145,8 @@ int launch_split(const gqa_decode_problem *p, const Derived &d, int64_t np, int 
         a.part_lse2 = part_lse2;
         a.out = static_cast<uint16_t *>(out);
         a.lse2_out = lse2_out;
-        err = gqa::launch_mla_split(a, bk, int(p->d_qk), int(p->d_v), direct, s);
+        const hipError_t err = gqa::launch_mla_split(a, bk, int(p->d_qk), int(p->d_v), direct, s);
+        return launch_status(err, "mla split");
     } else {
         gqa::GqaSplitArgs a;
         a.q = static_cast<const uint16_t *>(p->q);
@@ -160,9 +169,9 @@ int launch_split(const gqa_decode_problem *p, const Derived &d, int64_t np, int 
         a.part_lse2 = part_lse2;
         a.out = static_cast<uint16_t *>(out);
         a.lse2_out = lse2_out;
-        err = gqa::launch_gqa_split(a, bk, int(p->q_len * a.group), direct, s);
+        const hipError_t err = gqa::launch_gqa_split(a, bk, int(p->q_len * a.group), direct, s);
+        return launch_status(err, "gqa split");
     }
-    return err == hipSuccess ? GQA_OK : GQA_ERR_LAUNCH_FAILED;
 }
 
 int partial_bytes(const Derived &d, int64_t np, int64_t dv, size_t *o_bytes, size_t *l_bytes) {
@@ -208,9 +217,7 @@ extern "C" int splitk_reduce(int64_t rows, int64_t np, int64_t d_v, const float 
     a.rows = rows;
     a.np = int32_t(np);
     a.dv = int32_t(d_v);
-    return gqa::launch_splitk_reduce(a, reinterpret_cast<hipStream_t>(s)) == hipSuccess
-               ? GQA_OK
-               : GQA_ERR_LAUNCH_FAILED;
+    return launch_status(gqa::launch_splitk_reduce(a, reinterpret_cast<hipStream_t>(s)), "splitk_reduce");
 }
 
 extern "C" int decode_workspace_bytes(const gqa_decode_problem *p, int64_t np, size_t *bytes) {
@@ -263,11 +270,13 @@ extern "C" int fp8_e4m3_to_bf16(const void *in, int64_t n, void *out, gqa_stream
     if (!in || !out || n < 0) return GQA_ERR_INVALID_ARGUMENT;
     if (!aligned16(in) || !aligned16(out)) return GQA_ERR_UNSUPPORTED;
     if (n == 0) return GQA_OK;
-    return gqa::launch_fp8_to_bf16(static_cast<const uint8_t *>(in), n, static_cast<uint16_t *>(out),
-                                   reinterpret_cast<hipStream_t>(s)) == hipSuccess
-               ? GQA_OK
-               : GQA_ERR_LAUNCH_FAILED;
+    return launch_status(gqa::launch_fp8_to_bf16(static_cast<const uint8_t *>(in), n,
+                                                 static_cast<uint16_t *>(out),
+                                                 reinterpret_cast<hipStream_t>(s)),
+                         "fp8 conversion");
 }
+
+extern "C" const char *last_error_detail(void) { return g_last_error; }
 
 extern "C" const char *status_string(int status) {
     switch (status) {

@@ -7,72 +7,83 @@
 // partition's softmax-weighted mean of values and the base-2 log-sum-exp of its scores.
 //
 // Layout of the work:
-//   - 128 threads = 2 waves; wave w owns rows 16w..16w+15 of the CTA's 32.
-//   - Keys are processed in tiles of BK (32 or 64).  All 128 threads gather a tile (16 bytes per
-//     lane per load, slot ids read a tile ahead) into registers one tile ahead of the compute,
-//     then write it to LDS twice: row-major (the QK^T operand) and transposed (the PV operand).
-//   - QK^T and PV run on v_mfma_f32_16x16x32_bf16: the fp8 bytes are converted to bf16 exactly
-//     as they are read from LDS; kv_scale is folded into the score scale and the output scale.
-//   - Scores are S^T = K Q^T (rows = keys, columns = query rows), so each lane owns one query
-//     row's column: the row max / sum take two cross-lane exchanges, and the output O^T = V^T P^T
-//     has each lane's accumulators in a single query row, so the online-softmax rescale is a
-//     per-lane multiply.
+//   - 256 threads = 4 waves.  Waves 0/1 own query rows 0-15 / 16-31 of the CTA; waves 2/3 own
+//     the same rows.  For QK^T each pair splits the DQK contraction in halves and adds the two
+//     partial score tiles through LDS (both waves then hold identical scores); for PV each wave
+//     of the pair owns half of the DV output columns.  Each wave thus holds half of Q and half of
+//     the output accumulator, which keeps it near 160 VGPRs so two waves fit on every SIMD.
+//   - Keys are processed in tiles of BK (32 or 64).  The CTA gathers a tile (16 bytes per lane,
+//     consecutive lanes on consecutive chunks of a row, slot ids read a tile ahead) into
+//     registers one tile ahead of the compute, then writes it to LDS row-major, once.
+//   - QK^T (S^T = K Q^T) and PV (O^T = V^T P^T) run on v_mfma_f32_16x16x32_bf16.  K is read
+//     16 bytes per lane; V is read from the same row-major tile with ds_read_b64_tr_b8, which
+//     hands each lane 8 keys of one value column -- the K-major operand layout.  The fp8 bytes
+//     are converted to bf16 exactly as they are read; kv_scale is folded into the score scale and
+//     the output scale.
+//   - Each lane owns one query row's column of the score tile, so the row max / sum take two
+//     cross-lane exchanges and the online-softmax rescale is a per-lane multiply (skipped when no
+//     row's maximum moved).
+//
+// LDS tile layout (chunk-major, swizzled): 16-byte chunk c of tile key k sits in slot
+// c * BK + (k ^ 12 * bit4(k) ^ (c % 16)).  A score-operand read (16 consecutive keys, one chunk)
+// is then one contiguous 256-byte block; a transposed value read (keys 4g..4g+3 and 16+4g..
+// 16+4g+3 of a 32-key step) lands on 8 distinct 16-byte slots; and the gather's stores (one key,
+// consecutive chunks) land on distinct banks.  All three are free of bank conflicts, and the
+// tile needs no padding.
 #include "device_common.hpp"
 #include "kernels.hpp"
 
 namespace gqa {
 namespace {
 
-template <int BK, int DQK, int DV>
-struct MlaTile {
-    static constexpr int kThreads = 128;
-    static constexpr int kDLat = DQK - 64;            // latent width; V = first DV columns
-    static constexpr int kKSteps = DQK / 32;          // MFMA K-steps over the key row
-    static constexpr int kVBlocks = DV / 16;          // 16-wide blocks of the value width
-    static constexpr int kSBlocks = BK / 16;          // 16-key score blocks per tile
-    static constexpr int kPvSteps = BK / 32;          // 32-key PV steps per tile
-    static constexpr int kKStride = DQK + 8;          // bytes per K row in LDS (8 * odd)
-    static constexpr int kKeysPerThread = BK / 4;     // main gather: 32 chunks x 4 key groups
-    static constexpr int kExtraChunks = (DQK - 512) / 16;               // chunks past 512 bytes
-    static constexpr int kExtraPerThread = kExtraChunks * BK / kThreads;  // 0, 1 or 2
-    static constexpr int kVChunks = DV / 16;          // 16-byte chunks that are also values
-    static constexpr int kKBytes = BK * kKStride;
-    static constexpr int kVBytes = DV * BK;
-    static constexpr int kLdsBytes = kKBytes + kVBytes;
-    static_assert(DQK == 576 || DQK == 512, "row width");
-    static_assert(DV % 16 == 0 && DV <= kDLat, "value width");
-    static_assert(BK == 32 || BK == 64, "tile");
-    static_assert(kExtraChunks * BK % kThreads == 0, "extra chunks per thread");
-};
+typedef int int2v __attribute__((ext_vector_type(2)));
 
-// Position of a key inside the transposed V tile.  The PV MFMA consumes 32 keys per step; lane
-// group g (lanes 16g..16g+15) supplies k-slots 8g..8g+7, which hold keys 4g..4g+3 (from the
-// first 16-key score block) and 16+4g..16+4g+3 (from the second) -- exactly the keys that lane
-// group owns in the score output layout.  key_of_position inverts that order.
-__device__ __forceinline__ int key_of_position(int p) {
-    const int r = p & 31;
-    return (p & ~31) + ((r >> 2) & 1) * 16 + (r >> 3) * 4 + (r & 3);
+// Byte offset of byte d of tile key `key` (see the layout note above).
+template <int BK>
+__device__ __forceinline__ int tile_pos(int key, int d) {
+    const int c = d >> 4;
+    return ((c * BK + (key ^ (((key >> 4) & 1) * 12) ^ (c & 15))) << 4) + (d & 15);
 }
 
-// Byte offset of (value block vb, PV step kb, lane group grp, row j of the block) in the
-// transposed V tile.  Each (vb, kb, grp) owns 128 contiguous bytes = 16 slots of 8 keys; row j
-// sits in slot (j + vb) % 16.  Readers (16 lanes = 16 rows) hit 16 distinct slots; writers
-// (16 lanes = 16 value blocks, same row) also hit 16 distinct slots: both conflict-free.
-template <int NPV>
-__device__ __forceinline__ int vt_offset(int vb, int kb, int grp, int j) {
-    return ((((vb * NPV + kb) << 2) + grp) * 16 + ((j + vb) & 15)) * 8;
+template <int BK, int DQK, int DV>
+struct MlaTile {
+    static constexpr int kThreads = 256;
+    static constexpr int kDLat = DQK - 64;             // latent width; V = first DV columns
+    static constexpr int kHalfD = DQK / 2;             // QK contraction per wave
+    static constexpr int kKSteps = kHalfD / 32;        // MFMA K-steps per wave (9 or 8)
+    static constexpr int kPairs = kKSteps / 2;         // steps read as 16-byte pairs
+    static constexpr int kHalfV = DV / 2;              // output columns per wave
+    static constexpr int kVBlocks = kHalfV / 16;       // 16 or 14
+    static constexpr int kSBlocks = BK / 16;           // 16-key score blocks per tile
+    static constexpr int kPvSteps = BK / 32;           // 32-key PV steps per tile
+    static constexpr int kChunks = DQK / 16;           // 16-byte chunks per key row
+    static constexpr int kItems = BK * kChunks;        // chunks per tile
+    static constexpr int kItemsPerThread = (kItems + kThreads - 1) / kThreads;
+    static constexpr int kKBytes = BK * DQK;
+    static constexpr int kSxBytes = 4 * kSBlocks * 64 * 16;   // partial score exchange
+    static constexpr int kLdsBytes = kKBytes + kSxBytes;
+    static_assert(DQK == 576 || DQK == 512, "row width");
+    static_assert(DV % 32 == 0 && DV <= kDLat, "value width");
+    static_assert(BK == 32 || BK == 64, "tile");
+};
+
+// d offset (within the wave's half of the row) of k-step s, lane group g, slot 0: steps are read
+// in pairs as 16 contiguous bytes; an odd last step uses the plain 8-byte layout.
+template <int KSTEPS>
+__device__ __forceinline__ int kstep_offset(int s, int g) {
+    if (s < (KSTEPS & ~1)) return 64 * (s >> 1) + 16 * g + 8 * (s & 1);
+    return 32 * s + 8 * g;
 }
 
 template <int BK, int DQK, int DV, bool DIRECT>
-__global__ void __launch_bounds__(128) mla_split_kernel(const MlaSplitArgs a) {
+__global__ void __launch_bounds__(256, 2) mla_split_kernel(const MlaSplitArgs a) {
     using T = MlaTile<BK, DQK, DV>;
-    constexpr int KPT = T::kKeysPerThread;
-    constexpr int XPT = T::kExtraPerThread > 0 ? T::kExtraPerThread : 1;
-    constexpr int NPV = T::kPvSteps;
+    constexpr int IPT = T::kItemsPerThread;
+    constexpr int NSB = T::kSBlocks;
 
     __shared__ __attribute__((aligned(16))) uint8_t lds[T::kLdsBytes];
     uint8_t *const kbuf = lds;
-    uint8_t *const vbuf = lds + T::kKBytes;
+    f32x4 *const sx = reinterpret_cast<f32x4 *>(lds + T::kKBytes);
 
     const int logical = xcd_logical_block(blockIdx.x, a.total_ctas);
     if (logical < 0) return;
@@ -95,16 +106,18 @@ __global__ void __launch_bounds__(128) mla_split_kernel(const MlaSplitArgs a) {
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6, grp = lane >> 4, col = lane & 15;
+    const int rg = wave & 1, hf = wave >> 1;
 
     // The query row whose column this lane holds.
-    const int r_in = row_lo + wave * 16 + col;
+    const int r_in = row_lo + rg * 16 + col;
     const bool row_ok = r_in < a.rows_per_req;
     const int t = row_ok ? r_in / a.H : 0;
     const int h = row_ok ? r_in - t * a.H : 0;
     const int row_end = row_ok ? min(max(0, S - a.q_len + t + 1), k1) : k0;
-    const bool wave_active = row_lo + wave * 16 < a.rows_per_req;
+    const bool pair_active = row_lo + rg * 16 < a.rows_per_req;
 
-    // Q^T fragments (MFMA B operand): lane holds query row `col`, d = 32 s + 8 grp .. +7.
+    // Q^T fragments (MFMA B operand) for this wave's half of the contraction.
+    const int dbase = hf * T::kHalfD;
     bf16x8 qf[T::kKSteps];
     {
         const int64_t tok = int64_t(b) * a.q_len + t;
@@ -112,7 +125,7 @@ __global__ void __launch_bounds__(128) mla_split_kernel(const MlaSplitArgs a) {
         const uint16_t *qp = a.q_pe + tok * a.qpe_st_tok + int64_t(h) * a.qpe_st_head;
 #pragma unroll
         for (int s = 0; s < T::kKSteps; ++s) {
-            const int d = 32 * s + 8 * grp;
+            const int d = dbase + kstep_offset<T::kKSteps>(s, grp);
             uint4 v = make_uint4(0, 0, 0, 0);
             if (row_ok)
                 v = d < T::kDLat ? *reinterpret_cast<const uint4 *>(ql + d)
@@ -126,89 +139,34 @@ __global__ void __launch_bounds__(128) mla_split_kernel(const MlaSplitArgs a) {
 #pragma unroll
     for (int v = 0; v < T::kVBlocks; ++v) oacc[v] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // Gather mapping: thread (c, kg) moves 16-byte chunk c of the first 512 bytes of the KPT keys
-    // at tile positions kg*KPT .. kg*KPT+KPT-1, plus XPT chunks past 512 bytes (576-wide rows).
-    const int c = tid & 31, kg = tid >> 5;
-    uint4 st_main[KPT];
-    uint4 st_extra[XPT];
-    int idx_main[KPT];
-    int idx_extra[XPT];
-
-    auto load_indices = [&](int tile) {
+    // Gather: item i = tid + 256 u is chunk (i % kChunks) of tile key (i / kChunks).
+    uint4 stg[IPT];
+    int idx[IPT];
+    auto load_indices = [&](int tile) {   // branch-free: clamp to a valid key, then mask
         const int tb = k0 + tile * BK;
 #pragma unroll
-        for (int u = 0; u < KPT; ++u) {
-            const int k = tb + key_of_position(kg * KPT + u);
-            idx_main[u] = k < k1 ? a.kv_indices[base + k] : -1;
-        }
-        if (T::kExtraPerThread > 0) {
-#pragma unroll
-            for (int x = 0; x < XPT; ++x) {
-                const int item = tid + x * T::kThreads;
-                const int k = tb + item / T::kExtraChunks;
-                idx_extra[x] = k < k1 ? a.kv_indices[base + k] : -1;
-            }
+        for (int u = 0; u < IPT; ++u) {
+            const int item = min(tid + u * T::kThreads, T::kItems - 1);
+            const int k = tb + item / T::kChunks;
+            const int slot = a.kv_indices[base + min(k, k1 - 1)];
+            idx[u] = (tid + u * T::kThreads < T::kItems && k < k1) ? slot : -1;
         }
     };
     auto load_rows = [&]() {
 #pragma unroll
-        for (int u = 0; u < KPT; ++u) {
-            st_main[u] = make_uint4(0, 0, 0, 0);
-            if (idx_main[u] >= 0)
-                st_main[u] = *reinterpret_cast<const uint4 *>(
-                    a.kv + int64_t(idx_main[u]) * a.kv_stride + 16 * c);
-        }
-        if (T::kExtraPerThread > 0) {
-#pragma unroll
-            for (int x = 0; x < XPT; ++x) {
-                const int item = tid + x * T::kThreads;
-                const int ch = 32 + item % T::kExtraChunks;
-                st_extra[x] = make_uint4(0, 0, 0, 0);
-                if (idx_extra[x] >= 0)
-                    st_extra[x] = *reinterpret_cast<const uint4 *>(
-                        a.kv + int64_t(idx_extra[x]) * a.kv_stride + 16 * ch);
-            }
+        for (int u = 0; u < IPT; ++u) {
+            const int item = tid + u * T::kThreads;
+            const int64_t off = int64_t(idx[u] < 0 ? 0 : idx[u]) * a.kv_stride + 16 * (item % T::kChunks);
+            const uint4 v = *reinterpret_cast<const uint4 *>(a.kv + off);
+            stg[u] = idx[u] < 0 ? make_uint4(0, 0, 0, 0) : v;   // padding keys hold zeros
         }
     };
     auto store_tile = [&]() {
-        // K, row-major in natural key order (two 8-byte writes: rows are 8-byte aligned).
 #pragma unroll
-        for (int u = 0; u < KPT; ++u) {
-            uint2 *dst = reinterpret_cast<uint2 *>(kbuf + key_of_position(kg * KPT + u) * T::kKStride + 16 * c);
-            dst[0] = make_uint2(st_main[u].x, st_main[u].y);
-            dst[1] = make_uint2(st_main[u].z, st_main[u].w);
-        }
-        if (T::kExtraPerThread > 0) {
-#pragma unroll
-            for (int x = 0; x < XPT; ++x) {
-                const int item = tid + x * T::kThreads;
-                const int key = item / T::kExtraChunks;
-                const int ch = 32 + item % T::kExtraChunks;
-                uint2 *dst = reinterpret_cast<uint2 *>(kbuf + key * T::kKStride + 16 * ch);
-                dst[0] = make_uint2(st_extra[x].x, st_extra[x].y);
-                dst[1] = make_uint2(st_extra[x].z, st_extra[x].w);
-            }
-        }
-        // V^T: 4x4 byte transposes turn (4 keys x 16 values) into (16 values x 4 keys).
-        if (c < T::kVChunks) {
-#pragma unroll
-            for (int pg = 0; pg < KPT / 8; ++pg) {
-                const int p0 = kg * KPT + 8 * pg;
-                const int kb = p0 >> 5, g8 = (p0 & 31) >> 3;
-                uint32_t y[2][16];
-#pragma unroll
-                for (int qq = 0; qq < 2; ++qq) {
-                    const uint4 *x = st_main + 8 * pg + 4 * qq;
-                    transpose4x4_bytes(x[0].x, x[1].x, x[2].x, x[3].x, y[qq][0], y[qq][1], y[qq][2], y[qq][3]);
-                    transpose4x4_bytes(x[0].y, x[1].y, x[2].y, x[3].y, y[qq][4], y[qq][5], y[qq][6], y[qq][7]);
-                    transpose4x4_bytes(x[0].z, x[1].z, x[2].z, x[3].z, y[qq][8], y[qq][9], y[qq][10], y[qq][11]);
-                    transpose4x4_bytes(x[0].w, x[1].w, x[2].w, x[3].w, y[qq][12], y[qq][13], y[qq][14], y[qq][15]);
-                }
-#pragma unroll
-                for (int j = 0; j < 16; ++j)
-                    *reinterpret_cast<uint2 *>(vbuf + vt_offset<NPV>(c, kb, g8, j)) =
-                        make_uint2(y[0][j], y[1][j]);
-            }
+        for (int u = 0; u < IPT; ++u) {
+            const int item = tid + u * T::kThreads;
+            if (item < T::kItems)
+                *reinterpret_cast<uint4 *>(kbuf + tile_pos<BK>(item / T::kChunks, 16 * (item % T::kChunks))) = stg[u];
         }
     };
 
@@ -226,28 +184,48 @@ __global__ void __launch_bounds__(128) mla_split_kernel(const MlaSplitArgs a) {
             load_rows();
             if (it + 2 < ntiles) load_indices(it + 2);
         }
-        if (!wave_active) continue;
 
-        // S^T = K Q^T: block j covers keys 16j..16j+15; lane holds keys 16j+4grp+i of row col.
-        f32x4 sacc[T::kSBlocks];
+        // Partial S^T over this wave's half of the row: block j covers keys 16j..16j+15; lane
+        // holds keys 16j+4grp+i of row col.
+        f32x4 sacc[NSB];
+        if (pair_active) {
 #pragma unroll
-        for (int j = 0; j < T::kSBlocks; ++j) sacc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int j = 0; j < NSB; ++j) sacc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int s = 0; s < T::kKSteps; ++s) {
+            for (int p = 0; p < T::kPairs; ++p) {
 #pragma unroll
-            for (int j = 0; j < T::kSBlocks; ++j) {
-                const uint2 raw = *reinterpret_cast<const uint2 *>(
-                    kbuf + (16 * j + col) * T::kKStride + 32 * s + 8 * grp);
-                sacc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp8x8_to_bf16x8(raw.x, raw.y),
-                                                                  qf[s], sacc[j], 0, 0, 0);
+                for (int j = 0; j < NSB; ++j) {
+                    const uint4 raw = *reinterpret_cast<const uint4 *>(
+                        kbuf + tile_pos<BK>(16 * j + col, dbase + 64 * p + 16 * grp));
+                    sacc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp8x8_to_bf16x8(raw.x, raw.y),
+                                                                      qf[2 * p], sacc[j], 0, 0, 0);
+                    sacc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp8x8_to_bf16x8(raw.z, raw.w),
+                                                                      qf[2 * p + 1], sacc[j], 0, 0, 0);
+                }
             }
+            if (T::kKSteps & 1) {
+                constexpr int s = T::kKSteps - 1;
+#pragma unroll
+                for (int j = 0; j < NSB; ++j) {
+                    const uint2 raw = *reinterpret_cast<const uint2 *>(
+                        kbuf + tile_pos<BK>(16 * j + col, dbase + 32 * s + 8 * grp));
+                    sacc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp8x8_to_bf16x8(raw.x, raw.y),
+                                                                      qf[s], sacc[j], 0, 0, 0);
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < NSB; ++j) sx[(wave * NSB + j) * 64 + lane] = sacc[j];
         }
+        __syncthreads();
+        if (!pair_active) continue;
+#pragma unroll
+        for (int j = 0; j < NSB; ++j) sacc[j] += sx[((wave ^ 2) * NSB + j) * 64 + lane];
 
-        // Online softmax in base 2 over this tile.
+        // Online softmax in base 2 over this tile (identical in both waves of the pair).
         const int tb = k0 + it * BK;
         float mx = kNegInf;
 #pragma unroll
-        for (int j = 0; j < T::kSBlocks; ++j)
+        for (int j = 0; j < NSB; ++j)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int k = tb + 16 * j + 4 * grp + i;
@@ -262,7 +240,7 @@ __global__ void __launch_bounds__(128) mla_split_kernel(const MlaSplitArgs a) {
         const float alpha = fast_exp2(m_run - m_use);
         float psum = 0.f;
 #pragma unroll
-        for (int j = 0; j < T::kSBlocks; ++j)
+        for (int j = 0; j < NSB; ++j)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const float p = fast_exp2(sacc[j][i] - m_use);
@@ -273,52 +251,64 @@ __global__ void __launch_bounds__(128) mla_split_kernel(const MlaSplitArgs a) {
         psum += xor_shuffle(psum, 32);
         l_run = l_run * alpha + psum;
         m_run = m_new;
+        if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
 #pragma unroll
-        for (int v = 0; v < T::kVBlocks; ++v) oacc[v] *= alpha;
+            for (int v = 0; v < T::kVBlocks; ++v) oacc[v] *= alpha;
+        }
 
-        // O^T += V^T P^T, 32 keys per step.
+        // O^T += V^T P^T, 32 keys per step.  Lane (s = 2k + h) of group g points the transposed
+        // read at key 4g+k (k < 4) or 16+4g+k-4 (k >= 4), value bytes 8h..8h+7 of the block; the
+        // read returns, for value column `col`, those 8 keys in k order -- the keys P^T holds in
+        // slots 0..7 of lane group g.
+        const int sl = lane & 15;
+        const int kk = sl >> 1;
+        const int key_in_step = kk < 4 ? 4 * grp + kk : 12 + 4 * grp + kk;
+        const int vbase = hf * T::kHalfV + 8 * (sl & 1);
 #pragma unroll
-        for (int kb = 0; kb < NPV; ++kb) {
+        for (int kb = 0; kb < T::kPvSteps; ++kb) {
             bf16x8 pf;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 pf[i] = static_cast<__bf16>(sacc[2 * kb][i]);
                 pf[4 + i] = static_cast<__bf16>(sacc[2 * kb + 1][i]);
             }
+            const int vkey = 32 * kb + key_in_step;
 #pragma unroll
             for (int v = 0; v < T::kVBlocks; ++v) {
-                const uint2 raw = *reinterpret_cast<const uint2 *>(vbuf + vt_offset<NPV>(v, kb, grp, col));
-                oacc[v] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp8x8_to_bf16x8(raw.x, raw.y), pf,
-                                                                  oacc[v], 0, 0, 0);
+                const int2v raw = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                    (__attribute__((address_space(3))) int2v *)(kbuf + tile_pos<BK>(vkey, vbase + 16 * v)));
+                oacc[v] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    fp8x8_to_bf16x8(uint32_t(raw.x), uint32_t(raw.y)), pf, oacc[v], 0, 0, 0);
             }
         }
     }
 
     if (!row_ok) return;
-    // Lane holds O^T[16v + 4grp + i][col]: four consecutive values of its row.
+    // Lane holds O^T[hf*DV/2 + 16v + 4grp + i][col]: four consecutive values of its row.
     const int64_t row = int64_t(b) * a.rows_per_req + r_in;
     const float inv = l_run > 0.f ? a.out_scale / l_run : 0.f;
     const float lse2 = l_run > 0.f ? m_run + __log2f(l_run) : kNegInf;
+    const int c0 = hf * T::kHalfV + 4 * grp;
     if (DIRECT) {
-        uint16_t *o = a.out + row * DV + 4 * grp;
+        uint16_t *o = a.out + row * DV + c0;
 #pragma unroll
         for (int v = 0; v < T::kVBlocks; ++v)
             *reinterpret_cast<uint2 *>(o + 16 * v) =
                 make_uint2(pack_bf16x2(oacc[v][0] * inv, oacc[v][1] * inv),
                            pack_bf16x2(oacc[v][2] * inv, oacc[v][3] * inv));
-        if (grp == 0 && a.lse2_out) a.lse2_out[row] = lse2;
+        if (hf == 0 && grp == 0 && a.lse2_out) a.lse2_out[row] = lse2;
     } else {
-        float *o = a.part_o + (row * a.np + part) * DV + 4 * grp;
+        float *o = a.part_o + (row * a.np + part) * DV + c0;
 #pragma unroll
         for (int v = 0; v < T::kVBlocks; ++v)
             *reinterpret_cast<f32x4 *>(o + 16 * v) = oacc[v] * inv;
-        if (grp == 0) a.part_lse2[row * a.np + part] = lse2;
+        if (hf == 0 && grp == 0) a.part_lse2[row * a.np + part] = lse2;
     }
 }
 
 template <int BK, int DQK, int DV>
 hipError_t launch_shape(const MlaSplitArgs &a, bool direct, hipStream_t s) {
-    const dim3 grid(xcd_grid_size(a.total_ctas)), block(128);
+    const dim3 grid(xcd_grid_size(a.total_ctas)), block(256);
     if (direct)
         hipLaunchKernelGGL((mla_split_kernel<BK, DQK, DV, true>), grid, block, 0, s, a);
     else

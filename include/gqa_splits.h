@@ -197,6 +197,10 @@ int fp8_e4m3_to_bf16(const void *in, int64_t n, void *out, gqa_stream_t s);
 /* Static description of a status code. */
 const char *status_string(int status);
 
+/* Text of the HIP error behind the calling thread's most recent GQA_ERR_LAUNCH_FAILED ("" if
+ * none); valid until the thread's next failing call. */
+const char *last_error_detail(void);
+
 #ifdef __cplusplus
 }
 #endif

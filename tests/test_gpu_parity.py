@@ -10,8 +10,8 @@ import torch
 import gqa_plan_splits_amd as g
 import oracle
 import workloads
-from gpu_util import (compare, gqa_problem, log, mla_problem, oracle_gqa, oracle_mla, run_decode,
-                      sample_rows)
+from gpu_util import (LSE_RTOL, OUT_ATOL, OUT_REL, compare, gqa_problem, log, mla_problem,
+                      oracle_gqa, oracle_mla, run_decode, sample_rows)
 
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
@@ -133,8 +133,10 @@ def test_mla_split_partials_match_oracle_on_key_ranges():
             if e <= a:
                 assert np.all(got_l == -np.inf) and np.all(got_o == 0)
                 continue
-            assert np.abs(got_o - ro).max() <= 1e-3 * max(1.0, np.abs(ro).max())
-            assert np.all(np.abs(got_l - rl) <= 1e-4 * np.maximum(1, np.abs(rl)))
+            # the same bar as every output (fp32 partials; bf16 rounding of P bounds the error)
+            err = np.abs(got_o - ro).max()
+            assert err <= OUT_ATOL and err <= OUT_REL * np.abs(ro).max()
+            assert np.all(np.abs(got_l - rl) <= LSE_RTOL * np.maximum(1, np.abs(rl)))
 
 
 def test_mla_split_invariance_and_determinism():
@@ -242,8 +244,10 @@ def test_gqa_ragged_all_rows(Hq, Hkv, q_len, np_, bk):
 
 @pytest.mark.parametrize("page_size", [8, 32, 64])
 def test_gqa_page_sizes(page_size):
-    inp = workloads.gqa_inputs(B=3, Hq=16, Hkv=2, D=128, page_size=page_size, seq_lens=[333, 64, 1000],
-                               num_pages=100, seed=41, device=DEV)
+    lens = [333, 64, 1000]
+    pages = sum(-(-L // page_size) for L in lens)
+    inp = workloads.gqa_inputs(B=3, Hq=16, Hkv=2, D=128, page_size=page_size, seq_lens=lens,
+                               num_pages=pages + 7, seed=41, device=DEV)
     out, lse = run_decode(gqa_problem(inp), 128, 4, 32)
     torch.cuda.synchronize()
     ref_o, ref_l = oracle_gqa(inp)
