@@ -37,6 +37,7 @@ namespace gqa {
 namespace {
 
 typedef int int2v __attribute__((ext_vector_type(2)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 // Byte offset of byte d of tile key `key` (see the layout note above).
 template <int BK>
@@ -49,9 +50,8 @@ template <int BK, int DQK, int DV>
 struct MlaTile {
     static constexpr int kThreads = 256;
     static constexpr int kDLat = DQK - 64;             // latent width; V = first DV columns
-    static constexpr int kHalfD = DQK / 2;             // QK contraction per wave
-    static constexpr int kKSteps = kHalfD / 32;        // MFMA K-steps per wave (9 or 8)
-    static constexpr int kPairs = kKSteps / 2;         // steps read as 16-byte pairs
+    static constexpr int kF8Chunks = 2;                // 128-wide fp8 QK chunks per wave
+    static constexpr int kRopeSteps = (DQK - 512) / 32;  // bf16 k-steps past 512 bytes (wave 2/3)
     static constexpr int kHalfV = DV / 2;              // output columns per wave
     static constexpr int kVBlocks = kHalfV / 16;       // 16 or 14
     static constexpr int kSBlocks = BK / 16;           // 16-key score blocks per tile
@@ -67,12 +67,12 @@ struct MlaTile {
     static_assert(BK == 32 || BK == 64, "tile");
 };
 
-// d offset (within the wave's half of the row) of k-step s, lane group g, slot 0: steps are read
-// in pairs as 16 contiguous bytes; an odd last step uses the plain 8-byte layout.
-template <int KSTEPS>
-__device__ __forceinline__ int kstep_offset(int s, int g) {
-    if (s < (KSTEPS & ~1)) return 64 * (s >> 1) + 16 * g + 8 * (s & 1);
-    return 32 * s + 8 * g;
+// Loads 8 bf16 query values at d (< DQK) of one row: the latent part from q, the rope part from
+// q_pe.  8-element pieces never straddle the boundary (it is a multiple of 8).
+template <int DLAT>
+__device__ __forceinline__ u32x4 load_q8(const uint16_t *ql, const uint16_t *qp, int d) {
+    return d < DLAT ? *reinterpret_cast<const u32x4 *>(ql + d)
+                    : *reinterpret_cast<const u32x4 *>(qp + (d - DLAT));
 }
 
 template <int BK, int DQK, int DV, bool DIRECT>
@@ -116,21 +116,63 @@ __global__ void __launch_bounds__(256, 2) mla_split_kernel(const MlaSplitArgs a)
     const int row_end = row_ok ? min(max(0, S - a.q_len + t + 1), k1) : k0;
     const bool pair_active = row_lo + rg * 16 < a.rows_per_req;
 
-    // Q^T fragments (MFMA B operand) for this wave's half of the contraction.
-    const int dbase = hf * T::kHalfD;
-    bf16x8 qf[T::kKSteps];
+    // Q^T for the fp8 score MFMA (v_mfma_scale_f32_16x16x128_f8f6f4, unit scales): this wave's
+    // two 128-wide chunks of the row (d = 256 hf .. 256 hf + 255).  Lane (col, grp) holds
+    // d = 128 i + 32 grp .. +31 of chunk i.  A bf16 value has 8 significant bits, so with the row
+    // scaled by a power of two into [128, 256) it is the sum of two e4m3 values (hi = nearest,
+    // lo = the exact remainder) except for elements below 2^-12 of the row maximum, whose
+    // remainders fall under e4m3's subnormal step.  K is used as stored (fp8), so no K value is
+    // converted.  The 64-wide rope tail of 576-byte rows runs on bf16 MFMA in waves 2/3.
+    const int dbase = hf * 256;
+    i32x8 qhi[T::kF8Chunks], qlo[T::kF8Chunks];
+    float qinv;
+    bf16x8 qrope[T::kRopeSteps > 0 ? T::kRopeSteps : 1];
     {
         const int64_t tok = int64_t(b) * a.q_len + t;
         const uint16_t *ql = a.q + tok * a.q_st_tok + int64_t(h) * a.q_st_head;
         const uint16_t *qp = a.q_pe + tok * a.qpe_st_tok + int64_t(h) * a.qpe_st_head;
+        float qv[T::kF8Chunks][32];
+        float mx = 0.f;
 #pragma unroll
-        for (int s = 0; s < T::kKSteps; ++s) {
-            const int d = dbase + kstep_offset<T::kKSteps>(s, grp);
-            uint4 v = make_uint4(0, 0, 0, 0);
-            if (row_ok)
-                v = d < T::kDLat ? *reinterpret_cast<const uint4 *>(ql + d)
-                                 : *reinterpret_cast<const uint4 *>(qp + (d - T::kDLat));
-            qf[s] = as_bf16x8(v);
+        for (int i = 0; i < T::kF8Chunks; ++i)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                u32x4 v = u32x4{0u, 0u, 0u, 0u};
+                if (row_ok) v = load_q8<T::kDLat>(ql, qp, dbase + 128 * i + 32 * grp + 8 * e);
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    qv[i][8 * e + 2 * w] = bf16_lo(v[w]);
+                    qv[i][8 * e + 2 * w + 1] = bf16_hi(v[w]);
+                    mx = fmaxf(mx, fmaxf(fabsf(qv[i][8 * e + 2 * w]), fabsf(qv[i][8 * e + 2 * w + 1])));
+                }
+            }
+        mx = fmaxf(mx, xor_shuffle(mx, 16));
+        mx = fmaxf(mx, xor_shuffle(mx, 32));
+        int ex = 0;
+        if (mx > 0.f) frexpf(mx, &ex);             // mx = f * 2^ex, f in [0.5, 1)
+        const float qs = ldexpf(1.f, 8 - ex);      // row maximum scaled into [128, 256)
+        qinv = ldexpf(1.f, ex - 8);
+#pragma unroll
+        for (int i = 0; i < T::kF8Chunks; ++i)
+#pragma unroll
+            for (int w = 0; w < 8; ++w) {
+                const float x0 = qv[i][4 * w] * qs, x1 = qv[i][4 * w + 1] * qs;
+                const float x2 = qv[i][4 * w + 2] * qs, x3 = qv[i][4 * w + 3] * qs;
+                int hi = __builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, 0, false);
+                hi = __builtin_amdgcn_cvt_pk_fp8_f32(x2, x3, hi, true);
+                typedef float f32x2 __attribute__((ext_vector_type(2)));
+                const f32x2 h01 = __builtin_amdgcn_cvt_pk_f32_fp8(hi, false);
+                const f32x2 h23 = __builtin_amdgcn_cvt_pk_f32_fp8(hi, true);
+                int lo = __builtin_amdgcn_cvt_pk_fp8_f32(x0 - h01.x, x1 - h01.y, 0, false);
+                lo = __builtin_amdgcn_cvt_pk_fp8_f32(x2 - h23.x, x3 - h23.y, lo, true);
+                qhi[i][w] = hi;
+                qlo[i][w] = lo;
+            }
+#pragma unroll
+        for (int s = 0; s < T::kRopeSteps; ++s) {
+            u32x4 v = u32x4{0u, 0u, 0u, 0u};
+            if (row_ok && hf == 1) v = load_q8<T::kDLat>(ql, qp, 512 + 32 * s + 8 * grp);
+            qrope[s] = as_bf16x8(v);
         }
     }
 
@@ -139,50 +181,44 @@ __global__ void __launch_bounds__(256, 2) mla_split_kernel(const MlaSplitArgs a)
 #pragma unroll
     for (int v = 0; v < T::kVBlocks; ++v) oacc[v] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // Gather: item i = tid + 256 u is chunk (i % kChunks) of tile key (i / kChunks).
-    uint4 stg[IPT];
+    // Gather: item i = tid + 256 u is chunk (i % kChunks) of tile key (i / kChunks).  Keys past
+    // the partition end are clamped to its last key: their rows are real (finite) data, their
+    // scores are masked to -inf and their probabilities are 0, so nothing is predicated -- the
+    // loads stay unconditional and the slot-id loads never stall the wave before the compute.
+    u32x4 stg[IPT];
     int idx[IPT];
-    auto load_indices = [&](int tile) {   // branch-free: clamp to a valid key, then mask
-        const int tb = k0 + tile * BK;
+    int ichunk[IPT], ikey[IPT];   // loop-invariant: chunk and tile key of each gather item
 #pragma unroll
-        for (int u = 0; u < IPT; ++u) {
-            const int item = min(tid + u * T::kThreads, T::kItems - 1);
-            const int k = tb + item / T::kChunks;
-            const int slot = a.kv_indices[base + min(k, k1 - 1)];
-            idx[u] = (tid + u * T::kThreads < T::kItems && k < k1) ? slot : -1;
-        }
-    };
-    auto load_rows = [&]() {
-#pragma unroll
-        for (int u = 0; u < IPT; ++u) {
-            const int item = tid + u * T::kThreads;
-            const int64_t off = int64_t(idx[u] < 0 ? 0 : idx[u]) * a.kv_stride + 16 * (item % T::kChunks);
-            const uint4 v = *reinterpret_cast<const uint4 *>(a.kv + off);
-            stg[u] = idx[u] < 0 ? make_uint4(0, 0, 0, 0) : v;   // padding keys hold zeros
-        }
-    };
-    auto store_tile = [&]() {
-#pragma unroll
-        for (int u = 0; u < IPT; ++u) {
-            const int item = tid + u * T::kThreads;
-            if (item < T::kItems)
-                *reinterpret_cast<uint4 *>(kbuf + tile_pos<BK>(item / T::kChunks, 16 * (item % T::kChunks))) = stg[u];
-        }
-    };
+    for (int u = 0; u < IPT; ++u) {
+        const int item = min(tid + u * T::kThreads, T::kItems - 1);
+        ichunk[u] = 16 * (item % T::kChunks);
+        ikey[u] = item / T::kChunks;
+    }
+    const bool last_item_ok = tid + (IPT - 1) * T::kThreads < T::kItems;
+
+#define GQA_LOAD_INDICES(tile)                                                                \
+    _Pragma("unroll") for (int u = 0; u < IPT; ++u)                                           \
+        idx[u] = a.kv_indices[base + min(k0 + (tile) * BK + ikey[u], k1 - 1)];
+#define GQA_LOAD_ROWS()                                                                       \
+    _Pragma("unroll") for (int u = 0; u < IPT; ++u)                                           \
+        stg[u] = *reinterpret_cast<const u32x4 *>(a.kv + int64_t(idx[u]) * a.kv_stride + ichunk[u]);
 
     if (ntiles > 0) {
-        load_indices(0);
-        load_rows();
-        if (ntiles > 1) load_indices(1);
+        GQA_LOAD_INDICES(0)
+        GQA_LOAD_ROWS()
+        if (ntiles > 1) { GQA_LOAD_INDICES(1) }
     }
 
     for (int it = 0; it < ntiles; ++it) {
         __syncthreads();
-        store_tile();
+#pragma unroll
+        for (int u = 0; u < IPT; ++u)
+            if (u + 1 < IPT || last_item_ok)
+                *reinterpret_cast<u32x4 *>(kbuf + tile_pos<BK>(ikey[u], ichunk[u])) = stg[u];
         __syncthreads();
         if (it + 1 < ntiles) {
-            load_rows();
-            if (it + 2 < ntiles) load_indices(it + 2);
+            GQA_LOAD_ROWS()
+            if (it + 2 < ntiles) { GQA_LOAD_INDICES(it + 2) }
         }
 
         // Partial S^T over this wave's half of the row: block j covers keys 16j..16j+15; lane
@@ -191,26 +227,45 @@ __global__ void __launch_bounds__(256, 2) mla_split_kernel(const MlaSplitArgs a)
         if (pair_active) {
 #pragma unroll
             for (int j = 0; j < NSB; ++j) sacc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+            // the operands of two score blocks are read first, so the LDS latency is paid once
+            // per pair of blocks rather than once per MFMA
 #pragma unroll
-            for (int p = 0; p < T::kPairs; ++p) {
+            for (int j0 = 0; j0 < NSB; j0 += 2) {
+                i32x8 kraw[2][T::kF8Chunks];
 #pragma unroll
-                for (int j = 0; j < NSB; ++j) {
-                    const uint4 raw = *reinterpret_cast<const uint4 *>(
-                        kbuf + tile_pos<BK>(16 * j + col, dbase + 64 * p + 16 * grp));
-                    sacc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp8x8_to_bf16x8(raw.x, raw.y),
-                                                                      qf[2 * p], sacc[j], 0, 0, 0);
-                    sacc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp8x8_to_bf16x8(raw.z, raw.w),
-                                                                      qf[2 * p + 1], sacc[j], 0, 0, 0);
+                for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+                    for (int i = 0; i < T::kF8Chunks; ++i) {
+                        const int key = 16 * (j0 + jj) + col;
+                        const int d = dbase + 128 * i + 32 * grp;
+                        const u32x4 lo16 = *reinterpret_cast<const u32x4 *>(kbuf + tile_pos<BK>(key, d));
+                        const u32x4 hi16 = *reinterpret_cast<const u32x4 *>(kbuf + tile_pos<BK>(key, d + 16));
+                        kraw[jj][i] = i32x8{int(lo16.x), int(lo16.y), int(lo16.z), int(lo16.w),
+                                            int(hi16.x), int(hi16.y), int(hi16.z), int(hi16.w)};
+                    }
+#pragma unroll
+                for (int i = 0; i < T::kF8Chunks; ++i) {
+#pragma unroll
+                    for (int jj = 0; jj < 2; ++jj)
+                        sacc[j0 + jj] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                            kraw[jj][i], qhi[i], sacc[j0 + jj], 0, 0, 0, 127, 0, 127);
+#pragma unroll
+                    for (int jj = 0; jj < 2; ++jj)
+                        sacc[j0 + jj] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                            kraw[jj][i], qlo[i], sacc[j0 + jj], 0, 0, 0, 127, 0, 127);
                 }
-            }
-            if (T::kKSteps & 1) {
-                constexpr int s = T::kKSteps - 1;
 #pragma unroll
-                for (int j = 0; j < NSB; ++j) {
-                    const uint2 raw = *reinterpret_cast<const uint2 *>(
-                        kbuf + tile_pos<BK>(16 * j + col, dbase + 32 * s + 8 * grp));
-                    sacc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp8x8_to_bf16x8(raw.x, raw.y),
-                                                                      qf[s], sacc[j], 0, 0, 0);
+                for (int jj = 0; jj < 2; ++jj) sacc[j0 + jj] *= qinv;
+                if (T::kRopeSteps > 0 && hf == 1) {
+#pragma unroll
+                    for (int st = 0; st < T::kRopeSteps; ++st)
+#pragma unroll
+                        for (int jj = 0; jj < 2; ++jj) {
+                            const u32x2 raw = *reinterpret_cast<const u32x2 *>(
+                                kbuf + tile_pos<BK>(16 * (j0 + jj) + col, 512 + 32 * st + 8 * grp));
+                            sacc[j0 + jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                fp8x8_to_bf16x8(raw.x, raw.y), qrope[st], sacc[j0 + jj], 0, 0, 0);
+                        }
                 }
             }
 #pragma unroll
@@ -305,6 +360,9 @@ __global__ void __launch_bounds__(256, 2) mla_split_kernel(const MlaSplitArgs a)
         if (hf == 0 && grp == 0) a.part_lse2[row * a.np + part] = lse2;
     }
 }
+
+#undef GQA_LOAD_INDICES
+#undef GQA_LOAD_ROWS
 
 template <int BK, int DQK, int DV>
 hipError_t launch_shape(const MlaSplitArgs &a, bool direct, hipStream_t s) {
