@@ -131,6 +131,39 @@ class Case:
         return self.kv_bytes() + idx + q_bytes + writes
 
 
+SPLIT_SOURCES = ("mla_split.hip", "device_common.hpp", "kernels.hpp")
+
+
+def split_source_sha256():
+    """sha256 over the sources the MLA split kernel is compiled from, in a fixed order."""
+    import hashlib
+    h = hashlib.sha256()
+    for name in SPLIT_SOURCES:
+        with open(os.path.join(ROOT, "gqa_plan_splits_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per split launch from the committed rocprofv3 counter summary, scaled by the
+    plain-copy calibration recorded beside it; None unless the summary was taken on the current
+    kernel sources (their sha256 must match)."""
+    path = os.path.join(ROOT, "profiles", "mla_split_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        line = line.split("#", 1)[0].strip()
+        if "=" in line:
+            k, v = (x.strip() for x in line.split("=", 1))
+            vals[k] = v
+    if vals.get("kernel_source_sha256") != split_source_sha256():
+        return None
+    fetch = float(vals["fetch_kib_per_dispatch"]) * float(vals["copy_bytes"]) / float(vals["copy_fetch_kib"])
+    write = float(vals["write_kib_per_dispatch"]) * float(vals["copy_bytes"]) / float(vals["copy_write_kib"])
+    return int(fetch + write)
+
+
 def time_events(fn, n, stream):
     """Average ms per call of fn over n calls, HIP events recorded on `stream`."""
     import torch
@@ -281,7 +314,8 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": (measured_traffic()
+                        if case.is_mla and args.workload == "mla_h64_b16_s131072_q1" else None),
             "algorithmic_bytes": alg,
             "avg_launch_us": round(ms_split * 1e3, 2),
         },
