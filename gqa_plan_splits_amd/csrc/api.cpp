@@ -117,10 +117,13 @@ int resolve_plan(const gqa_decode_problem *p, const Derived &d, int64_t np_or_0,
 
 int launch_split(const gqa_decode_problem *p, const Derived &d, int64_t np, int bk,
                  float *part_o, float *part_lse2, void *out, float *lse2_out, hipStream_t s) {
-    const int64_t total = p->batch * np * d.cta_rows;
-    if (total > (int64_t(1) << 30)) return GQA_ERR_UNSUPPORTED;
     const bool direct = out != nullptr;
     if (d.is_mla) {
+        // the kernel's own row blocks (the planner's 32-row CTA count only sizes the split)
+        const int64_t rpc = gqa::mla_rows_per_cta();
+        const int64_t row_blocks = (d.rows_per_req + rpc - 1) / rpc;
+        const int64_t total = p->batch * np * row_blocks;
+        if (total > (int64_t(1) << 30)) return GQA_ERR_UNSUPPORTED;
         gqa::MlaSplitArgs a;
         a.q = static_cast<const uint16_t *>(p->q);
         a.q_st_tok = p->q_stride_tok;
@@ -137,17 +140,20 @@ int launch_split(const gqa_decode_problem *p, const Derived &d, int64_t np, int 
         a.H = int32_t(p->num_heads);
         a.np = int32_t(np);
         a.rows_per_req = int32_t(d.rows_per_req);
-        a.row_blocks = int32_t(d.cta_rows);
+        a.row_blocks = int32_t(row_blocks);
         a.total_ctas = int32_t(total);
+        a.block_k = bk;
         a.score_scale = p->scale * p->kv_scale * kLog2e;
         a.out_scale = p->kv_scale;
         a.part_o = part_o;
         a.part_lse2 = part_lse2;
         a.out = static_cast<uint16_t *>(out);
         a.lse2_out = lse2_out;
-        const hipError_t err = gqa::launch_mla_split(a, bk, int(p->d_qk), int(p->d_v), direct, s);
+        const hipError_t err = gqa::launch_mla_split(a, int(p->d_qk), int(p->d_v), direct, s);
         return launch_status(err, "mla split");
     } else {
+        const int64_t total = p->batch * np * d.cta_rows;
+        if (total > (int64_t(1) << 30)) return GQA_ERR_UNSUPPORTED;
         gqa::GqaSplitArgs a;
         a.q = static_cast<const uint16_t *>(p->q);
         a.q_st_tok = p->q_stride_tok;

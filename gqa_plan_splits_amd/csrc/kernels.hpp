@@ -18,6 +18,7 @@ struct MlaSplitArgs {
     int64_t kv_stride;            // bytes between rows
     const int32_t *kv_indices, *kv_indptr, *seq_lens;
     int32_t q_len, H, np, rows_per_req, row_blocks, total_ctas;
+    int32_t block_k;              // partition lengths are rounded up to a multiple of this
     float score_scale;            // scale * kv_scale * log2(e): scores in base-2 units
     float out_scale;              // kv_scale: the raw fp8 values are accumulated unscaled
     float *part_o;                // [rows, np, DV]
@@ -48,8 +49,9 @@ struct ReduceArgs {
 };
 
 // Launchers: return hipSuccess or the launch error.  All enqueue on `s` only.
-hipError_t launch_mla_split(const MlaSplitArgs &a, int block_k, int d_qk, int d_v, bool direct,
-                            hipStream_t s);
+// Query rows one MLA split CTA covers (row_blocks = ceil(rows per request / this)).
+int mla_rows_per_cta();
+hipError_t launch_mla_split(const MlaSplitArgs &a, int d_qk, int d_v, bool direct, hipStream_t s);
 hipError_t launch_gqa_split(const GqaSplitArgs &a, int block_k, int rows_per_cta, bool direct,
                             hipStream_t s);
 hipError_t launch_splitk_reduce(const ReduceArgs &a, hipStream_t s);

@@ -2,70 +2,96 @@
 //
 // What it computes (moonmath-amd README, "MLA decode"; Modular MAX planner page, MLA-style
 // bullet): every key row of the pool is one fused fp8 e4m3 row that serves as K (all DQK bytes)
-// and as V (its first DV bytes), dequantized with one per-tensor kv_scale.  A CTA packs 32 query
-// rows (BM = 32) of one request and walks one partition of that request's keys, writing the
+// and as V (its first DV bytes), dequantized with one per-tensor kv_scale.  A CTA owns up to 64
+// query rows of one request and walks one partition of that request's keys, writing the
 // partition's softmax-weighted mean of values and the base-2 log-sum-exp of its scores.
 //
-// Layout of the work:
-//   - 256 threads = 4 waves.  Waves 0/1 own query rows 0-15 / 16-31 of the CTA; waves 2/3 own
-//     the same rows.  For QK^T each pair splits the DQK contraction in halves and adds the two
-//     partial score tiles through LDS (both waves then hold identical scores); for PV each wave
-//     of the pair owns half of the DV output columns.  Each wave thus holds half of Q and half of
-//     the output accumulator, which keeps it near 160 VGPRs so two waves fit on every SIMD.
-//   - Keys are processed in tiles of BK (32 or 64).  The CTA gathers a tile (16 bytes per lane,
-//     consecutive lanes on consecutive chunks of a row, slot ids read a tile ahead) into
-//     registers one tile ahead of the compute, then writes it to LDS row-major, once.
-//   - QK^T (S^T = K Q^T) and PV (O^T = V^T P^T) run on v_mfma_f32_16x16x32_bf16.  K is read
-//     16 bytes per lane; V is read from the same row-major tile with ds_read_b64_tr_b8, which
-//     hands each lane 8 keys of one value column -- the K-major operand layout.  The fp8 bytes
-//     are converted to bf16 exactly as they are read; kv_scale is folded into the score scale and
-//     the output scale.
-//   - Each lane owns one query row's column of the score tile, so the row max / sum take two
-//     cross-lane exchanges and the online-softmax rescale is a per-lane multiply (skipped when no
-//     row's maximum moved).
+// Layout of the work (512 threads = 8 waves, one CTA per CU, two waves per SIMD):
+//   - Keys arrive in tiles of 64.  Each tile is copied straight from HBM into LDS with
+//     global_load_lds_dwordx4 (no register staging), three tiles ahead of the compute, into a
+//     ring of four LDS tile buffers.  The copies are issued from inline assembly and waited for
+//     with explicit vmcnt counts: the compiler cannot tell which LDS reads a direct copy feeds,
+//     and would otherwise drain every copy in flight before each LDS read.
+//   - QK^T: wave w computes the scores of key block kb = w % 2 (32 keys) for query-row quarter
+//     rq = w / 2 (16 rows) over the whole row width, on the block-scaled fp8 MFMA
+//     v_mfma_scale_f32_16x16x128_f8f6f4 with unit scales (the 64-wide rope tail of 576-byte rows
+//     on v_mfma_f32_16x16x32_fp8_fp8).  K is used as stored.  A bf16 query row, scaled by a power
+//     of two so its largest element lies in [128, 256), is the exact sum of two e4m3 vectors (hi =
+//     nearest, lo = remainder) except below e4m3's subnormal step; each product runs twice.
+//   - Softmax: each wave reduces its own 16 rows x 32 keys.  The running maximum is kept as an
+//     integer (the ceiling of the base-2 score), so probabilities produced by different waves, or
+//     in different tiles, differ by exact powers of two.  Probabilities are written to LDS as fp8
+//     hi/lo pairs of p * 2^8 (p <= 1), together with each (row, key block) maximum and two sums:
+//     of the quantized probabilities (the weights PV applies, which normalize the output) and of
+//     the exact ones (which give the log-sum-exp).
+//   - PV: wave w owns output columns 32w..32w+31 and 32(w+8).. for all 64 rows, on the 32x32x64
+//     block-scaled fp8 MFMA.  V^T is read from the fp8 tile with ds_read_b64_tr_b8 (no
+//     conversion); P^T comes from LDS, and the power of two that aligns each 32-key block with
+//     the row's running maximum is the MFMA's per-lane B scale.
 //
-// LDS tile layout (chunk-major, swizzled): 16-byte chunk c of tile key k sits in slot
-// c * BK + (k ^ 12 * bit4(k) ^ (c % 16)).  A score-operand read (16 consecutive keys, one chunk)
-// is then one contiguous 256-byte block; a transposed value read (keys 4g..4g+3 and 16+4g..
-// 16+4g+3 of a 32-key step) lands on 8 distinct 16-byte slots; and the gather's stores (one key,
-// consecutive chunks) land on distinct banks.  All three are free of bank conflicts, and the
-// tile needs no padding.
+// LDS tile layout: 16-byte chunk c of tile key k sits at c * 1024 + 16 * (k ^ 8 * (c % 2)).  A
+// direct copy writes 64 consecutive 16-byte slots, so one copy instruction moves chunk c of all 64
+// keys; a wave always copies chunks of one parity, hence one key per lane for the whole tile.
+// Score-operand reads (16 keys of one chunk), transposed value reads (8 keys x 16 bytes of two
+// neighbouring chunks) and the copies are all free of bank conflicts.
 #include "device_common.hpp"
 #include "kernels.hpp"
 
 namespace gqa {
 namespace {
 
-typedef int int2v __attribute__((ext_vector_type(2)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int int2v __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-// Byte offset of byte d of tile key `key` (see the layout note above).
-template <int BK>
-__device__ __forceinline__ int tile_pos(int key, int d) {
-    const int c = d >> 4;
-    return ((c * BK + (key ^ (((key >> 4) & 1) * 12) ^ (c & 15))) << 4) + (d & 15);
-}
+constexpr int kBM = 64;            // query rows per CTA
+constexpr int kBK = 64;            // keys per tile
+constexpr int kThreads = 512;
+constexpr int kBufs = 4;           // LDS tile ring
+constexpr int kNoMax = -(1 << 20); // integer maximum of a block with no visible key
 
-template <int BK, int DQK, int DV>
-struct MlaTile {
-    static constexpr int kThreads = 256;
-    static constexpr int kDLat = DQK - 64;             // latent width; V = first DV columns
-    static constexpr int kF8Chunks = 2;                // 128-wide fp8 QK chunks per wave
-    static constexpr int kRopeSteps = (DQK - 512) / 32;  // bf16 k-steps past 512 bytes (wave 2/3)
-    static constexpr int kHalfV = DV / 2;              // output columns per wave
-    static constexpr int kVBlocks = kHalfV / 16;       // 16 or 14
-    static constexpr int kSBlocks = BK / 16;           // 16-key score blocks per tile
-    static constexpr int kPvSteps = BK / 32;           // 32-key PV steps per tile
-    static constexpr int kChunks = DQK / 16;           // 16-byte chunks per key row
-    static constexpr int kItems = BK * kChunks;        // chunks per tile
-    static constexpr int kItemsPerThread = (kItems + kThreads - 1) / kThreads;
-    static constexpr int kKBytes = BK * DQK;
-    static constexpr int kSxBytes = 4 * kSBlocks * 64 * 16;   // partial score exchange
-    static constexpr int kLdsBytes = kKBytes + kSxBytes;
+template <int DQK, int DV>
+struct MlaShape {
+    static constexpr int kChunks = DQK / 16;              // 16-byte chunks per key row
+    static constexpr int kTileBytes = kBK * DQK;
+    static constexpr int kRopeSteps = (DQK - 512) / 32;   // 32-wide fp8 steps past byte 512
+    static constexpr int kDvBlocks = DV / 32;             // 32-column output blocks
+    static constexpr int kPOff = kBufs * kTileBytes;      // P hi [64 rows][64 keys], then P lo
+    // per row: m0, m1 (int); quantized sums q0, q1; exact sums e0, e1 (float); two pad words
+    static constexpr int kMlOff = kPOff + 2 * kBM * kBK;
+    static constexpr int kIdxOff = kMlOff + kBM * 32;     // per wave, two slots of 64 slot ids
+    static constexpr int kLdsBytes = kIdxOff + 8 * 2 * 256;
     static_assert(DQK == 576 || DQK == 512, "row width");
-    static_assert(DV % 32 == 0 && DV <= kDLat, "value width");
-    static_assert(BK == 32 || BK == 64, "tile");
+    static_assert(DV % 32 == 0 && DV <= 512, "value width");
+    static_assert(kLdsBytes <= 160 * 1024, "LDS");
 };
+
+__device__ __forceinline__ int tpos(int c, int key) { return c * 1024 + ((key ^ ((c & 1) << 3)) << 4); }
+
+// Direct HBM -> LDS copy of 16 bytes per lane: lane L's bytes land at m0 + OFF + 16 L; the
+// immediate offset applies to the global address too.
+template <int OFF>
+__device__ __forceinline__ void copy16(const uint8_t *g, uint32_t m0) {
+    asm volatile("global_load_lds_dwordx4 %0, off offset:%1" ::"v"(g), "i"(OFF), "{m0}"(m0) : "memory");
+}
+// Same, 4 bytes per lane (lane L -> m0 + 4 L).
+__device__ __forceinline__ void copy4(const int32_t *g, uint32_t m0) {
+    asm volatile("global_load_lds_dword %0, off" ::"v"(g), "{m0}"(m0) : "memory");
+}
+// s_waitcnt vmcnt(n) for a wave-uniform n in [0, 15].
+__device__ __forceinline__ void wait_vmem(int n) {
+    switch (n) {
+#define GQA_WAIT_CASE(k) \
+    case k: asm volatile("s_waitcnt vmcnt(" #k ")" ::: "memory"); break;
+        GQA_WAIT_CASE(0) GQA_WAIT_CASE(1) GQA_WAIT_CASE(2) GQA_WAIT_CASE(3) GQA_WAIT_CASE(4)
+        GQA_WAIT_CASE(5) GQA_WAIT_CASE(6) GQA_WAIT_CASE(7) GQA_WAIT_CASE(8) GQA_WAIT_CASE(9)
+        GQA_WAIT_CASE(10) GQA_WAIT_CASE(11) GQA_WAIT_CASE(12) GQA_WAIT_CASE(13) GQA_WAIT_CASE(14)
+#undef GQA_WAIT_CASE
+        default: asm volatile("s_waitcnt vmcnt(15)" ::: "memory"); break;
+    }
+}
 
 // Loads 8 bf16 query values at d (< DQK) of one row: the latent part from q, the rope part from
 // q_pe.  8-element pieces never straddle the boundary (it is a multiple of 8).
@@ -75,315 +101,400 @@ __device__ __forceinline__ u32x4 load_q8(const uint16_t *ql, const uint16_t *qp,
                     : *reinterpret_cast<const u32x4 *>(qp + (d - DLAT));
 }
 
-template <int BK, int DQK, int DV, bool DIRECT>
-__global__ void __launch_bounds__(256, 2) mla_split_kernel(const MlaSplitArgs a) {
-    using T = MlaTile<BK, DQK, DV>;
-    constexpr int IPT = T::kItemsPerThread;
-    constexpr int NSB = T::kSBlocks;
+// x (|x| < 448) -> (hi, lo) e4m3 quads: hi = nearest, lo = nearest to the remainder.
+__device__ __forceinline__ void split_fp8x4(float x0, float x1, float x2, float x3, int &hi, int &lo) {
+    hi = __builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, 0, false);
+    hi = __builtin_amdgcn_cvt_pk_fp8_f32(x2, x3, hi, true);
+    const f32x2 h01 = __builtin_amdgcn_cvt_pk_f32_fp8(hi, false);
+    const f32x2 h23 = __builtin_amdgcn_cvt_pk_f32_fp8(hi, true);
+    lo = __builtin_amdgcn_cvt_pk_fp8_f32(x0 - h01.x, x1 - h01.y, 0, false);
+    lo = __builtin_amdgcn_cvt_pk_fp8_f32(x2 - h23.x, x3 - h23.y, lo, true);
+}
 
-    __shared__ __attribute__((aligned(16))) uint8_t lds[T::kLdsBytes];
-    uint8_t *const kbuf = lds;
-    f32x4 *const sx = reinterpret_cast<f32x4 *>(lds + T::kKBytes);
+template <int DQK, int DV, bool DIRECT>
+__global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const MlaSplitArgs a) {
+    using T = MlaShape<DQK, DV>;
+    constexpr int DLAT = DQK - 64;
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[T::kLdsBytes];
 
     const int logical = xcd_logical_block(blockIdx.x, a.total_ctas);
     if (logical < 0) return;
-    const int rb = logical % a.row_blocks;
+    const int rblk = logical % a.row_blocks;
     const int rest = logical / a.row_blocks;
     const int part = rest % a.np;
     const int b = rest / a.np;
 
-    // Keys of this partition: ceil(S / np) rounded up to the tile, the last ones possibly empty;
-    // no row of the block sees past the block's widest draft window.
+    // Keys of this partition: ceil(S / np) rounded up to block_k, the last ones possibly empty;
+    // no row of the block sees past the block's latest draft token.
     const int S = a.seq_lens[b];
     const int base = a.kv_indptr[b];
-    const int chunk = ((S + a.np - 1) / a.np + BK - 1) / BK * BK;
+    const int chunk = ((S + a.np - 1) / a.np + a.block_k - 1) / a.block_k * a.block_k;
     const int k0 = part * chunk;
-    const int row_lo = rb * 32;
-    const int row_last = min(row_lo + 32, a.rows_per_req) - 1;
-    const int block_keys = max(0, S - a.q_len + row_last / a.H + 1);
-    const int k1 = min(block_keys, k0 + chunk);
-    const int ntiles = k1 > k0 ? (k1 - k0 + BK - 1) / BK : 0;
+    const int row0 = rblk * kBM;
+    const int nrows = min(kBM, a.rows_per_req - row0);
+    const int k1 = min(max(0, S - a.q_len + (row0 + nrows - 1) / a.H + 1), k0 + chunk);
+    const int kfull = min(k1, max(0, S - a.q_len + row0 / a.H + 1));  // keys every row sees
+    const int ntiles = k1 > k0 ? (k1 - k0 + kBK - 1) / kBK : 0;
 
-    const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6, grp = lane >> 4, col = lane & 15;
-    const int rg = wave & 1, hf = wave >> 1;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int kb = wave & 1, rq = wave >> 1;
+    const int n16 = lane & 15, g = lane >> 4;   // 16x16 operand / result coordinates
+    const int n32 = lane & 31, h = lane >> 5;   // 32x32 operand / result coordinates
 
-    // The query row whose column this lane holds.
-    const int r_in = row_lo + rg * 16 + col;
-    const bool row_ok = r_in < a.rows_per_req;
-    const int t = row_ok ? r_in / a.H : 0;
-    const int h = row_ok ? r_in - t * a.H : 0;
-    const int row_end = row_ok ? min(max(0, S - a.q_len + t + 1), k1) : k0;
-    const bool pair_active = row_lo + rg * 16 < a.rows_per_req;
-
-    // Q^T for the fp8 score MFMA (v_mfma_scale_f32_16x16x128_f8f6f4, unit scales): this wave's
-    // two 128-wide chunks of the row (d = 256 hf .. 256 hf + 255).  Lane (col, grp) holds
-    // d = 128 i + 32 grp .. +31 of chunk i.  A bf16 value has 8 significant bits, so with the row
-    // scaled by a power of two into [128, 256) it is the sum of two e4m3 values (hi = nearest,
-    // lo = the exact remainder) except for elements below 2^-12 of the row maximum, whose
-    // remainders fall under e4m3's subnormal step.  K is used as stored (fp8), so no K value is
-    // converted.  The 64-wide rope tail of 576-byte rows runs on bf16 MFMA in waves 2/3.
-    const int dbase = hf * 256;
-    i32x8 qhi[T::kF8Chunks], qlo[T::kF8Chunks];
-    float qinv;
-    bf16x8 qrope[T::kRopeSteps > 0 ? T::kRopeSteps : 1];
+    // ---- producer row (QK^T and softmax): row 16 rq + n16 of the block
+    const int prow = 16 * rq + n16;
+    const bool prow_ok = prow < nrows;
+    const bool producer = 16 * rq < nrows;
+    int p_end;   // keys visible to this row
+    float c_row; // base-2 score per unit of the raw product
+    i32x8 qhi[4], qlo[4];
+    long qrh[T::kRopeSteps > 0 ? T::kRopeSteps : 1], qrl[T::kRopeSteps > 0 ? T::kRopeSteps : 1];
     {
+        const int r = row0 + prow;
+        const int t = prow_ok ? r / a.H : 0;
+        const int hh = prow_ok ? r - t * a.H : 0;
+        p_end = prow_ok ? min(max(0, S - a.q_len + t + 1), k1) : k0;
         const int64_t tok = int64_t(b) * a.q_len + t;
-        const uint16_t *ql = a.q + tok * a.q_st_tok + int64_t(h) * a.q_st_head;
-        const uint16_t *qp = a.q_pe + tok * a.qpe_st_tok + int64_t(h) * a.qpe_st_head;
-        float qv[T::kF8Chunks][32];
+        const uint16_t *ql = a.q + tok * a.q_st_tok + int64_t(hh) * a.q_st_head;
+        const uint16_t *qp = a.q_pe + tok * a.qpe_st_tok + int64_t(hh) * a.qpe_st_head;
+        // lane (n16, g) holds d = 128 s + 32 g + e of step s, and d = 512 + 32 st + 8 g + e of
+        // rope step st
+        float qv[4][32];
+        float qr[T::kRopeSteps > 0 ? T::kRopeSteps : 1][8];
         float mx = 0.f;
 #pragma unroll
-        for (int i = 0; i < T::kF8Chunks; ++i)
+        for (int s = 0; s < 4; ++s)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 u32x4 v = u32x4{0u, 0u, 0u, 0u};
-                if (row_ok) v = load_q8<T::kDLat>(ql, qp, dbase + 128 * i + 32 * grp + 8 * e);
+                if (prow_ok) v = load_q8<DLAT>(ql, qp, 128 * s + 32 * g + 8 * e);
 #pragma unroll
                 for (int w = 0; w < 4; ++w) {
-                    qv[i][8 * e + 2 * w] = bf16_lo(v[w]);
-                    qv[i][8 * e + 2 * w + 1] = bf16_hi(v[w]);
-                    mx = fmaxf(mx, fmaxf(fabsf(qv[i][8 * e + 2 * w]), fabsf(qv[i][8 * e + 2 * w + 1])));
+                    qv[s][8 * e + 2 * w] = bf16_lo(v[w]);
+                    qv[s][8 * e + 2 * w + 1] = bf16_hi(v[w]);
+                    mx = fmaxf(mx, fmaxf(fabsf(qv[s][8 * e + 2 * w]), fabsf(qv[s][8 * e + 2 * w + 1])));
                 }
             }
+#pragma unroll
+        for (int st = 0; st < T::kRopeSteps; ++st) {
+            u32x4 v = u32x4{0u, 0u, 0u, 0u};
+            if (prow_ok) v = load_q8<DLAT>(ql, qp, 512 + 32 * st + 8 * g);
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                qr[st][2 * w] = bf16_lo(v[w]);
+                qr[st][2 * w + 1] = bf16_hi(v[w]);
+                mx = fmaxf(mx, fmaxf(fabsf(qr[st][2 * w]), fabsf(qr[st][2 * w + 1])));
+            }
+        }
         mx = fmaxf(mx, xor_shuffle(mx, 16));
         mx = fmaxf(mx, xor_shuffle(mx, 32));
         int ex = 0;
-        if (mx > 0.f) frexpf(mx, &ex);             // mx = f * 2^ex, f in [0.5, 1)
-        const float qs = ldexpf(1.f, 8 - ex);      // row maximum scaled into [128, 256)
-        qinv = ldexpf(1.f, ex - 8);
+        if (mx > 0.f) frexpf(mx, &ex);            // mx = f * 2^ex, f in [0.5, 1)
+        const float qs = ldexpf(1.f, 8 - ex);     // row maximum scaled into [128, 256)
+        c_row = a.score_scale * ldexpf(1.f, ex - 8);
 #pragma unroll
-        for (int i = 0; i < T::kF8Chunks; ++i)
+        for (int s = 0; s < 4; ++s)
 #pragma unroll
             for (int w = 0; w < 8; ++w) {
-                const float x0 = qv[i][4 * w] * qs, x1 = qv[i][4 * w + 1] * qs;
-                const float x2 = qv[i][4 * w + 2] * qs, x3 = qv[i][4 * w + 3] * qs;
-                int hi = __builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, 0, false);
-                hi = __builtin_amdgcn_cvt_pk_fp8_f32(x2, x3, hi, true);
-                typedef float f32x2 __attribute__((ext_vector_type(2)));
-                const f32x2 h01 = __builtin_amdgcn_cvt_pk_f32_fp8(hi, false);
-                const f32x2 h23 = __builtin_amdgcn_cvt_pk_f32_fp8(hi, true);
-                int lo = __builtin_amdgcn_cvt_pk_fp8_f32(x0 - h01.x, x1 - h01.y, 0, false);
-                lo = __builtin_amdgcn_cvt_pk_fp8_f32(x2 - h23.x, x3 - h23.y, lo, true);
-                qhi[i][w] = hi;
-                qlo[i][w] = lo;
+                int hi, lo;
+                split_fp8x4(qv[s][4 * w] * qs, qv[s][4 * w + 1] * qs, qv[s][4 * w + 2] * qs,
+                            qv[s][4 * w + 3] * qs, hi, lo);
+                qhi[s][w] = hi;
+                qlo[s][w] = lo;
             }
 #pragma unroll
-        for (int s = 0; s < T::kRopeSteps; ++s) {
-            u32x4 v = u32x4{0u, 0u, 0u, 0u};
-            if (row_ok && hf == 1) v = load_q8<T::kDLat>(ql, qp, 512 + 32 * s + 8 * grp);
-            qrope[s] = as_bf16x8(v);
+        for (int st = 0; st < T::kRopeSteps; ++st) {
+            int h0, l0, h1, l1;
+            split_fp8x4(qr[st][0] * qs, qr[st][1] * qs, qr[st][2] * qs, qr[st][3] * qs, h0, l0);
+            split_fp8x4(qr[st][4] * qs, qr[st][5] * qs, qr[st][6] * qs, qr[st][7] * qs, h1, l1);
+            qrh[st] = long(uint32_t(h0)) | (long(uint32_t(h1)) << 32);
+            qrl[st] = long(uint32_t(l0)) | (long(uint32_t(l1)) << 32);
         }
     }
 
-    float m_run = kNegInf, l_run = 0.f;
-    f32x4 oacc[T::kVBlocks];
+    // ---- consumer state (PV): rows 32 rb + n32, output blocks wave and wave + 8
+    constexpr int kMyBlocks = 2;
+    const bool has_blk1 = wave + 8 < T::kDvBlocks;
+    int mc[2] = {kNoMax, kNoMax};
+    float lc[2] = {0.f, 0.f};   // sum of applied (quantized) weights
+    float le[2] = {0.f, 0.f};   // exact sum, for the log-sum-exp
+    f32x16 oacc[2][kMyBlocks];
 #pragma unroll
-    for (int v = 0; v < T::kVBlocks; ++v) oacc[v] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    // Gather: item i = tid + 256 u is chunk (i % kChunks) of tile key (i / kChunks).  Keys past
-    // the partition end are clamped to its last key: their rows are real (finite) data, their
-    // scores are masked to -inf and their probabilities are 0, so nothing is predicated -- the
-    // loads stay unconditional and the slot-id loads never stall the wave before the compute.
-    u32x4 stg[IPT];
-    int idx[IPT];
-    int ichunk[IPT], ikey[IPT];   // loop-invariant: chunk and tile key of each gather item
+    for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-    for (int u = 0; u < IPT; ++u) {
-        const int item = min(tid + u * T::kThreads, T::kItems - 1);
-        ichunk[u] = 16 * (item % T::kChunks);
-        ikey[u] = item / T::kChunks;
-    }
-    const bool last_item_ok = tid + (IPT - 1) * T::kThreads < T::kItems;
+        for (int j = 0; j < kMyBlocks; ++j)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) oacc[rb][j][i] = 0.f;
 
-#define GQA_LOAD_INDICES(tile)                                                                \
-    _Pragma("unroll") for (int u = 0; u < IPT; ++u)                                           \
-        idx[u] = a.kv_indices[base + min(k0 + (tile) * BK + ikey[u], k1 - 1)];
-#define GQA_LOAD_ROWS()                                                                       \
-    _Pragma("unroll") for (int u = 0; u < IPT; ++u)                                           \
-        stg[u] = *reinterpret_cast<const u32x4 *>(a.kv + int64_t(idx[u]) * a.kv_stride + ichunk[u]);
+    // ---- tile copies.  Wave w copies chunks w, w + 8, ... of every tile; its lane L carries key
+    // L ^ 8 (w % 2), whose slot id it first copies into its own LDS index slot.
+    const int n_copy = (T::kChunks - wave + 7) >> 3;   // 5 or 4 copies per tile
+    const int my_key = lane ^ ((wave & 1) << 3);
+    const int32_t *const ibase = a.kv_indices + base;
+    const uint32_t lds_addr = uint32_t(reinterpret_cast<uintptr_t>(lds));
+    const int32_t *const idx_lds = reinterpret_cast<const int32_t *>(lds + T::kIdxOff) + wave * 128;
+    const uint64_t kv_stride = uint64_t(a.kv_stride);
+
+    auto issue_idx = [&](int tile) {
+        const int key = min(k0 + tile * kBK + my_key, k1 - 1);
+        copy4(ibase + key, lds_addr + T::kIdxOff + (wave * 2 + (tile & 1)) * 256);
+    };
+    auto issue_rows = [&](int tile) {
+        const int id = idx_lds[(tile & 1) * 64 + lane];
+        const uint8_t *row = a.kv + uint64_t(uint32_t(id)) * kv_stride + 16 * wave;
+        const uint32_t m0 = lds_addr + (tile & (kBufs - 1)) * T::kTileBytes + wave * 1024;
+        // copy u moves chunk wave + 8 u: LDS + 8 KiB, global + 128 bytes per step
+        copy16<0>(row, m0);
+        copy16<128>(row, m0 + 8192 - 128);
+        copy16<256>(row, m0 + 16384 - 256);
+        copy16<384>(row, m0 + 24576 - 384);
+        if (n_copy > 4) copy16<512>(row, m0 + 32768 - 512);
+    };
+    // Copies retire in issue order.  Per tile j (issue order): slot ids of j + 1, then rows of j.
+    // Before the rows of j + 3: the ids of j + 3 landed; after them came rows j + 2 and ids j + 4.
+    auto wait_ids = [&](int j) {
+        wait_vmem((j + 2 >= 0 && j + 2 < ntiles ? n_copy : 0) + (j + 4 < ntiles ? 1 : 0));
+    };
+    // Before compute on tile t + 1: its rows landed; after them came ids t + 3, rows t + 2,
+    // ids t + 4, rows t + 3.
+    auto wait_rows = [&](int t) {
+        wait_vmem((t + 3 < ntiles ? 1 + n_copy : 0) + (t + 2 < ntiles ? n_copy : 0) +
+                  (t + 4 < ntiles ? 1 : 0));
+    };
+
+    uint8_t *const P = lds + T::kPOff;
+    uint8_t *const ML = lds + T::kMlOff;
+
+    // PV for tile t (LDS buffer t % 4, probabilities of tile t in LDS).
+    auto pv = [&](int t) {
+        const uint8_t *tb = lds + (t & (kBufs - 1)) * T::kTileBytes;
+        i32x8 ph[2], pl[2];
+        int sc[2] = {0, 0};
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+            ph[rb] = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
+            pl[rb] = ph[rb];
+            if (32 * rb >= nrows) continue;
+            const int row = 32 * rb + n32;
+            const i32x4 ml = *reinterpret_cast<const i32x4 *>(ML + row * 32);
+            const f32x2 ex = *reinterpret_cast<const f32x2 *>(ML + row * 32 + 16);
+            const int m_new = max(mc[rb], max(ml.x, ml.y));
+            const float alpha = ldexpf(1.f, mc[rb] - m_new);
+            lc[rb] = lc[rb] * alpha + ldexpf(__int_as_float(ml.z), ml.x - m_new - 8) +
+                     ldexpf(__int_as_float(ml.w), ml.y - m_new - 8);
+            le[rb] = le[rb] * alpha + ldexpf(ex.x, ml.x - m_new - 8) + ldexpf(ex.y, ml.y - m_new - 8);
+            mc[rb] = m_new;
+            sc[rb] = max(0, 127 - 8 + (h ? ml.y : ml.x) - m_new);
+            if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
+#pragma unroll
+                for (int j = 0; j < kMyBlocks; ++j) oacc[rb][j] *= alpha;
+            }
+            // lane (n32, h): keys 16h..16h+15 and 32+16h..32+16h+15 of the row
+            const int sw = (row >> 2) & 3;
+            const u32x4 a0 = *reinterpret_cast<const u32x4 *>(P + row * 64 + ((h ^ sw) << 4));
+            const u32x4 a1 = *reinterpret_cast<const u32x4 *>(P + row * 64 + (((2 + h) ^ sw) << 4));
+            const u32x4 b0 = *reinterpret_cast<const u32x4 *>(P + 4096 + row * 64 + ((h ^ sw) << 4));
+            const u32x4 b1 = *reinterpret_cast<const u32x4 *>(P + 4096 + row * 64 + (((2 + h) ^ sw) << 4));
+            ph[rb] = i32x8{int(a0.x), int(a0.y), int(a0.z), int(a0.w), int(a1.x), int(a1.y), int(a1.z), int(a1.w)};
+            pl[rb] = i32x8{int(b0.x), int(b0.y), int(b0.z), int(b0.w), int(b1.x), int(b1.y), int(b1.z), int(b1.w)};
+        }
+        // V^T operand: lane (m = dv column, h) holds keys 16h + 0..15 (bytes 0-15) and
+        // 32 + 16h + 0..15 (bytes 16-31).  Each transposed read gives 8 keys of one column: lane
+        // s = 2k + hh of a 16-lane group points at key k of the read, column bytes 8hh..8hh+7.
+        const int kk = (lane & 15) >> 1, hh = lane & 1, half = (lane >> 4) & 1;
+#pragma unroll
+        for (int j = 0; j < kMyBlocks; ++j) {
+            if (j == 1 && !has_blk1) continue;
+            const int c = 2 * (wave + 8 * j) + half;
+            int2v raw[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int key = 32 * (r >> 1) + 16 * h + 8 * (r & 1) + kk;
+                raw[r] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                    (__attribute__((address_space(3))) int2v *)(tb + tpos(c, key) + 8 * hh));
+            }
+            const i32x8 vt = i32x8{raw[0].x, raw[0].y, raw[1].x, raw[1].y,
+                                   raw[2].x, raw[2].y, raw[3].x, raw[3].y};
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb) {
+                if (32 * rb >= nrows) continue;
+                oacc[rb][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                    vt, ph[rb], oacc[rb][j], 0, 0, 0, 127, 0, sc[rb]);
+                oacc[rb][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                    vt, pl[rb], oacc[rb][j], 0, 0, 0, 127, 0, sc[rb]);
+            }
+        }
+    };
 
     if (ntiles > 0) {
-        GQA_LOAD_INDICES(0)
-        GQA_LOAD_ROWS()
-        if (ntiles > 1) { GQA_LOAD_INDICES(1) }
+        issue_idx(0);
+#pragma unroll
+        for (int j = -3; j < 0; ++j) {
+            if (j + 4 < ntiles) issue_idx(j + 4);
+            if (j + 3 < ntiles) {
+                wait_ids(j);
+                issue_rows(j + 3);
+            }
+        }
+        wait_rows(-1);
+        __syncthreads();
     }
 
-    for (int it = 0; it < ntiles; ++it) {
-        __syncthreads();
-#pragma unroll
-        for (int u = 0; u < IPT; ++u)
-            if (u + 1 < IPT || last_item_ok)
-                *reinterpret_cast<u32x4 *>(kbuf + tile_pos<BK>(ikey[u], ichunk[u])) = stg[u];
-        __syncthreads();
-        if (it + 1 < ntiles) {
-            GQA_LOAD_ROWS()
-            if (it + 2 < ntiles) { GQA_LOAD_INDICES(it + 2) }
-        }
+    for (int t = 0; t < ntiles; ++t) {
+        if (t > 0) pv(t - 1);
 
-        // Partial S^T over this wave's half of the row: block j covers keys 16j..16j+15; lane
-        // holds keys 16j+4grp+i of row col.
-        f32x4 sacc[NSB];
-        if (pair_active) {
+        // Scores of key block kb: lane (n16, g) holds keys 32 kb + 16 sb + 4 g + i of row prow.
+        const uint8_t *tb = lds + (t & (kBufs - 1)) * T::kTileBytes;
+        f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+        if (producer) {
 #pragma unroll
-            for (int j = 0; j < NSB; ++j) sacc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-            // the operands of two score blocks are read first, so the LDS latency is paid once
-            // per pair of blocks rather than once per MFMA
+            for (int s = 0; s < 4; ++s)
 #pragma unroll
-            for (int j0 = 0; j0 < NSB; j0 += 2) {
-                i32x8 kraw[2][T::kF8Chunks];
-#pragma unroll
-                for (int jj = 0; jj < 2; ++jj)
-#pragma unroll
-                    for (int i = 0; i < T::kF8Chunks; ++i) {
-                        const int key = 16 * (j0 + jj) + col;
-                        const int d = dbase + 128 * i + 32 * grp;
-                        const u32x4 lo16 = *reinterpret_cast<const u32x4 *>(kbuf + tile_pos<BK>(key, d));
-                        const u32x4 hi16 = *reinterpret_cast<const u32x4 *>(kbuf + tile_pos<BK>(key, d + 16));
-                        kraw[jj][i] = i32x8{int(lo16.x), int(lo16.y), int(lo16.z), int(lo16.w),
-                                            int(hi16.x), int(hi16.y), int(hi16.z), int(hi16.w)};
-                    }
-#pragma unroll
-                for (int i = 0; i < T::kF8Chunks; ++i) {
-#pragma unroll
-                    for (int jj = 0; jj < 2; ++jj)
-                        sacc[j0 + jj] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                            kraw[jj][i], qhi[i], sacc[j0 + jj], 0, 0, 0, 127, 0, 127);
-#pragma unroll
-                    for (int jj = 0; jj < 2; ++jj)
-                        sacc[j0 + jj] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                            kraw[jj][i], qlo[i], sacc[j0 + jj], 0, 0, 0, 127, 0, 127);
+                for (int sb = 0; sb < 2; ++sb) {
+                    const int key = 32 * kb + 16 * sb + n16;
+                    const int c = 8 * s + 2 * g;
+                    const u32x4 lo16 = *reinterpret_cast<const u32x4 *>(tb + tpos(c, key));
+                    const u32x4 hi16 = *reinterpret_cast<const u32x4 *>(tb + tpos(c + 1, key));
+                    const i32x8 kraw = i32x8{int(lo16.x), int(lo16.y), int(lo16.z), int(lo16.w),
+                                             int(hi16.x), int(hi16.y), int(hi16.z), int(hi16.w)};
+                    sacc[sb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                        kraw, qhi[s], sacc[sb], 0, 0, 0, 127, 0, 127);
+                    sacc[sb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                        kraw, qlo[s], sacc[sb], 0, 0, 0, 127, 0, 127);
                 }
 #pragma unroll
-                for (int jj = 0; jj < 2; ++jj) sacc[j0 + jj] *= qinv;
-                if (T::kRopeSteps > 0 && hf == 1) {
+            for (int st = 0; st < T::kRopeSteps; ++st)
 #pragma unroll
-                    for (int st = 0; st < T::kRopeSteps; ++st)
-#pragma unroll
-                        for (int jj = 0; jj < 2; ++jj) {
-                            const u32x2 raw = *reinterpret_cast<const u32x2 *>(
-                                kbuf + tile_pos<BK>(16 * (j0 + jj) + col, 512 + 32 * st + 8 * grp));
-                            sacc[j0 + jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                                fp8x8_to_bf16x8(raw.x, raw.y), qrope[st], sacc[j0 + jj], 0, 0, 0);
-                        }
+                for (int sb = 0; sb < 2; ++sb) {
+                    const int key = 32 * kb + 16 * sb + n16;
+                    const long kr = *reinterpret_cast<const long *>(
+                        tb + tpos(32 + 2 * st + (g >> 1), key) + 8 * (g & 1));
+                    sacc[sb] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(kr, qrh[st], sacc[sb], 0, 0, 0);
+                    sacc[sb] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(kr, qrl[st], sacc[sb], 0, 0, 0);
                 }
-            }
-#pragma unroll
-            for (int j = 0; j < NSB; ++j) sx[(wave * NSB + j) * 64 + lane] = sacc[j];
         }
-        __syncthreads();
-        if (!pair_active) continue;
-#pragma unroll
-        for (int j = 0; j < NSB; ++j) sacc[j] += sx[((wave ^ 2) * NSB + j) * 64 + lane];
 
-        // Online softmax in base 2 over this tile (identical in both waves of the pair).
-        const int tb = k0 + it * BK;
-        float mx = kNegInf;
+        // Softmax of this wave's block in base 2, with an integer maximum m:
+        // p * 2^8 = 2^(score - m + 8) in (0, 256].
+        const int kt = k0 + t * kBK + 32 * kb;
+        if (k0 + t * kBK + kBK > kfull) {
 #pragma unroll
-        for (int j = 0; j < NSB; ++j)
+            for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int k = tb + 16 * j + 4 * grp + i;
-                const float sv = k < row_end ? sacc[j][i] * a.score_scale : kNegInf;
-                sacc[j][i] = sv;
-                mx = fmaxf(mx, sv);
-            }
+                for (int i = 0; i < 4; ++i)
+                    if (kt + 16 * sb + 4 * g + i >= p_end) sacc[sb][i] = kNegInf;
+        }
+        float mx = fmaxf(fmaxf(fmaxf(sacc[0][0], sacc[0][1]), fmaxf(sacc[0][2], sacc[0][3])),
+                         fmaxf(fmaxf(sacc[1][0], sacc[1][1]), fmaxf(sacc[1][2], sacc[1][3])));
         mx = fmaxf(mx, xor_shuffle(mx, 16));
         mx = fmaxf(mx, xor_shuffle(mx, 32));
-        const float m_new = fmaxf(m_run, mx);
-        const float m_use = m_new == kNegInf ? 0.f : m_new;
-        const float alpha = fast_exp2(m_run - m_use);
-        float psum = 0.f;
+        const int m = mx == kNegInf ? kNoMax : int(ceilf(mx * c_row));
+        const float bias = float(8 - m);
+        // The row sum adds the probabilities as quantized (hi + lo), the weights PV applies: a
+        // dominant key then carries no quantization error into the normalized output.
+        float lsum = 0.f, esum = 0.f;
+        int whi[2], wlo[2];
 #pragma unroll
-        for (int j = 0; j < NSB; ++j)
+        for (int sb = 0; sb < 2; ++sb) {
+            float p[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const float p = fast_exp2(sacc[j][i] - m_use);
-                sacc[j][i] = p;
-                psum += p;
+                p[i] = fast_exp2(fmaf(sacc[sb][i], c_row, bias));
+                esum += p[i];
             }
-        psum += xor_shuffle(psum, 16);
-        psum += xor_shuffle(psum, 32);
-        l_run = l_run * alpha + psum;
-        m_run = m_new;
-        if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
-#pragma unroll
-            for (int v = 0; v < T::kVBlocks; ++v) oacc[v] *= alpha;
+            split_fp8x4(p[0], p[1], p[2], p[3], whi[sb], wlo[sb]);
+            const f32x2 h01 = __builtin_amdgcn_cvt_pk_f32_fp8(whi[sb], false);
+            const f32x2 h23 = __builtin_amdgcn_cvt_pk_f32_fp8(whi[sb], true);
+            const f32x2 l01 = __builtin_amdgcn_cvt_pk_f32_fp8(wlo[sb], false);
+            const f32x2 l23 = __builtin_amdgcn_cvt_pk_f32_fp8(wlo[sb], true);
+            lsum += ((h01.x + l01.x) + (h01.y + l01.y)) + ((h23.x + l23.x) + (h23.y + l23.y));
         }
+        lsum += xor_shuffle(lsum, 16);
+        lsum += xor_shuffle(lsum, 32);
+        esum += xor_shuffle(esum, 16);
+        esum += xor_shuffle(esum, 32);
 
-        // O^T += V^T P^T, 32 keys per step.  Lane (s = 2k + h) of group g points the transposed
-        // read at key 4g+k (k < 4) or 16+4g+k-4 (k >= 4), value bytes 8h..8h+7 of the block; the
-        // read returns, for value column `col`, those 8 keys in k order -- the keys P^T holds in
-        // slots 0..7 of lane group g.
-        const int sl = lane & 15;
-        const int kk = sl >> 1;
-        const int key_in_step = kk < 4 ? 4 * grp + kk : 12 + 4 * grp + kk;
-        const int vbase = hf * T::kHalfV + 8 * (sl & 1);
+        __syncthreads();   // every wave is done with PV(t - 1): P, ML and buffer (t - 1) % 4 free
+
+        {
+            const int sw = (prow >> 2) & 3;
 #pragma unroll
-        for (int kb = 0; kb < T::kPvSteps; ++kb) {
-            bf16x8 pf;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                pf[i] = static_cast<__bf16>(sacc[2 * kb][i]);
-                pf[4 + i] = static_cast<__bf16>(sacc[2 * kb + 1][i]);
+            for (int sb = 0; sb < 2; ++sb) {
+                const int off = prow * 64 + (((2 * kb + sb) ^ sw) << 4) + 4 * g;
+                *reinterpret_cast<int *>(P + off) = whi[sb];
+                *reinterpret_cast<int *>(P + 4096 + off) = wlo[sb];
             }
-            const int vkey = 32 * kb + key_in_step;
-#pragma unroll
-            for (int v = 0; v < T::kVBlocks; ++v) {
-                const int2v raw = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-                    (__attribute__((address_space(3))) int2v *)(kbuf + tile_pos<BK>(vkey, vbase + 16 * v)));
-                oacc[v] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                    fp8x8_to_bf16x8(uint32_t(raw.x), uint32_t(raw.y)), pf, oacc[v], 0, 0, 0);
+            if (g == 0) {
+                *reinterpret_cast<int *>(ML + prow * 32 + 4 * kb) = m;
+                *reinterpret_cast<float *>(ML + prow * 32 + 8 + 4 * kb) = lsum;
+                *reinterpret_cast<float *>(ML + prow * 32 + 16 + 4 * kb) = esum;
             }
         }
+        if (t + 4 < ntiles) issue_idx(t + 4);
+        if (t + 3 < ntiles) {
+            wait_ids(t);
+            issue_rows(t + 3);
+        }
+        if (t + 1 < ntiles) wait_rows(t);
+        __syncthreads();   // P(t) and tile t + 1 visible to every wave
     }
+    if (ntiles > 0) pv(ntiles - 1);
 
-    if (!row_ok) return;
-    // Lane holds O^T[hf*DV/2 + 16v + 4grp + i][col]: four consecutive values of its row.
-    const int64_t row = int64_t(b) * a.rows_per_req + r_in;
-    const float inv = l_run > 0.f ? a.out_scale / l_run : 0.f;
-    const float lse2 = l_run > 0.f ? m_run + __log2f(l_run) : kNegInf;
-    const int c0 = hf * T::kHalfV + 4 * grp;
-    if (DIRECT) {
-        uint16_t *o = a.out + row * DV + c0;
+    // ---- epilogue: lane (n32, h) of block j holds columns 32 (wave + 8 j) + 8 q + 4 h + i of
+    // row 32 rb + n32, i = 0..3, for q = 0..3
 #pragma unroll
-        for (int v = 0; v < T::kVBlocks; ++v)
-            *reinterpret_cast<uint2 *>(o + 16 * v) =
-                make_uint2(pack_bf16x2(oacc[v][0] * inv, oacc[v][1] * inv),
-                           pack_bf16x2(oacc[v][2] * inv, oacc[v][3] * inv));
-        if (hf == 0 && grp == 0 && a.lse2_out) a.lse2_out[row] = lse2;
-    } else {
-        float *o = a.part_o + (row * a.np + part) * DV + c0;
+    for (int rb = 0; rb < 2; ++rb) {
+        const int rl = 32 * rb + n32;
+        if (rl >= nrows) continue;
+        const int64_t row = int64_t(b) * a.rows_per_req + row0 + rl;
+        const float inv = lc[rb] > 0.f ? a.out_scale / lc[rb] : 0.f;
+        const float lse2 = le[rb] > 0.f ? float(mc[rb]) + __log2f(le[rb]) : kNegInf;
 #pragma unroll
-        for (int v = 0; v < T::kVBlocks; ++v)
-            *reinterpret_cast<f32x4 *>(o + 16 * v) = oacc[v] * inv;
-        if (hf == 0 && grp == 0) a.part_lse2[row * a.np + part] = lse2;
+        for (int j = 0; j < kMyBlocks; ++j) {
+            if (j == 1 && !has_blk1) continue;
+            const int cbase = 32 * (wave + 8 * j) + 4 * h;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const float v0 = oacc[rb][j][4 * q] * inv, v1 = oacc[rb][j][4 * q + 1] * inv;
+                const float v2 = oacc[rb][j][4 * q + 2] * inv, v3 = oacc[rb][j][4 * q + 3] * inv;
+                if (DIRECT) {
+                    *reinterpret_cast<uint2 *>(a.out + row * DV + cbase + 8 * q) =
+                        make_uint2(pack_bf16x2(v0, v1), pack_bf16x2(v2, v3));
+                } else {
+                    *reinterpret_cast<f32x4 *>(a.part_o + (row * a.np + part) * DV + cbase + 8 * q) =
+                        f32x4{v0, v1, v2, v3};
+                }
+            }
+        }
+        if (wave == 0 && h == 0) {
+            if (DIRECT) {
+                if (a.lse2_out) a.lse2_out[row] = lse2;
+            } else {
+                a.part_lse2[row * a.np + part] = lse2;
+            }
+        }
     }
 }
 
-#undef GQA_LOAD_INDICES
-#undef GQA_LOAD_ROWS
-
-template <int BK, int DQK, int DV>
+template <int DQK, int DV>
 hipError_t launch_shape(const MlaSplitArgs &a, bool direct, hipStream_t s) {
-    const dim3 grid(xcd_grid_size(a.total_ctas)), block(256);
+    const dim3 grid(xcd_grid_size(a.total_ctas)), block(kThreads);
     if (direct)
-        hipLaunchKernelGGL((mla_split_kernel<BK, DQK, DV, true>), grid, block, 0, s, a);
+        hipLaunchKernelGGL((mla_split_kernel<DQK, DV, true>), grid, block, 0, s, a);
     else
-        hipLaunchKernelGGL((mla_split_kernel<BK, DQK, DV, false>), grid, block, 0, s, a);
+        hipLaunchKernelGGL((mla_split_kernel<DQK, DV, false>), grid, block, 0, s, a);
     return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_mla_split(const MlaSplitArgs &a, int block_k, int d_qk, int d_v, bool direct,
-                            hipStream_t s) {
-    if (d_qk == 576 && d_v == 512)
-        return block_k == 32 ? launch_shape<32, 576, 512>(a, direct, s)
-                             : launch_shape<64, 576, 512>(a, direct, s);
-    if (d_qk == 512 && d_v == 448)
-        return block_k == 32 ? launch_shape<32, 512, 448>(a, direct, s)
-                             : launch_shape<64, 512, 448>(a, direct, s);
+int mla_rows_per_cta() { return kBM; }
+
+hipError_t launch_mla_split(const MlaSplitArgs &a, int d_qk, int d_v, bool direct, hipStream_t s) {
+    if (a.block_k != 32 && a.block_k != 64) return hipErrorInvalidValue;
+    if (d_qk == 576 && d_v == 512) return launch_shape<576, 512>(a, direct, s);
+    if (d_qk == 512 && d_v == 448) return launch_shape<512, 448>(a, direct, s);
     return hipErrorInvalidValue;
 }
 
