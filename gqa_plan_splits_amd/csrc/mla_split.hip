@@ -37,6 +37,8 @@
 #include "device_common.hpp"
 #include "kernels.hpp"
 
+#include <type_traits>
+
 namespace gqa {
 namespace {
 
@@ -145,7 +147,6 @@ __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const MlaSplitAr
     // ---- producer row (QK^T and softmax): row 16 rq + n16 of the block
     const int prow = 16 * rq + n16;
     const bool prow_ok = prow < nrows;
-    const bool producer = 16 * rq < nrows;
     int p_end;   // keys visible to this row
     float c_row; // base-2 score per unit of the raw product
     i32x8 qhi[4], qlo[4];
@@ -266,19 +267,68 @@ __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const MlaSplitAr
     uint8_t *const P = lds + T::kPOff;
     uint8_t *const ML = lds + T::kMlOff;
 
-    // PV for tile t (LDS buffer t % 4, probabilities of tile t in LDS).
-    auto pv = [&](int t) {
-        const uint8_t *tb = lds + (t & (kBufs - 1)) * T::kTileBytes;
-        i32x8 ph[2], pl[2];
-        int sc[2] = {0, 0};
+    // Loop-invariant LDS byte offsets of this lane's operands; a tile base and immediates are
+    // added per read.
+    //   score operand, key 32 kb + 16 sb + n16: chunk 8 s + 2 g (even) and the odd one after it
+    const int k_even = 2048 * g + ((32 * kb + n16) << 4);
+    const int k_odd = 1024 + 2048 * g + ((32 * kb + (n16 ^ 8)) << 4);
+    //   rope operand: chunk 32 + 2 st + g / 2, bytes 8 (g % 2)..
+    const int k_rope = (32 + (g >> 1)) * 1024 + ((32 * kb + (n16 ^ ((g >> 1) << 3))) << 4) + 8 * (g & 1);
+    //   V^T operand: lane (m = dv column, h) holds keys 16h + 0..15 (bytes 0-15) and 32 + 16h +
+    //   0..15 (bytes 16-31).  A transposed read gives 8 keys of one column: lane s = 2k + hh of a
+    //   16-lane group points at key k of the read (keys 32 (r / 2) + 16 h + 8 (r % 2) + k of
+    //   chunk 2 (wave + 8 j) + half), column bytes 8hh..8hh+7.
+    const int kk = (lane & 15) >> 1, hh = lane & 1, half = (lane >> 4) & 1;
+    const int v_base0 = (2 * wave + half) * 1024 + ((16 * h + kk) << 4) + 128 * half + 8 * hh;
+    const int v_base1 = v_base0 + 128 - 256 * half;
+    //   P^T operand of row 32 rb + n32: keys 16h.. and 32 + 16h.. (16-byte chunks, swizzled by row)
+    const int p_sw = (n32 >> 2) & 3;
+    const int p_rd0 = n32 * 64 + ((h ^ p_sw) << 4), p_rd1 = n32 * 64 + (((2 + h) ^ p_sw) << 4);
+    //   this producer lane's words: keys 32 kb + 16 sb + 4 g .. + 3 of row prow
+    const int pw_sw = (prow >> 2) & 3;
+    const int p_wr0 = prow * 64 + (((2 * kb) ^ pw_sw) << 4) + 4 * g;
+    const int p_wr1 = prow * 64 + (((2 * kb + 1) ^ pw_sw) << 4) + 4 * g;
+    // the last output block of a 448-wide value exists for waves 0-5 only; the others read a
+    // valid (unused) chunk and drop the result
+    const int v_blk1 = has_blk1 ? 16384 : 0;
+    // Tiles whose keys every row of the block sees need no mask.
+    const int n_full = min(ntiles, max(0, (kfull - k0) / kBK));
+
+    auto tile_ptr = [&](int t) -> const uint8_t * { return lds + (t & (kBufs - 1)) * T::kTileBytes; };
+
+    auto qk = [&](const uint8_t *tb, f32x4 (&sacc)[2]) {
+        sacc[0] = f32x4{0.f, 0.f, 0.f, 0.f};
+        sacc[1] = sacc[0];
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+            for (int sb = 0; sb < 2; ++sb) {
+                const u32x4 lo16 = *reinterpret_cast<const u32x4 *>(tb + k_even + 8192 * s + 256 * sb);
+                const u32x4 hi16 = *reinterpret_cast<const u32x4 *>(tb + k_odd + 8192 * s + 256 * sb);
+                const i32x8 kraw = i32x8{int(lo16.x), int(lo16.y), int(lo16.z), int(lo16.w),
+                                         int(hi16.x), int(hi16.y), int(hi16.z), int(hi16.w)};
+                sacc[sb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                    kraw, qhi[s], sacc[sb], 0, 0, 0, 127, 0, 127);
+                sacc[sb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                    kraw, qlo[s], sacc[sb], 0, 0, 0, 127, 0, 127);
+            }
+#pragma unroll
+        for (int st = 0; st < T::kRopeSteps; ++st)
+#pragma unroll
+            for (int sb = 0; sb < 2; ++sb) {
+                const long kr = *reinterpret_cast<const long *>(tb + k_rope + 2048 * st + 256 * sb);
+                sacc[sb] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(kr, qrh[st], sacc[sb], 0, 0, 0);
+                sacc[sb] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(kr, qrl[st], sacc[sb], 0, 0, 0);
+            }
+    };
+
+    // PV bookkeeping for the probabilities now in LDS: new running maxima and sums, the rescale
+    // of the accumulators when a maximum moved, and each lane's B scale.
+    auto pv_prep = [&](int (&sc)[2]) {
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb) {
-            ph[rb] = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
-            pl[rb] = ph[rb];
-            if (32 * rb >= nrows) continue;
-            const int row = 32 * rb + n32;
-            const i32x4 ml = *reinterpret_cast<const i32x4 *>(ML + row * 32);
-            const f32x2 ex = *reinterpret_cast<const f32x2 *>(ML + row * 32 + 16);
+            const i32x4 ml = *reinterpret_cast<const i32x4 *>(ML + n32 * 32 + 1024 * rb);
+            const f32x2 ex = *reinterpret_cast<const f32x2 *>(ML + n32 * 32 + 1024 * rb + 16);
             const int m_new = max(mc[rb], max(ml.x, ml.y));
             const float alpha = ldexpf(1.f, mc[rb] - m_new);
             lc[rb] = lc[rb] * alpha + ldexpf(__int_as_float(ml.z), ml.x - m_new - 8) +
@@ -290,35 +340,32 @@ __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const MlaSplitAr
 #pragma unroll
                 for (int j = 0; j < kMyBlocks; ++j) oacc[rb][j] *= alpha;
             }
-            // lane (n32, h): keys 16h..16h+15 and 32+16h..32+16h+15 of the row
-            const int sw = (row >> 2) & 3;
-            const u32x4 a0 = *reinterpret_cast<const u32x4 *>(P + row * 64 + ((h ^ sw) << 4));
-            const u32x4 a1 = *reinterpret_cast<const u32x4 *>(P + row * 64 + (((2 + h) ^ sw) << 4));
-            const u32x4 b0 = *reinterpret_cast<const u32x4 *>(P + 4096 + row * 64 + ((h ^ sw) << 4));
-            const u32x4 b1 = *reinterpret_cast<const u32x4 *>(P + 4096 + row * 64 + (((2 + h) ^ sw) << 4));
+        }
+    };
+
+    auto pv_mma = [&](const uint8_t *tb, const int (&sc)[2]) {
+        i32x8 ph[2], pl[2];
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+            const u32x4 a0 = *reinterpret_cast<const u32x4 *>(P + p_rd0 + 2048 * rb);
+            const u32x4 a1 = *reinterpret_cast<const u32x4 *>(P + p_rd1 + 2048 * rb);
+            const u32x4 b0 = *reinterpret_cast<const u32x4 *>(P + 4096 + p_rd0 + 2048 * rb);
+            const u32x4 b1 = *reinterpret_cast<const u32x4 *>(P + 4096 + p_rd1 + 2048 * rb);
             ph[rb] = i32x8{int(a0.x), int(a0.y), int(a0.z), int(a0.w), int(a1.x), int(a1.y), int(a1.z), int(a1.w)};
             pl[rb] = i32x8{int(b0.x), int(b0.y), int(b0.z), int(b0.w), int(b1.x), int(b1.y), int(b1.z), int(b1.w)};
         }
-        // V^T operand: lane (m = dv column, h) holds keys 16h + 0..15 (bytes 0-15) and
-        // 32 + 16h + 0..15 (bytes 16-31).  Each transposed read gives 8 keys of one column: lane
-        // s = 2k + hh of a 16-lane group points at key k of the read, column bytes 8hh..8hh+7.
-        const int kk = (lane & 15) >> 1, hh = lane & 1, half = (lane >> 4) & 1;
 #pragma unroll
         for (int j = 0; j < kMyBlocks; ++j) {
-            if (j == 1 && !has_blk1) continue;
-            const int c = 2 * (wave + 8 * j) + half;
+            const uint8_t *vb = tb + (j ? v_blk1 : 0);
             int2v raw[4];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int key = 32 * (r >> 1) + 16 * h + 8 * (r & 1) + kk;
+            for (int r = 0; r < 4; ++r)
                 raw[r] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-                    (__attribute__((address_space(3))) int2v *)(tb + tpos(c, key) + 8 * hh));
-            }
+                    (__attribute__((address_space(3))) int2v *)(vb + ((r & 1) ? v_base1 : v_base0) + 512 * (r >> 1)));
             const i32x8 vt = i32x8{raw[0].x, raw[0].y, raw[1].x, raw[1].y,
                                    raw[2].x, raw[2].y, raw[3].x, raw[3].y};
 #pragma unroll
             for (int rb = 0; rb < 2; ++rb) {
-                if (32 * rb >= nrows) continue;
                 oacc[rb][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
                     vt, ph[rb], oacc[rb][j], 0, 0, 0, 127, 0, sc[rb]);
                 oacc[rb][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
@@ -327,6 +374,132 @@ __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const MlaSplitAr
         }
     };
 
+    // Softmax of this wave's block in base 2 with an integer maximum m:
+    // p * 2^8 = 2^(score - m + 8) in (0, 256].  Returns the hi/lo words, m and both row sums.
+    struct Probs {
+        int whi[2], wlo[2];
+        int m;
+        float lsum, esum;
+    };
+    auto softmax = [&](int t, f32x4 (&sacc)[2], auto masked) -> Probs {
+        if constexpr (decltype(masked)::value) {
+            const int kt = k0 + t * kBK + 32 * kb;
+#pragma unroll
+            for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (kt + 16 * sb + 4 * g + i >= p_end) sacc[sb][i] = kNegInf;
+        }
+        Probs r;
+        float mx = fmaxf(fmaxf(fmaxf(sacc[0][0], sacc[0][1]), fmaxf(sacc[0][2], sacc[0][3])),
+                         fmaxf(fmaxf(sacc[1][0], sacc[1][1]), fmaxf(sacc[1][2], sacc[1][3])));
+        mx = fmaxf(mx, xor_shuffle(mx, 16));
+        mx = fmaxf(mx, xor_shuffle(mx, 32));
+        r.m = mx == kNegInf ? kNoMax : int(ceilf(mx * c_row));
+        const float bias = float(8 - r.m);
+        // The row sum adds the probabilities as quantized (hi + lo), the weights PV applies: a
+        // dominant key then carries no quantization error into the normalized output.
+        float lsum = 0.f, esum = 0.f;
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb) {
+            float p[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                p[i] = fast_exp2(fmaf(sacc[sb][i], c_row, bias));
+                esum += p[i];
+            }
+            split_fp8x4(p[0], p[1], p[2], p[3], r.whi[sb], r.wlo[sb]);
+            const f32x2 h01 = __builtin_amdgcn_cvt_pk_f32_fp8(r.whi[sb], false);
+            const f32x2 h23 = __builtin_amdgcn_cvt_pk_f32_fp8(r.whi[sb], true);
+            const f32x2 l01 = __builtin_amdgcn_cvt_pk_f32_fp8(r.wlo[sb], false);
+            const f32x2 l23 = __builtin_amdgcn_cvt_pk_f32_fp8(r.wlo[sb], true);
+            lsum += ((h01.x + l01.x) + (h01.y + l01.y)) + ((h23.x + l23.x) + (h23.y + l23.y));
+        }
+        lsum += xor_shuffle(lsum, 16);
+        r.lsum = lsum + xor_shuffle(lsum, 32);
+        esum += xor_shuffle(esum, 16);
+        r.esum = esum + xor_shuffle(esum, 32);
+        return r;
+    };
+
+    auto publish = [&](const Probs &pr) {
+        *reinterpret_cast<int *>(P + p_wr0) = pr.whi[0];
+        *reinterpret_cast<int *>(P + p_wr1) = pr.whi[1];
+        *reinterpret_cast<int *>(P + 4096 + p_wr0) = pr.wlo[0];
+        *reinterpret_cast<int *>(P + 4096 + p_wr1) = pr.wlo[1];
+        if (g == 0) {
+            *reinterpret_cast<int *>(ML + prow * 32 + 4 * kb) = pr.m;
+            *reinterpret_cast<float *>(ML + prow * 32 + 8 + 4 * kb) = pr.lsum;
+            *reinterpret_cast<float *>(ML + prow * 32 + 16 + 4 * kb) = pr.esum;
+        }
+    };
+
+    // Copies for later tiles, then the wait for tile t + 1 (constant counts in steady state).
+    auto advance = [&](int t) {
+        if (t + 4 < ntiles) {
+            issue_idx(t + 4);
+            if (n_copy > 4) {
+                asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
+                issue_rows(t + 3);
+                asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
+            } else {
+                asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
+                issue_rows(t + 3);
+                asm volatile("s_waitcnt vmcnt(10)" ::: "memory");
+            }
+        } else {
+            if (t + 3 < ntiles) {
+                wait_ids(t);
+                issue_rows(t + 3);
+            }
+            if (t + 1 < ntiles) wait_rows(t);
+        }
+    };
+
+    // One tile: scores of t, PV of t - 1 and the softmax of t in one straight-line block (so the
+    // MFMAs of one overlap the VALU work of the other), then the exchange of P(t).
+    auto step = [&](int t, auto masked, auto first) {
+        int sc[2] = {0, 0};
+        if constexpr (!decltype(first)::value) pv_prep(sc);
+        f32x4 sacc[2];
+        qk(tile_ptr(t), sacc);
+        // scores: each step's four operand reads go out one step ahead of its four MFMAs
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+        for (int s = 0; s < 4 + T::kRopeSteps / 2; ++s) {
+            __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (!decltype(first)::value) pv_mma(tile_ptr(t - 1), sc);
+        const Probs pr = softmax(t, sacc, masked);
+        if constexpr (!decltype(first)::value) {
+            // PV's operand reads first, then its eight MFMAs spread through the softmax VALU work
+            __builtin_amdgcn_sched_group_barrier(0x100, 16, 1);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+                __builtin_amdgcn_sched_group_barrier(0x002, 12, 1);
+            }
+        }
+        if constexpr (!decltype(first)::value) {
+            // an empty use of the accumulators here keeps the PV MFMAs in this block (the
+            // compiler would otherwise sink them past the barrier, away from the softmax)
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+                for (int j = 0; j < kMyBlocks; ++j) asm volatile("" : "+v"(oacc[rb][j]));
+        }
+        __builtin_amdgcn_sched_barrier(0);   // keep the softmax ahead of the barrier
+        if constexpr (!decltype(first)::value)
+            __syncthreads();   // every wave is done with PV(t - 1): P, ML and buffer (t - 1) % 4 free
+        publish(pr);
+        advance(t);
+        __syncthreads();       // P(t) and tile t + 1 visible to every wave
+    };
+
+    using yes = std::integral_constant<bool, true>;
+    using no = std::integral_constant<bool, false>;
     if (ntiles > 0) {
         issue_idx(0);
 #pragma unroll
@@ -339,107 +512,15 @@ __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const MlaSplitAr
         }
         wait_rows(-1);
         __syncthreads();
+
+        step(0, yes{}, yes{});
+        int t = 1;
+        for (; t < n_full; ++t) step(t, no{}, no{});
+        for (; t < ntiles; ++t) step(t, yes{}, no{});
+        int sc[2] = {0, 0};
+        pv_prep(sc);
+        pv_mma(tile_ptr(ntiles - 1), sc);
     }
-
-    for (int t = 0; t < ntiles; ++t) {
-        if (t > 0) pv(t - 1);
-
-        // Scores of key block kb: lane (n16, g) holds keys 32 kb + 16 sb + 4 g + i of row prow.
-        const uint8_t *tb = lds + (t & (kBufs - 1)) * T::kTileBytes;
-        f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-        if (producer) {
-#pragma unroll
-            for (int s = 0; s < 4; ++s)
-#pragma unroll
-                for (int sb = 0; sb < 2; ++sb) {
-                    const int key = 32 * kb + 16 * sb + n16;
-                    const int c = 8 * s + 2 * g;
-                    const u32x4 lo16 = *reinterpret_cast<const u32x4 *>(tb + tpos(c, key));
-                    const u32x4 hi16 = *reinterpret_cast<const u32x4 *>(tb + tpos(c + 1, key));
-                    const i32x8 kraw = i32x8{int(lo16.x), int(lo16.y), int(lo16.z), int(lo16.w),
-                                             int(hi16.x), int(hi16.y), int(hi16.z), int(hi16.w)};
-                    sacc[sb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                        kraw, qhi[s], sacc[sb], 0, 0, 0, 127, 0, 127);
-                    sacc[sb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                        kraw, qlo[s], sacc[sb], 0, 0, 0, 127, 0, 127);
-                }
-#pragma unroll
-            for (int st = 0; st < T::kRopeSteps; ++st)
-#pragma unroll
-                for (int sb = 0; sb < 2; ++sb) {
-                    const int key = 32 * kb + 16 * sb + n16;
-                    const long kr = *reinterpret_cast<const long *>(
-                        tb + tpos(32 + 2 * st + (g >> 1), key) + 8 * (g & 1));
-                    sacc[sb] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(kr, qrh[st], sacc[sb], 0, 0, 0);
-                    sacc[sb] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(kr, qrl[st], sacc[sb], 0, 0, 0);
-                }
-        }
-
-        // Softmax of this wave's block in base 2, with an integer maximum m:
-        // p * 2^8 = 2^(score - m + 8) in (0, 256].
-        const int kt = k0 + t * kBK + 32 * kb;
-        if (k0 + t * kBK + kBK > kfull) {
-#pragma unroll
-            for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    if (kt + 16 * sb + 4 * g + i >= p_end) sacc[sb][i] = kNegInf;
-        }
-        float mx = fmaxf(fmaxf(fmaxf(sacc[0][0], sacc[0][1]), fmaxf(sacc[0][2], sacc[0][3])),
-                         fmaxf(fmaxf(sacc[1][0], sacc[1][1]), fmaxf(sacc[1][2], sacc[1][3])));
-        mx = fmaxf(mx, xor_shuffle(mx, 16));
-        mx = fmaxf(mx, xor_shuffle(mx, 32));
-        const int m = mx == kNegInf ? kNoMax : int(ceilf(mx * c_row));
-        const float bias = float(8 - m);
-        // The row sum adds the probabilities as quantized (hi + lo), the weights PV applies: a
-        // dominant key then carries no quantization error into the normalized output.
-        float lsum = 0.f, esum = 0.f;
-        int whi[2], wlo[2];
-#pragma unroll
-        for (int sb = 0; sb < 2; ++sb) {
-            float p[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                p[i] = fast_exp2(fmaf(sacc[sb][i], c_row, bias));
-                esum += p[i];
-            }
-            split_fp8x4(p[0], p[1], p[2], p[3], whi[sb], wlo[sb]);
-            const f32x2 h01 = __builtin_amdgcn_cvt_pk_f32_fp8(whi[sb], false);
-            const f32x2 h23 = __builtin_amdgcn_cvt_pk_f32_fp8(whi[sb], true);
-            const f32x2 l01 = __builtin_amdgcn_cvt_pk_f32_fp8(wlo[sb], false);
-            const f32x2 l23 = __builtin_amdgcn_cvt_pk_f32_fp8(wlo[sb], true);
-            lsum += ((h01.x + l01.x) + (h01.y + l01.y)) + ((h23.x + l23.x) + (h23.y + l23.y));
-        }
-        lsum += xor_shuffle(lsum, 16);
-        lsum += xor_shuffle(lsum, 32);
-        esum += xor_shuffle(esum, 16);
-        esum += xor_shuffle(esum, 32);
-
-        __syncthreads();   // every wave is done with PV(t - 1): P, ML and buffer (t - 1) % 4 free
-
-        {
-            const int sw = (prow >> 2) & 3;
-#pragma unroll
-            for (int sb = 0; sb < 2; ++sb) {
-                const int off = prow * 64 + (((2 * kb + sb) ^ sw) << 4) + 4 * g;
-                *reinterpret_cast<int *>(P + off) = whi[sb];
-                *reinterpret_cast<int *>(P + 4096 + off) = wlo[sb];
-            }
-            if (g == 0) {
-                *reinterpret_cast<int *>(ML + prow * 32 + 4 * kb) = m;
-                *reinterpret_cast<float *>(ML + prow * 32 + 8 + 4 * kb) = lsum;
-                *reinterpret_cast<float *>(ML + prow * 32 + 16 + 4 * kb) = esum;
-            }
-        }
-        if (t + 4 < ntiles) issue_idx(t + 4);
-        if (t + 3 < ntiles) {
-            wait_ids(t);
-            issue_rows(t + 3);
-        }
-        if (t + 1 < ntiles) wait_rows(t);
-        __syncthreads();   // P(t) and tile t + 1 visible to every wave
-    }
-    if (ntiles > 0) pv(ntiles - 1);
 
     // ---- epilogue: lane (n32, h) of block j holds columns 32 (wave + 8 j) + 8 q + 4 h + i of
     // row 32 rb + n32, i = 0..3, for q = 0..3
