@@ -29,11 +29,14 @@
 //     conversion); P^T comes from LDS, and the power of two that aligns each 32-key block with
 //     the row's running maximum is the MFMA's per-lane B scale.
 //
-// LDS tile layout: 16-byte chunk c of tile key k sits at c * 1024 + 16 * (k ^ 8 * (c % 2)).  A
-// direct copy writes 64 consecutive 16-byte slots, so one copy instruction moves chunk c of all 64
-// keys; a wave always copies chunks of one parity, hence one key per lane for the whole tile.
-// Score-operand reads (16 keys of one chunk), transposed value reads (8 keys x 16 bytes of two
-// neighbouring chunks) and the copies are all free of bank conflicts.
+// LDS tile layout: a key row is cut into 128-byte lines (eight 16-byte chunks; the 64-byte rope
+// tail of 576-byte rows is a half line).  Line j < 4 of all 64 keys fills 8 KiB at j * 8192, key k
+// at k * 128, its chunks permuted by an XOR with swz8(k); the half line fills 4 KiB at 32768, key
+// k at k * 64, chunks permuted with swz4(k).  A direct copy writes 64 consecutive 16-byte slots,
+// so one copy instruction moves whole lines (8 keys x 8 chunks, or 16 keys x 4 chunks of the half
+// line) and each cache line of a row is fetched once.  The permutations keep the score-operand reads (16
+// keys, one chunk pair), the transposed value reads (8 keys x 16 bytes) and the copies free of
+// bank conflicts.
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -70,7 +73,13 @@ struct MlaShape {
     static_assert(kLdsBytes <= 160 * 1024, "LDS");
 };
 
-__device__ __forceinline__ int tpos(int c, int key) { return c * 1024 + ((key ^ ((c & 1) << 3)) << 4); }
+__device__ __forceinline__ int swz8(int key) { return (((key >> 1) & 3) << 1) | ((key >> 3) & 1); }
+__device__ __forceinline__ int swz4(int key) { return (key >> 2) & 3; }
+// Byte offset of 16-byte chunk c of tile key `key` (see the layout note above).
+__device__ __forceinline__ int tpos(int c, int key) {
+    return c < 32 ? (c >> 3) * 8192 + key * 128 + (((c & 7) ^ swz8(key)) << 4)
+                  : 32768 + key * 64 + (((c & 3) ^ swz4(key)) << 4);
+}
 
 // Direct HBM -> LDS copy of 16 bytes per lane: lane L's bytes land at m0 + OFF + 16 L; the
 // immediate offset applies to the global address too.
@@ -228,29 +237,36 @@ __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const MlaSplitAr
 #pragma unroll
             for (int i = 0; i < 16; ++i) oacc[rb][j][i] = 0.f;
 
-    // ---- tile copies.  Wave w copies chunks w, w + 8, ... of every tile; its lane L carries key
-    // L ^ 8 (w % 2), whose slot id it first copies into its own LDS index slot.
-    const int n_copy = (T::kChunks - wave + 7) >> 3;   // 5 or 4 copies per tile
-    const int my_key = lane ^ ((wave & 1) << 3);
+    // ---- tile copies.  Wave w copies lines 0-3 of keys 8w..8w+7 (lane L: key 8w + L/8, chunk
+    // L%8 ^ swz8(key) of the line) and, for 576-byte rows and w < 4, the half line of keys
+    // 16w..16w+15 (lane L: key 16w + L/4).  It first copies the tile's 64 slot ids (lane L: key L)
+    // into its own LDS index slot.
+    const int n_copy = 4 + (T::kChunks > 32 && wave < 4 ? 1 : 0);   // copies per tile
+    const int key_a = 8 * wave + (lane >> 3), key_b = 16 * (wave & 3) + (lane >> 2);
+    const int chunk_a = 16 * ((lane & 7) ^ swz8(key_a));           // byte offset in the line
+    const int chunk_b = 512 + 16 * ((lane & 3) ^ swz4(key_b));
     const int32_t *const ibase = a.kv_indices + base;
     const uint32_t lds_addr = uint32_t(reinterpret_cast<uintptr_t>(lds));
     const int32_t *const idx_lds = reinterpret_cast<const int32_t *>(lds + T::kIdxOff) + wave * 128;
     const uint64_t kv_stride = uint64_t(a.kv_stride);
 
     auto issue_idx = [&](int tile) {
-        const int key = min(k0 + tile * kBK + my_key, k1 - 1);
+        const int key = min(k0 + tile * kBK + lane, k1 - 1);
         copy4(ibase + key, lds_addr + T::kIdxOff + (wave * 2 + (tile & 1)) * 256);
     };
     auto issue_rows = [&](int tile) {
-        const int id = idx_lds[(tile & 1) * 64 + lane];
-        const uint8_t *row = a.kv + uint64_t(uint32_t(id)) * kv_stride + 16 * wave;
+        const int32_t *ids = idx_lds + (tile & 1) * 64;
+        const uint8_t *row = a.kv + uint64_t(uint32_t(ids[key_a])) * kv_stride + chunk_a;
         const uint32_t m0 = lds_addr + (tile & (kBufs - 1)) * T::kTileBytes + wave * 1024;
-        // copy u moves chunk wave + 8 u: LDS + 8 KiB, global + 128 bytes per step
+        // copy u moves line u: LDS + 8 KiB, global + 128 bytes per step
         copy16<0>(row, m0);
         copy16<128>(row, m0 + 8192 - 128);
         copy16<256>(row, m0 + 16384 - 256);
         copy16<384>(row, m0 + 24576 - 384);
-        if (n_copy > 4) copy16<512>(row, m0 + 32768 - 512);
+        if (n_copy > 4) {
+            const uint8_t *row_b = a.kv + uint64_t(uint32_t(ids[key_b])) * kv_stride + chunk_b;
+            copy16<0>(row_b, m0 + 32768);
+        }
     };
     // Copies retire in issue order.  Per tile j (issue order): slot ids of j + 1, then rows of j.
     // Before the rows of j + 3: the ids of j + 3 landed; after them came rows j + 2 and ids j + 4.
@@ -269,18 +285,21 @@ __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const MlaSplitAr
 
     // Loop-invariant LDS byte offsets of this lane's operands; a tile base and immediates are
     // added per read.
-    //   score operand, key 32 kb + 16 sb + n16: chunk 8 s + 2 g (even) and the odd one after it
-    const int k_even = 2048 * g + ((32 * kb + n16) << 4);
-    const int k_odd = 1024 + 2048 * g + ((32 * kb + (n16 ^ 8)) << 4);
-    //   rope operand: chunk 32 + 2 st + g / 2, bytes 8 (g % 2)..
-    const int k_rope = (32 + (g >> 1)) * 1024 + ((32 * kb + (n16 ^ ((g >> 1) << 3))) << 4) + 8 * (g & 1);
+    //   score operand, key 32 kb + 16 sb + n16: chunks 8 s + 2 g and 8 s + 2 g + 1 (line s; sb
+    //   adds 16 keys = 2048 bytes)
+    const int k_even = tpos(2 * g, 32 * kb + n16);
+    const int k_odd = tpos(2 * g + 1, 32 * kb + n16);
+    //   rope operand: chunk 32 + 2 st + g / 2, bytes 8 (g % 2).. (sb adds 16 keys = 1024 bytes)
+    const int k_rope0 = tpos(32 + (g >> 1), 32 * kb + n16) + 8 * (g & 1);
+    const int k_rope1 = tpos(34 + (g >> 1), 32 * kb + n16) + 8 * (g & 1);
     //   V^T operand: lane (m = dv column, h) holds keys 16h + 0..15 (bytes 0-15) and 32 + 16h +
     //   0..15 (bytes 16-31).  A transposed read gives 8 keys of one column: lane s = 2k + hh of a
     //   16-lane group points at key k of the read (keys 32 (r / 2) + 16 h + 8 (r % 2) + k of
-    //   chunk 2 (wave + 8 j) + half), column bytes 8hh..8hh+7.
+    //   chunk 2 (wave + 8 j) + half), column bytes 8hh..8hh+7.  32 keys = 4096 bytes; j adds two
+    //   lines.
     const int kk = (lane & 15) >> 1, hh = lane & 1, half = (lane >> 4) & 1;
-    const int v_base0 = (2 * wave + half) * 1024 + ((16 * h + kk) << 4) + 128 * half + 8 * hh;
-    const int v_base1 = v_base0 + 128 - 256 * half;
+    const int v_base0 = tpos(2 * wave + half, 16 * h + kk) + 8 * hh;
+    const int v_base1 = tpos(2 * wave + half, 16 * h + 8 + kk) + 8 * hh;
     //   P^T operand of row 32 rb + n32: keys 16h.. and 32 + 16h.. (16-byte chunks, swizzled by row)
     const int p_sw = (n32 >> 2) & 3;
     const int p_rd0 = n32 * 64 + ((h ^ p_sw) << 4), p_rd1 = n32 * 64 + (((2 + h) ^ p_sw) << 4);
@@ -303,8 +322,8 @@ __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const MlaSplitAr
         for (int s = 0; s < 4; ++s)
 #pragma unroll
             for (int sb = 0; sb < 2; ++sb) {
-                const u32x4 lo16 = *reinterpret_cast<const u32x4 *>(tb + k_even + 8192 * s + 256 * sb);
-                const u32x4 hi16 = *reinterpret_cast<const u32x4 *>(tb + k_odd + 8192 * s + 256 * sb);
+                const u32x4 lo16 = *reinterpret_cast<const u32x4 *>(tb + k_even + 8192 * s + 2048 * sb);
+                const u32x4 hi16 = *reinterpret_cast<const u32x4 *>(tb + k_odd + 8192 * s + 2048 * sb);
                 const i32x8 kraw = i32x8{int(lo16.x), int(lo16.y), int(lo16.z), int(lo16.w),
                                          int(hi16.x), int(hi16.y), int(hi16.z), int(hi16.w)};
                 sacc[sb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
@@ -316,7 +335,7 @@ __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const MlaSplitAr
         for (int st = 0; st < T::kRopeSteps; ++st)
 #pragma unroll
             for (int sb = 0; sb < 2; ++sb) {
-                const long kr = *reinterpret_cast<const long *>(tb + k_rope + 2048 * st + 256 * sb);
+                const long kr = *reinterpret_cast<const long *>(tb + (st ? k_rope1 : k_rope0) + 1024 * sb);
                 sacc[sb] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(kr, qrh[st], sacc[sb], 0, 0, 0);
                 sacc[sb] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(kr, qrl[st], sacc[sb], 0, 0, 0);
             }
@@ -361,7 +380,7 @@ __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const MlaSplitAr
 #pragma unroll
             for (int r = 0; r < 4; ++r)
                 raw[r] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-                    (__attribute__((address_space(3))) int2v *)(vb + ((r & 1) ? v_base1 : v_base0) + 512 * (r >> 1)));
+                    (__attribute__((address_space(3))) int2v *)(vb + ((r & 1) ? v_base1 : v_base0) + 4096 * (r >> 1)));
             const i32x8 vt = i32x8{raw[0].x, raw[0].y, raw[1].x, raw[1].y,
                                    raw[2].x, raw[2].y, raw[3].x, raw[3].y};
 #pragma unroll
