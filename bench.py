@@ -38,6 +38,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle sample")
     ap.add_argument("--table-steps", type=int, default=20)
+    ap.add_argument("--settle-ms", type=float, default=150.0,
+                    help="untimed run of each workload's step before its warmup, so clocks settle")
     ap.add_argument("--block-k", type=int, default=0,
                     help="force the split kernel's key tile (0: the CTA-keyed tile rule)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -164,6 +166,19 @@ def measured_traffic():
     return int(fetch + write)
 
 
+def settle(fn, ms):
+    """Untimed: repeat fn for about `ms` milliseconds of wall time so that the GPU clocks reach
+    their steady state under this load before the counted warmup and timed steps."""
+    import torch
+    if ms <= 0:
+        return
+    t0 = time.perf_counter()
+    while (time.perf_counter() - t0) * 1e3 < ms:
+        for _ in range(8):
+            fn()
+        torch.cuda.synchronize()
+
+
 def time_events(fn, n, stream):
     """Average ms per call of fn over n calls, HIP events recorded on `stream`."""
     import torch
@@ -252,6 +267,7 @@ def main():
         is_head = name == args.workload
         steps = args.steps if is_head else args.table_steps
         warm = args.warmup if is_head else max(3, args.warmup // 2)
+        settle(case.step, args.settle_ms)
         for _ in range(warm):
             case.step()
         torch.cuda.synchronize()

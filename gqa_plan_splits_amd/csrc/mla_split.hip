@@ -112,6 +112,21 @@ __device__ __forceinline__ u32x4 load_q8(const uint16_t *ql, const uint16_t *qp,
                     : *reinterpret_cast<const u32x4 *>(qp + (d - DLAT));
 }
 
+// Max / sum over the four lanes l, l ^ 16, l ^ 32, l ^ 48 (one per 16-lane row), identical in all
+// four: v_permlane32_swap and v_permlane16_swap exchange rows without going through LDS.
+__device__ __forceinline__ float rows4_max(float x) {
+    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float rows4_sum(float x) {
+    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 // x (|x| < 448) -> (hi, lo) e4m3 quads: hi = nearest, lo = nearest to the remainder.
 __device__ __forceinline__ void split_fp8x4(float x0, float x1, float x2, float x3, int &hi, int &lo) {
     hi = __builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, 0, false);
@@ -412,8 +427,7 @@ __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const MlaSplitAr
         Probs r;
         float mx = fmaxf(fmaxf(fmaxf(sacc[0][0], sacc[0][1]), fmaxf(sacc[0][2], sacc[0][3])),
                          fmaxf(fmaxf(sacc[1][0], sacc[1][1]), fmaxf(sacc[1][2], sacc[1][3])));
-        mx = fmaxf(mx, xor_shuffle(mx, 16));
-        mx = fmaxf(mx, xor_shuffle(mx, 32));
+        mx = rows4_max(mx);
         r.m = mx == kNegInf ? kNoMax : int(ceilf(mx * c_row));
         const float bias = float(8 - r.m);
         // The row sum adds the probabilities as quantized (hi + lo), the weights PV applies: a
@@ -434,10 +448,8 @@ __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const MlaSplitAr
             const f32x2 l23 = __builtin_amdgcn_cvt_pk_f32_fp8(r.wlo[sb], true);
             lsum += ((h01.x + l01.x) + (h01.y + l01.y)) + ((h23.x + l23.x) + (h23.y + l23.y));
         }
-        lsum += xor_shuffle(lsum, 16);
-        r.lsum = lsum + xor_shuffle(lsum, 32);
-        esum += xor_shuffle(esum, 16);
-        r.esum = esum + xor_shuffle(esum, 32);
+        r.lsum = rows4_sum(lsum);
+        r.esum = rows4_sum(esum);
         return r;
     };
 
@@ -479,7 +491,6 @@ __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const MlaSplitAr
     // MFMAs of one overlap the VALU work of the other), then the exchange of P(t).
     auto step = [&](int t, auto masked, auto first) {
         int sc[2] = {0, 0};
-        if constexpr (!decltype(first)::value) pv_prep(sc);
         f32x4 sacc[2];
         qk(tile_ptr(t), sacc);
         // scores: each step's four operand reads go out one step ahead of its four MFMAs
@@ -490,6 +501,8 @@ __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const MlaSplitAr
             __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
         }
         __builtin_amdgcn_sched_barrier(0);
+        // the PV bookkeeping's VALU work runs while the score MFMAs drain
+        if constexpr (!decltype(first)::value) pv_prep(sc);
         if constexpr (!decltype(first)::value) pv_mma(tile_ptr(t - 1), sc);
         const Probs pr = softmax(t, sacc, masked);
         if constexpr (!decltype(first)::value) {
