@@ -175,7 +175,8 @@ int launch_split(const gqa_decode_problem *p, const Derived &d, int64_t np, int 
         a.part_lse2 = part_lse2;
         a.out = static_cast<uint16_t *>(out);
         a.lse2_out = lse2_out;
-        const hipError_t err = gqa::launch_gqa_split(a, bk, int(p->q_len * a.group), direct, s);
+        a.block_k = bk;
+        const hipError_t err = gqa::launch_gqa_split(a, direct, s);
         return launch_status(err, "gqa split");
     }
 }

@@ -3,32 +3,70 @@
 // What it computes (moonmath-amd README, gfx950 "forward_paged": caches
 // [pages, page_size, kv_heads, 128], kv_indptr counting pages per sequence, kv_page_indices;
 // Modular MAX planner page, MHA-style bullet: one CTA per (kv head, request) per partition):
-// for one kv head of one request and one partition of its tokens, the query rows of that
-// head group (q_len x group <= 16 of them) attend the partition's tokens; the CTA writes each
-// row's softmax-weighted mean of values and the base-2 log-sum-exp of its scores.
+// for one kv head of one request and one partition of its tokens, the query rows of that head
+// group (q_len x group <= 16 of them) attend the partition's tokens; the CTA writes each row's
+// softmax-weighted mean of values and the base-2 log-sum-exp of its scores.
 //
-// Layout of the work (one wave per CTA):
-//   - QK^T on v_mfma_f32_16x16x32_bf16 as S^T = K Q^T: each lane loads 16-byte pieces of one
-//     token's K row straight into the A-operand layout (token = lane % 16), so K never touches
-//     LDS; the query rows fill the 16 B-operand columns (unused columns are zero).
-//   - Online softmax in base 2 in the MFMA output layout (lane column = query row).
-//   - PV on the vector ALU: this path reads 8 flop per byte and is HBM-bound, and each lane
-//     owning 8 value columns lets V rows be read as plain coalesced 16-byte loads with no
-//     transpose.  Probabilities pass through 2 KB of LDS.
+// Layout of the work: one wave per CTA and no barriers.  This path reads 8 flop per byte, so it
+// only has to keep HBM busy: the wave streams its tokens in tiles of 16 through a ring of four
+// LDS slots, three tiles in flight, each tile's K and V rows (256 bytes per token) copied straight
+// from HBM into LDS with global_load_lds_dwordx4.  The copies are issued from inline assembly and
+// waited for with explicit vmcnt counts (the compiler would drain every copy before each LDS
+// read); page ids come through scalar loads, which count on a different counter.
+//   - QK^T on v_mfma_f32_16x16x32_bf16 as S^T = K Q^T: the query rows are the 16 B-operand
+//     columns (unused columns are zero); lane (row, g) then holds the scores of tokens 4g..4g+3.
+//   - PV on v_mfma_f32_16x16x16_bf16 as O^T = V^T P^T: those four probabilities are exactly the
+//     lane's B operand, and ds_read_b64_tr_b16 hands each lane 4 tokens of one value column.
+//
+// LDS slot layout: token t's 256-byte row at t * 256, its 16-byte chunk c at chunk position
+// c ^ swz(t) with swz a permutation of the 4 token bits.  Score-operand reads (16 tokens, one
+// chunk) and transposed value reads (4 tokens x 2 chunks) are free of bank conflicts.
 #include "device_common.hpp"
 #include "kernels.hpp"
 
 namespace gqa {
 namespace {
 
-constexpr int kD = 128;
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 
-template <int BK, int NR, bool DIRECT>
+constexpr int kD = 128;
+constexpr int kTile = 16;        // tokens per tile
+constexpr int kSlots = 4;        // LDS ring
+constexpr int kRowBytes = kD * 2;
+constexpr int kSlotBytes = 2 * kTile * kRowBytes;   // K then V
+
+__device__ __forceinline__ int swz(int t) {
+    return ((t & 3) << 1) | ((t >> 2) & 1) | (t & 8);
+}
+// Byte offset, inside a K or V block, of 16-byte chunk c of tile token t.
+__device__ __forceinline__ int vpos(int t, int c) { return t * kRowBytes + ((c ^ swz(t)) << 4); }
+
+__device__ __forceinline__ void copy16(const void *g, uint32_t m0) {
+    asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(m0) : "memory");
+}
+// s_waitcnt vmcnt(n) for a wave-uniform n in {0, 8, 16, 24}.
+__device__ __forceinline__ void wait_tiles(int later) {
+    if (later >= 3) asm volatile("s_waitcnt vmcnt(24)" ::: "memory");
+    else if (later == 2) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+    else if (later == 1) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+__device__ __forceinline__ float rows4_max(float x) {
+    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float rows4_sum(float x) {
+    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+template <bool DIRECT>
 __global__ void __launch_bounds__(64) gqa_split_kernel(const GqaSplitArgs a) {
-    constexpr int NSB = BK / 16;       // 16-token score blocks per tile
-    constexpr int TPL = BK / 4;        // tokens per lane in the PV pass (4 token groups)
-    __shared__ float pbuf[BK][17];     // probabilities [token][row], padded
-    __shared__ float rowbuf[3][16];    // alpha, m, l per row
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[kSlots * kSlotBytes];
 
     const int logical = xcd_logical_block(blockIdx.x, a.total_ctas);
     if (logical < 0) return;
@@ -37,17 +75,19 @@ __global__ void __launch_bounds__(64) gqa_split_kernel(const GqaSplitArgs a) {
     const int part = rest % a.np;
     const int b = rest / a.np;
 
-    const int lane = threadIdx.x, grp = lane >> 4, col = lane & 15;
+    const int lane = threadIdx.x, g = lane >> 4, col = lane & 15;
     const int rows_cta = a.q_len * a.group;
     const int page_mask = (1 << a.page_shift) - 1;
 
+    // Tokens of this partition: ceil(S / np) rounded up to block_k (a multiple of the tile), the
+    // last ones possibly empty; no row sees past the latest draft token.
     const int S = a.seq_lens[b];
     const int pbase = a.kv_indptr[b];
-    const int chunk = ((S + a.np - 1) / a.np + BK - 1) / BK * BK;
+    const int chunk = ((S + a.np - 1) / a.np + a.block_k - 1) / a.block_k * a.block_k;
     const int k0 = part * chunk;
-    const int block_keys = max(0, S - a.q_len + (rows_cta - 1) / a.group + 1);
-    const int k1 = min(block_keys, k0 + chunk);
-    const int ntiles = k1 > k0 ? (k1 - k0 + BK - 1) / BK : 0;
+    const int k1 = min(max(0, S - a.q_len + (rows_cta - 1) / a.group + 1), k0 + chunk);
+    const int kfull = min(k1, max(0, S - a.q_len + 1));   // tokens every row sees
+    const int ntiles = k1 > k0 ? (k1 - k0 + kTile - 1) / kTile : 0;
 
     // Query row in MFMA column `col`.
     const bool row_ok = col < rows_cta;
@@ -55,184 +95,147 @@ __global__ void __launch_bounds__(64) gqa_split_kernel(const GqaSplitArgs a) {
     const int head = kvh * a.group + (row_ok ? col - t * a.group : 0);
     const int row_end = row_ok ? min(max(0, S - a.q_len + t + 1), k1) : k0;
 
-    bf16x8 qf[4];  // B operand: row col, d = 32 s + 8 grp .. +7
+    bf16x8 qf[4];  // B operand: row col, d = 32 s + 8 g .. +7
     {
         const uint16_t *q = a.q + (int64_t(b) * a.q_len + t) * a.q_st_tok + int64_t(head) * a.q_st_head;
 #pragma unroll
         for (int s = 0; s < 4; ++s)
-            qf[s] = as_bf16x8(row_ok ? *reinterpret_cast<const uint4 *>(q + 32 * s + 8 * grp)
-                                     : make_uint4(0, 0, 0, 0));
+            qf[s] = as_bf16x8(row_ok ? *reinterpret_cast<const u32x4 *>(q + 32 * s + 8 * g)
+                                     : u32x4{0u, 0u, 0u, 0u});
     }
 
-    const size_t kv_head_off = size_t(kvh) * kD;
-    auto row_ptr = [&](const uint16_t *cache, int token) -> const uint16_t * {
-        const int page = a.page_indices[pbase + (token >> a.page_shift)];
-        const int64_t tok_slot = (int64_t(page) << a.page_shift) | (token & page_mask);
-        return cache + tok_slot * (int64_t(a.Hkv) * kD) + kv_head_off;
+    // ---- copies.  Copy i of a block moves tokens 4i..4i+3: lane L carries token 4i + L/16 and
+    // lands on chunk position L % 16 of its row, i.e. global chunk (L % 16) ^ swz(token).
+    const uint32_t lds_addr = uint32_t(reinterpret_cast<uintptr_t>(lds));
+    const int64_t row_stride = int64_t(a.Hkv) * kRowBytes;       // bytes between tokens of a page
+    const uint8_t *const kbase = reinterpret_cast<const uint8_t *>(a.k_cache) + int64_t(kvh) * kRowBytes;
+    const uint8_t *const vbase = reinterpret_cast<const uint8_t *>(a.v_cache) + int64_t(kvh) * kRowBytes;
+    // read-only, uniform: the constant address space makes these scalar loads
+    typedef const __attribute__((address_space(4))) int32_t *const_ids;
+    const const_ids pids = (const_ids)(uintptr_t)(a.page_indices + pbase);
+    // Page ids of a tile (scalar loads): tokens tb..tb+15 lie on at most two pages.
+    struct Pages { int p0, p1; };
+    auto tile_pages = [&](int tile) -> Pages {
+        const int tb = k0 + tile * kTile;
+        const int last = min(tb + kTile, k1) - 1;
+        return Pages{pids[tb >> a.page_shift], pids[last >> a.page_shift]};
+    };
+    auto issue_tile = [&](int tile, Pages pg) {
+        const int tb = k0 + tile * kTile;
+        const int first_page_end = ((tb >> a.page_shift) + 1) << a.page_shift;
+        const uint32_t m0 = lds_addr + (tile & (kSlots - 1)) * kSlotBytes;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int tl = 4 * i + (lane >> 4);
+            const int tok = min(tb + tl, k1 - 1);
+            const int page = tok < first_page_end ? pg.p0 : pg.p1;
+            const int64_t slot = (int64_t(page) << a.page_shift) | (tok & page_mask);
+            const int64_t off = slot * row_stride + (((lane & 15) ^ swz(tl)) << 4);
+            copy16(kbase + off, m0 + i * 1024);
+            copy16(vbase + off, m0 + kTile * kRowBytes + i * 1024);
+        }
     };
 
-    // Register tiles: K in A-operand layout (token 16 kb + col, d = 32 s + 8 grp) and V chunks
-    // (token grp + 4 m, values 8 col .. 8 col + 7).
-    uint4 kreg[NSB][4], vreg[TPL];
-    auto load_tile = [&](int tile) {
-        const int tb = k0 + tile * BK;
+    // Loop-invariant LDS offsets: score operand (token col, chunk 4 s + g) and the transposed value
+    // read (lane s = col of group g points at token 4 g + s / 4, columns 16 blk + 4 (s % 4)..+3,
+    // i.e. chunk 2 blk + (s % 4) / 2, byte 8 (s % 2)).
+    int k_off[4];
 #pragma unroll
-        for (int j = 0; j < NSB; ++j) {
-            const int tok = tb + 16 * j + col;
-            const bool ok = tok < k1;
-            const uint16_t *p = ok ? row_ptr(a.k_cache, tok) : nullptr;
-#pragma unroll
-            for (int s = 0; s < 4; ++s)
-                kreg[j][s] = ok ? *reinterpret_cast<const uint4 *>(p + 32 * s + 8 * grp)
-                                : make_uint4(0, 0, 0, 0);
-        }
-#pragma unroll
-        for (int m = 0; m < TPL; ++m) {
-            const int tok = tb + grp + 4 * m;
-            vreg[m] = tok < k1 ? *reinterpret_cast<const uint4 *>(row_ptr(a.v_cache, tok) + 8 * col)
-                               : make_uint4(0, 0, 0, 0);
-        }
-    };
+    for (int s = 0; s < 4; ++s) k_off[s] = vpos(col, 4 * s + g);
+    const int v_tok = 4 * g + (col >> 2);
+    const int v_c = (col & 3) >> 1, v_b = 8 * (col & 1);
 
     float m_run = kNegInf, l_run = 0.f;
-    float o[NR][8];
+    f32x4 oacc[8];
 #pragma unroll
-    for (int n = 0; n < NR; ++n)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) o[n][e] = 0.f;
+    for (int j = 0; j < 8; ++j) oacc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    if (ntiles > 0) load_tile(0);
+    Pages next_pages{0, 0};
+    if (ntiles > 0) {
+#pragma unroll
+        for (int j = 0; j < 3; ++j)
+            if (j < ntiles) issue_tile(j, tile_pages(j));
+        if (3 < ntiles) next_pages = tile_pages(3);
+    }
+
     for (int it = 0; it < ntiles; ++it) {
-        uint4 kcur[NSB][4], vcur[TPL];
-#pragma unroll
-        for (int j = 0; j < NSB; ++j)
-#pragma unroll
-            for (int s = 0; s < 4; ++s) kcur[j][s] = kreg[j][s];
-#pragma unroll
-        for (int m = 0; m < TPL; ++m) vcur[m] = vreg[m];
-        if (it + 1 < ntiles) load_tile(it + 1);
-
-        f32x4 sacc[NSB];
-#pragma unroll
-        for (int j = 0; j < NSB; ++j) {
-            sacc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int s = 0; s < 4; ++s)
-                sacc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kcur[j][s]), qf[s], sacc[j], 0, 0, 0);
+        // slot (it + 3) % 4 held tile it - 1, whose reads all finished last iteration
+        if (it + 3 < ntiles) {
+            issue_tile(it + 3, next_pages);
+            if (it + 4 < ntiles) next_pages = tile_pages(it + 4);
         }
+        wait_tiles(min(3, ntiles - 1 - it));
+        const uint8_t *kt = lds + (it & (kSlots - 1)) * kSlotBytes;
+        const uint8_t *vt = kt + kTile * kRowBytes;
 
-        const int tb = k0 + it * BK;
-        float mx = kNegInf;
+        f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int j = 0; j < NSB; ++j)
+        for (int s = 0; s < 4; ++s)
+            sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                as_bf16x8(*reinterpret_cast<const u32x4 *>(kt + k_off[s])), qf[s], sacc, 0, 0, 0);
+
+        // Online softmax in base 2; lane (col, g) holds tokens tb + 4 g + i of row col.
+        const int tb = k0 + it * kTile;
+        float sv[4];
+        const bool masked = tb + kTile > kfull;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int k = tb + 16 * j + 4 * grp + i;
-                const float sv = k < row_end ? sacc[j][i] * a.score_scale : kNegInf;
-                sacc[j][i] = sv;
-                mx = fmaxf(mx, sv);
-            }
-        mx = fmaxf(mx, xor_shuffle(mx, 16));
-        mx = fmaxf(mx, xor_shuffle(mx, 32));
+        for (int i = 0; i < 4; ++i) {
+            sv[i] = sacc[i] * a.score_scale;
+            if (masked && tb + 4 * g + i >= row_end) sv[i] = kNegInf;
+        }
+        const float mx = rows4_max(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])));
         const float m_new = fmaxf(m_run, mx);
         const float m_use = m_new == kNegInf ? 0.f : m_new;
         const float alpha = fast_exp2(m_run - m_use);
-        float psum = 0.f;
+        float p[4];
 #pragma unroll
-        for (int j = 0; j < NSB; ++j)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float p = fast_exp2(sacc[j][i] - m_use);
-                psum += p;
-                pbuf[16 * j + 4 * grp + i][col] = p;
-            }
-        psum += xor_shuffle(psum, 16);
-        psum += xor_shuffle(psum, 32);
-        l_run = l_run * alpha + psum;
+        for (int i = 0; i < 4; ++i) p[i] = fast_exp2(sv[i] - m_use);
+        l_run = l_run * alpha + rows4_sum((p[0] + p[1]) + (p[2] + p[3]));
         m_run = m_new;
-        if (grp == 0) rowbuf[0][col] = alpha;
-        __syncthreads();
-
+        if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
 #pragma unroll
-        for (int n = 0; n < NR; ++n) {
-            const float al = rowbuf[0][n];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) o[n][e] *= al;
+            for (int j = 0; j < 8; ++j) oacc[j] *= alpha;
         }
+        const s16x4 pb = __builtin_bit_cast(s16x4, u32x2{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])});
 #pragma unroll
-        for (int m = 0; m < TPL; ++m) {
-            const int tok = grp + 4 * m;
-            float v[8];
-            v[0] = bf16_lo(vcur[m].x); v[1] = bf16_hi(vcur[m].x);
-            v[2] = bf16_lo(vcur[m].y); v[3] = bf16_hi(vcur[m].y);
-            v[4] = bf16_lo(vcur[m].z); v[5] = bf16_hi(vcur[m].z);
-            v[6] = bf16_lo(vcur[m].w); v[7] = bf16_hi(vcur[m].w);
-#pragma unroll
-            for (int n = 0; n < NR; ++n) {
-                const float p = pbuf[tok][n];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) o[n][e] = fmaf(p, v[e], o[n][e]);
-            }
-        }
-        __syncthreads();
-    }
-
-    // Sum the four token groups' partial outputs; lanes 0..15 then own value columns 8 col..+7.
-#pragma unroll
-    for (int n = 0; n < NR; ++n)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            o[n][e] += xor_shuffle(o[n][e], 16);
-            o[n][e] += xor_shuffle(o[n][e], 32);
-        }
-    if (grp == 0) {
-        rowbuf[1][col] = m_run;
-        rowbuf[2][col] = l_run;
-    }
-    __syncthreads();
-    if (grp != 0) return;
-#pragma unroll
-    for (int n = 0; n < NR; ++n) {
-        if (n >= rows_cta) continue;
-        const int tn = n / a.group;
-        const int hn = kvh * a.group + (n - tn * a.group);
-        const int64_t row = (int64_t(b) * a.q_len + tn) * a.Hq + hn;
-        const float l = rowbuf[2][n];
-        const float inv = l > 0.f ? 1.f / l : 0.f;
-        if (DIRECT) {
-            uint4 w;
-            w.x = pack_bf16x2(o[n][0] * inv, o[n][1] * inv);
-            w.y = pack_bf16x2(o[n][2] * inv, o[n][3] * inv);
-            w.z = pack_bf16x2(o[n][4] * inv, o[n][5] * inv);
-            w.w = pack_bf16x2(o[n][6] * inv, o[n][7] * inv);
-            *reinterpret_cast<uint4 *>(a.out + row * kD + 8 * col) = w;
-            if (col == 0 && a.lse2_out) a.lse2_out[row] = l > 0.f ? rowbuf[1][n] + __log2f(l) : kNegInf;
-        } else {
-            float *dst = a.part_o + (row * a.np + part) * kD + 8 * col;
-            *reinterpret_cast<f32x4 *>(dst) = f32x4{o[n][0] * inv, o[n][1] * inv, o[n][2] * inv, o[n][3] * inv};
-            *reinterpret_cast<f32x4 *>(dst + 4) = f32x4{o[n][4] * inv, o[n][5] * inv, o[n][6] * inv, o[n][7] * inv};
-            if (col == 0) a.part_lse2[row * a.np + part] = l > 0.f ? rowbuf[1][n] + __log2f(l) : kNegInf;
+        for (int j = 0; j < 8; ++j) {
+            const s16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) s16x4 *)(vt + vpos(v_tok, 2 * j + v_c) + v_b));
+            oacc[j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb, oacc[j], 0, 0, 0);
         }
     }
-}
 
-template <int BK, int NR>
-hipError_t launch_shape(const GqaSplitArgs &a, bool direct, hipStream_t s) {
-    const dim3 grid(xcd_grid_size(a.total_ctas)), block(64);
-    if (direct)
-        hipLaunchKernelGGL((gqa_split_kernel<BK, NR, true>), grid, block, 0, s, a);
-    else
-        hipLaunchKernelGGL((gqa_split_kernel<BK, NR, false>), grid, block, 0, s, a);
-    return hipGetLastError();
+    // Lane (col, g) of block j holds value columns 16 j + 4 g .. + 3 of row col.
+    if (!row_ok) return;
+    const int64_t row = (int64_t(b) * a.q_len + t) * a.Hq + head;
+    const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+    const float lse2 = l_run > 0.f ? m_run + __log2f(l_run) : kNegInf;
+    if (DIRECT) {
+        uint16_t *o = a.out + row * kD + 4 * g;
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            *reinterpret_cast<uint2 *>(o + 16 * j) =
+                make_uint2(pack_bf16x2(oacc[j][0] * inv, oacc[j][1] * inv),
+                           pack_bf16x2(oacc[j][2] * inv, oacc[j][3] * inv));
+        if (g == 0 && a.lse2_out) a.lse2_out[row] = lse2;
+    } else {
+        float *o = a.part_o + (row * a.np + part) * kD + 4 * g;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) *reinterpret_cast<f32x4 *>(o + 16 * j) = oacc[j] * inv;
+        if (g == 0) a.part_lse2[row * a.np + part] = lse2;
+    }
 }
 
 }  // namespace
 
-hipError_t launch_gqa_split(const GqaSplitArgs &a, int block_k, int rows_per_cta, bool direct,
-                            hipStream_t s) {
-    if (rows_per_cta <= 8)
-        return block_k == 32 ? launch_shape<32, 8>(a, direct, s) : launch_shape<64, 8>(a, direct, s);
-    return block_k == 32 ? launch_shape<32, 16>(a, direct, s) : launch_shape<64, 16>(a, direct, s);
+hipError_t launch_gqa_split(const GqaSplitArgs &a, bool direct, hipStream_t s) {
+    if (a.block_k % kTile) return hipErrorInvalidValue;
+    const dim3 grid(xcd_grid_size(a.total_ctas)), block(64);
+    if (direct)
+        hipLaunchKernelGGL((gqa_split_kernel<true>), grid, block, 0, s, a);
+    else
+        hipLaunchKernelGGL((gqa_split_kernel<false>), grid, block, 0, s, a);
+    return hipGetLastError();
 }
 
 }  // namespace gqa

@@ -34,6 +34,7 @@ struct GqaSplitArgs {
     const uint16_t *k_cache, *v_cache;  // bf16 [pages, page_size, Hkv, 128]
     const int32_t *page_indices, *kv_indptr, *seq_lens;
     int32_t q_len, Hq, Hkv, group, page_shift, np, total_ctas;
+    int32_t block_k;              // partition lengths are rounded up to a multiple of this
     float score_scale;            // scale * log2(e)
     float *part_o, *part_lse2;
     uint16_t *out;
@@ -52,8 +53,7 @@ struct ReduceArgs {
 // Query rows one MLA split CTA covers (row_blocks = ceil(rows per request / this)).
 int mla_rows_per_cta();
 hipError_t launch_mla_split(const MlaSplitArgs &a, int d_qk, int d_v, bool direct, hipStream_t s);
-hipError_t launch_gqa_split(const GqaSplitArgs &a, int block_k, int rows_per_cta, bool direct,
-                            hipStream_t s);
+hipError_t launch_gqa_split(const GqaSplitArgs &a, bool direct, hipStream_t s);
 hipError_t launch_splitk_reduce(const ReduceArgs &a, hipStream_t s);
 hipError_t launch_fp8_to_bf16(const uint8_t *in, int64_t n, uint16_t *out, hipStream_t s);
 
