@@ -41,8 +41,10 @@ __device__ __forceinline__ int swz(int t) {
 // Byte offset, inside a K or V block, of 16-byte chunk c of tile token t.
 __device__ __forceinline__ int vpos(int t, int c) { return t * kRowBytes + ((c ^ swz(t)) << 4); }
 
+// Direct HBM -> LDS copy of 16 bytes per lane (lane L -> m0 + 16 L), non-temporal: each page is
+// read once, and the streaming hint raises gfx950's read bandwidth.
 __device__ __forceinline__ void copy16(const void *g, uint32_t m0) {
-    asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(m0) : "memory");
+    asm volatile("global_load_lds_dwordx4 %0, off nt" ::"v"(g), "{m0}"(m0) : "memory");
 }
 // s_waitcnt vmcnt(n) for a wave-uniform n in {0, 8, 16, 24}.
 __device__ __forceinline__ void wait_tiles(int later) {
