@@ -7,39 +7,44 @@
 // partition's softmax-weighted mean of values and the base-2 log-sum-exp of its scores.
 //
 // Work split (512 threads = 8 waves, one CTA per CU; waves w and w + 4 share SIMD w):
-//   - Score waves 0-3: wave w computes S^T = K Q^T for query rows 32 (w & 1) .. +31 against tile
-//     keys 32 (w >> 1) .. +31 on the block-scaled fp8 MFMA v_mfma_scale_f32_32x32x64_f8f6f4 (unit
-//     scales), then the block's softmax.  K is used as stored.  A bf16 query row, scaled by a power
-//     of two so its largest element lies in [128, 256), is the exact sum of two e4m3 vectors (hi =
-//     nearest, lo = remainder) except below e4m3's subnormal step; each product runs twice.  The
-//     block maximum is kept as an integer (the ceiling of the base-2 score), so probabilities of
-//     different blocks differ by exact powers of two; they go to LDS as fp8 hi/lo pairs of
-//     p * 2^8 (p <= 1), with the block maximum and two block sums: of the quantized probabilities
-//     (the weights PV applies, which normalize the output, so that a dominant key carries no
-//     quantization error into it) and of the exact ones (which give the log-sum-exp).
+//   - Score waves 0-3: wave w computes S^T = K Q^T for query rows 16 w .. 16 w + 15 against the 64
+//     keys of a tile on the block-scaled fp8 MFMA v_mfma_scale_f32_16x16x128_f8f6f4 (unit scales),
+//     one accumulator per 16-key block, then the rows' softmax.  K is used as stored.  A bf16 query
+//     row, scaled by a power of two so its largest element lies in [128, 256), is the exact sum of
+//     two e4m3 vectors (hi = nearest, lo = remainder) except below e4m3's subnormal step; each
+//     product runs twice.  The row maximum of a tile is kept as an integer (the ceiling of the
+//     base-2 score), so probabilities of different tiles differ by exact powers of two; they go to
+//     LDS as fp8 hi/lo pairs of p * 2^8 (p <= 1), with the maximum and two row sums: of the
+//     quantized probabilities (the weights PV applies, which normalize the output, so that a
+//     dominant key carries no quantization error into it) and of the exact ones (which give the
+//     log-sum-exp).
 //   - Value waves 4-7: wave 4 + v accumulates output columns 128 v .. +127 (line v of the key rows)
 //     for all 64 rows on the same MFMA: V^T comes from the fp8 tile through ds_read_b64_tr_b8, P^T
-//     from LDS, and the power of two that aligns each 32-key block with the row's running maximum
-//     is the MFMA's per-lane B scale.  The value waves also move the data: wave 4 + v copies line v
+//     from LDS, and the power of two that aligns the tile's row maximum with the row's running
+//     maximum is the MFMA's per-lane B scale.  The value waves also move the data: wave 4 + v copies line v
 //     of every key of a tile (and a quarter of the 64-byte rope tails of 576-byte rows) straight
 //     from HBM into LDS with global_load_lds_dwordx4, two tiles ahead, after loading the tile's
 //     slot ids the same way two tiles before that.  The copies are issued from inline assembly and
 //     waited for with explicit vmcnt counts (the compiler would drain every copy in flight before
 //     each LDS read).
-//   - One barrier per tile: in step t the score waves work on tile t while the value waves apply
-//     tile t - 1, so on each SIMD the MFMAs of one role overlap the vector work of the other.
+//   - One barrier per tile, and the score waves run one tile ahead: in step t a score wave issues
+//     the MFMAs of tile t + 1 and, between them, computes the softmax of tile t, while the value
+//     waves apply tile t - 1.  So on each SIMD the matrix core stays busy with one role's MFMAs
+//     while the vector ALU runs the other role's softmax and bookkeeping.
 //
-// LDS tile (one slot of a three-slot ring): line j (bytes 128 j .. 128 j + 127 of the key rows) of
-// the 64 keys fills 8 KiB at j * 8192, tile position P at P * 128, its 16-byte chunks permuted by
-// an XOR with (P >> 1) & 7; the 64-byte rope tails of 576-byte rows fill 4 KiB at 32768, position
-// P at P * 64, chunks permuted with (P >> 2) & 3.  A copy instruction writes 1 KiB of consecutive
-// 16-byte slots, so it moves whole 128-byte lines: one line of 8 keys (positions 8 i .. 8 i + 7
-// hold keys i, 8 + i, .., 56 + i of the tile, so that each lane's keys over the 8 instructions are
-// consecutive in the slot list), or 16 rope tails.  With these permutations the score-operand
-// reads, the transposed value reads (whose two 16-column halves take chunks c and c ^ 4) and the
-// copies are free of bank conflicts.
+// LDS (160 KiB): a four-slot ring of the key rows' first 512 bytes and a three-slot ring of the
+// 64-byte rope tails of 576-byte rows.  Line j (bytes 128 j .. 128 j + 127 of the rows) of a
+// slot's 64 keys fills 8 KiB at j * 8192, tile position P at P * 128, its 16-byte chunks permuted
+// by an XOR with (P >> 1) & 7; a tail slot holds position P at P * 64, chunks permuted with
+// (P >> 2) & 3.  A copy instruction writes 1 KiB of consecutive 16-byte slots, so it moves whole
+// 128-byte lines: one line of 8 keys (positions 8 i .. 8 i + 7 hold keys i, 8 + i, .., 56 + i of
+// the tile, so that each lane's keys over the 8 instructions are consecutive in the slot list),
+// or 16 rope tails.  With these permutations the score-operand reads, the transposed value reads
+// (whose two 16-column halves take chunks c and c ^ 4) and the copies are free of bank conflicts.
 #include "device_common.hpp"
 #include "kernels.hpp"
+
+#include <type_traits>
 
 namespace gqa {
 namespace {
@@ -53,33 +58,34 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 constexpr int kBM = 64;            // query rows per CTA
 constexpr int kBK = 64;            // keys per tile
 constexpr int kThreads = 512;
-constexpr int kSlots = 3;          // LDS tile ring
-constexpr int kIdSlots = 4;        // per value wave: ring of slot-id lists
+constexpr int kLineSlots = 4;      // ring of the rows' first 512 bytes
+constexpr int kTailSlots = 3;      // ring of the 64-byte rope tails (576-byte rows)
+constexpr int kIdSlots = 4;        // ring of slot-id lists
 constexpr int kNoMax = -(1 << 20); // integer maximum of a block with no visible key
 
 template <int DQK>
 struct MlaLayout {
-    static constexpr int kSteps = DQK / 64;               // 64-byte contraction steps per row
-    static constexpr bool kTail = DQK == 576;             // rope tails in their own region
-    static constexpr int kSlotBytes = 32768 + (kTail ? 4096 : 0);
-    static constexpr int kPOff = kSlots * kSlotBytes;     // P [2 buffers][hi, lo][64 rows][64 keys]
-    static constexpr int kMlOff = kPOff + 2 * 2 * 4096;   // ML [2][64 rows][2 blocks][m, lq, le, -]
-    static constexpr int kIdOff = kMlOff + 2 * 2048;      // ids [4 value waves][4][64]
-    static constexpr int kLdsBytes = kIdOff + 4 * kIdSlots * 256;
-    static constexpr int kCopies = 8 + (kTail ? 1 : 0);   // copy instructions per tile per wave
+    static constexpr int kSteps = DQK / 64;                 // 64-byte contraction steps per row
+    static constexpr bool kTail = DQK == 576;               // rope tails in their own ring
+    static constexpr int kTailOff = kLineSlots * 32768;
+    static constexpr int kPOff = kTailOff + (kTail ? kTailSlots * 4096 : 0);
+    static constexpr int kMlOff = kPOff + 2 * 8192;         // P [2][hi, lo][64 rows][64 keys]
+    static constexpr int kMlBytes = 3 * 256;                // M, Q, E [64 rows]
+    static constexpr int kIdOff = kMlOff + 2 * kMlBytes;
+    static constexpr int kLdsBytes = kIdOff + kIdSlots * 256;
+    static constexpr int kCopies = 8 + (kTail ? 1 : 0);     // copy instructions per tile per wave
     static_assert(DQK == 576 || DQK == 512, "row width");
     static_assert(kLdsBytes <= 160 * 1024, "LDS");
 };
 
 __device__ __forceinline__ int swz_line(int pos) { return (pos >> 1) & 7; }
 __device__ __forceinline__ int swz_tail(int pos) { return (pos >> 2) & 3; }
-// Byte offsets inside a tile slot of 16-byte chunk c of a line (c < 8) or of a rope tail (c < 4).
+// Byte offsets inside a line slot of 16-byte chunk c (< 8) of line `line`, and inside a tail slot
+// of chunk c (< 4) of a rope tail.
 __device__ __forceinline__ int line_off(int line, int pos, int c) {
     return line * 8192 + pos * 128 + ((c ^ swz_line(pos)) << 4);
 }
-__device__ __forceinline__ int tail_off(int pos, int c) {
-    return 32768 + pos * 64 + ((c ^ swz_tail(pos)) << 4);
-}
+__device__ __forceinline__ int tail_off(int pos, int c) { return pos * 64 + ((c ^ swz_tail(pos)) << 4); }
 // Slot-list index (0..63, relative to the tile) of the key at tile position pos.
 __device__ __forceinline__ int key_of_pos(int pos) { return 8 * (pos & 7) + (pos >> 3); }
 
@@ -123,15 +129,20 @@ __device__ __forceinline__ void split_fp8x4(float x0, float x1, float x2, float 
     lo = __builtin_amdgcn_cvt_pk_fp8_f32(x2 - h23.x, x3 - h23.y, lo, true);
 }
 
-// Max / sum of the values of lanes l and l ^ 32, identical in both: v_permlane32_swap hands back
-// the values of lanes l & 31 and (l & 31) + 32.
-__device__ __forceinline__ float pair_max(float x) {
-    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+// Max / sum over the four lanes l, l ^ 16, l ^ 32, l ^ 48 (one per 16-lane row of a 16x16 MFMA
+// result), identical in all four: v_permlane32_swap and v_permlane16_swap hand back the values of
+// both lanes of a pair.
+__device__ __forceinline__ float rows4_max(float x) {
+    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
-__device__ __forceinline__ float pair_sum(float x) {
-    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+__device__ __forceinline__ float rows4_sum(float x) {
+    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
 template <int DQK, int DV, bool DIRECT>
@@ -167,15 +178,21 @@ __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const MlaSplitAr
     const uint32_t lds_addr = uint32_t(reinterpret_cast<uintptr_t>(lds));
     uint8_t *const P = lds + T::kPOff;
     uint8_t *const ML = lds + T::kMlOff;
+    const int32_t *const id_ring = reinterpret_cast<const int32_t *>(lds + T::kIdOff);
 
     if (wave < 4) {
         // ================================ score wave ================================
-        const int rb = wave & 1, kb = wave >> 1;
-        const int rl = 32 * rb + n;             // row within the block
+        // Score wave w: query rows 16 w .. 16 w + 15 against all 64 keys of a tile, on the 16x16x128
+        // block-scaled fp8 MFMA (unit scales), one accumulator per 16-key block.  Lane (n16, g)
+        // holds bytes 32 g .. 32 g + 31 of each 128-byte contraction step; the 64-byte rope tail of
+        // 576-byte rows is one more step whose upper half is zero.
+        const int n16 = lane & 15, g = lane >> 4;
+        const int rl = 16 * wave + n16;         // row within the block
         const bool row_ok = rl < nrows;
+        constexpr int NS = (DQK + 127) / 128;   // contraction steps
         int p_end;                              // keys visible to this row
         float c_row;                            // base-2 score per unit of the raw product
-        i32x8 qhi[T::kSteps], qlo[T::kSteps];
+        i32x8 qhi[NS], qlo[NS];
         {
             const int r = row0 + rl;
             const int t = row_ok ? r / a.H : 0;
@@ -184,22 +201,20 @@ __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const MlaSplitAr
             const int64_t tok = int64_t(b) * a.q_len + t;
             const uint16_t *ql = a.q + tok * a.q_st_tok + int64_t(hh) * a.q_st_head;
             const uint16_t *qp = a.q_pe + tok * a.qpe_st_tok + int64_t(hh) * a.qpe_st_head;
-            // lane (n, h) of step s holds d = 64 s + 16 h + e (operand bytes 0-15) and
-            // d = 64 s + 32 + 16 h + e (bytes 16-31), e = 0..15; piece p of 8 values starts at
-            // 64 s + 32 (p >> 1) + 16 h + 8 (p & 1)
+            // piece pc (0..3) of step s: 8 values at d = 128 s + 32 g + 8 pc (none past DQK)
+            auto piece_ok = [&](int s, int pc) { return row_ok && 128 * s + 32 * g + 8 * pc < DQK; };
             float mx = 0.f;
-            if (row_ok) {
 #pragma unroll
-                for (int s = 0; s < T::kSteps; ++s)
+            for (int s = 0; s < NS; ++s)
 #pragma unroll
-                    for (int pc = 0; pc < 4; ++pc) {
-                        const u32x4 w4 = load_q8<DLAT>(ql, qp, 64 * s + 32 * (pc >> 1) + 16 * h + 8 * (pc & 1));
+                for (int pc = 0; pc < 4; ++pc) {
+                    if (!piece_ok(s, pc)) continue;
+                    const u32x4 w4 = load_q8<DLAT>(ql, qp, 128 * s + 32 * g + 8 * pc);
 #pragma unroll
-                        for (int w = 0; w < 4; ++w)
-                            mx = fmaxf(mx, fmaxf(fabsf(bf16_lo(w4[w])), fabsf(bf16_hi(w4[w]))));
-                    }
-            }
-            mx = pair_max(mx);
+                    for (int w = 0; w < 4; ++w)
+                        mx = fmaxf(mx, fmaxf(fabsf(bf16_lo(w4[w])), fabsf(bf16_hi(w4[w]))));
+                }
+            mx = rows4_max(mx);
             int ex = 0;
             if (mx > 0.f) frexpf(mx, &ex);            // mx = f * 2^ex, f in [0.5, 1)
             const float qs = ldexpf(1.f, 8 - ex);     // row maximum scaled into [128, 256)
@@ -207,11 +222,11 @@ __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const MlaSplitAr
             // second pass over the same (cached) values: the first pass's registers are free
             asm volatile("" ::: "memory");
 #pragma unroll
-            for (int s = 0; s < T::kSteps; ++s)
+            for (int s = 0; s < NS; ++s)
 #pragma unroll
                 for (int pc = 0; pc < 4; ++pc) {
-                    const u32x4 w4 = row_ok ? load_q8<DLAT>(ql, qp, 64 * s + 32 * (pc >> 1) + 16 * h + 8 * (pc & 1))
-                                            : u32x4{0u, 0u, 0u, 0u};
+                    const u32x4 w4 = piece_ok(s, pc) ? load_q8<DLAT>(ql, qp, 128 * s + 32 * g + 8 * pc)
+                                                     : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
                     for (int w = 0; w < 4; w += 2) {
                         int hi, lo;
@@ -223,89 +238,156 @@ __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const MlaSplitAr
                 }
         }
 
-        // Loop-invariant LDS offsets of this lane's K operand (key at tile position 32 kb + n):
-        // bytes 0-15 are chunk 4 (s & 1) + h of line s / 2, bytes 16-31 chunk 4 (s & 1) + 2 + h.
-        const int pos = 32 * kb + n;
-        const int k_off00 = line_off(0, pos, h), k_off01 = line_off(0, pos, 2 + h);
-        const int k_off10 = line_off(0, pos, 4 + h), k_off11 = line_off(0, pos, 6 + h);
-        const int k_tail0 = tail_off(pos, h), k_tail1 = tail_off(pos, 2 + h);
-        // P words of this lane: keys 32 kb + 8 q + 4 h .. + 3 of row rl (q = 0..3), at 16-byte
-        // chunk 2 kb + q / 2 of the 64-byte row, chunks swizzled by the row
+        // Loop-invariant LDS offsets of this lane's K operand (key at tile position 16 kbk + n16,
+        // chunks 2 g and 2 g + 1 of line s; the swizzle does not depend on kbk, so 16-key block kbk
+        // adds 2048 bytes, line s 8192).  Rope tails: chunks 2 g, 2 g + 1 (g < 2), block kbk
+        // adds 1024 bytes.
+        const int k_off0 = line_off(0, n16, 2 * g), k_off1 = line_off(0, n16, 2 * g + 1);
+        const int k_tail0 = T::kTailOff + tail_off(n16, (2 * g) & 3);
+        const int k_tail1 = T::kTailOff + tail_off(n16, (2 * g + 1) & 3);
+        // P words of this lane: keys 16 kbk + 4 g .. + 3 of row rl, 16-byte chunk kbk of the 64-byte
+        // row, chunks swizzled by the row
         const int p_sw = (rl >> 2) & 3;
         int p_wr[4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-            p_wr[q] = rl * 64 + (((2 * kb + (q >> 1)) ^ p_sw) << 4) + 8 * (q & 1) + 4 * h;
-        // Score v (= 4 q + r) of this lane is key 8 q + 4 h + r of the block, tile position
-        // 32 kb + 8 q + 4 h + r, slot-list index 32 h + 8 r + 4 kb + q (key_of_pos).
-        const int kidx_base = 32 * h + 4 * kb;
+        for (int kbk = 0; kbk < 4; ++kbk) p_wr[kbk] = rl * 64 + ((kbk ^ p_sw) << 4) + 4 * g;
+        // Score i of block kbk of this lane is tile position 16 kbk + 4 g + i, slot-list index
+        // 32 (g & 1) + (g >> 1) + 8 i + 2 kbk (key_of_pos).
+        const int kidx_base = 32 * (g & 1) + (g >> 1);
 
-        for (int t = 0; t < ntiles; ++t) {
-            if (t == 0) __syncthreads();   // tile 0 landed (the value waves' prologue)
-            const uint8_t *tb = lds + (t % kSlots) * T::kSlotBytes;
-            f32x16 sacc;
+        // K operand reads and the MFMAs of 16-key block kbk of the scores of tile t (10 for
+        // 576-byte rows, 8 for 512-byte rows).
+        auto qk_block = [&](int t, int kbk, f32x4 &sacc) {
+            const uint8_t *lb = lds + (t % kLineSlots) * 32768 + 2048 * kbk;
+            const uint8_t *tlb = lds + (t % kTailSlots) * 4096 + 1024 * kbk;
+            sacc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int i = 0; i < 16; ++i) sacc[i] = 0.f;
-#pragma unroll
-            for (int s = 0; s < T::kSteps; ++s) {
+            for (int s = 0; s < NS; ++s) {
                 u32x4 lo16, hi16;
-                if (T::kTail && s == T::kSteps - 1) {
-                    lo16 = *reinterpret_cast<const u32x4 *>(tb + k_tail0);
-                    hi16 = *reinterpret_cast<const u32x4 *>(tb + k_tail1);
+                if (T::kTail && s == NS - 1) {
+                    // lanes g >= 2 read the chunks of lanes g - 2; their query bytes are zero
+                    lo16 = *reinterpret_cast<const u32x4 *>(tlb + k_tail0);
+                    hi16 = *reinterpret_cast<const u32x4 *>(tlb + k_tail1);
                 } else {
-                    const int lb = (s >> 1) * 8192;
-                    lo16 = *reinterpret_cast<const u32x4 *>(tb + lb + ((s & 1) ? k_off10 : k_off00));
-                    hi16 = *reinterpret_cast<const u32x4 *>(tb + lb + ((s & 1) ? k_off11 : k_off01));
+                    lo16 = *reinterpret_cast<const u32x4 *>(lb + 8192 * s + k_off0);
+                    hi16 = *reinterpret_cast<const u32x4 *>(lb + 8192 * s + k_off1);
                 }
                 const i32x8 kraw = i32x8{int(lo16.x), int(lo16.y), int(lo16.z), int(lo16.w),
                                          int(hi16.x), int(hi16.y), int(hi16.z), int(hi16.w)};
-                sacc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kraw, qhi[s], sacc, 0, 0, 0, 127, 0, 127);
-                sacc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kraw, qlo[s], sacc, 0, 0, 0, 127, 0, 127);
+                sacc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(kraw, qhi[s], sacc, 0, 0, 0, 127, 0, 127);
+                sacc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(kraw, qlo[s], sacc, 0, 0, 0, 127, 0, 127);
             }
+        };
 
-            // Softmax of this 32-key block in base 2 with an integer maximum m:
-            // p * 2^8 = 2^(score - m + 8) in (0, 256].
-            if (t >= n_full) {
+        // Softmax of this lane's row over tile t in base 2 with an integer maximum m:
+        // p * 2^8 = 2^(score - m + 8) in (0, 256], written to P(t) with m and the row sums.
+        struct Soft {
+            float bias, esum, qsum;
+            int m;
+        };
+        auto sm_max = [&](int t, f32x4 (&sacc)[4], auto masked) -> Soft {
+            if constexpr (decltype(masked)::value) {
                 const int thr = p_end - k0 - t * kBK - kidx_base;   // visible: index - base < thr
 #pragma unroll
-                for (int vv = 0; vv < 16; ++vv)
-                    if (8 * (vv & 3) + (vv >> 2) >= thr) sacc[vv] = kNegInf;
-            }
-            float mx = sacc[0];
+                for (int kbk = 0; kbk < 4; ++kbk)
 #pragma unroll
-            for (int vv = 1; vv < 16; ++vv) mx = fmaxf(mx, sacc[vv]);
-            mx = pair_max(mx);
-            const int m = mx == kNegInf ? kNoMax : int(ceilf(mx * c_row));
-            const float bias = float(8 - m);
-            float p[16];
-            float esum = 0.f, qsum = 0.f;
-#pragma unroll
-            for (int vv = 0; vv < 16; ++vv) {
-                p[vv] = fast_exp2(fmaf(sacc[vv], c_row, bias));
-                esum += p[vv];
+                    for (int i = 0; i < 4; ++i)
+                        if (8 * i + 2 * kbk >= thr) sacc[kbk][i] = kNegInf;
             }
-            int whi[4], wlo[4];
+            float m4[4];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                split_fp8x4(p[4 * q], p[4 * q + 1], p[4 * q + 2], p[4 * q + 3], whi[q], wlo[q]);
-                const f32x2 h01 = __builtin_amdgcn_cvt_pk_f32_fp8(whi[q], false);
-                const f32x2 h23 = __builtin_amdgcn_cvt_pk_f32_fp8(whi[q], true);
-                const f32x2 l01 = __builtin_amdgcn_cvt_pk_f32_fp8(wlo[q], false);
-                const f32x2 l23 = __builtin_amdgcn_cvt_pk_f32_fp8(wlo[q], true);
-                qsum += ((h01.x + l01.x) + (h01.y + l01.y)) + ((h23.x + l23.x) + (h23.y + l23.y));
-            }
-            esum = pair_sum(esum);
-            qsum = pair_sum(qsum);
+            for (int kbk = 0; kbk < 4; ++kbk)
+                m4[kbk] = fmaxf(fmaxf(sacc[kbk][0], sacc[kbk][1]), fmaxf(sacc[kbk][2], sacc[kbk][3]));
+            const float mx = rows4_max(fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3])));
+            Soft sf;
+            sf.m = mx == kNegInf ? kNoMax : int(ceilf(mx * c_row));
+            sf.bias = float(8 - sf.m);
+            sf.esum = sf.qsum = 0.f;
+            return sf;
+        };
+        auto sm_block = [&](int t, const f32x4 &sc, int kbk, Soft &sf) {
+            const float p0 = fast_exp2(fmaf(sc[0], c_row, sf.bias));
+            const float p1 = fast_exp2(fmaf(sc[1], c_row, sf.bias));
+            const float p2 = fast_exp2(fmaf(sc[2], c_row, sf.bias));
+            const float p3 = fast_exp2(fmaf(sc[3], c_row, sf.bias));
+            int whi, wlo;
+            split_fp8x4(p0, p1, p2, p3, whi, wlo);
+            const f32x2 h01 = __builtin_amdgcn_cvt_pk_f32_fp8(whi, false);
+            const f32x2 h23 = __builtin_amdgcn_cvt_pk_f32_fp8(whi, true);
+            const f32x2 l01 = __builtin_amdgcn_cvt_pk_f32_fp8(wlo, false);
+            const f32x2 l23 = __builtin_amdgcn_cvt_pk_f32_fp8(wlo, true);
+            sf.esum += (p0 + p1) + (p2 + p3);
+            sf.qsum += ((h01.x + l01.x) + (h01.y + l01.y)) + ((h23.x + l23.x) + (h23.y + l23.y));
             uint8_t *pb = P + (t & 1) * 8192;
+            *reinterpret_cast<int *>(pb + p_wr[kbk]) = whi;
+            *reinterpret_cast<int *>(pb + 4096 + p_wr[kbk]) = wlo;
+        };
+        auto sm_finish = [&](int t, Soft &sf) {
+            const float esum = rows4_sum(sf.esum);
+            const float qsum = rows4_sum(sf.qsum);
+            // the four lanes of a row hold the same values and all store them (no branch, which
+            // would split the step's scheduling region)
+            uint8_t *mlb = ML + (t & 1) * T::kMlBytes + rl * 4;
+            *reinterpret_cast<int *>(mlb) = sf.m;
+            *reinterpret_cast<float *>(mlb + 256) = qsum;
+            *reinterpret_cast<float *>(mlb + 512) = esum;
+        };
+
+        // Step t: the MFMAs of tile t + 1 (the last tile again at the end; its scores are then
+        // unused), one 16-key block per scheduling region, each region also holding a piece of
+        // the softmax of tile t (whose scores `cur` holds), so the MFMAs and the vector work
+        // overlap while only one block's K operands are in registers.
+        auto step = [&](int t, f32x4 (&cur)[4], f32x4 (&next)[4], auto masked) {
+            const int tq = min(t + 1, ntiles - 1);
+            qk_block(tq, 0, next[0]);
+            Soft sf = sm_max(t, cur, masked);
+            __builtin_amdgcn_sched_barrier(0);
+            qk_block(tq, 1, next[1]);
+            sm_block(t, cur[0], 0, sf);
+            __builtin_amdgcn_sched_barrier(0);
+            qk_block(tq, 2, next[2]);
+            sm_block(t, cur[1], 1, sf);
+            __builtin_amdgcn_sched_barrier(0);
+            qk_block(tq, 3, next[3]);
+            sm_block(t, cur[2], 2, sf);
+            sm_block(t, cur[3], 3, sf);
+            sm_finish(t, sf);
+            __syncthreads();   // P(t) published; tile t + 2 landed
+        };
+
+        using yes = std::integral_constant<bool, true>;
+        using no = std::integral_constant<bool, false>;
+        if (ntiles > 0) {
+            __syncthreads();   // slot ids of tiles 0-3 loaded
+            __syncthreads();   // their reads done
+            __syncthreads();   // tiles 0 and 1 landed
+            f32x4 sa[4], sb[4];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                *reinterpret_cast<int *>(pb + p_wr[q]) = whi[q];
-                *reinterpret_cast<int *>(pb + 4096 + p_wr[q]) = wlo[q];
+            for (int kbk = 0; kbk < 4; ++kbk) {
+                qk_block(0, kbk, sa[kbk]);
+                __builtin_amdgcn_sched_barrier(0);   // one block's K operands in registers at a time
             }
-            if (h == 0)
-                *reinterpret_cast<i32x4 *>(ML + (t & 1) * 2048 + rl * 32 + kb * 16) =
-                    i32x4{m, __float_as_int(qsum), __float_as_int(esum), 0};
-            __syncthreads();   // P(t) published; tile t + 1 landed
+            __syncthreads();   // tile 0 read: step 0's copies may refill its tail slot
+            int t = 0;
+            for (; t + 1 < n_full; t += 2) {
+                step(t, sa, sb, no{});
+                step(t + 1, sb, sa, no{});
+            }
+            if (t < n_full) {   // one unmasked tile left: its scores are in sa
+                step(t, sa, sb, no{});
+                ++t;
+                for (; t + 1 < ntiles; t += 2) {
+                    step(t, sb, sa, yes{});
+                    step(t + 1, sa, sb, yes{});
+                }
+                if (t < ntiles) step(t, sb, sa, yes{});
+            } else {
+                for (; t + 1 < ntiles; t += 2) {
+                    step(t, sa, sb, yes{});
+                    step(t + 1, sb, sa, yes{});
+                }
+                if (t < ntiles) step(t, sa, sb, yes{});
+            }
         }
         return;
     }
@@ -315,6 +397,7 @@ __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const MlaSplitAr
     // ---- copies.  Instruction i writes tile positions 8 i .. 8 i + 7 of line v: lane L carries
     // slot-list key 8 (L >> 3) + i at position 8 i + (L >> 3), chunk position L & 7, i.e. global
     // chunk (L & 7) ^ swz_line(position).  The tail copy writes positions 16 v .. 16 v + 15.
+    // Value wave 0 also loads every tile's slot ids into the shared id ring.
     const int jgrp = lane >> 3;
     const int tail_pos = 16 * v + (lane >> 2);
     const int tail_chunk = 512 + 16 * ((lane & 3) ^ swz_tail(tail_pos));
@@ -322,39 +405,38 @@ __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const MlaSplitAr
     const int32_t *const ibase = a.kv_indices + base;
     const uint64_t kv_stride = uint64_t(a.kv_stride);
     const uint8_t *const kv_line = a.kv + 128 * v;
-    const uint32_t id_lds = lds_addr + T::kIdOff + v * (kIdSlots * 256);
-    const int32_t *const id_ring = reinterpret_cast<const int32_t *>(lds + T::kIdOff + v * (kIdSlots * 256));
+    const bool id_loader = v == 0;
 
     auto issue_ids = [&](int tile) {
-        if (tile < ntiles)
-            copy4(ibase + min(k0 + tile * kBK + lane, k1 - 1), id_lds + (tile % kIdSlots) * 256);
+        if (id_loader && tile < ntiles)
+            copy4(ibase + min(k0 + tile * kBK + lane, k1 - 1),
+                  lds_addr + T::kIdOff + (tile % kIdSlots) * 256);
     };
     auto issue_rows = [&](int tile) {
         if (tile >= ntiles) return;
         const int32_t *ids = id_ring + (tile % kIdSlots) * 64;
         const u32x4 ia = *reinterpret_cast<const u32x4 *>(ids + 8 * jgrp);
         const u32x4 ib = *reinterpret_cast<const u32x4 *>(ids + 8 * jgrp + 4);
-        const uint32_t slot = lds_addr + (tile % kSlots) * T::kSlotBytes;
+        const uint32_t lslot = lds_addr + (tile % kLineSlots) * 32768 + v * 8192;
         const uint32_t idv[8] = {ia.x, ia.y, ia.z, ia.w, ib.x, ib.y, ib.z, ib.w};
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const int gc = (lane & 7) ^ (((i & 1) << 2) | (jgrp >> 1));
-            copy16(kv_line + uint64_t(idv[i]) * kv_stride + 16 * gc, slot + v * 8192 + 1024 * i);
+            copy16(kv_line + uint64_t(idv[i]) * kv_stride + 16 * gc, lslot + 1024 * i);
         }
         if (T::kTail) {
             const uint32_t idt = uint32_t(ids[tail_key]);
-            copy16(a.kv + uint64_t(idt) * kv_stride + tail_chunk, slot + 32768 + 1024 * v);
+            copy16(a.kv + uint64_t(idt) * kv_stride + tail_chunk,
+                   lds_addr + T::kTailOff + (tile % kTailSlots) * 4096 + 1024 * v);
         }
     };
-    // Issue order: ids(0), ids(1), then rows(j), ids(j + 2) for j = 0, 1, 2, ...; operations for
-    // tiles >= ntiles are skipped.  Copies retire in issue order.
+    // Issue order: ids(0..3), then rows(0), rows(1), rows(2), ids(4), ids(5), then rows(j),
+    // ids(j + 3) for j = 3, 4, ...; ids only in value wave 0, operations for tiles >= ntiles
+    // skipped.  Copies retire in issue order.  Rows(j) are read in step j - 1 (the scores of tile
+    // j) and step j + 1 (its values); ids(j) in step j - 3 (the copies of rows(j)).
     constexpr int NC = T::kCopies;
     auto cnt_rows = [&](int j) { return j >= 0 && j < ntiles ? NC : 0; };
-    auto cnt_ids = [&](int j) { return j >= 0 && j < ntiles ? 1 : 0; };
-    // before rows(j): ids(j) landed; issued after it: rows(j - 1), ids(j + 1)
-    auto wait_ids = [&](int j) { wait_vmem(cnt_rows(j - 1) + cnt_ids(j + 1)); };
-    // rows(j) landed; issued after it: ids(j + 2), rows(j + 1), ids(j + 3)
-    auto wait_rows = [&](int j) { wait_vmem(cnt_ids(j + 2) + cnt_rows(j + 1) + cnt_ids(j + 3)); };
+    auto cnt_ids = [&](int j) { return id_loader && j >= 0 && j < ntiles ? 1 : 0; };
 
     // ---- PV operands.  V^T (A operand) of column block cb: lane (m, h) holds keys 16 h + 0..15
     // (bytes 0-15) and 32 + 16 h + 0..15 (bytes 16-31) of column m; a transposed read hands a
@@ -390,20 +472,20 @@ __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const MlaSplitAr
     // PV of tile t: running maxima and sums, the rescale when a maximum moved, then 16 MFMAs.
     auto pv = [&](int t) {
         const uint8_t *pbuf = P + (t & 1) * 8192;
-        const uint8_t *mlb = ML + (t & 1) * 2048;
+        const uint8_t *mlb = ML + (t & 1) * T::kMlBytes;
         int sc[2];
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb) {
-            const i32x4 m0 = *reinterpret_cast<const i32x4 *>(mlb + (32 * rb + n) * 32);
-            const i32x4 m1 = *reinterpret_cast<const i32x4 *>(mlb + (32 * rb + n) * 32 + 16);
-            const int m_new = max(mc[rb], max(m0.x, m1.x));
+            const int row = 32 * rb + n;
+            const int mt = *reinterpret_cast<const int *>(mlb + row * 4);
+            const float qt = *reinterpret_cast<const float *>(mlb + 256 + row * 4);
+            const float et = *reinterpret_cast<const float *>(mlb + 512 + row * 4);
+            const int m_new = max(mc[rb], mt);
             const float alpha = ldexpf(1.f, mc[rb] - m_new);
-            lq[rb] = lq[rb] * alpha + ldexpf(__int_as_float(m0.y), m0.x - m_new - 8) +
-                     ldexpf(__int_as_float(m1.y), m1.x - m_new - 8);
-            le[rb] = le[rb] * alpha + ldexpf(__int_as_float(m0.z), m0.x - m_new - 8) +
-                     ldexpf(__int_as_float(m1.z), m1.x - m_new - 8);
+            lq[rb] = lq[rb] * alpha + ldexpf(qt, mt - m_new - 8);
+            le[rb] = le[rb] * alpha + ldexpf(et, mt - m_new - 8);
             mc[rb] = m_new;
-            sc[rb] = max(0, 127 - 8 + (h ? m1.x : m0.x) - m_new);
+            sc[rb] = max(0, 127 - 8 + mt - m_new);
             if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
 #pragma unroll
                 for (int cb = 0; cb < 4; ++cb) oacc[rb][cb] *= alpha;
@@ -419,14 +501,14 @@ __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const MlaSplitAr
             ph[rb] = i32x8{int(a0.x), int(a0.y), int(a0.z), int(a0.w), int(a1.x), int(a1.y), int(a1.z), int(a1.w)};
             pl[rb] = i32x8{int(b0.x), int(b0.y), int(b0.z), int(b0.w), int(b1.x), int(b1.y), int(b1.z), int(b1.w)};
         }
-        const uint8_t *tb = lds + (t % kSlots) * T::kSlotBytes;
+        const uint8_t *lb = lds + (t % kLineSlots) * 32768;
 #pragma unroll
         for (int cb = 0; cb < 4; ++cb) {
             int2v raw[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r)
                 raw[r] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-                    (__attribute__((address_space(3))) int2v *)(tb + v_off[cb][r]));
+                    (__attribute__((address_space(3))) int2v *)(lb + v_off[cb][r]));
             const i32x8 vt = i32x8{raw[0].x, raw[0].y, raw[1].x, raw[1].y,
                                    raw[2].x, raw[2].y, raw[3].x, raw[3].y};
 #pragma unroll
@@ -442,24 +524,32 @@ __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const MlaSplitAr
     if (ntiles > 0) {
         issue_ids(0);
         issue_ids(1);
-        wait_ids(0);
-        issue_rows(0);
         issue_ids(2);
-        wait_ids(1);
-        issue_rows(1);
         issue_ids(3);
-        wait_rows(0);
-        __syncthreads();   // tile 0 landed
+        wait_vmem(0);
+        __syncthreads();   // slot ids of tiles 0-3 loaded
+        issue_rows(0);
+        issue_rows(1);
+        issue_rows(2);
+        __syncthreads();   // every read of id slots 0-2 done
+        issue_ids(4);
+        issue_ids(5);
+        // rows(0), rows(1) landed; issued after rows(1): rows(2), ids(4), ids(5)
+        wait_vmem(cnt_rows(2) + cnt_ids(4) + cnt_ids(5));
+        __syncthreads();   // tiles 0 and 1 landed
+        __syncthreads();   // the score waves read tile 0 (tail slot 0 is refilled in step 0)
         for (int t = 0; t < ntiles; ++t) {
             if (t > 0) pv(t - 1);
-            // slot (t + 2) % 3 held tile t - 1: every read of it is done (the score waves' in the
-            // previous step, this wave's own line just above)
+            // line slot (t + 3) % 4 held tile t - 1 and tail slot (t + 3) % 3 tile t: every read
+            // of them is done (the score waves' before the previous barrier, this wave's own
+            // line just above)
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-            wait_ids(t + 2);
-            issue_rows(t + 2);
-            issue_ids(t + 4);
-            if (t + 1 < ntiles) wait_rows(t + 1);
-            __syncthreads();   // P(t) published; tile t + 1 landed
+            issue_rows(t + 3);
+            issue_ids(t + 6);
+            // rows(t + 2) and ids(t + 4) landed: everything issued before ids(t + 5) (value wave
+            // 0) or before rows(t + 3) (the others)
+            wait_vmem(cnt_ids(t + 5) + cnt_rows(t + 3) + cnt_ids(t + 6));
+            __syncthreads();   // P(t) published; tile t + 2 landed
         }
         pv(ntiles - 1);
     }
