@@ -133,24 +133,35 @@ class Case:
         return self.kv_bytes() + idx + q_bytes + writes
 
 
-SPLIT_SOURCES = ("mla_split.hip", "device_common.hpp", "kernels.hpp")
+# Counter summaries under profiles/, per timed workload: the file and the sources its kernel is
+# compiled from (hashed in this order).
+COUNTER_PROFILES = {
+    "mla_h64_b16_s131072_q1": ("mla_split_b16_s131072_counters.txt",
+                               ("mla_split.hip", "device_common.hpp", "kernels.hpp")),
+    "gqa_b32_hq64_hkv8_d128_p16": ("gqa_split_b32_hq64_hkv8_counters.txt",
+                                   ("gqa_split.hip", "device_common.hpp", "kernels.hpp")),
+}
 
 
-def split_source_sha256():
-    """sha256 over the sources the MLA split kernel is compiled from, in a fixed order."""
+def source_sha256(names):
+    """sha256 over kernel sources under the package's csrc/, in the given order."""
     import hashlib
     h = hashlib.sha256()
-    for name in SPLIT_SOURCES:
+    for name in names:
         with open(os.path.join(ROOT, "gqa_plan_splits_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
 
 
-def measured_traffic():
-    """HBM bytes per split launch from the committed rocprofv3 counter summary, scaled by the
-    plain-copy calibration recorded beside it; None unless the summary was taken on the current
-    kernel sources (their sha256 must match)."""
-    path = os.path.join(ROOT, "profiles", "mla_split_traffic.txt")
+def measured_counters(workload):
+    """HBM bytes per split launch and the MFMA busy fraction, from the committed rocprofv3 counter
+    summary of this workload; FETCH_SIZE / WRITE_SIZE are scaled by the plain-copy calibration
+    recorded beside them. None unless the summary was taken on the current kernel sources (their
+    sha256 must match)."""
+    if workload not in COUNTER_PROFILES:
+        return None
+    fname, sources = COUNTER_PROFILES[workload]
+    path = os.path.join(ROOT, "profiles", fname)
     if not os.path.exists(path):
         return None
     vals = {}
@@ -159,11 +170,14 @@ def measured_traffic():
         if "=" in line:
             k, v = (x.strip() for x in line.split("=", 1))
             vals[k] = v
-    if vals.get("kernel_source_sha256") != split_source_sha256():
+    if vals.get("kernel_source_sha256") != source_sha256(sources):
         return None
     fetch = float(vals["fetch_kib_per_dispatch"]) * float(vals["copy_bytes"]) / float(vals["copy_fetch_kib"])
     write = float(vals["write_kib_per_dispatch"]) * float(vals["copy_bytes"]) / float(vals["copy_write_kib"])
-    return int(fetch + write)
+    # SQ_VALU_MFMA_BUSY_CYCLES is summed over every SIMD; GRBM_GUI_ACTIVE over the XCDs.
+    busy = float(vals["mfma_busy_cycles"]) / (
+        float(vals["grbm_gui_active"]) / float(vals["xcds"]) * float(vals["simds"]))
+    return {"traffic": int(fetch + write), "mfma_busy": round(busy, 4)}
 
 
 def settle(fn, ms):
@@ -298,6 +312,7 @@ def main():
     case, ms, ms_split, steps = headline
     alg = case.split_algorithmic_bytes()
     achieved = alg / (ms_split * 1e-3) / 1e9
+    counters = measured_counters(args.workload)
     inp = case.inp
     result = {
         "metric": "split-KV decode KV-read GB/s (% of HBM peak) and us/call per config",
@@ -330,8 +345,8 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": (measured_traffic()
-                        if case.is_mla and args.workload == "mla_h64_b16_s131072_q1" else None),
+            "traffic": counters["traffic"] if counters else None,
+            "mfma_busy": counters["mfma_busy"] if counters else None,
             "algorithmic_bytes": alg,
             "avg_launch_us": round(ms_split * 1e3, 2),
         },
