@@ -163,6 +163,7 @@ int launch_split(const gqa_decode_problem *p, const Derived &d, int64_t np, int 
         a.page_indices = p->kv_indices;
         a.kv_indptr = p->kv_indptr;
         a.seq_lens = p->seq_lens;
+        a.batch = int32_t(p->batch);
         a.q_len = int32_t(p->q_len);
         a.Hq = int32_t(p->num_heads);
         a.Hkv = int32_t(p->num_kv_heads);

@@ -8,15 +8,21 @@
 // softmax-weighted mean of values and the base-2 log-sum-exp of its scores.
 //
 // Layout of the work: one wave per CTA and no barriers.  This path reads 8 flop per byte, so it
-// only has to keep HBM busy: the wave streams its tokens in tiles of 16 through a ring of four
-// LDS slots, three tiles in flight, each tile's K and V rows (256 bytes per token) copied straight
-// from HBM into LDS with global_load_lds_dwordx4.  The copies are issued from inline assembly and
+// only has to keep HBM busy: the wave streams its tokens in tiles of 16 through a ring of three
+// LDS slots, two tiles in flight, each tile's K and V rows (256 bytes per token) copied straight
+// from HBM into LDS with global_load_lds_dwordx4.  The small ring (24 KiB) lets six CTAs share a
+// CU; on MI355X more waves with shallower rings move more bytes than fewer with deeper ones.  The copies are issued from inline assembly and
 // waited for with explicit vmcnt counts (the compiler would drain every copy before each LDS
 // read); page ids come through scalar loads, which count on a different counter.
 //   - QK^T on v_mfma_f32_16x16x32_bf16 as S^T = K Q^T: the query rows are the 16 B-operand
 //     columns (unused columns are zero); lane (row, g) then holds the scores of tokens 4g..4g+3.
 //   - PV on v_mfma_f32_16x16x16_bf16 as O^T = V^T P^T: those four probabilities are exactly the
 //     lane's B operand, and ds_read_b64_tr_b16 hands each lane 4 tokens of one value column.
+//
+// Order of the CTAs: CTAs share no data, so they are dispatched in plain order, which deals them
+// round-robin over the 8 XCDs and gives each XCD an equal share of every request.  A CTA's work
+// is proportional to its request's length, so (for batches of up to 64 requests) requests are
+// taken longest first: the CTAs that start last are the shortest, and the grid drains evenly.
 //
 // LDS slot layout: token t's 256-byte row at t * 256, its 16-byte chunk c at chunk position
 // c ^ swz(t) with swz a permutation of the 4 token bits.  Score-operand reads (16 tokens, one
@@ -31,7 +37,7 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kD = 128;
 constexpr int kTile = 16;        // tokens per tile
-constexpr int kSlots = 4;        // LDS ring
+constexpr int kSlots = 3;        // LDS ring
 constexpr int kRowBytes = kD * 2;
 constexpr int kSlotBytes = 2 * kTile * kRowBytes;   // K then V
 
@@ -46,10 +52,11 @@ __device__ __forceinline__ int vpos(int t, int c) { return t * kRowBytes + ((c ^
 __device__ __forceinline__ void copy16(const void *g, uint32_t m0) {
     asm volatile("global_load_lds_dwordx4 %0, off nt" ::"v"(g), "{m0}"(m0) : "memory");
 }
-// s_waitcnt vmcnt(n) for a wave-uniform n in {0, 8, 16, 24}.
+// s_waitcnt vmcnt(n) for a wave-uniform n in {0, 8, 16}: the copies of `later` younger tiles
+// (8 copy instructions each) may still be in flight.
 __device__ __forceinline__ void wait_tiles(int later) {
-    if (later >= 3) asm volatile("s_waitcnt vmcnt(24)" ::: "memory");
-    else if (later == 2) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+    static_assert(kSlots == 3, "wait_tiles covers up to two younger tiles");
+    if (later >= 2) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
     else if (later == 1) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
     else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
@@ -66,18 +73,32 @@ __device__ __forceinline__ float rows4_sum(float x) {
     return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
+// The request of rank r when the batch is ordered by decreasing length (ties by index), for
+// batches of up to 64 requests (lane i ranks request i); larger batches keep their own order.
+__device__ __forceinline__ int request_by_length(const int32_t *seq_lens, int batch, int r, int lane) {
+    if (batch > 64) return r;
+    const int si = lane < batch ? seq_lens[lane] : -1;
+    int rank = 0;
+    for (int j = 0; j < batch; ++j) {
+        const int sj = __builtin_amdgcn_readlane(si, j);
+        rank += (sj > si) | ((sj == si) & (j < lane));
+    }
+    // ranks are a permutation of 0 .. batch - 1, so exactly one lane matches r < batch
+    const uint64_t m = __builtin_amdgcn_ballot_w64(lane < batch && rank == r);
+    return __builtin_amdgcn_readfirstlane(int(__builtin_ctzll(m)));
+}
+
 template <bool DIRECT>
 __global__ void __launch_bounds__(64) gqa_split_kernel(const GqaSplitArgs a) {
     __shared__ __attribute__((aligned(1024))) uint8_t lds[kSlots * kSlotBytes];
 
-    const int logical = xcd_logical_block(blockIdx.x, a.total_ctas);
-    if (logical < 0) return;
+    const int logical = blockIdx.x;
+    if (logical >= a.total_ctas) return;
+    const int lane = threadIdx.x, g = lane >> 4, col = lane & 15;
     const int kvh = logical % a.Hkv;
     const int rest = logical / a.Hkv;
     const int part = rest % a.np;
-    const int b = rest / a.np;
-
-    const int lane = threadIdx.x, g = lane >> 4, col = lane & 15;
+    const int b = request_by_length(a.seq_lens, a.batch, rest / a.np, lane);
     const int rows_cta = a.q_len * a.group;
     const int page_mask = (1 << a.page_shift) - 1;
 
@@ -125,7 +146,7 @@ __global__ void __launch_bounds__(64) gqa_split_kernel(const GqaSplitArgs a) {
     auto issue_tile = [&](int tile, Pages pg) {
         const int tb = k0 + tile * kTile;
         const int first_page_end = ((tb >> a.page_shift) + 1) << a.page_shift;
-        const uint32_t m0 = lds_addr + (tile & (kSlots - 1)) * kSlotBytes;
+        const uint32_t m0 = lds_addr + (tile % kSlots) * kSlotBytes;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int tl = 4 * i + (lane >> 4);
@@ -155,19 +176,19 @@ __global__ void __launch_bounds__(64) gqa_split_kernel(const GqaSplitArgs a) {
     Pages next_pages{0, 0};
     if (ntiles > 0) {
 #pragma unroll
-        for (int j = 0; j < 3; ++j)
+        for (int j = 0; j < kSlots - 1; ++j)
             if (j < ntiles) issue_tile(j, tile_pages(j));
-        if (3 < ntiles) next_pages = tile_pages(3);
+        if (kSlots - 1 < ntiles) next_pages = tile_pages(kSlots - 1);
     }
 
     for (int it = 0; it < ntiles; ++it) {
-        // slot (it + 3) % 4 held tile it - 1, whose reads all finished last iteration
-        if (it + 3 < ntiles) {
-            issue_tile(it + 3, next_pages);
-            if (it + 4 < ntiles) next_pages = tile_pages(it + 4);
+        // slot (it + 2) % 3 held tile it - 1, whose reads all finished last iteration
+        if (it + kSlots - 1 < ntiles) {
+            issue_tile(it + kSlots - 1, next_pages);
+            if (it + kSlots < ntiles) next_pages = tile_pages(it + kSlots);
         }
-        wait_tiles(min(3, ntiles - 1 - it));
-        const uint8_t *kt = lds + (it & (kSlots - 1)) * kSlotBytes;
+        wait_tiles(min(kSlots - 1, ntiles - 1 - it));
+        const uint8_t *kt = lds + (it % kSlots) * kSlotBytes;
         const uint8_t *vt = kt + kTile * kRowBytes;
 
         f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -232,7 +253,7 @@ __global__ void __launch_bounds__(64) gqa_split_kernel(const GqaSplitArgs a) {
 
 hipError_t launch_gqa_split(const GqaSplitArgs &a, bool direct, hipStream_t s) {
     if (a.block_k % kTile) return hipErrorInvalidValue;
-    const dim3 grid(xcd_grid_size(a.total_ctas)), block(64);
+    const dim3 grid(a.total_ctas), block(64);
     if (direct)
         hipLaunchKernelGGL((gqa_split_kernel<true>), grid, block, 0, s, a);
     else

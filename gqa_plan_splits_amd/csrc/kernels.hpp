@@ -33,7 +33,7 @@ struct GqaSplitArgs {
     int64_t q_st_tok, q_st_head;
     const uint16_t *k_cache, *v_cache;  // bf16 [pages, page_size, Hkv, 128]
     const int32_t *page_indices, *kv_indptr, *seq_lens;
-    int32_t q_len, Hq, Hkv, group, page_shift, np, total_ctas;
+    int32_t batch, q_len, Hq, Hkv, group, page_shift, np, total_ctas;
     int32_t block_k;              // partition lengths are rounded up to a multiple of this
     float score_scale;            // scale * log2(e)
     float *part_o, *part_lse2;

@@ -254,6 +254,23 @@ def test_gqa_page_sizes(page_size):
     compare(out, lse, ref_o, ref_l, "gqa page %d" % page_size)
 
 
+@pytest.mark.parametrize("B", [20, 64, 70])
+def test_gqa_batch_order(B):
+    # CTAs take requests longest first (batches of up to 64): tied lengths, empty requests and a
+    # batch past 64 (kept in its own order) must all land on the right rows
+    rng = np.random.default_rng(B)
+    lens = [int(x) for x in rng.choice([0, 5, 16, 17, 90, 90, 90, 250, 251], size=B)]
+    pages = sum(-(-L // 16) for L in lens)
+    inp = workloads.gqa_inputs(B=B, Hq=8, Hkv=2, D=128, page_size=16, seq_lens=lens,
+                               num_pages=pages + 5, seed=57 + B, device=DEV)
+    log("gqa batch order B=%d" % B)
+    for np_ in (1, 4):
+        out, lse = run_decode(gqa_problem(inp), 128, np_, 32)
+        torch.cuda.synchronize()
+        ref_o, ref_l = oracle_gqa(inp)
+        compare(out, lse, ref_o, ref_l, "gqa batch order B=%d np=%d" % (B, np_))
+
+
 def test_gqa_full_size_sampled():
     inp = workloads.gqa_paged(DEV)
     p = gqa_problem(inp)
