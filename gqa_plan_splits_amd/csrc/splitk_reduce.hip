@@ -3,19 +3,27 @@
 // What it computes (Modular MAX planner page, "AMD reducer constraint": the reducer merges up
 // to parts_per_lane x WARP_SIZE partitions, 4 x 64 = 256): for each row,
 //   lse2 = log2(sum_i 2^lse2_i),   o = sum_i 2^(lse2_i - lse2) * o_i,
-// with the weights summed in partition order 0..np-1 (a fixed association, so the result is
-// deterministic).  Output rounded to bf16, nearest even (moonmath-amd README, gfx950 RTNE).
+// in fp32 with a fixed association (so the result is deterministic).  Output rounded to bf16,
+// nearest even (moonmath-amd README, gfx950 RTNE).
 //
-// One wave64 per row: each lane holds up to four partition LSEs, the row max and the weight
-// sum are two butterfly reductions, and the weights are shared through LDS while every lane
-// streams 16-byte pieces of the partial outputs.
+// Layout of the work, per (row, column chunk) item; four waves per block.  A chunk is 256
+// columns (64 lanes x 4) when rows are few, the whole row when there are enough of them.
+//   - Many items (or few partitions): one wave per item.
+//   - Few items and many partitions (a small batch split 64 ways): one block per item, wave w
+//     summing partitions w, w + 4, .., so that a few long rows still spread over the chip; the
+//     four waves' sums are added in wave order through LDS.
+// Every wave computes the row's LSE maximum and weights itself (each lane holds up to four
+// partition LSEs; two butterfly reductions) and keeps them in its own LDS slice; each lane sums
+// its four columns over its partitions four at a time (four loads in flight, one accumulator
+// each).  The association is fixed for a given shape, so the result is deterministic.
 #include "device_common.hpp"
 #include "kernels.hpp"
 
 namespace gqa {
 namespace {
 
-constexpr int kWavesPerBlock = 4;
+constexpr int kWaves = 4;
+constexpr int kMaxBlocks = 1 << 20;   // larger inputs loop over their items
 
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
@@ -28,57 +36,103 @@ __device__ __forceinline__ float wave_sum(float v) {
     return v;
 }
 
-__global__ void __launch_bounds__(256) splitk_reduce_kernel(const ReduceArgs a) {
-    __shared__ float wbuf[kWavesPerBlock][256];
+// SPLIT: the block's four waves share one item and split its partitions (stride 4, first w);
+// otherwise wave w of block x owns item 4 x + w and every partition (stride 1).
+template <bool SPLIT>
+__global__ void __launch_bounds__(256) splitk_reduce_kernel(const ReduceArgs a, int chunks, int chunk_vec) {
+    __shared__ float wbuf[kWaves][256];
+    __shared__ f32x4 sums[kWaves - 1][64];
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    const int64_t row = int64_t(blockIdx.x) * kWavesPerBlock + w;
-    if (row >= a.rows) return;   // whole waves exit together: no block barrier is used below
-
-    const float *lp = a.part_lse2 + row * a.np;
-    float l4[4];
-    float mx = kNegInf;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        const int p = lane + 64 * k;
-        l4[k] = p < a.np ? lp[p] : kNegInf;
-        mx = fmaxf(mx, l4[k]);
-    }
-    mx = wave_max(mx);
     const int nvec = a.dv >> 2;
-    uint16_t *out = a.out + row * a.dv;
-    if (mx == kNegInf) {   // no partition saw a key: the row is 0 with lse2 = -inf
-        for (int v = lane; v < nvec; v += 64)
-            *reinterpret_cast<uint2 *>(out + 4 * v) = make_uint2(0, 0);
-        if (lane == 0 && a.lse2_out) a.lse2_out[row] = kNegInf;
-        return;
-    }
-    float wsum = 0.f;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        const int p = lane + 64 * k;
-        const float wgt = fast_exp2(l4[k] - mx);   // -inf -> 0
-        if (p < a.np) wbuf[w][p] = wgt;
-        wsum += wgt;
-    }
-    wsum = wave_sum(wsum);
-    const float inv = 1.f / wsum;
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const int64_t items = a.rows * chunks;
+    const int64_t step = SPLIT ? int64_t(gridDim.x) : int64_t(gridDim.x) * kWaves;
+    const int pstep = SPLIT ? kWaves : 1;
 
-    const float *po = a.part_o + row * int64_t(a.np) * a.dv;
-    for (int v = lane; v < nvec; v += 64) {
-        f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-        for (int p = 0; p < a.np; ++p) {
-            const float wgt = wbuf[w][p];
-            if (wgt == 0.f) continue;   // empty partition: its output is not read
-            acc += wgt * *reinterpret_cast<const f32x4 *>(po + int64_t(p) * a.dv + 4 * v);
+    for (int64_t item = SPLIT ? blockIdx.x : int64_t(blockIdx.x) * kWaves + w; item < items; item += step) {
+        const int64_t row = item / chunks;
+        const int chunk = int(item - row * chunks);
+        const int c_end = min(nvec, (chunk + 1) * chunk_vec);
+        const bool lead = !SPLIT || w == 0;   // the wave that writes the item's output
+
+        const float *lp = a.part_lse2 + row * a.np;
+        float l4[4];
+        float mx = kNegInf;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int p = lane + 64 * k;
+            l4[k] = p < a.np ? lp[p] : kNegInf;
+            mx = fmaxf(mx, l4[k]);
         }
-        acc *= inv;
-        *reinterpret_cast<uint2 *>(out + 4 * v) =
-            make_uint2(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]));
+        mx = wave_max(mx);   // with SPLIT identical in the four waves: the branch is block-uniform
+        uint16_t *out = a.out + row * a.dv;
+        if (mx == kNegInf) {   // no partition saw a key: the row is 0 with lse2 = -inf
+            if (lead)
+                for (int c4 = chunk * chunk_vec + lane; c4 < c_end; c4 += 64)
+                    *reinterpret_cast<uint2 *>(out + 4 * c4) = make_uint2(0, 0);
+            if (lead && lane == 0 && chunk == 0 && a.lse2_out) a.lse2_out[row] = kNegInf;
+            continue;
+        }
+        float wsum = 0.f;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int p = lane + 64 * k;
+            const float wgt = fast_exp2(l4[k] - mx);   // -inf -> 0
+            if (p < a.np) wbuf[w][p] = wgt;
+            wsum += wgt;
+        }
+        wsum = wave_sum(wsum);
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+        // Lane columns 4 c4 .. 4 c4 + 3.  Four partitions per iteration, each into its own
+        // accumulator.  A partition without weight contributes nothing, whatever its output holds.
+        // (With SPLIT a chunk is one pass of 64 lanes, so every wave reaches the barriers once.)
+        const float inv = 1.f / wsum;
+        for (int base = chunk * chunk_vec; base < c_end; base += 64) {
+            const int c4 = base + lane;
+            const bool col_ok = c4 < c_end;
+            f32x4 acc[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (col_ok) {
+                const float *po = a.part_o + row * int64_t(a.np) * a.dv + 4 * c4;
+                int p = SPLIT ? w : 0;
+                for (; p + 3 * pstep < a.np; p += 4 * pstep) {
+                    f32x4 x[4];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        x[j] = *reinterpret_cast<const f32x4 *>(po + int64_t(p + pstep * j) * a.dv);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const float wgt = wbuf[w][p + pstep * j];
+                        if (wgt != 0.f) acc[j] += wgt * x[j];
+                    }
+                }
+#pragma unroll
+                for (int j = 0; j < 3; ++j) {   // at most three left
+                    const int q = p + pstep * j;
+                    if (q < a.np) {
+                        const float wgt = wbuf[w][q];
+                        if (wgt != 0.f) acc[j] += wgt * *reinterpret_cast<const f32x4 *>(po + int64_t(q) * a.dv);
+                    }
+                }
+            }
+            f32x4 tot = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+            if (SPLIT) {
+                if (w > 0) sums[w - 1][lane] = tot;
+                __syncthreads();
+                if (w == 0) tot = ((tot + sums[0][lane]) + sums[1][lane]) + sums[2][lane];
+                __syncthreads();   // sums are reused by the next item
+            }
+            if (lead && col_ok) {
+                tot *= inv;
+                *reinterpret_cast<uint2 *>(out + 4 * c4) =
+                    make_uint2(pack_bf16x2(tot[0], tot[1]), pack_bf16x2(tot[2], tot[3]));
+            }
+        }
+        if (lead && lane == 0 && chunk == 0 && a.lse2_out) a.lse2_out[row] = mx + __log2f(wsum);
     }
-    if (lane == 0 && a.lse2_out) a.lse2_out[row] = mx + __log2f(wsum);
 }
 
 __global__ void __launch_bounds__(256) fp8_to_bf16_kernel(const uint8_t *in, int64_t n, uint16_t *out) {
@@ -97,8 +151,25 @@ __global__ void __launch_bounds__(256) fp8_to_bf16_kernel(const uint8_t *in, int
 }  // namespace
 
 hipError_t launch_splitk_reduce(const ReduceArgs &a, hipStream_t s) {
-    const int64_t blocks = (a.rows + kWavesPerBlock - 1) / kWavesPerBlock;
-    hipLaunchKernelGGL(splitk_reduce_kernel, dim3(unsigned(blocks)), dim3(64 * kWavesPerBlock), 0, s, a);
+    const int nvec = a.dv >> 2;
+    const int c256 = (nvec + 63) / 64;   // 256-column chunks per row
+    // Whole rows per wave once there are enough rows to fill the chip; otherwise 256-column
+    // chunks, and the partitions of one chunk split over four waves when the chunks alone would
+    // leave the chip mostly idle and there are enough partitions to share.
+    const bool whole = a.rows >= 4096;
+    const int chunks = whole ? 1 : c256;
+    const int chunk_vec = whole ? 64 * c256 : 64;
+    const int64_t items = a.rows * chunks;
+    if (!whole && items < 1024 && a.np >= 8) {
+        const int64_t blocks = items < kMaxBlocks ? items : kMaxBlocks;
+        hipLaunchKernelGGL(splitk_reduce_kernel<true>, dim3(unsigned(blocks)), dim3(64 * kWaves), 0, s, a,
+                           chunks, chunk_vec);
+    } else {
+        const int64_t need = (items + kWaves - 1) / kWaves;
+        const int64_t blocks = need < kMaxBlocks ? need : kMaxBlocks;
+        hipLaunchKernelGGL(splitk_reduce_kernel<false>, dim3(unsigned(blocks)), dim3(64 * kWaves), 0, s, a,
+                           chunks, chunk_vec);
+    }
     return hipGetLastError();
 }
 

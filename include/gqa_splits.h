@@ -166,8 +166,9 @@ int decode_split(const gqa_decode_problem *p, int64_t np, int block_k, float *pa
                  float *partial_lse2, gqa_stream_t s);
 
 /* Reducer: for every row, lse2 = log2(sum_i 2^lse2_i) and o = sum_i 2^(lse2_i - lse2) * o_i,
- * summed in partition order 0..np-1 in fp32 (deterministic); partitions with lse2_i = -inf
- * carry no weight and a row with none gets o = 0, lse2 = -inf [MAX, AMD reducer constraint].
+ * summed in fp32 in a fixed order (deterministic); partitions with lse2_i = -inf carry no
+ * weight (their partial_o is not used) and a row with none gets o = 0, lse2 = -inf [MAX, AMD
+ * reducer constraint].
  *   partial_o [rows, np, d_v] fp32, partial_lse2 [rows, np] fp32 (inputs)
  *   out       [rows, d_v] bf16, rounded to nearest even (output)
  *   lse2_out  [rows] fp32 (output; may be NULL)

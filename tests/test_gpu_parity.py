@@ -36,7 +36,9 @@ def test_fp8_conversion_matches_definition():
 
 
 @pytest.mark.parametrize("rows,np_,dv", [(1, 1, 512), (7, 2, 512), (33, 5, 448), (64, 64, 512),
-                                         (10, 256, 128), (5, 37, 128), (300, 16, 512)])
+                                         (10, 256, 128), (5, 37, 128), (300, 16, 512),
+                                         (3, 13, 1024), (9, 250, 4), (128, 64, 512),
+                                         (4100, 3, 448), (4500, 9, 1024)])
 def test_reduce_matches_oracle_merge(rows, np_, dv):
     gen = torch.Generator(device="cpu").manual_seed(rows * 1000 + np_)
     po = torch.randn((rows, np_, dv), generator=gen) * 0.3
@@ -47,9 +49,13 @@ def test_reduce_matches_oracle_merge(rows, np_, dv):
     pl[0, :] = -float("inf")          # a row no partition saw
     po[0, :] = 0
     ref_o, ref_l = oracle.lse_merge(po.double().numpy(), pl.double().numpy())
+    # a partition without weight is not read: NaN there must not reach the output
+    po_dev = po.clone()
+    po_dev[drop] = float("nan")
+    po_dev[0, :] = float("nan")
     out = torch.empty((rows, dv), dtype=torch.bfloat16, device=DEV)
     lse = torch.empty((rows,), dtype=torch.float32, device=DEV)
-    g.splitk_reduce(rows, np_, dv, po.to(DEV), pl.to(DEV), out, lse)
+    g.splitk_reduce(rows, np_, dv, po_dev.to(DEV), pl.to(DEV), out, lse)
     torch.cuda.synchronize()
     compare(out, lse, ref_o, ref_l, "reduce rows=%d np=%d dv=%d" % (rows, np_, dv))
     # bf16 output of an fp32 merge: within one bf16 rounding of the fp64 merge
