@@ -25,8 +25,10 @@ from ._lib import (  # noqa: F401
     gqa_problem,
     last_error_detail,
     library_path,
+    merge_ranks,
     mla_problem,
     plan_splits,
     splitk_reduce,
+    splitk_reduce_f32,
     status_string,
 )

@@ -14,7 +14,7 @@ FP8_E4M3FNUZ = 1
 
 # Every function include/gqa_splits.h declares.
 _SYMBOLS = ("plan_splits", "block_k_for", "device_sm_count", "decode_plan", "decode_split",
-            "splitk_reduce", "decode_workspace_bytes", "decode", "fp8_e4m3_to_bf16",
+            "splitk_reduce", "splitk_reduce_f32", "merge_ranks", "decode_workspace_bytes", "decode", "fp8_e4m3_to_bf16",
             "status_string", "last_error_detail")
 
 
@@ -55,6 +55,9 @@ class DecodeProblem(ctypes.Structure):
         ("seq_lens", ctypes.c_void_p),
         ("scale", ctypes.c_float),
         ("kv_scale", ctypes.c_float),
+        ("glen", ctypes.c_void_p),
+        ("cp_rank", ctypes.c_int32),
+        ("cp_world", ctypes.c_int32),
     ]
 
     # tensors whose memory the struct points at (kept alive with it)
@@ -94,6 +97,8 @@ def _load():
     lib.decode_plan.argtypes = [pp, i64, i32, i64, ctypes.POINTER(i64), ctypes.POINTER(i32)]
     lib.decode_split.argtypes = [pp, i64, i32, vp, vp, vp]
     lib.splitk_reduce.argtypes = [i64, i64, i64, vp, vp, vp, vp, vp]
+    lib.splitk_reduce_f32.argtypes = [i64, i64, i64, vp, vp, vp, vp, vp]
+    lib.merge_ranks.argtypes = [i64, i64, i64, vp, vp, vp, vp, vp]
     lib.decode_workspace_bytes.argtypes = [pp, i64, ctypes.POINTER(ctypes.c_size_t)]
     lib.decode.argtypes = [pp, i64, i32, vp, ctypes.c_size_t, vp, vp, vp]
     lib.fp8_e4m3_to_bf16.argtypes = [vp, i64, vp, vp]
@@ -194,9 +199,12 @@ def _strides(t):
 
 
 def mla_problem(q_lat, q_pe, pool, kv_indices, kv_indptr, seq_lens, *, batch, q_len, num_heads,
-                max_num_keys, scale, kv_scale, d_v=None, fp8_format=FP8_E4M3FN) -> DecodeProblem:
+                max_num_keys, scale, kv_scale, d_v=None, fp8_format=FP8_E4M3FN, glen=None,
+                cp_rank=0, cp_world=1) -> DecodeProblem:
     """Absorbed-MLA (or sparse top-k) problem: q_lat [B*q_len, H, d_lat], q_pe [.., H, d_rope]
-    bf16 views; pool [N, d_qk] fp8 bytes (uint8 or float8); int32 index tensors."""
+    bf16 views; pool [N, d_qk] fp8 bytes (uint8 or float8); int32 index tensors.  With glen
+    (int32 [B] global lengths), the call is rank cp_rank of cp_world decode-context-parallel
+    ranks: seq_lens and the index lists hold that rank's positions."""
     p = DecodeProblem()
     p.kind = KIND_MLA_FUSED
     p.fp8_format = fp8_format
@@ -217,7 +225,10 @@ def mla_problem(q_lat, q_pe, pool, kv_indices, kv_indptr, seq_lens, *, batch, q_
     p.seq_lens = seq_lens.data_ptr()
     p.scale = scale
     p.kv_scale = kv_scale
-    p._keep = (q_lat, q_pe, pool, kv_indices, kv_indptr, seq_lens)
+    if glen is not None:
+        p.glen = glen.data_ptr()
+        p.cp_rank, p.cp_world = cp_rank, cp_world
+    p._keep = (q_lat, q_pe, pool, kv_indices, kv_indptr, seq_lens, glen)
     return p
 
 
@@ -264,6 +275,19 @@ def splitk_reduce(rows: int, np: int, d_v: int, partial_o, partial_lse2, out, ls
                   stream=None):
     _check(_load().splitk_reduce(rows, np, d_v, _ptr(partial_o), _ptr(partial_lse2), _ptr(out),
                                  _ptr(lse2_out), _stream(stream)), "splitk_reduce")
+
+
+def splitk_reduce_f32(rows: int, np: int, d_v: int, partial_o, partial_lse2, out, lse2_out=None,
+                      stream=None):
+    _check(_load().splitk_reduce_f32(rows, np, d_v, _ptr(partial_o), _ptr(partial_lse2), _ptr(out),
+                                     _ptr(lse2_out), _stream(stream)), "splitk_reduce_f32")
+
+
+def merge_ranks(world: int, rows: int, d_v: int, parts, lse2, out, lse2_out=None, stream=None):
+    """Merge of decode-context-parallel rank outputs: parts [world, rows, d_v] fp32 (each rank's
+    splitk_reduce_f32 output), lse2 [world, rows] fp32 -> out [rows, d_v] bf16 (+ lse2_out)."""
+    _check(_load().merge_ranks(world, rows, d_v, _ptr(parts), _ptr(lse2), _ptr(out), _ptr(lse2_out),
+                               _stream(stream)), "merge_ranks")
 
 
 def decode_workspace_bytes(problem: DecodeProblem, np: int = 0) -> int:

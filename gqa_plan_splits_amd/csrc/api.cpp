@@ -69,11 +69,20 @@ int check_problem(const gqa_decode_problem *p, Derived *d) {
             return GQA_ERR_UNSUPPORTED;
         if (p->q_pe_stride_tok % 8 || p->q_pe_stride_head % 8 || !aligned16(p->q_pe))
             return GQA_ERR_UNSUPPORTED;
+        // decode context parallelism: wide rows, a rank within the world, the global lengths
+        if (p->cp_world > 1 || p->glen) {
+            if (!p->glen || p->cp_rank < 0 || p->cp_rank >= p->cp_world) return GQA_ERR_INVALID_ARGUMENT;
+            if (!wide || p->cp_world > kMaxPartitions) return GQA_ERR_UNSUPPORTED;
+        } else if (p->cp_rank != 0 || p->cp_world < 0) {
+            return GQA_ERR_INVALID_ARGUMENT;
+        }
         d->is_mla = true;
         d->cta_rows = (rows_per_req + kMlaRowsPerCta - 1) / kMlaRowsPerCta;
         d->hpg = rows_per_req;
     } else if (p->kind == GQA_KIND_GQA_PAGED) {
         if (!p->k_cache || !p->v_cache || p->num_kv_heads < 1) return GQA_ERR_INVALID_ARGUMENT;
+        if (p->cp_world > 1 || p->glen) return GQA_ERR_UNSUPPORTED;
+        if (p->cp_rank != 0 || p->cp_world < 0) return GQA_ERR_INVALID_ARGUMENT;
         if (p->num_heads % p->num_kv_heads) return GQA_ERR_INVALID_ARGUMENT;
         if (p->d_qk != kGqaHeadDim || p->d_v != kGqaHeadDim || p->d_rope != 0)
             return GQA_ERR_UNSUPPORTED;
@@ -136,6 +145,10 @@ int launch_split(const gqa_decode_problem *p, const Derived &d, int64_t np, int 
         a.kv_indices = p->kv_indices;
         a.kv_indptr = p->kv_indptr;
         a.seq_lens = p->seq_lens;
+        const bool cp = p->cp_world > 1 || p->glen;
+        a.glen = cp ? p->glen : nullptr;
+        a.cp_rank = cp ? p->cp_rank : 0;
+        a.cp_world = cp ? p->cp_world : 1;
         a.q_len = int32_t(p->q_len);
         a.H = int32_t(p->num_heads);
         a.np = int32_t(np);
@@ -210,22 +223,56 @@ extern "C" int decode_split(const gqa_decode_problem *p, int64_t np, int block_k
                         reinterpret_cast<hipStream_t>(s));
 }
 
-extern "C" int splitk_reduce(int64_t rows, int64_t np, int64_t d_v, const float *partial_o,
-                             const float *partial_lse2, void *out, float *lse2_out,
-                             gqa_stream_t s) {
-    if (rows < 0 || !partial_o || !partial_lse2 || !out) return GQA_ERR_INVALID_ARGUMENT;
+namespace {
+
+// The merge behind splitk_reduce, splitk_reduce_f32 and merge_ranks: np inputs per row with the
+// given element strides, bf16 or fp32 output.
+int launch_merge(int64_t rows, int64_t np, int64_t d_v, const float *po, const float *pl,
+                 void *out, bool f32_out, float *lse2_out, int64_t o_row, int64_t o_part,
+                 int64_t l_row, int64_t l_part, gqa_stream_t s, const char *what) {
+    if (rows < 0 || !po || !pl || !out) return GQA_ERR_INVALID_ARGUMENT;
     if (np < 1 || np > kMaxPartitions || d_v < 4 || d_v > 1024 || d_v % 4) return GQA_ERR_UNSUPPORTED;
     if (rows > (int64_t(1) << 30)) return GQA_ERR_UNSUPPORTED;
+    if (!aligned16(po) || reinterpret_cast<uintptr_t>(out) % (f32_out ? 16 : 8)) return GQA_ERR_UNSUPPORTED;
     if (rows == 0) return GQA_OK;
     gqa::ReduceArgs a;
-    a.part_o = partial_o;
-    a.part_lse2 = partial_lse2;
-    a.out = static_cast<uint16_t *>(out);
+    a.part_o = po;
+    a.part_lse2 = pl;
+    a.out = f32_out ? nullptr : static_cast<uint16_t *>(out);
+    a.out_f32 = f32_out ? static_cast<float *>(out) : nullptr;
     a.lse2_out = lse2_out;
     a.rows = rows;
     a.np = int32_t(np);
     a.dv = int32_t(d_v);
-    return launch_status(gqa::launch_splitk_reduce(a, reinterpret_cast<hipStream_t>(s)), "splitk_reduce");
+    a.o_row = o_row;
+    a.o_part = o_part;
+    a.l_row = l_row;
+    a.l_part = l_part;
+    return launch_status(gqa::launch_splitk_reduce(a, reinterpret_cast<hipStream_t>(s)), what);
+}
+
+}  // namespace
+
+extern "C" int splitk_reduce(int64_t rows, int64_t np, int64_t d_v, const float *partial_o,
+                             const float *partial_lse2, void *out, float *lse2_out,
+                             gqa_stream_t s) {
+    // [rows, np, d_v] and [rows, np]
+    return launch_merge(rows, np, d_v, partial_o, partial_lse2, out, false, lse2_out, np * d_v, d_v,
+                        np, 1, s, "splitk_reduce");
+}
+
+extern "C" int splitk_reduce_f32(int64_t rows, int64_t np, int64_t d_v, const float *partial_o,
+                                 const float *partial_lse2, float *out, float *lse2_out,
+                                 gqa_stream_t s) {
+    return launch_merge(rows, np, d_v, partial_o, partial_lse2, out, true, lse2_out, np * d_v, d_v,
+                        np, 1, s, "splitk_reduce_f32");
+}
+
+extern "C" int merge_ranks(int64_t world, int64_t rows, int64_t d_v, const float *parts,
+                           const float *lse2, void *out, float *lse2_out, gqa_stream_t s) {
+    // [world, rows, d_v] and [world, rows]
+    return launch_merge(rows, world, d_v, parts, lse2, out, false, lse2_out, d_v, rows * d_v, 1, rows,
+                        s, "merge_ranks");
 }
 
 extern "C" int decode_workspace_bytes(const gqa_decode_problem *p, int64_t np, size_t *bytes) {

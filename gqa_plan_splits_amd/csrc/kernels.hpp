@@ -17,6 +17,8 @@ struct MlaSplitArgs {
     const uint8_t *kv;            // fp8 rows
     int64_t kv_stride;            // bytes between rows
     const int32_t *kv_indices, *kv_indptr, *seq_lens;
+    const int32_t *glen;          // global lengths under context parallelism (cp_world > 1)
+    int32_t cp_rank, cp_world;    // key j is global position j * cp_world + cp_rank
     int32_t q_len, H, np, rows_per_req, row_blocks, total_ctas;
     int32_t block_k;              // partition lengths are rounded up to a multiple of this
     float score_scale;            // scale * kv_scale * log2(e): scores in base-2 units
@@ -43,10 +45,13 @@ struct GqaSplitArgs {
 
 struct ReduceArgs {
     const float *part_o, *part_lse2;
-    uint16_t *out;
+    uint16_t *out;                // bf16 [rows, dv] (or out_f32)
+    float *out_f32;               // fp32 [rows, dv] instead, when not null
     float *lse2_out;
     int64_t rows;
     int32_t np, dv;
+    // element strides: partial output (row, partition) and partial lse2 (row, partition)
+    int64_t o_row, o_part, l_row, l_part;
 };
 
 // Launchers: return hipSuccess or the launch error.  All enqueue on `s` only.

@@ -4,7 +4,9 @@
 // bullet): every key row of the pool is one fused fp8 e4m3 row that serves as K (all DQK bytes)
 // and as V (its first DV bytes), dequantized with one per-tensor kv_scale.  A CTA owns up to 64
 // query rows of one request and walks one partition of that request's keys, writing the
-// partition's softmax-weighted mean of values and the base-2 log-sum-exp of its scores.
+// partition's softmax-weighted mean of values and the base-2 log-sum-exp of its scores.  Under
+// decode context parallelism (same README section) the call holds one rank's share of each
+// request's positions, and the draft window is taken on the global positions.
 //
 // Work split (512 threads = 8 waves, one CTA per CU; waves w and w + 4 share SIMD w):
 //   - Score waves 0-3: wave w computes S^T = K Q^T for query rows 16 w .. 16 w + 15 against the 64
@@ -170,12 +172,20 @@ __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const MlaSplitAr
     // no row of the block sees past the block's latest draft token.
     const int S = a.seq_lens[b];
     const int base = a.kv_indptr[b];
+    // Keys draft position t sees: 0 .. S - q_len + t, or under context parallelism the local keys
+    // whose global positions j * cp_world + cp_rank are at most glen - q_len + t.
+    const int G = a.cp_world > 1 ? a.glen[b] : S;
+    auto visible = [&](int t) {
+        const int last = G - a.q_len + t;   // last visible global position
+        if (a.cp_world == 1) return max(0, last + 1);
+        return last >= a.cp_rank ? min(S, (last - a.cp_rank) / a.cp_world + 1) : 0;
+    };
     const int chunk = ((S + a.np - 1) / a.np + a.block_k - 1) / a.block_k * a.block_k;
     const int k0 = part * chunk;
     const int row0 = rblk * kBM;
     const int nrows = min(kBM, a.rows_per_req - row0);
-    const int k1 = min(max(0, S - a.q_len + (row0 + nrows - 1) / a.H + 1), k0 + chunk);
-    const int kfull = min(k1, max(0, S - a.q_len + row0 / a.H + 1));  // keys every row sees
+    const int k1 = min(visible((row0 + nrows - 1) / a.H), k0 + chunk);
+    const int kfull = min(k1, visible(row0 / a.H));  // keys every row sees
     const int ntiles = k1 > k0 ? (k1 - k0 + kBK - 1) / kBK : 0;
     // Tiles whose keys every row of the block sees need no mask.
     const int n_full = min(ntiles, max(0, (kfull - k0) / kBK));
@@ -205,7 +215,7 @@ __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const MlaSplitAr
             const int r = row0 + rl;
             const int t = row_ok ? r / a.H : 0;
             const int hh = row_ok ? r - t * a.H : 0;
-            p_end = row_ok ? min(max(0, S - a.q_len + t + 1), k1) : k0;
+            p_end = row_ok ? min(visible(t), k1) : k0;
             const int64_t tok = int64_t(b) * a.q_len + t;
             const uint16_t *ql = a.q + tok * a.q_st_tok + int64_t(hh) * a.q_st_head;
             const uint16_t *qp = a.q_pe + tok * a.qpe_st_tok + int64_t(hh) * a.qpe_st_head;

@@ -1,10 +1,12 @@
 // splitk_reduce.hip -- fp32 base-2 LSE merge of up to 256 partitions, gfx950.
 //
 // What it computes (Modular MAX planner page, "AMD reducer constraint": the reducer merges up
-// to parts_per_lane x WARP_SIZE partitions, 4 x 64 = 256): for each row,
+// to parts_per_lane x WARP_SIZE partitions, 4 x 64 = 256; the same merge combines the ranks of
+// decode context parallelism, moonmath-amd README "MLA decode"): for each row,
 //   lse2 = log2(sum_i 2^lse2_i),   o = sum_i 2^(lse2_i - lse2) * o_i,
 // in fp32 with a fixed association (so the result is deterministic).  Output rounded to bf16,
-// nearest even (moonmath-amd README, gfx950 RTNE).
+// nearest even (moonmath-amd README, gfx950 RTNE), or kept in fp32 for a caller that merges
+// further (a context-parallel rank).
 //
 // Layout of the work, per (row, column chunk) item; four waves per block.  A chunk is 256
 // columns (64 lanes x 4) when rows are few, the whole row when there are enough of them.
@@ -36,9 +38,21 @@ __device__ __forceinline__ float wave_sum(float v) {
     return v;
 }
 
+__device__ __forceinline__ f32x4 load4(const float *p) { return *reinterpret_cast<const f32x4 *>(p); }
+
+// Four output values: bf16 rounded to nearest even, or fp32.
+template <bool F32OUT>
+__device__ __forceinline__ void store4(const ReduceArgs &a, int64_t row, int c4, f32x4 v) {
+    if (F32OUT)
+        *reinterpret_cast<f32x4 *>(a.out_f32 + row * a.dv + 4 * c4) = v;
+    else
+        *reinterpret_cast<uint2 *>(a.out + row * a.dv + 4 * c4) =
+            make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+}
+
 // SPLIT: the block's four waves share one item and split its partitions (stride 4, first w);
 // otherwise wave w of block x owns item 4 x + w and every partition (stride 1).
-template <bool SPLIT>
+template <bool SPLIT, bool F32OUT>
 __global__ void __launch_bounds__(256) splitk_reduce_kernel(const ReduceArgs a, int chunks, int chunk_vec) {
     __shared__ float wbuf[kWaves][256];
     __shared__ f32x4 sums[kWaves - 1][64];
@@ -54,21 +68,20 @@ __global__ void __launch_bounds__(256) splitk_reduce_kernel(const ReduceArgs a, 
         const int c_end = min(nvec, (chunk + 1) * chunk_vec);
         const bool lead = !SPLIT || w == 0;   // the wave that writes the item's output
 
-        const float *lp = a.part_lse2 + row * a.np;
+        const float *lp = a.part_lse2 + row * a.l_row;
         float l4[4];
         float mx = kNegInf;
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
             const int p = lane + 64 * k;
-            l4[k] = p < a.np ? lp[p] : kNegInf;
+            l4[k] = p < a.np ? lp[p * a.l_part] : kNegInf;
             mx = fmaxf(mx, l4[k]);
         }
         mx = wave_max(mx);   // with SPLIT identical in the four waves: the branch is block-uniform
-        uint16_t *out = a.out + row * a.dv;
         if (mx == kNegInf) {   // no partition saw a key: the row is 0 with lse2 = -inf
             if (lead)
                 for (int c4 = chunk * chunk_vec + lane; c4 < c_end; c4 += 64)
-                    *reinterpret_cast<uint2 *>(out + 4 * c4) = make_uint2(0, 0);
+                    store4<F32OUT>(a, row, c4, f32x4{0.f, 0.f, 0.f, 0.f});
             if (lead && lane == 0 && chunk == 0 && a.lse2_out) a.lse2_out[row] = kNegInf;
             continue;
         }
@@ -96,13 +109,13 @@ __global__ void __launch_bounds__(256) splitk_reduce_kernel(const ReduceArgs a, 
 #pragma unroll
             for (int j = 0; j < 4; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
             if (col_ok) {
-                const float *po = a.part_o + row * int64_t(a.np) * a.dv + 4 * c4;
+                const float *po = a.part_o + row * a.o_row + 4 * c4;
                 int p = SPLIT ? w : 0;
                 for (; p + 3 * pstep < a.np; p += 4 * pstep) {
                     f32x4 x[4];
 #pragma unroll
                     for (int j = 0; j < 4; ++j)
-                        x[j] = *reinterpret_cast<const f32x4 *>(po + int64_t(p + pstep * j) * a.dv);
+                        x[j] = load4(po + int64_t(p + pstep * j) * a.o_part);
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
                         const float wgt = wbuf[w][p + pstep * j];
@@ -114,7 +127,7 @@ __global__ void __launch_bounds__(256) splitk_reduce_kernel(const ReduceArgs a, 
                     const int q = p + pstep * j;
                     if (q < a.np) {
                         const float wgt = wbuf[w][q];
-                        if (wgt != 0.f) acc[j] += wgt * *reinterpret_cast<const f32x4 *>(po + int64_t(q) * a.dv);
+                        if (wgt != 0.f) acc[j] += wgt * load4(po + int64_t(q) * a.o_part);
                     }
                 }
             }
@@ -125,11 +138,7 @@ __global__ void __launch_bounds__(256) splitk_reduce_kernel(const ReduceArgs a, 
                 if (w == 0) tot = ((tot + sums[0][lane]) + sums[1][lane]) + sums[2][lane];
                 __syncthreads();   // sums are reused by the next item
             }
-            if (lead && col_ok) {
-                tot *= inv;
-                *reinterpret_cast<uint2 *>(out + 4 * c4) =
-                    make_uint2(pack_bf16x2(tot[0], tot[1]), pack_bf16x2(tot[2], tot[3]));
-            }
+            if (lead && col_ok) store4<F32OUT>(a, row, c4, tot * inv);
         }
         if (lead && lane == 0 && chunk == 0 && a.lse2_out) a.lse2_out[row] = mx + __log2f(wsum);
     }
@@ -160,16 +169,18 @@ hipError_t launch_splitk_reduce(const ReduceArgs &a, hipStream_t s) {
     const int chunks = whole ? 1 : c256;
     const int chunk_vec = whole ? 64 * c256 : 64;
     const int64_t items = a.rows * chunks;
-    if (!whole && items < 1024 && a.np >= 8) {
-        const int64_t blocks = items < kMaxBlocks ? items : kMaxBlocks;
-        hipLaunchKernelGGL(splitk_reduce_kernel<true>, dim3(unsigned(blocks)), dim3(64 * kWaves), 0, s, a,
-                           chunks, chunk_vec);
-    } else {
-        const int64_t need = (items + kWaves - 1) / kWaves;
-        const int64_t blocks = need < kMaxBlocks ? need : kMaxBlocks;
-        hipLaunchKernelGGL(splitk_reduce_kernel<false>, dim3(unsigned(blocks)), dim3(64 * kWaves), 0, s, a,
-                           chunks, chunk_vec);
-    }
+    const bool split = !whole && items < 1024 && a.np >= 8;
+    const int64_t need = split ? items : (items + kWaves - 1) / kWaves;
+    const dim3 grid(unsigned(need < kMaxBlocks ? need : kMaxBlocks)), block(64 * kWaves);
+    const bool f32 = a.out_f32 != nullptr;
+    if (split && f32)
+        hipLaunchKernelGGL((splitk_reduce_kernel<true, true>), grid, block, 0, s, a, chunks, chunk_vec);
+    else if (split)
+        hipLaunchKernelGGL((splitk_reduce_kernel<true, false>), grid, block, 0, s, a, chunks, chunk_vec);
+    else if (f32)
+        hipLaunchKernelGGL((splitk_reduce_kernel<false, true>), grid, block, 0, s, a, chunks, chunk_vec);
+    else
+        hipLaunchKernelGGL((splitk_reduce_kernel<false, false>), grid, block, 0, s, a, chunks, chunk_vec);
     return hipGetLastError();
 }
 

@@ -115,6 +115,17 @@ typedef struct gqa_decode_problem {
 
     float scale;           /* softmax scale applied to q . k */
     float kv_scale;        /* MLA: per-tensor dequantization scale of the fp8 pool; GQA: 1 */
+
+    /* Decode context parallelism [MM, MLA decode] (MLA with d_qk 576 only; cp_world 0 or 1 and
+     * glen NULL: off).  The keys of each request are dealt over cp_world ranks by position
+     * (global position p belongs to rank p % cp_world); this call holds rank cp_rank's share:
+     * seq_lens[b] counts its positions and key j of request b is global position
+     * j * cp_world + cp_rank.  glen: int32 [B] device, the global lengths; draft position t
+     * sees the global positions 0 .. glen[b] - q_len + t.  The ranks' outputs (each with its
+     * lse2) are combined by merge_ranks. */
+    const int32_t *glen;
+    int32_t cp_rank;
+    int32_t cp_world;
 } gqa_decode_problem;
 
 /* ---------------------------------------------------------------------------------------- */
@@ -172,9 +183,27 @@ int decode_split(const gqa_decode_problem *p, int64_t np, int block_k, float *pa
  *   partial_o [rows, np, d_v] fp32, partial_lse2 [rows, np] fp32 (inputs)
  *   out       [rows, d_v] bf16, rounded to nearest even (output)
  *   lse2_out  [rows] fp32 (output; may be NULL)
- * np in 1..256, d_v a multiple of 4 up to 1024. */
+ * np in 1..256, d_v a multiple of 4 up to 1024; partial_o 16-byte and out 8-byte aligned
+ * (UNSUPPORTED otherwise). */
 int splitk_reduce(int64_t rows, int64_t np, int64_t d_v, const float *partial_o,
                   const float *partial_lse2, void *out, float *lse2_out, gqa_stream_t s);
+
+/* The same reducer with an fp32 output [rows, d_v], 16-byte aligned (for a caller that merges
+ * further: a decode-context-parallel rank hands merge_ranks its fp32 output).  Arguments and
+ * errors as splitk_reduce. */
+int splitk_reduce_f32(int64_t rows, int64_t np, int64_t d_v, const float *partial_o,
+                      const float *partial_lse2, float *out, float *lse2_out, gqa_stream_t s);
+
+/* Merge of the outputs of cp_world decode-context-parallel ranks [MM, MLA decode]: the same
+ * base-2 LSE merge as splitk_reduce, over the ranks' outputs (decode_split then
+ * splitk_reduce_f32 on each rank) stacked rank-major.
+ *   parts [world, rows, d_v] fp32, lse2 [world, rows] fp32 (inputs; a rank that saw no key of a
+ *   row has lse2 = -inf there and its output is not used)
+ *   out   [rows, d_v] bf16 RNE (output), lse2_out [rows] fp32 (output; may be NULL)
+ * world in 1..256, d_v a multiple of 4 up to 1024; parts 16-byte and out 8-byte aligned.
+ * Errors: INVALID_ARGUMENT, UNSUPPORTED, LAUNCH_FAILED. */
+int merge_ranks(int64_t world, int64_t rows, int64_t d_v, const float *parts, const float *lse2,
+                void *out, float *lse2_out, gqa_stream_t s);
 
 /* Workspace decode() needs for np partitions (np = 0: the planner's choice on the current
  * device): the fp32 partials, 256-byte aligned; 0 when np == 1 (the split kernel then writes

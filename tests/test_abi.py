@@ -177,6 +177,43 @@ def test_reduce_argument_rejections():
     g.splitk_reduce(0, 4, 512, FAKE, FAKE, FAKE)   # no rows: nothing to enqueue
 
 
+def test_context_parallel_rejections():
+    # rank outside the world, a world without global lengths, shapes that have no DCP kernel
+    p = mla_fake()
+    p.glen, p.cp_world, p.cp_rank = FAKE, 4, 4
+    expect_status(lambda: g.decode_split(p, 4, 32, FAKE, FAKE), -1)
+    p.cp_rank = -1
+    expect_status(lambda: g.decode_split(p, 4, 32, FAKE, FAKE), -1)
+    p = mla_fake()
+    p.cp_world, p.cp_rank = 4, 1
+    expect_status(lambda: g.decode_split(p, 4, 32, FAKE, FAKE), -1)
+    p = mla_fake()
+    p.cp_rank = 1   # a rank without a world
+    expect_status(lambda: g.decode_split(p, 4, 32, FAKE, FAKE), -1)
+    p = mla_fake()
+    p.glen, p.cp_world, p.cp_rank = FAKE, 257, 0
+    expect_status(lambda: g.decode_split(p, 4, 32, FAKE, FAKE), -2)
+    p = mla_fake()
+    p.d_qk, p.d_v = 512, 448   # sparse rows
+    p.glen, p.cp_world, p.cp_rank = FAKE, 2, 1
+    expect_status(lambda: g.decode_split(p, 4, 32, FAKE, FAKE), -2)
+    p = gqa_fake()
+    p.glen, p.cp_world, p.cp_rank = FAKE, 2, 1
+    expect_status(lambda: g.decode_split(p, 4, 32, FAKE, FAKE), -2)
+
+
+def test_merge_ranks_argument_rejections():
+    expect_status(lambda: g.merge_ranks(4, -1, 512, FAKE, FAKE, FAKE), -1)
+    expect_status(lambda: g.merge_ranks(0, 8, 512, FAKE, FAKE, FAKE), -2)
+    expect_status(lambda: g.merge_ranks(257, 8, 512, FAKE, FAKE, FAKE), -2)
+    expect_status(lambda: g.merge_ranks(4, 8, 510, FAKE, FAKE, FAKE), -2)
+    expect_status(lambda: g.merge_ranks(4, 8, 512, FAKE + 4, FAKE, FAKE), -2)
+    expect_status(lambda: g.merge_ranks(4, 8, 512, 0, FAKE, FAKE), -1)
+    expect_status(lambda: g.merge_ranks(4, 8, 512, FAKE, 0, FAKE), -1)
+    expect_status(lambda: g.merge_ranks(4, 8, 512, FAKE, FAKE, 0), -1)
+    g.merge_ranks(4, 0, 512, FAKE, FAKE, FAKE)   # no rows: nothing to enqueue
+
+
 def test_workspace_contract():
     p = mla_fake(B=2, H=64)
     need = g.decode_workspace_bytes(p, 64)

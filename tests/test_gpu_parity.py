@@ -63,6 +63,26 @@ def test_reduce_matches_oracle_merge(rows, np_, dv):
     assert np.all(np.abs(o - ref_o) <= np.abs(ref_o) * 2 ** -8 + 1e-6)
 
 
+def test_reduce_f32_output_matches_oracle_merge():
+    gen = torch.Generator(device="cpu").manual_seed(17)
+    rows, np_, dv = 40, 24, 512
+    po = torch.randn((rows, np_, dv), generator=gen) * 0.3
+    pl = torch.randn((rows, np_), generator=gen) * 4 + 12
+    pl[2, :] = -float("inf")
+    po[2, :] = 0
+    ref_o, ref_l = oracle.lse_merge(po.double().numpy(), pl.double().numpy())
+    out = torch.empty((rows, dv), dtype=torch.float32, device=DEV)
+    lse = torch.empty((rows,), dtype=torch.float32, device=DEV)
+    g.splitk_reduce_f32(rows, np_, dv, po.to(DEV), pl.to(DEV), out, lse)
+    torch.cuda.synchronize()
+    o = out.cpu().double().numpy()
+    # an fp32 merge: far inside the bf16 bar
+    assert np.all(o[2] == 0) and np.isneginf(lse[2].item())
+    assert np.abs(o - ref_o).max() <= 1e-5
+    ok = ~np.isinf(ref_l)
+    assert np.all(np.abs(lse.cpu().double().numpy()[ok] - ref_l[ok]) <= 1e-5 * np.maximum(1, np.abs(ref_l[ok])))
+
+
 def test_reduce_is_deterministic():
     po = torch.randn((64, 200, 512), device=DEV)
     pl = torch.randn((64, 200), device=DEV) * 3
@@ -143,6 +163,77 @@ def test_mla_split_partials_match_oracle_on_key_ranges():
             err = np.abs(got_o - ro).max()
             assert err <= OUT_ATOL and err <= OUT_REL * np.abs(ro).max()
             assert np.all(np.abs(got_l - rl) <= LSE_RTOL * np.maximum(1, np.abs(rl)))
+
+
+def dcp_rank_problem(inp, world, rank, glen):
+    """Rank `rank` of `world` decode-context-parallel ranks: the positions p % world == rank of
+    every request (in position order), with the global lengths in glen."""
+    idx = inp.kv_indices.cpu()
+    indptr = inp.kv_indptr.cpu()
+    lens = inp.seq_lens.cpu()
+    parts, new_lens, new_indptr = [], [], [0]
+    for b in range(inp.B):
+        a, S = int(indptr[b]), int(lens[b])
+        sel = idx[a + rank:a + S:world]
+        parts.append(sel)
+        new_lens.append(len(sel))
+        new_indptr.append(new_indptr[-1] + len(sel))
+    kv_idx = torch.cat(parts) if new_indptr[-1] else torch.zeros(1, dtype=torch.int32)
+    kv_idx = kv_idx.to(DEV)
+    kv_indptr = torch.tensor(new_indptr, dtype=torch.int32, device=DEV)
+    seq = torch.tensor(new_lens, dtype=torch.int32, device=DEV)
+    return g.mla_problem(inp.q_lat, inp.q_pe, inp.pool, kv_idx, kv_indptr, seq, batch=inp.B,
+                         q_len=inp.q_len, num_heads=inp.H, max_num_keys=max(new_lens),
+                         scale=inp.scale, kv_scale=inp.kv_scale, d_v=inp.d_v, glen=glen,
+                         cp_rank=rank, cp_world=world)
+
+
+@pytest.mark.parametrize("world", [2, 3, 8])
+@pytest.mark.parametrize("q_len", [1, 4])
+def test_mla_context_parallel_ranks_merge_to_unsplit(world, q_len):
+    # each rank decodes its interleaved share of the positions (window on global positions);
+    # merging the ranks' outputs equals attention over the whole sequence
+    lens = [700, 5, 0, 1500, 3]
+    inp = workloads.mla_inputs(B=5, q_len=q_len, H=16, seq_lens=lens, pool_rows=2300, seed=91,
+                               device=DEV)
+    log("mla dcp world=%d q_len=%d" % (world, q_len))
+    rows = inp.rows
+    parts = torch.empty((world, rows, 512), dtype=torch.float32, device=DEV)
+    lses = torch.empty((world, rows), dtype=torch.float32, device=DEV)
+    for r in range(world):
+        # each rank: its split, then its own merge to an fp32 output
+        p = dcp_rank_problem(inp, world, r, inp.seq_lens)
+        np_, bk = g.decode_plan(p, 0 if r % 2 else 4, 0 if r % 2 else 32)
+        po = torch.empty((rows, np_, 512), dtype=torch.float32, device=DEV)
+        pl = torch.empty((rows, np_), dtype=torch.float32, device=DEV)
+        g.decode_split(p, np_, bk, po, pl)
+        g.splitk_reduce_f32(rows, np_, 512, po, pl, parts[r], lses[r])
+    out = torch.empty((rows, 512), dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty((rows,), dtype=torch.float32, device=DEV)
+    g.merge_ranks(world, rows, 512, parts, lses, out, lse)
+    torch.cuda.synchronize()
+    ref_o, ref_l = oracle_mla(inp)
+    compare(out, lse, ref_o, ref_l, "mla dcp world=%d q_len=%d" % (world, q_len))
+
+
+def test_merge_ranks_matches_oracle_merge():
+    gen = torch.Generator(device="cpu").manual_seed(5)
+    world, rows, dv = 6, 70, 512
+    parts = torch.randn((world, rows, dv), generator=gen) * 0.3
+    lses = torch.randn((world, rows), generator=gen) * 4 + 12
+    lses[torch.rand((world, rows), generator=gen) < 0.3] = -float("inf")
+    lses[:, 3] = -float("inf")   # a row no rank saw
+    po = parts.double().numpy().transpose(1, 0, 2).copy()
+    pl = lses.double().numpy().T.copy()
+    po[np.isinf(pl)] = 0
+    ref_o, ref_l = oracle.lse_merge(po, pl)
+    dev_parts = parts.clone()
+    dev_parts[torch.isinf(lses)] = float("nan")   # a rank without weight is not read
+    out = torch.empty((rows, dv), dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty((rows,), dtype=torch.float32, device=DEV)
+    g.merge_ranks(world, rows, dv, dev_parts.to(DEV), lses.to(DEV), out, lse)
+    torch.cuda.synchronize()
+    compare(out, lse, ref_o, ref_l, "merge_ranks")
 
 
 def test_mla_split_invariance_and_determinism():
