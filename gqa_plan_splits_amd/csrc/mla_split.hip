@@ -279,6 +279,7 @@ __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const MlaSplitAr
             const uint8_t *lb = lds + (t % kLineSlots) * 32768 + 2048 * kbk;
             const uint8_t *tlb = lds + (t % kTailSlots) * 4096 + 1024 * kbk;
             sacc = f32x4{0.f, 0.f, 0.f, 0.f};
+            f32x4 slo = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int s = 0; s < NS; ++s) {
                 u32x4 lo16, hi16;
@@ -292,9 +293,11 @@ __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const MlaSplitAr
                 }
                 const i32x8 kraw = i32x8{int(lo16.x), int(lo16.y), int(lo16.z), int(lo16.w),
                                          int(hi16.x), int(hi16.y), int(hi16.z), int(hi16.w)};
+                // hi and lo products in two chains, so consecutive MFMAs do not depend on each other
                 sacc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(kraw, qhi[s], sacc, 0, 0, 0, 127, 0, 127);
-                sacc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(kraw, qlo[s], sacc, 0, 0, 0, 127, 0, 127);
+                slo = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(kraw, qlo[s], slo, 0, 0, 0, 127, 0, 127);
             }
+            sacc += slo;
         };
 
         // Softmax of this lane's row over tile t in base 2 with an integer maximum m:
@@ -529,13 +532,16 @@ __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const MlaSplitAr
                     (__attribute__((address_space(3))) int2v *)(lb + v_off[cb][r]));
             const i32x8 vt = i32x8{raw[0].x, raw[0].y, raw[1].x, raw[1].y,
                                    raw[2].x, raw[2].y, raw[3].x, raw[3].y};
+            // hi products of both row blocks, then the lo products: no MFMA waits on the one
+            // just before it
 #pragma unroll
-            for (int rb = 0; rb < 2; ++rb) {
+            for (int rb = 0; rb < 2; ++rb)
                 oacc[rb][cb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
                     vt, ph[rb], oacc[rb][cb], 0, 0, 0, 127, 0, sc[rb]);
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb)
                 oacc[rb][cb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
                     vt, pl[rb], oacc[rb][cb], 0, 0, 0, 127, 0, sc[rb]);
-            }
         }
     };
 
