@@ -6,7 +6,9 @@
 // query rows of one request and walks one partition of that request's keys, writing the
 // partition's softmax-weighted mean of values and the base-2 log-sum-exp of its scores.  Under
 // decode context parallelism (same README section) the call holds one rank's share of each
-// request's positions, and the draft window is taken on the global positions.
+// request's positions, and the draft window is taken on the global positions.  A negative slot
+// id is a skipped key (the top-k lists' has_invalid case, AITER issue "[Perf]
+// pa_decode_sparse", Measurements): its position counts, its weight is zero.
 //
 // Work split (512 threads = 8 waves, one CTA per CU; waves w and w + 4 share SIMD w):
 //   - Score waves 0-3: wave w computes S^T = K Q^T for query rows 16 w .. 16 w + 15 against the 64
@@ -82,7 +84,8 @@ struct MlaLayout {
     static constexpr int kMlOff = kPOff + 2 * 8192;         // P [2][hi, lo][64 rows][64 keys]
     static constexpr int kMlBytes = 3 * 256;                // M, Q, E [64 rows]
     static constexpr int kIdOff = kMlOff + 2 * kMlBytes;
-    static constexpr int kLdsBytes = kIdOff + kIdSlots * 256;
+    static constexpr int kBadOff = kIdOff + kIdSlots * 256;   // per tile: 64-bit mask of skipped keys
+    static constexpr int kLdsBytes = kBadOff + kIdSlots * 8;
     static constexpr int kCopies = 8 + (kTail ? 1 : 0);     // copy instructions per tile per wave
     static_assert(DQK == 576 || DQK == 512, "row width");
     static_assert(kLdsBytes <= 160 * 1024, "LDS");
@@ -197,6 +200,7 @@ __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const MlaSplitAr
     uint8_t *const P = lds + T::kPOff;
     uint8_t *const ML = lds + T::kMlOff;
     const int32_t *const id_ring = reinterpret_cast<const int32_t *>(lds + T::kIdOff);
+    uint64_t *const bad_ring = reinterpret_cast<uint64_t *>(lds + T::kBadOff);
 
     if (wave < 4) {
         // ================================ score wave ================================
@@ -306,7 +310,18 @@ __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const MlaSplitAr
             float bias, esum, qsum;
             int m;
         };
+        // Masked variant (tiles past some row's window or the partition end, and tiles with
+        // skipped keys): scores of keys a row does not see become -inf, without branches.
         auto sm_max = [&](int t, f32x4 (&sacc)[4], auto masked) -> Soft {
+            if constexpr (decltype(masked)::value) {
+                // keys whose slot id is negative (bit k: slot-list index k of the tile)
+                const uint32_t bad = uint32_t(bad_ring[t % kIdSlots] >> kidx_base);
+#pragma unroll
+                for (int kbk = 0; kbk < 4; ++kbk)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        if ((bad >> (8 * i + 2 * kbk)) & 1) sacc[kbk][i] = kNegInf;
+            }
             if constexpr (decltype(masked)::value) {
                 const int thr = p_end - k0 - t * kBK - kidx_base;   // visible: index - base < thr
 #pragma unroll
@@ -358,8 +373,11 @@ __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const MlaSplitAr
         // unused), one 16-key block per scheduling region, each region also holding a piece of
         // the softmax of tile t (whose scores `cur` holds), so the MFMAs and the vector work
         // overlap while only one block's K operands are in registers.
-        auto step = [&](int t, f32x4 (&cur)[4], f32x4 (&next)[4], auto masked) {
+        // Returns whether tile t + 1 has skipped keys (read here, off the critical path: its mask
+        // was published steps ago), which picks the next step's variant.
+        auto step = [&](int t, f32x4 (&cur)[4], f32x4 (&next)[4], auto masked) -> bool {
             const int tq = min(t + 1, ntiles - 1);
+            const bool next_bad = bad_ring[tq % kIdSlots] != 0;
             qk_block(tq, 0, next[0]);
             Soft sf = sm_max(t, cur, masked);
             __builtin_amdgcn_sched_barrier(0);
@@ -374,6 +392,7 @@ __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const MlaSplitAr
             sm_block(t, cur[3], 3, sf);
             sm_finish(t, sf);
             __syncthreads();   // P(t) published; tile t + 2 landed
+            return next_bad;
         };
 
         using yes = std::integral_constant<bool, true>;
@@ -390,12 +409,13 @@ __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const MlaSplitAr
             }
             __syncthreads();   // tile 0 read: step 0's copies may refill its tail slot
             int t = 0;
+            bool bad = bad_ring[0] != 0;
             for (; t + 1 < n_full; t += 2) {
-                step(t, sa, sb, no{});
-                step(t + 1, sb, sa, no{});
+                bad = bad ? step(t, sa, sb, yes{}) : step(t, sa, sb, no{});
+                bad = bad ? step(t + 1, sb, sa, yes{}) : step(t + 1, sb, sa, no{});
             }
-            if (t < n_full) {   // one unmasked tile left: its scores are in sa
-                step(t, sa, sb, no{});
+            if (t < n_full) {   // one full tile left: its scores are in sa
+                bad ? step(t, sa, sb, yes{}) : step(t, sa, sb, no{});
                 ++t;
                 for (; t + 1 < ntiles; t += 2) {
                     step(t, sb, sa, yes{});
@@ -433,20 +453,29 @@ __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const MlaSplitAr
             copy4(ibase + min(k0 + tile * kBK + lane, k1 - 1),
                   lds_addr + T::kIdOff + (tile % kIdSlots) * 256);
     };
+    // A negative slot id marks a key to skip: its copies read row 0 instead, and value wave 0
+    // publishes the tile's mask of such keys for the score waves.
     auto issue_rows = [&](int tile) {
         if (tile >= ntiles) return;
         const int32_t *ids = id_ring + (tile % kIdSlots) * 64;
-        const u32x4 ia = *reinterpret_cast<const u32x4 *>(ids + 8 * jgrp);
-        const u32x4 ib = *reinterpret_cast<const u32x4 *>(ids + 8 * jgrp + 4);
+        const i32x4 ia = *reinterpret_cast<const i32x4 *>(ids + 8 * jgrp);
+        const i32x4 ib = *reinterpret_cast<const i32x4 *>(ids + 8 * jgrp + 4);
         const uint32_t lslot = lds_addr + (tile % kLineSlots) * 32768 + v * 8192;
-        const uint32_t idv[8] = {ia.x, ia.y, ia.z, ia.w, ib.x, ib.y, ib.z, ib.w};
+        const uint32_t idv[8] = {uint32_t(max(ia.x, 0)), uint32_t(max(ia.y, 0)), uint32_t(max(ia.z, 0)),
+                                 uint32_t(max(ia.w, 0)), uint32_t(max(ib.x, 0)), uint32_t(max(ib.y, 0)),
+                                 uint32_t(max(ib.z, 0)), uint32_t(max(ib.w, 0))};
+        if (id_loader) {
+            // every lane stores the same mask (no branch)
+            const uint64_t bad = __builtin_amdgcn_ballot_w64(ids[lane] < 0);
+            bad_ring[tile % kIdSlots] = bad;
+        }
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const int gc = (lane & 7) ^ swz_line(8 * i + jgrp);
             copy16(kv_line + uint64_t(idv[i]) * kv_stride + 16 * gc, lslot + 1024 * i);
         }
         if (T::kTail) {
-            const uint32_t idt = uint32_t(ids[tail_key]);
+            const uint32_t idt = uint32_t(max(ids[tail_key], 0));
             copy16(a.kv + uint64_t(idt) * kv_stride + tail_chunk,
                    lds_addr + T::kTailOff + (tile % kTailSlots) * 4096 + 1024 * v);
         }

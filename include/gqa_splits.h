@@ -106,7 +106,9 @@ typedef struct gqa_decode_problem {
     const void *k_cache;
     const void *v_cache;
 
-    /* MLA: kv_indices[kv_indptr[b] + j] is the pool row of key j of request b.
+    /* MLA: kv_indices[kv_indptr[b] + j] is the pool row of key j of request b; a negative
+     *      entry is a skipped key (the top-k lists' has_invalid case [AITER, Measurements]): it
+     *      keeps its list position and carries no weight.
      * GQA: kv_indices[kv_indptr[b] + j / page_size] is the page of token j of request b.
      * kv_indptr: int32 [B + 1]; seq_lens: int32 [B] keys (tokens) per request. */
     const int32_t *kv_indices;

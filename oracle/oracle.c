@@ -14,6 +14,9 @@
  *    attending KV [0, S - q_len + t]) and the gfx950 "forward_paged" description (K/V caches
  *    [pages, page_size, kv_heads, D] addressed through kv_indptr / kv_page_indices); the
  *    "Numerics" section fixes the comparison target as attention over the same dequantized KV.
+ *  - Skipped keys: AITER issue "[Perf] pa_decode_sparse ...", section "Measurements" (the
+ *    has_invalid flag of the top-k index lists): a negative slot id in an MLA index list is a
+ *    key that is not attended.
  *  - Merge: base-2 log-sum-exp combination of partial results, the operation behind
  *    mla_splitk_reduce ("AMD reducer constraint") and mla_dcp_lse_merge_ranks.
  *
@@ -181,6 +184,10 @@ static void mla_scores(const attn_job *j, int64_t r, int64_t b, int64_t L, doubl
         qv[j->d_lat + d] = oracle_bf16_value(j->q_pe[r * j->d_rope + d]);
     for (int64_t k = 0; k < L; ++k) {
         const int64_t slot = j->kv_indices[j->kv_indptr[b] + k];
+        if (slot < 0) {   /* a skipped key: no weight */
+            s[k] = -INFINITY;
+            continue;
+        }
         const uint8_t *row = j->pool + slot * dqk;
         double dot = 0.0;
         for (int64_t d = 0; d < dqk; ++d) dot += qv[d] * (j->fp8_table[row[d]] * j->kv_scale);
@@ -253,9 +260,15 @@ static void *attn_worker(void *arg) {
         double m = s[0];
         for (int64_t k = 1; k < L; ++k)
             if (s[k] > m) m = s[k];
+        if (m == -INFINITY) {   /* every key skipped: as if the row saw none */
+            for (int64_t d = 0; d < j->dv; ++d) o[d] = 0.0;
+            j->lse2_out[i] = -INFINITY;
+            continue;
+        }
         double l = 0.0;
         for (int64_t d = 0; d < j->dv; ++d) acc[d] = 0.0;
         for (int64_t k = 0; k < L; ++k) {
+            if (s[k] == -INFINITY) continue;   /* a skipped key */
             const double p = exp(s[k] - m);
             l += p;
             if (j->is_mla) {
@@ -333,7 +346,7 @@ int oracle_mla_decode(int64_t B, int64_t q_len, int64_t H, int64_t d_lat, int64_
         if (seq_lens[b] < 0 || kv_indptr[b + 1] - kv_indptr[b] < seq_lens[b]) return -1;
         for (int64_t k = 0; k < seq_lens[b]; ++k) {
             const int32_t slot = kv_indices[kv_indptr[b] + k];
-            if (slot < 0 || slot >= pool_rows) return -1;
+            if (slot >= pool_rows) return -1;   /* negative: a skipped key */
         }
     }
     double table[256];

@@ -46,7 +46,8 @@ int oracle_block_k(int64_t ctas, int64_t sm_count);
  *   q_lat  [B*q_len, H, d_lat]  bf16 bits, contiguous
  *   q_pe   [B*q_len, H, d_rope] bf16 bits, contiguous (may be NULL when d_rope == 0)
  *   pool   [pool_rows, d_lat + d_rope] fp8 bytes, contiguous; key j of request b is row
- *          kv_indices[kv_indptr[b] + j]; the value part is the first d_v columns of that row
+ *          kv_indices[kv_indptr[b] + j]; the value part is the first d_v columns of that row;
+ *          a negative entry is a skipped key (it takes a list position but no weight)
  *   seq_lens[b] keys per request; row (b, t, h) sees keys 0 .. seq_lens[b] - q_len + t
  *   rows / n_rows: the rows to compute (NULL: all B*q_len*H rows in order)
  *   o_out [n_rows, d_v], lse2_out [n_rows]: output and base-2 log-sum-exp of the scores

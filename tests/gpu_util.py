@@ -67,11 +67,16 @@ def oracle_mla(inp, rows=None, n_threads=0):
     indptr = inp.kv_indptr.cpu()
     lens = inp.seq_lens.cpu()
     pools, idx, new_indptr, new_lens = [], [], [0], []
+    n_pool = 0
     for b in reqs:
         a, e = int(indptr[b]), int(indptr[b]) + int(lens[b])
-        sel = inp.kv_indices[a:e].long()
-        pools.append(inp.pool[sel].cpu())
-        idx.append(torch.arange(new_indptr[-1], new_indptr[-1] + (e - a), dtype=torch.int32))
+        sel = inp.kv_indices[a:e].long().cpu()
+        ok = sel >= 0   # negative: a skipped key, kept as -1 in the new list
+        pools.append(inp.pool[sel[ok].to(inp.pool.device)].cpu())
+        new_idx = torch.full((e - a,), -1, dtype=torch.int32)
+        new_idx[ok] = torch.arange(n_pool, n_pool + int(ok.sum()), dtype=torch.int32)
+        n_pool += int(ok.sum())
+        idx.append(new_idx)
         new_indptr.append(new_indptr[-1] + (e - a))
         new_lens.append(e - a)
     pool = torch.cat(pools) if pools else torch.zeros((1, inp.d_qk), dtype=torch.uint8)

@@ -165,6 +165,38 @@ def test_mla_split_partials_match_oracle_on_key_ranges():
             assert np.all(np.abs(got_l - rl) <= LSE_RTOL * np.maximum(1, np.abs(rl)))
 
 
+@pytest.mark.parametrize("q_len", [1, 4])
+def test_mla_skipped_keys_match_oracle(q_len):
+    # negative slot ids (the top-k lists' has_invalid case) are keys with no weight; request 2's
+    # list is all -1
+    lens = [900, 40, 3, 300]
+    inp = workloads.mla_inputs(B=4, q_len=q_len, H=32, seq_lens=lens, pool_rows=1300, seed=61,
+                               device=DEV)
+    gen = torch.Generator(device="cpu").manual_seed(61)
+    idx = inp.kv_indices.cpu()
+    idx[torch.rand(idx.shape, generator=gen) < 0.3] = -1
+    a = int(inp.kv_indptr[2])
+    idx[a:a + 3] = -1
+    inp.kv_indices = idx.to(DEV)
+    ref_o, ref_l = oracle_mla(inp)
+    for np_, bk in [(1, 64), (3, 32), (0, 0)]:
+        log("mla skipped keys q_len=%d np=%d bk=%d" % (q_len, np_, bk))
+        out, lse = run_decode(mla_problem(inp), 512, np_, bk)
+        torch.cuda.synchronize()
+        compare(out, lse, ref_o, ref_l, "mla skipped keys q_len=%d np=%d" % (q_len, np_))
+
+
+def test_sparse_skipped_keys_match_oracle():
+    inp = workloads.sparse_mla_inputs(num_queries=24, invalid_frac=0.25, all_invalid=(5,), seed=4100,
+                                      device=DEV)
+    log("sparse skipped keys")
+    out, lse = run_decode(mla_problem(inp), 448)
+    torch.cuda.synchronize()
+    ref_o, ref_l = oracle_mla(inp)
+    compare(out, lse, ref_o, ref_l, "sparse skipped keys")
+    assert torch.all(lse[5 * 64:6 * 64] == -float("inf"))
+
+
 def dcp_rank_problem(inp, world, rank, glen):
     """Rank `rank` of `world` decode-context-parallel ranks: the positions p % world == rank of
     every request (in position order), with the global lengths in glen."""

@@ -325,6 +325,60 @@ def test_gqa_page_placement_invariance():
     assert np.array_equal(o, o2) and np.array_equal(l, l2)
 
 
+def with_skipped_keys(inp, seed, per_request):
+    """The same requests with `per_request[b]` entries of -1 (skipped keys) inserted at seeded
+    positions of each index list."""
+    g = torch.Generator().manual_seed(seed)
+    idx, indptr, lens = [], [0], []
+    for b in range(inp.B):
+        a, e = int(inp.kv_indptr[b]), int(inp.kv_indptr[b]) + int(inp.seq_lens[b])
+        seg = list(inp.kv_indices[a:e].tolist())
+        for _ in range(per_request[b]):
+            seg.insert(int(torch.randint(0, len(seg) + 1, (1,), generator=g)), -1)
+        idx += seg
+        indptr.append(len(idx))
+        lens.append(len(seg))
+    return idx, indptr, lens
+
+
+def test_skipped_keys_equal_their_removal():
+    # skipped entries (negative slot ids; the top-k lists' has_invalid case) carry no weight:
+    # every row equals the same request with those entries removed, bit for bit
+    inp = small_mla(seed=41, q_len=1, lens=(5, 1, 17, 9), B=4)
+    o, l = run_mla(inp)
+    idx, indptr, lens = with_skipped_keys(inp, 7, [3, 2, 6, 0])
+    inp.kv_indices = torch.tensor(idx, dtype=torch.int32)
+    inp.kv_indptr = torch.tensor(indptr, dtype=torch.int32)
+    inp.seq_lens = torch.tensor(lens, dtype=torch.int32)
+    o2, l2 = run_mla(inp)
+    assert np.array_equal(o, o2) and np.array_equal(l, l2)
+
+
+def test_all_skipped_request_is_empty():
+    inp = small_mla(seed=42, q_len=2, lens=(5, 3, 4), B=3)
+    a, e = int(inp.kv_indptr[1]), int(inp.kv_indptr[1]) + 3
+    inp.kv_indices[a:e] = -1
+    o, l = run_mla(inp)
+    rows = [r for r in range(inp.rows) if r // (inp.q_len * inp.H) == 1]
+    assert np.all(o[rows] == 0) and np.all(l[rows] == -np.inf)
+    others = [r for r in range(inp.rows) if r not in rows]
+    assert np.all(np.isfinite(l[others]))
+
+
+def test_skipped_key_with_one_valid_key_closed_form():
+    # [-1, j, -1]: the row sees one key, so o = v_j and lse2 = s_j / ln 2
+    inp = small_mla(seed=43, q_len=1, lens=(3,), B=1, pool_rows=8)
+    j = int(inp.kv_indices[1])
+    inp.kv_indices[0] = -1
+    inp.kv_indices[2] = -1
+    o, l = run_mla(inp)
+    pool = inp.pool.view(torch.float8_e4m3fn).to(torch.float64) * inp.kv_scale
+    q = torch.cat([inp.q_lat, inp.q_pe], dim=-1).to(torch.float64)[0]   # [H, d_qk]
+    s = inp.scale * (q @ pool[j])
+    np.testing.assert_array_equal(o, pool[j, :inp.d_v].expand(inp.H, -1).numpy())
+    np.testing.assert_allclose(l, (s / LN2).numpy(), rtol=1e-13)
+
+
 def test_invalid_index_is_rejected():
     inp = small_mla(seed=30)
     inp.kv_indices[0] = inp.pool.shape[0]

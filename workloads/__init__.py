@@ -155,9 +155,12 @@ def mla_inputs(*, B: int, q_len: int, H: int, seq_lens: Sequence[int], pool_rows
 
 
 def sparse_mla_inputs(*, num_queries: int, topk: int = 2048, cache_rows: int = 262144, H: int = 64,
-                      seed: int = 4000, device="cpu", name: str = "") -> MlaInputs:
+                      seed: int = 4000, device="cpu", name: str = "", invalid_frac: float = 0.0,
+                      all_invalid: Sequence[int] = ()) -> MlaInputs:
     """Sparse top-k MLA decode: each query is its own request whose keys are `topk` cache rows
-    drawn without replacement; rows are 512 fp8 bytes (448 NoPE + 64 RoPE), value = NoPE part."""
+    drawn without replacement; rows are 512 fp8 bytes (448 NoPE + 64 RoPE), value = NoPE part.
+    invalid_frac: that fraction of the index entries (seeded positions) is -1, a skipped key;
+    all_invalid: queries whose whole list is -1."""
     nq = num_queries
     q = _randn((nq, H, 512), seed + 1, device, torch.bfloat16)
     pool = _fp8_pool(cache_rows, 512, seed + 3, device)
@@ -166,6 +169,11 @@ def sparse_mla_inputs(*, num_queries: int, topk: int = 2048, cache_rows: int = 2
     for _ in range(nq):
         rows.append(torch.randperm(cache_rows, generator=g, device=device)[:topk])
     kv_indices = torch.cat(rows).to(torch.int32) if nq else torch.empty(0, dtype=torch.int32, device=device)
+    if invalid_frac > 0 and nq:
+        drop = torch.rand(kv_indices.shape, generator=_gen(device, seed + 5), device=device) < invalid_frac
+        kv_indices[drop] = -1
+    for qi in all_invalid:
+        kv_indices[qi * topk:(qi + 1) * topk] = -1
     kv_indptr = (torch.arange(nq + 1, device=device, dtype=torch.int32) * topk)
     sl = torch.full((nq,), topk, dtype=torch.int32, device=device)
     return MlaInputs(B=nq, q_len=1, H=H, d_qk=512, d_rope=64, d_v=448, q_lat=q[..., :448],
