@@ -207,6 +207,110 @@ def time_events(fn, n, stream):
     return start.elapsed_time(end) / n
 
 
+def time_graph(fn, n, stream):
+    """Average ms per replay of a HIP graph holding one call of fn (captured on `stream`), so
+    that host launch work is out of the timing; None if capture fails."""
+    import torch
+    try:
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            fn()
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):   # a replay runs on the current stream
+            for _ in range(3):
+                graph.replay()
+            return time_events(graph.replay, n, stream)
+    except RuntimeError:
+        torch.cuda.synchronize()
+        return None
+
+
+def dcp_line(stream, steps, world=8):
+    """Decode context parallelism at the headline shape, one GPU: rank 0 of `world` ranks (every
+    `world`-th position of each 131072-key request: its split and its fp32 merge), and the merge
+    of `world` rank outputs (the ranks' copies of rank 0's output stand in for the others)."""
+    import torch
+    import gqa_plan_splits_amd as g
+    import workloads as w
+    inp = w.mla_long(16, 1, "cuda")
+    B, S = inp.B, int(inp.max_num_keys)
+    idx = inp.kv_indices.view(B, S)[:, 0::world].contiguous().view(-1)
+    local = S // world
+    indptr = torch.arange(B + 1, dtype=torch.int32, device="cuda") * local
+    lens = torch.full((B,), local, dtype=torch.int32, device="cuda")
+    p = g.mla_problem(inp.q_lat, inp.q_pe, inp.pool, idx, indptr, lens, batch=B, q_len=1,
+                      num_heads=inp.H, max_num_keys=local, scale=inp.scale, kv_scale=inp.kv_scale,
+                      d_v=512, glen=inp.seq_lens, cp_rank=0, cp_world=world)
+    np_, bk = g.decode_plan(p)
+    rows = p.rows
+    po = torch.empty((rows, np_, 512), dtype=torch.float32, device="cuda")
+    pl = torch.empty((rows, np_), dtype=torch.float32, device="cuda")
+    parts = torch.empty((world, rows, 512), dtype=torch.float32, device="cuda")
+    lses = torch.empty((world, rows), dtype=torch.float32, device="cuda")
+    out = torch.empty((rows, 512), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((rows,), dtype=torch.float32, device="cuda")
+
+    def rank():
+        g.decode_split(p, np_, bk, po, pl, stream=stream)
+        g.splitk_reduce_f32(rows, np_, 512, po, pl, parts[0], lses[0], stream=stream)
+
+    def merge():
+        g.merge_ranks(world, rows, 512, parts, lses, out, lse, stream=stream)
+
+    for _ in range(5):
+        rank()
+    torch.cuda.synchronize()
+    for r in range(1, world):
+        parts[r].copy_(parts[0])
+        lses[r].copy_(lses[0])
+    rank_ms = time_events(rank, steps, stream)
+    merge_ms = time_events(merge, steps, stream)
+    kv = B * local * 576
+    return {"world": world, "rank_keys_per_request": local, "np": np_, "block_k": bk,
+            "rank_us": round(rank_ms * 1e3, 2), "rank_kv_gbs": round(kv / (rank_ms * 1e-3) / 1e9, 1),
+            "merge_us": round(merge_ms * 1e3, 2)}
+
+
+def wave_sweep(stream, steps):
+    """The planner's one-wave / two-wave choice for MLA with 16 heads (the page's exception,
+    where the two-wave count is the planner's), timed at both counts: batch 4 over 32K-128K
+    keys and batches 8 and 16 at short context."""
+    import torch
+    import gqa_plan_splits_amd as g
+    import workloads as w
+    sm = g.device_sm_count()
+    res = {}
+    for B, S in ((4, 32768), (4, 65536), (4, 131072), (8, 16384), (16, 16384)):
+        inp = w.mla_inputs(B=B, q_len=1, H=16, seq_lens=[S] * B, pool_rows=B * S, seed=5000,
+                           device="cuda", name="h16")
+        p = g.mla_problem(inp.q_lat, inp.q_pe, inp.pool, inp.kv_indices, inp.kv_indptr,
+                          inp.seq_lens, batch=B, q_len=1, num_heads=16, max_num_keys=S,
+                          scale=inp.scale, kv_scale=inp.kv_scale, d_v=512)
+        ctas = B   # one 32-row head block per request at 16 heads
+        pages = -(-S // 256)
+        counts = {"one_wave": max(1, min(sm // ctas, pages, 256)),
+                  "two_wave": max(1, min(2 * sm // ctas, pages, 256)),
+                  "planner": g.decode_plan(p)[0]}
+        row = {}
+        for name, n in counts.items():
+            bk = g.block_k_for(B * n, sm)
+            ws = torch.empty((g.decode_workspace_bytes(p, n) // 4 + 64,), dtype=torch.float32, device="cuda")
+            out = torch.empty((p.rows, 512), dtype=torch.bfloat16, device="cuda")
+            lse = torch.empty((p.rows,), dtype=torch.float32, device="cuda")
+            fn = (lambda n=n, bk=bk, ws=ws, out=out, lse=lse:
+                  g.decode(p, out, lse, np=n, block_k=bk, workspace=ws, stream=stream))
+            for _ in range(5):
+                fn()
+            ms = time_graph(fn, steps, stream) or time_events(fn, steps, stream)
+            row[name] = {"np": n, "us_per_call": round(ms * 1e3, 2)}
+        row["two_wave_speedup"] = round(row["one_wave"]["us_per_call"] / row["two_wave"]["us_per_call"], 3)
+        res["mla_h16_b%d_s%d" % (B, S)] = row
+        del inp, p
+        torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(case, target_s):
     """The oracle as it stands, on a bounded sample of rows of the headline workload, with the
     sampled parity of the GPU output against it."""
@@ -286,6 +390,7 @@ def main():
             case.step()
         torch.cuda.synchronize()
         ms = time_events(case.step, steps, stream)
+        ms_graph = time_graph(case.step, steps, stream)
         ms_split = time_events(case.split_only, steps, stream)
         ms_red = time_events(case.reduce_only, steps, stream) if case.np > 1 else 0.0
         case.step()
@@ -294,6 +399,7 @@ def main():
             "us_per_call": round(ms * 1e3, 2),
             "kv_gbs": round(case.kv_bytes() / (ms * 1e-3) / 1e9, 1),
             "pct_hbm_peak": round(100 * case.kv_bytes() / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 1),
+            "us_per_call_graph": round(ms_graph * 1e3, 2) if ms_graph else None,
             "split_us": round(ms_split * 1e3, 2),
             "reduce_us": round(ms_red * 1e3, 2),
             "np": case.np, "block_k": case.bk, "kv_bytes": case.kv_bytes(),
@@ -352,6 +458,11 @@ def main():
         },
         "per_config": table,
     }
+    if not args.headline_only:
+        result["dcp"] = dcp_line(stream, args.table_steps)
+        print("# dcp %s" % json.dumps(result["dcp"]), file=sys.stderr, flush=True)
+        result["planner_waves"] = wave_sweep(stream, args.table_steps)
+        print("# planner_waves %s" % json.dumps(result["planner_waves"]), file=sys.stderr, flush=True)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)
     print(json.dumps(result), flush=True)

@@ -309,6 +309,49 @@ def test_mla_graph_replay_matches_eager():
         assert torch.equal(out, eager_o) and torch.equal(lse, eager_l)
 
 
+def test_graph_replay_with_new_lengths():
+    # the partition count is fixed when the graph is captured (from the host-known maximum);
+    # lengths, index lists and windows are read on the device at every replay, so one captured
+    # decode serves new lengths with no host work
+    lens_a, lens_b = [3000, 700, 1500], [2999, 0, 2048]
+    inp = workloads.mla_inputs(B=3, q_len=2, H=64, seq_lens=lens_a, pool_rows=6000, seed=71,
+                               device=DEV)
+    inp_b = workloads.mla_inputs(B=3, q_len=2, H=64, seq_lens=lens_b, pool_rows=6000, seed=72,
+                                 device=DEV)
+    # the new index list must fit the captured buffer: pad it to the old length
+    idx = torch.zeros_like(inp.kv_indices)
+    idx[:inp_b.kv_indices.numel()] = inp_b.kv_indices
+    p = g.mla_problem(inp.q_lat, inp.q_pe, inp.pool, inp.kv_indices, inp.kv_indptr, inp.seq_lens,
+                      batch=3, q_len=2, num_heads=64, max_num_keys=3000, scale=inp.scale,
+                      kv_scale=inp.kv_scale, d_v=512)
+    np_, bk = g.decode_plan(p)
+    ws = torch.empty((g.decode_workspace_bytes(p, np_) // 4 + 64,), dtype=torch.float32, device=DEV)
+    out = torch.empty((inp.rows, 512), dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty((inp.rows,), dtype=torch.float32, device=DEV)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        g.decode(p, out, lse, np=np_, block_k=bk, workspace=ws, stream=s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=s):
+        g.decode(p, out, lse, np=np_, block_k=bk, workspace=ws, stream=s)
+    # the lengths-a and lengths-b contents of the captured buffers
+    data = {False: (inp.q_lat.clone(), inp.q_pe.clone(), inp.pool.clone(), inp.kv_indices.clone(),
+                    inp.kv_indptr.clone(), inp.seq_lens.clone()),
+            True: (inp_b.q_lat, inp_b.q_pe, inp_b.pool, idx, inp_b.kv_indptr, inp_b.seq_lens)}
+    refs = {False: oracle_mla(inp), True: oracle_mla(inp_b)}
+    for new in (True, False, True):
+        for dst, src in zip((inp.q_lat, inp.q_pe, inp.pool, inp.kv_indices, inp.kv_indptr,
+                             inp.seq_lens), data[new]):
+            dst.copy_(src)
+        out.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        ref_o, ref_l = refs[new]
+        compare(out, lse, ref_o, ref_l, "graph replay lengths %s" % (lens_b if new else lens_a))
+
+
 FULL_MLA = [("b2_s65536", lambda: workloads.mla_b2_s65536(DEV)),
             ("b8_s131072_q1", lambda: workloads.mla_long(8, 1, DEV)),
             ("b16_s131072_q1", lambda: workloads.mla_long(16, 1, DEV)),
