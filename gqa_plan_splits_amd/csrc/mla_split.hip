@@ -223,32 +223,34 @@ __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const MlaSplitAr
             const int64_t tok = int64_t(b) * a.q_len + t;
             const uint16_t *ql = a.q + tok * a.q_st_tok + int64_t(hh) * a.q_st_head;
             const uint16_t *qp = a.q_pe + tok * a.qpe_st_tok + int64_t(hh) * a.qpe_st_head;
-            // piece pc (0..3) of step s: 8 values at d = 128 s + 32 g + 8 pc (none past DQK)
+            // piece pc (0..3) of step s: 8 values at d = 128 s + 32 g + 8 pc (none past DQK); all
+            // loaded at once (one memory round trip), kept in registers for the split
             auto piece_ok = [&](int s, int pc) { return row_ok && 128 * s + 32 * g + 8 * pc < DQK; };
+            u32x4 qraw[NS][4];
+#pragma unroll
+            for (int s = 0; s < NS; ++s)
+#pragma unroll
+                for (int pc = 0; pc < 4; ++pc)
+                    qraw[s][pc] = piece_ok(s, pc) ? load_q8<DLAT>(ql, qp, 128 * s + 32 * g + 8 * pc)
+                                                  : u32x4{0u, 0u, 0u, 0u};
             float mx = 0.f;
 #pragma unroll
             for (int s = 0; s < NS; ++s)
 #pragma unroll
-                for (int pc = 0; pc < 4; ++pc) {
-                    if (!piece_ok(s, pc)) continue;
-                    const u32x4 w4 = load_q8<DLAT>(ql, qp, 128 * s + 32 * g + 8 * pc);
+                for (int pc = 0; pc < 4; ++pc)
 #pragma unroll
                     for (int w = 0; w < 4; ++w)
-                        mx = fmaxf(mx, fmaxf(fabsf(bf16_lo(w4[w])), fabsf(bf16_hi(w4[w]))));
-                }
+                        mx = fmaxf(mx, fmaxf(fabsf(bf16_lo(qraw[s][pc][w])), fabsf(bf16_hi(qraw[s][pc][w]))));
             mx = rows4_max(mx);
             int ex = 0;
             if (mx > 0.f) frexpf(mx, &ex);            // mx = f * 2^ex, f in [0.5, 1)
             const float qs = ldexpf(1.f, 8 - ex);     // row maximum scaled into [128, 256)
             c_row = a.score_scale * ldexpf(1.f, ex - 8);
-            // second pass over the same (cached) values: the first pass's registers are free
-            asm volatile("" ::: "memory");
 #pragma unroll
             for (int s = 0; s < NS; ++s)
 #pragma unroll
                 for (int pc = 0; pc < 4; ++pc) {
-                    const u32x4 w4 = piece_ok(s, pc) ? load_q8<DLAT>(ql, qp, 128 * s + 32 * g + 8 * pc)
-                                                     : u32x4{0u, 0u, 0u, 0u};
+                    const u32x4 w4 = qraw[s][pc];
 #pragma unroll
                     for (int w = 0; w < 4; w += 2) {
                         int hi, lo;
@@ -398,8 +400,6 @@ __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const MlaSplitAr
         using yes = std::integral_constant<bool, true>;
         using no = std::integral_constant<bool, false>;
         if (ntiles > 0) {
-            __syncthreads();   // slot ids of tiles 0-3 loaded
-            __syncthreads();   // their reads done
             __syncthreads();   // tiles 0 and 1 landed
             f32x4 sa[4], sb[4];
 #pragma unroll
@@ -455,35 +455,55 @@ __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const MlaSplitAr
     };
     // A negative slot id marks a key to skip: its copies read row 0 instead, and value wave 0
     // publishes the tile's mask of such keys for the score waves.
-    auto issue_rows = [&](int tile) {
-        if (tile >= ntiles) return;
-        const int32_t *ids = id_ring + (tile % kIdSlots) * 64;
-        const i32x4 ia = *reinterpret_cast<const i32x4 *>(ids + 8 * jgrp);
-        const i32x4 ib = *reinterpret_cast<const i32x4 *>(ids + 8 * jgrp + 4);
+    // The copies of one tile given its slot ids: this lane's eight line keys 8 jgrp + i, its rope
+    // tail key, and (value wave 0) the key numbered by the lane, whose sign makes the mask.
+    auto copy_rows = [&](int tile, const int32_t (&kid)[8], int32_t tid, int32_t mid) {
         const uint32_t lslot = lds_addr + (tile % kLineSlots) * 32768 + v * 8192;
-        const uint32_t idv[8] = {uint32_t(max(ia.x, 0)), uint32_t(max(ia.y, 0)), uint32_t(max(ia.z, 0)),
-                                 uint32_t(max(ia.w, 0)), uint32_t(max(ib.x, 0)), uint32_t(max(ib.y, 0)),
-                                 uint32_t(max(ib.z, 0)), uint32_t(max(ib.w, 0))};
         if (id_loader) {
             // every lane stores the same mask (no branch)
-            const uint64_t bad = __builtin_amdgcn_ballot_w64(ids[lane] < 0);
+            const uint64_t bad = __builtin_amdgcn_ballot_w64(mid < 0);
             bad_ring[tile % kIdSlots] = bad;
         }
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const int gc = (lane & 7) ^ swz_line(8 * i + jgrp);
-            copy16(kv_line + uint64_t(idv[i]) * kv_stride + 16 * gc, lslot + 1024 * i);
+            copy16(kv_line + uint64_t(uint32_t(max(kid[i], 0))) * kv_stride + 16 * gc, lslot + 1024 * i);
         }
-        if (T::kTail) {
-            const uint32_t idt = uint32_t(max(ids[tail_key], 0));
-            copy16(a.kv + uint64_t(idt) * kv_stride + tail_chunk,
+        if (T::kTail)
+            copy16(a.kv + uint64_t(uint32_t(max(tid, 0))) * kv_stride + tail_chunk,
                    lds_addr + T::kTailOff + (tile % kTailSlots) * 4096 + 1024 * v);
-        }
     };
-    // Issue order: ids(0..3), then rows(0), rows(1), rows(2), ids(4), ids(5), then rows(j),
-    // ids(j + 3) for j = 3, 4, ...; ids only in value wave 0, operations for tiles >= ntiles
-    // skipped.  Copies retire in issue order.  Rows(j) are read in step j - 1 (the scores of tile
-    // j) and step j + 1 (its values); ids(j) in step j - 3 (the copies of rows(j)).
+    // ... with the ids taken from the shared ring
+    auto issue_rows = [&](int tile) {
+        if (tile >= ntiles) return;
+        const int32_t *ids = id_ring + (tile % kIdSlots) * 64;
+        const i32x4 ia = *reinterpret_cast<const i32x4 *>(ids + 8 * jgrp);
+        const i32x4 ib = *reinterpret_cast<const i32x4 *>(ids + 8 * jgrp + 4);
+        const int32_t kid[8] = {ia.x, ia.y, ia.z, ia.w, ib.x, ib.y, ib.z, ib.w};
+        copy_rows(tile, kid, ids[tail_key], ids[lane]);
+    };
+    // Slot ids of tiles 0-2, straight from global memory into registers (so the first copies do
+    // not wait on a workgroup barrier, which the score waves reach only after preparing Q).
+    int32_t pre_kid[3][8], pre_tid[3], pre_mid[3];
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+        const int kb = k0 + j * kBK;
+        const int last = max(k1 - 1, k0);   // clamped like the ring's loads (k1 > k0 when used)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) pre_kid[j][i] = 0;
+        pre_tid[j] = pre_mid[j] = 0;
+        if (j < ntiles) {
+            const int32_t *src = a.kv_indices + base;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) pre_kid[j][i] = src[min(kb + 8 * jgrp + i, last)];
+            pre_tid[j] = src[min(kb + tail_key, last)];
+            pre_mid[j] = src[min(kb + lane, last)];
+        }
+    }
+    // Issue order: ids(3), rows(0), rows(1), rows(2), ids(4), ids(5), then rows(j), ids(j + 3)
+    // for j = 3, 4, ...; ids only in value wave 0, operations for tiles >= ntiles skipped.
+    // Copies retire in issue order.  Rows(j) are read in step j - 1 (the scores of tile j) and
+    // step j + 1 (its values); ids(j) in step j - 3 (the copies of rows(j)).
     constexpr int NC = T::kCopies;
     auto cnt_rows = [&](int j) { return j >= 0 && j < ntiles ? NC : 0; };
     auto cnt_ids = [&](int j) { return id_loader && j >= 0 && j < ntiles ? 1 : 0; };
@@ -575,21 +595,16 @@ __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const MlaSplitAr
     };
 
     if (ntiles > 0) {
-        issue_ids(0);
-        issue_ids(1);
-        issue_ids(2);
+        wait_vmem(0);   // the slot ids of tiles 0-2 are in registers
         issue_ids(3);
-        wait_vmem(0);
-        __syncthreads();   // slot ids of tiles 0-3 loaded
-        issue_rows(0);
-        issue_rows(1);
-        issue_rows(2);
-        __syncthreads();   // every read of id slots 0-2 done
+#pragma unroll
+        for (int j = 0; j < 3; ++j)
+            if (j < ntiles) copy_rows(j, pre_kid[j], pre_tid[j], pre_mid[j]);
         issue_ids(4);
         issue_ids(5);
-        // rows(0), rows(1) landed; issued after rows(1): rows(2), ids(4), ids(5)
+        // ids(3), rows(0), rows(1) landed; issued after rows(1): rows(2), ids(4), ids(5)
         wait_vmem(cnt_rows(2) + cnt_ids(4) + cnt_ids(5));
-        __syncthreads();   // tiles 0 and 1 landed
+        __syncthreads();   // tiles 0 and 1, the ids of tile 3 and the masks of tiles 0-2 landed
         __syncthreads();   // the score waves read tile 0 (tail slot 0 is refilled in step 0)
         for (int t = 0; t < ntiles; ++t) {
             if (t > 0) pv(t - 1);
