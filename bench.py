@@ -226,6 +226,24 @@ def time_graph(fn, n, stream):
         return None
 
 
+def time_cold(fn, n, stream, flush):
+    """Average ms per call of fn with the caches cold: before each call, outside its event pair,
+    a 512 MiB buffer is written, which evicts L2 and the 256 MB MALL."""
+    import torch
+    total = 0.0
+    for _ in range(n):
+        with torch.cuda.stream(stream):
+            flush.fill_(1.0)
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        start.record(stream)
+        fn()
+        end.record(stream)
+        end.synchronize()
+        total += start.elapsed_time(end)
+    return total / n
+
+
 def dcp_line(stream, steps, world=8):
     """Decode context parallelism at the headline shape, one GPU: rank 0 of `world` ranks (every
     `world`-th position of each 131072-key request: its split and its fp32 merge), and the merge
@@ -372,6 +390,7 @@ def main():
         return
     stream = torch.cuda.Stream()
     sm = g.device_sm_count()
+    flush = torch.empty((512 << 20) // 4, dtype=torch.float32, device="cuda")
 
     table = {}
     headline = None
@@ -390,6 +409,7 @@ def main():
             case.step()
         torch.cuda.synchronize()
         ms = time_events(case.step, steps, stream)
+        ms_cold = time_cold(case.step, max(5, steps // 4), stream, flush)
         ms_graph = time_graph(case.step, steps, stream)
         ms_split = time_events(case.split_only, steps, stream)
         ms_red = time_events(case.reduce_only, steps, stream) if case.np > 1 else 0.0
@@ -399,6 +419,8 @@ def main():
             "us_per_call": round(ms * 1e3, 2),
             "kv_gbs": round(case.kv_bytes() / (ms * 1e-3) / 1e9, 1),
             "pct_hbm_peak": round(100 * case.kv_bytes() / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 1),
+            "us_per_call_cold": round(ms_cold * 1e3, 2),
+            "pct_hbm_peak_cold": round(100 * case.kv_bytes() / (ms_cold * 1e-3) / 1e9 / HBM_PEAK_GBS, 1),
             "us_per_call_graph": round(ms_graph * 1e3, 2) if ms_graph else None,
             "split_us": round(ms_split * 1e3, 2),
             "reduce_us": round(ms_red * 1e3, 2),
