@@ -226,6 +226,19 @@ def time_graph(fn, n, stream):
         return None
 
 
+def time_interleaved(fns, n, stream):
+    """Average ms per call of each fn over n calls each, timed in five interleaved rounds of
+    n / 5 calls (when 5 divides n) so that slow drifts of the clock weigh on all of them alike."""
+    rounds = 5 if n % 5 == 0 and n >= 5 else 1
+    k = n // rounds
+    tot = [0.0] * len(fns)
+    for _ in range(rounds):
+        for i, fn in enumerate(fns):
+            if fn is not None:
+                tot[i] += time_events(fn, k, stream) * k
+    return [t / n for t in tot]
+
+
 def time_cold(fn, n, stream, flush):
     """Average ms per call of fn with the caches cold: before each call, outside its event pair,
     a 512 MiB buffer is written, which evicts L2 and the 256 MB MALL."""
@@ -408,11 +421,10 @@ def main():
         for _ in range(warm):
             case.step()
         torch.cuda.synchronize()
-        ms = time_events(case.step, steps, stream)
+        ms, ms_split, ms_red = time_interleaved(
+            [case.step, case.split_only, case.reduce_only if case.np > 1 else None], steps, stream)
         ms_cold = time_cold(case.step, max(5, steps // 4), stream, flush)
         ms_graph = time_graph(case.step, steps, stream)
-        ms_split = time_events(case.split_only, steps, stream)
-        ms_red = time_events(case.reduce_only, steps, stream) if case.np > 1 else 0.0
         case.step()
         torch.cuda.synchronize()
         entry = {
