@@ -212,6 +212,11 @@ __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const MlaSplitAr
         const int rl = 16 * wave + n16;         // row within the block
         const bool row_ok = rl < nrows;
         constexpr int NS = (DQK + 127) / 128;   // contraction steps
+        // MFMAs per 16-key block: hi and lo products of every step, except that the rope tail of
+        // 576-byte rows needs one: lanes g >= 2, whose K bytes repeat those of lanes g - 2, hold the
+        // lo part of the query tail where the hi part of the other lanes is, so one product sums
+        // K (Q_hi + Q_lo) over the 64 tail bytes.
+        constexpr int NQK = 2 * NS - (T::kTail ? 1 : 0);
         int p_end;                              // keys visible to this row
         float c_row;                            // base-2 score per unit of the raw product
         i32x8 qhi[NS], qlo[NS];
@@ -223,15 +228,17 @@ __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const MlaSplitAr
             const int64_t tok = int64_t(b) * a.q_len + t;
             const uint16_t *ql = a.q + tok * a.q_st_tok + int64_t(hh) * a.q_st_head;
             const uint16_t *qp = a.q_pe + tok * a.qpe_st_tok + int64_t(hh) * a.qpe_st_head;
-            // piece pc (0..3) of step s: 8 values at d = 128 s + 32 g + 8 pc (none past DQK); all
-            // loaded at once (one memory round trip), kept in registers for the split
-            auto piece_ok = [&](int s, int pc) { return row_ok && 128 * s + 32 * g + 8 * pc < DQK; };
+            // piece pc (0..3) of step s: 8 values at d = 128 s + 32 g + 8 pc (none past DQK; in the
+            // rope tail lanes g >= 2 load those of lanes g - 2); all loaded at once (one memory
+            // round trip), kept in registers for the split
+            auto gq = [&](int s) { return T::kTail && s == NS - 1 ? (g & 1) : g; };
+            auto piece_ok = [&](int s, int pc) { return row_ok && 128 * s + 32 * gq(s) + 8 * pc < DQK; };
             u32x4 qraw[NS][4];
 #pragma unroll
             for (int s = 0; s < NS; ++s)
 #pragma unroll
                 for (int pc = 0; pc < 4; ++pc)
-                    qraw[s][pc] = piece_ok(s, pc) ? load_q8<DLAT>(ql, qp, 128 * s + 32 * g + 8 * pc)
+                    qraw[s][pc] = piece_ok(s, pc) ? load_q8<DLAT>(ql, qp, 128 * s + 32 * gq(s) + 8 * pc)
                                                   : u32x4{0u, 0u, 0u, 0u};
             float mx = 0.f;
 #pragma unroll
@@ -260,6 +267,7 @@ __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const MlaSplitAr
                         qlo[s][2 * pc + w / 2] = lo;
                     }
                 }
+            if (T::kTail && g >= 2) qhi[NS - 1] = qlo[NS - 1];
         }
 
         // Loop-invariant LDS offsets of this lane's K operand (key at tile position 16 kbk + n16,
@@ -279,7 +287,7 @@ __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const MlaSplitAr
         // 32 (g & 1) + (g >> 1) + 8 i + 2 kbk (key_of_pos).
         const int kidx_base = 32 * (g & 1) + (g >> 1);
 
-        // K operand reads and the MFMAs of 16-key block kbk of the scores of tile t (10 for
+        // K operand reads and the MFMAs of 16-key block kbk of the scores of tile t (9 for
         // 576-byte rows, 8 for 512-byte rows).
         auto qk_block = [&](int t, int kbk, f32x4 &sacc) {
             const uint8_t *lb = lds + (t % kLineSlots) * 32768 + 2048 * kbk;
@@ -290,7 +298,7 @@ __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const MlaSplitAr
             for (int s = 0; s < NS; ++s) {
                 u32x4 lo16, hi16;
                 if (T::kTail && s == NS - 1) {
-                    // lanes g >= 2 read the chunks of lanes g - 2; their query bytes are zero
+                    // lanes g >= 2 read the chunks of lanes g - 2 (their query operand is the lo tail)
                     lo16 = *reinterpret_cast<const u32x4 *>(tlb + k_tail0);
                     hi16 = *reinterpret_cast<const u32x4 *>(tlb + k_tail1);
                 } else {
@@ -301,7 +309,8 @@ __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const MlaSplitAr
                                          int(hi16.x), int(hi16.y), int(hi16.z), int(hi16.w)};
                 // hi and lo products in two chains, so consecutive MFMAs do not depend on each other
                 sacc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(kraw, qhi[s], sacc, 0, 0, 0, 127, 0, 127);
-                slo = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(kraw, qlo[s], slo, 0, 0, 0, 127, 0, 127);
+                if (!(T::kTail && s == NS - 1))
+                    slo = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(kraw, qlo[s], slo, 0, 0, 0, 127, 0, 127);
             }
             sacc += slo;
         };
