@@ -71,6 +71,8 @@ def _load():
         lib.oracle_plan_splits.argtypes = [_i64, _i64, _i64, _i64, _int]
         lib.oracle_block_k.restype = _int
         lib.oracle_block_k.argtypes = [_i64, _i64]
+        lib.oracle_plan_sparse_splits.restype = _int
+        lib.oracle_plan_sparse_splits.argtypes = [_i64, _i64, _i64, _i64, _i64, _i64, _i64, _vp, _vp]
         lib.oracle_mla_decode.restype = _int
         lib.oracle_mla_decode.argtypes = [_i64, _i64, _i64, _i64, _i64, _i64, _vp, _vp, _vp, _i64,
                                           _vp, _vp, _vp, _dbl, _dbl, _int, _vp, _i64, _vp, _vp,
@@ -122,6 +124,17 @@ def plan_splits(batch_size: int, num_keys: int, heads_per_group: int, sm_count: 
     parity unpinned against the page for that branch (only its caps are pinned)."""
     return int(_load().oracle_plan_splits(batch_size, num_keys, heads_per_group, sm_count,
                                           int(bool(is_mla))))
+
+
+def plan_sparse_splits(num_tokens: int, num_heads: int, topk: int, extra_topk: int = 0, *,
+                       num_sms: int, max_splits: int = 16, head_tiles: int = 1):
+    """(num_splits, chunks_per_block) of the sparse top-k planner on the FlashInfer API page
+    "cake_sparse_mla_sm120_dsv4_nvfp4_plan_splits", or None where the C oracle returns -1."""
+    ns = ctypes.c_int64(0)
+    cpb = ctypes.c_int64(0)
+    rc = _load().oracle_plan_sparse_splits(num_tokens, num_heads, topk, extra_topk, num_sms,
+                                           max_splits, head_tiles, ctypes.byref(ns), ctypes.byref(cpb))
+    return None if rc != 0 else (int(ns.value), int(cpb.value))
 
 
 def block_k(ctas: int, sm_count: int) -> int:

@@ -140,6 +140,75 @@ int oracle_block_k(int64_t ctas, int64_t sm_count) {
     return ctas > sm_count ? 32 : 64;
 }
 
+/* Sparse top-k split planner (FlashInfer API page "cake_sparse_mla_sm120_dsv4_nvfp4_plan_splits",
+ * the measured split rules and the GB10 paragraph), in the page's order:
+ *  1. Work: candidates in chunks of 64, counted per cache (a chunk holds one cache's slots);
+ *     CTAs of 16 * head_tiles heads, so the unsplit grid is num_tokens * ceil(heads / that).
+ *  2. Two chunks (or fewer) never split.
+ *  3. While the unsplit grid covers at most 40 % of the SMs, the largest power-of-two split
+ *     (up to max_splits) whose grid stays within 80 % of the SMs and that leaves every CTA at
+ *     least two chunks -- one chunk per CTA is allowed for a lone CTA only.
+ *     Fewer than 64 SMs (the GB10 paragraph): the grid stays within SMs / 3 CTAs instead, the
+ *     gather streams num_tokens * splits within SMs / 6, and two chunks per CTA hold for a lone
+ *     CTA too.
+ *  4. Once the unsplit grid fills the SMs, a split in two only for 16-chunk work whose doubled
+ *     grid ends in a wave at least half full (not below 64 SMs: no wave-quantization split).
+ *  5. Everything else unsplit.
+ *  6. Independently, at most 16 chunks per CTA (the CTA index table): at least ceil(chunks / 16)
+ *     splits, an error when max_splits is below that.
+ *  7. chunks_per_block = ceil(chunks / num_splits).
+ * Percentages are compared exactly in integers (10 * grid <= 4 * SMs, 10 * grid <= 8 * SMs). */
+int oracle_plan_sparse_splits(int64_t num_tokens, int64_t num_heads, int64_t topk,
+                              int64_t extra_topk, int64_t num_sms, int64_t max_splits,
+                              int64_t head_tiles, int64_t *num_splits, int64_t *chunks_per_block) {
+    if (num_tokens <= 0 || num_heads <= 0 || num_sms <= 0 || max_splits <= 0 || head_tiles <= 0 ||
+        topk < 0 || extra_topk < 0 || !num_splits || !chunks_per_block)
+        return -1;
+
+    /* step 1 */
+    const int64_t CHUNK = 64;
+    const int64_t MAX_CHUNKS_PER_BLOCK = 16;
+    const int64_t chunks = ceil_div(topk, CHUNK) + ceil_div(extra_topk, CHUNK);
+    const int64_t grid = num_tokens * ceil_div(num_heads, 16 * head_tiles);
+    const int small_device = num_sms < 64;
+
+    int64_t splits = 1;
+    if (chunks <= 2) {
+        /* step 2 */
+        splits = 1;
+    } else if (10 * grid <= 4 * num_sms) {
+        /* step 3 */
+        const int lone = grid == 1 && !small_device;
+        for (int64_t s = 1; s <= max_splits; s *= 2) {
+            int ok;
+            if (small_device)
+                ok = grid * s <= num_sms / 3 && num_tokens * s <= num_sms / 6;
+            else
+                ok = 10 * grid * s <= 8 * num_sms;
+            ok = ok && (lone ? chunks >= s : chunks >= 2 * s);
+            if (ok) splits = s;
+        }
+    } else if (grid >= num_sms) {
+        /* step 4 */
+        if (!small_device && chunks == 16) {
+            const int64_t last = (2 * grid) % num_sms;
+            if (last == 0 || 2 * last >= num_sms) splits = 2;
+        }
+    }
+    /* step 5: otherwise unsplit */
+
+    /* step 6 */
+    const int64_t forced = ceil_div(chunks, MAX_CHUNKS_PER_BLOCK);
+    if (forced > max_splits) return -1;
+    splits = max64(splits, forced);
+    splits = min64(splits, max_splits);
+
+    /* step 7 */
+    *num_splits = splits;
+    *chunks_per_block = chunks > 0 ? ceil_div(chunks, splits) : 0;
+    return 0;
+}
+
 /* ------------------------------------------------------------------------------------------ */
 /* Attention                                                                                   */
 /* ------------------------------------------------------------------------------------------ */

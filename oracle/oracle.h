@@ -42,6 +42,15 @@ int64_t oracle_plan_splits(int64_t batch_size, int64_t num_keys, int64_t heads_p
  * non-positive arguments. */
 int oracle_block_k(int64_t ctas, int64_t sm_count);
 
+/* (num_splits, chunks_per_block) of the sparse top-k split planner on the FlashInfer API page
+ * "cake_sparse_mla_sm120_dsv4_nvfp4_plan_splits".  Candidates come in chunks of 64 (16 chunks =
+ * the 1024-candidate CTA index table); the grid is counted in CTAs of 16 * head_tiles heads.
+ * Returns 0 and writes both outputs, or -1 on a non-positive size or head_tiles, a negative
+ * candidate count, and when max_splits is below the split count the index table forces. */
+int oracle_plan_sparse_splits(int64_t num_tokens, int64_t num_heads, int64_t topk,
+                              int64_t extra_topk, int64_t num_sms, int64_t max_splits,
+                              int64_t head_tiles, int64_t *num_splits, int64_t *chunks_per_block);
+
 /* Unsplit softmax attention of absorbed MLA decode over a page_size-1 fp8 pool.
  *   q_lat  [B*q_len, H, d_lat]  bf16 bits, contiguous
  *   q_pe   [B*q_len, H, d_rope] bf16 bits, contiguous (may be NULL when d_rope == 0)

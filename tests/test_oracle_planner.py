@@ -108,3 +108,54 @@ def test_two_wave_is_read_left_to_right():
     # tell the readings apart (its CTA counts all divide 256).  At sm=260 and 8 CTAs the two
     # readings give 65 and 64, which bucket to 128 and 64.
     assert oracle.plan_splits(4, 1 << 20, 64, 260, True) == 128
+
+
+# ---- sparse top-k planner: FlashInfer API page "cake_sparse_mla_sm120_dsv4_nvfp4_plan_splits"
+
+def test_sparse_planner_page_statements(golden):
+    for nt, nh, topk, extra, sms, mx, ht, ns, cpb in golden("sparse_planner_statements.txt"):
+        got = oracle.plan_sparse_splits(nt, nh, topk, extra, num_sms=sms, max_splits=mx, head_tiles=ht)
+        assert got == (ns, cpb), (nt, nh, topk, extra, sms, mx, ht, got)
+
+
+def test_sparse_planner_index_table_bound():
+    # "chunks_per_block <= max_chunks_per_block always holds": more than 1024 candidates force at
+    # least ceil(chunks / 16) splits, and a max_splits below that is an error.
+    for topk in (0, 64, 1000, 1024, 1025, 2048, 4096, 8192):
+        chunks = -(-topk // 64)
+        forced = max(1, -(-chunks // 16))
+        for mx in (1, 2, 4, 8, 16, 64):
+            for nt, sms in ((1, 48), (3, 170), (200, 170), (1, 256), (512, 256)):
+                got = oracle.plan_sparse_splits(nt, 16, topk, 0, num_sms=sms, max_splits=mx)
+                if forced > mx:
+                    assert got is None
+                    continue
+                ns, cpb = got
+                assert forced <= ns <= mx
+                assert cpb <= 16 and ns * cpb >= chunks
+                if chunks <= 2:
+                    assert ns == 1
+
+
+def test_sparse_planner_split_is_largest_admissible():
+    # The small-grid rule, re-checked by brute force over every power of two: the planner's split
+    # is the largest one that keeps the grid within 80 % of the SMs (SMs / 3 and gather streams
+    # within SMs / 6 below 64 SMs) and leaves two chunks per CTA (one for a lone CTA on a large
+    # device), unless the index table forces more.
+    for sms in (48, 170, 188, 256):
+        for nt in (1, 2, 3, 5, 8, 16):
+            for nh in (16, 64, 128):
+                for topk in (192, 256, 512, 1024):
+                    grid = nt * -(-nh // 16)
+                    if 10 * grid > 4 * sms:
+                        continue
+                    chunks = -(-topk // 64)
+                    ns, _ = oracle.plan_sparse_splits(nt, nh, topk, 0, num_sms=sms)
+                    lone = grid == 1 and sms >= 64
+                    best = 1
+                    for s in (1, 2, 4, 8, 16):
+                        room = (grid * s <= sms // 3 and nt * s <= sms // 6) if sms < 64 else 10 * grid * s <= 8 * sms
+                        enough = chunks >= s if lone else chunks >= 2 * s
+                        if room and enough and chunks > 2:
+                            best = s
+                    assert ns == best, (sms, nt, nh, topk, ns, best)
