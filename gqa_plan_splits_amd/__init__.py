@@ -27,6 +27,7 @@ from ._lib import (  # noqa: F401
     library_path,
     merge_ranks,
     mla_problem,
+    plan_sparse_splits,
     plan_splits,
     splitk_reduce,
     splitk_reduce_f32,

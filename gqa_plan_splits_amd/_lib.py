@@ -13,7 +13,7 @@ FP8_E4M3FN = 0
 FP8_E4M3FNUZ = 1
 
 # Every function include/gqa_splits.h declares.
-_SYMBOLS = ("plan_splits", "block_k_for", "device_sm_count", "decode_plan", "decode_split",
+_SYMBOLS = ("plan_splits", "plan_sparse_splits", "block_k_for", "device_sm_count", "decode_plan", "decode_split",
             "splitk_reduce", "splitk_reduce_f32", "merge_ranks", "decode_workspace_bytes", "decode", "fp8_e4m3_to_bf16",
             "status_string", "last_error_detail")
 
@@ -93,6 +93,8 @@ def _load():
     pp = ctypes.POINTER(DecodeProblem)
     lib.plan_splits.argtypes = [i64, i64, i64, i64, i32, ctypes.POINTER(i64)]
     lib.block_k_for.argtypes = [i64, i64]
+    lib.plan_sparse_splits.argtypes = [i64, i64, i64, i64, i64, i64, i64, ctypes.POINTER(i64),
+                                       ctypes.POINTER(i64)]
     lib.device_sm_count.argtypes = [ctypes.POINTER(i64)]
     lib.decode_plan.argtypes = [pp, i64, i32, i64, ctypes.POINTER(i64), ctypes.POINTER(i32)]
     lib.decode_split.argtypes = [pp, i64, i32, vp, vp, vp]
@@ -164,6 +166,17 @@ def plan_splits(batch_size: int, num_keys: int, heads_per_group: int, sm_count: 
     _check(_load().plan_splits(batch_size, num_keys, heads_per_group, sm_count, int(bool(is_mla)),
                                ctypes.byref(out)), "plan_splits")
     return out.value
+
+
+def plan_sparse_splits(num_tokens: int, num_heads: int, topk: int, extra_topk: int = 0, *,
+                       num_sms: int = 0, max_splits: int = 16, head_tiles: int = 4):
+    """(num_splits, chunks_per_block) of the sparse top-k planner (chunks of 64 candidates)."""
+    ns = ctypes.c_int64(0)
+    cpb = ctypes.c_int64(0)
+    _check(_load().plan_sparse_splits(num_tokens, num_heads, topk, extra_topk, num_sms, max_splits,
+                                      head_tiles, ctypes.byref(ns), ctypes.byref(cpb)),
+           "plan_sparse_splits")
+    return int(ns.value), int(cpb.value)
 
 
 def block_k_for(ctas: int, sm_count: int) -> int:

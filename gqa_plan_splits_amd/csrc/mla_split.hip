@@ -216,7 +216,6 @@ __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const MlaSplitAr
         // 576-byte rows needs one: lanes g >= 2, whose K bytes repeat those of lanes g - 2, hold the
         // lo part of the query tail where the hi part of the other lanes is, so one product sums
         // K (Q_hi + Q_lo) over the 64 tail bytes.
-        constexpr int NQK = 2 * NS - (T::kTail ? 1 : 0);
         int p_end;                              // keys visible to this row
         float c_row;                            // base-2 score per unit of the raw product
         i32x8 qhi[NS], qlo[NS];

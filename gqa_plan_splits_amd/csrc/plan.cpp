@@ -2,6 +2,8 @@
 //
 // Planner: Modular MAX API page "hip_mha_decoding_num_partitions" (MI355X MHA + MLA decode).
 // Tile rule: AITER issue "[Perf] pa_decode_sparse: BLOCK_K=64 is suboptimal above the CU count".
+// Sparse top-k planner: FlashInfer API page "cake_sparse_mla_sm120_dsv4_nvfp4_plan_splits" (the
+// measured split rules and the GB10 paragraph).
 //
 // Readings where the planner page is silent (kept identical to the written spec the tests
 // check against):
@@ -14,6 +16,7 @@
 //     batch 8 up), limited to the page count, and kept >= 1.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdint>
 #include <mutex>
 
@@ -133,4 +136,68 @@ extern "C" int block_k_for(int64_t ctas, int64_t sm_count) {
     // While every CTA has a CU of its own the 64-key tile does more work per CU; beyond that
     // the 32-key tile packs several CTAs per CU and hides the gather latency better.
     return ctas > sm_count ? 32 : 64;
+}
+
+// ---- sparse top-k planner.  Readings where the page is silent (kept identical to the written
+// spec the tests check against): candidates are chunked per cache (a chunk of 64 holds one
+// cache's slots); "at least two chunks per CTA" is floor(chunks / splits) >= 2; the percentages
+// are exact (10 * grid against 4 or 8 * SMs); "ends in a wave at least half full" is a last wave
+// that is full or holds at least half the SMs; the GB10 caps (SMs / 3 CTAs, SMs / 6 gather
+// streams, no lone-CTA exception, no wave-quantization split) apply below 64 SMs.
+namespace {
+
+constexpr int64_t kSparseChunk = 64;            // candidates per chunk
+constexpr int64_t kSparseMaxChunksPerCta = 16;  // the CTA index table: 1024 candidates
+constexpr int64_t kSparseHeadsPerTile = 16;
+
+inline int64_t floor_pow2(int64_t v) {  // largest power of two <= v, for v >= 1
+    int64_t p = 1;
+    while (p <= v / 2) p *= 2;
+    return p;
+}
+
+}  // namespace
+
+extern "C" int plan_sparse_splits(int64_t num_tokens, int64_t num_heads, int64_t topk,
+                                  int64_t extra_topk, int64_t num_sms, int64_t max_splits,
+                                  int64_t head_tiles, int64_t *num_splits_out,
+                                  int64_t *chunks_per_block_out) {
+    if (!num_splits_out || !chunks_per_block_out || num_tokens < 1 || num_heads < 1 ||
+        max_splits < 1 || head_tiles < 1 || topk < 0 || extra_topk < 0)
+        return GQA_ERR_INVALID_ARGUMENT;
+    if (num_sms <= 0) {
+        const int rc = device_sm_count(&num_sms);
+        if (rc != GQA_OK) return rc;
+    }
+    const int64_t chunks = div_up(topk, kSparseChunk) + div_up(extra_topk, kSparseChunk);
+    const int64_t ctas = num_tokens * div_up(num_heads, kSparseHeadsPerTile * head_tiles);
+    const bool gb10 = num_sms < 64;
+    // The CTA index table holds 16 chunks: fewer splits than this cannot be launched.
+    const int64_t min_splits = div_up(chunks, kSparseMaxChunksPerCta);
+    if (min_splits > max_splits) return GQA_ERR_INVALID_ARGUMENT;
+
+    int64_t splits = 1;
+    if (chunks > 2) {   // two chunks: one CTA pipelining both beats two plus a merge
+        if (10 * ctas <= 4 * num_sms) {
+            // small grid: the largest power of two the caps allow
+            int64_t cap = max_splits;
+            if (gb10) {
+                cap = std::min(cap, (num_sms / 3) / ctas);         // grid within SMs / 3
+                cap = std::min(cap, (num_sms / 6) / num_tokens);   // gather streams within SMs / 6
+                cap = std::min(cap, chunks / 2);
+            } else {
+                cap = std::min(cap, (8 * num_sms) / (10 * ctas));  // grid within 80 % of the SMs
+                cap = std::min(cap, ctas == 1 ? chunks : chunks / 2);
+            }
+            if (cap >= 1) splits = floor_pow2(cap);
+        } else if (ctas >= num_sms && !gb10 && chunks == kSparseMaxChunksPerCta) {
+            // full grid: two splits only when the doubled grid's last wave is at least half full
+            const int64_t tail = (2 * ctas) % num_sms;
+            if (tail == 0 || 2 * tail >= num_sms) splits = 2;
+        }
+    }
+    splits = std::min(std::max(splits, min_splits), max_splits);
+    *num_splits_out = splits;
+    *chunks_per_block_out = chunks > 0 ? div_up(chunks, splits) : 0;
+    return GQA_OK;
 }

@@ -151,6 +151,26 @@ int plan_splits(int64_t batch_size, int64_t num_keys, int64_t heads_per_group, i
  * else 64.  Returns 32 or 64, or GQA_ERR_INVALID_ARGUMENT when ctas < 1 or sm_count < 1. */
 int block_k_for(int64_t ctas, int64_t sm_count);
 
+/* Split plan of the sparse top-k planner on the FlashInfer API page
+ * "cake_sparse_mla_sm120_dsv4_nvfp4_plan_splits" (its measured split rules and GB10 paragraph),
+ * for one decode call of sparse MLA:
+ *   num_tokens   query tokens in the call (>= 1)
+ *   num_heads    query heads per token (>= 1)
+ *   topk         candidate slots per token in the main cache (>= 0)
+ *   extra_topk   candidate slots per token in a second cache (>= 0; 0 without one)
+ *   num_sms      CUs the grid is sized for; <= 0 queries the current HIP device (cached)
+ *   max_splits   upper bound on the split count (>= 1)
+ *   head_tiles   the grid is counted in CTAs of 16 * head_tiles heads (>= 1; this library's
+ *                MLA kernel runs 64 query rows per CTA, head_tiles = 4)
+ * Candidates are chunked by 64, each cache on its own.  Writes the split count to *num_splits_out
+ * and ceil(chunks / splits) to *chunks_per_block_out (at most 16: the page's CTA index table).
+ * Pure host integer arithmetic when num_sms > 0.  Errors: INVALID_ARGUMENT (a NULL output, a
+ * size below its bound, or max_splits below the ceil(chunks / 16) splits the index table forces),
+ * DEVICE (num_sms <= 0 and no device). */
+int plan_sparse_splits(int64_t num_tokens, int64_t num_heads, int64_t topk, int64_t extra_topk,
+                       int64_t num_sms, int64_t max_splits, int64_t head_tiles,
+                       int64_t *num_splits_out, int64_t *chunks_per_block_out);
+
 /* CU count of the current HIP device, cached per device after the first query. */
 int device_sm_count(int64_t *sm_out);
 

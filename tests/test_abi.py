@@ -61,6 +61,37 @@ def test_block_k_matches_oracle():
         assert g.block_k_for(ctas, sm) == oracle.block_k(ctas, sm)
 
 
+def test_sparse_planner_matches_oracle_sweep():
+    # bit-exact against the oracle's reading of the FlashInfer sparse planner page
+    tokens = [1, 2, 3, 4, 7, 8, 16, 24, 32, 34, 48, 60, 64, 100, 128, 170, 200, 250, 256, 512, 1024]
+    heads = [1, 16, 17, 32, 64, 128]
+    topks = [0, 64, 65, 128, 129, 256, 512, 1000, 1024, 1025, 2048, 4096]
+    extras = [0, 64, 100, 512]
+    for nt, nh, topk, extra in itertools.product(tokens, heads, topks, extras):
+        for sms, mx, ht in ((48, 16, 1), (170, 16, 1), (188, 16, 2), (256, 16, 4), (256, 4, 4), (304, 64, 1)):
+            want = oracle.plan_sparse_splits(nt, nh, topk, extra, num_sms=sms, max_splits=mx, head_tiles=ht)
+            if want is None:
+                with pytest.raises(g.GqaError):
+                    g.plan_sparse_splits(nt, nh, topk, extra, num_sms=sms, max_splits=mx, head_tiles=ht)
+            else:
+                assert g.plan_sparse_splits(nt, nh, topk, extra, num_sms=sms, max_splits=mx,
+                                            head_tiles=ht) == want, (nt, nh, topk, extra, sms, mx, ht)
+
+
+def test_sparse_planner_rejections():
+    for args in [(0, 64, 2048), (1, 0, 2048), (1, 64, -1)]:
+        with pytest.raises(g.GqaError):
+            g.plan_sparse_splits(*args, num_sms=256)
+    with pytest.raises(g.GqaError):
+        g.plan_sparse_splits(1, 64, 2048, -1, num_sms=256)
+    with pytest.raises(g.GqaError):
+        g.plan_sparse_splits(1, 64, 2048, num_sms=256, max_splits=0)
+    with pytest.raises(g.GqaError):
+        g.plan_sparse_splits(1, 64, 2048, num_sms=256, head_tiles=0)
+    with pytest.raises(g.GqaError):   # 32 chunks need 2 splits
+        g.plan_sparse_splits(1, 64, 2048, num_sms=256, max_splits=1)
+
+
 def test_planner_rejections():
     for args in [(0, 1, 1, 256), (1, -1, 1, 256), (1, 1, 0, 256)]:
         with pytest.raises(g.GqaError) as e:
