@@ -35,6 +35,8 @@ def parse():
     ap.add_argument("--headline-only", action="store_true",
                     help="time only the headline workload (no per-workload table)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--sparse-sweep", action="store_true",
+                    help="only time the sparse top-k split sweep and print it")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle sample")
     ap.add_argument("--table-steps", type=int, default=20)
@@ -193,6 +195,14 @@ def settle(fn, ms):
         torch.cuda.synchronize()
 
 
+def check_slots(inp):
+    """Host check of the device-data contract before a launch: every MLA slot id is a pool row
+    (or negative, a skipped key).  The kernels trust the ids."""
+    hi = int(inp.kv_indices.max()) if inp.kv_indices.numel() else -1
+    if hi >= inp.pool.shape[0]:
+        raise RuntimeError("%s: slot id %d outside a pool of %d rows" % (inp.name, hi, inp.pool.shape[0]))
+
+
 def time_events(fn, n, stream):
     """Average ms per call of fn over n calls, HIP events recorded on `stream`."""
     import torch
@@ -264,12 +274,15 @@ def dcp_line(stream, steps, world=8):
     import torch
     import gqa_plan_splits_amd as g
     import workloads as w
-    inp = w.mla_long(16, 1, "cuda")
-    B, S = inp.B, int(inp.max_num_keys)
-    idx = inp.kv_indices.view(B, S)[:, 0::world].contiguous().view(-1)
-    local = S // world
-    indptr = torch.arange(B + 1, dtype=torch.int32, device="cuda") * local
-    lens = torch.full((B,), local, dtype=torch.int32, device="cuda")
+    with torch.cuda.stream(stream):
+        inp = w.mla_long(16, 1, "cuda")
+        B, S = inp.B, int(inp.max_num_keys)
+        idx = inp.kv_indices.view(B, S)[:, 0::world].contiguous().view(-1)
+        local = S // world
+        indptr = torch.arange(B + 1, dtype=torch.int32, device="cuda") * local
+        lens = torch.full((B,), local, dtype=torch.int32, device="cuda")
+    torch.cuda.synchronize()   # the inputs exist before any kernel on `stream` reads them
+    check_slots(inp)
     p = g.mla_problem(inp.q_lat, inp.q_pe, inp.pool, idx, indptr, lens, batch=B, q_len=1,
                       num_heads=inp.H, max_num_keys=local, scale=inp.scale, kv_scale=inp.kv_scale,
                       d_v=512, glen=inp.seq_lens, cp_rank=0, cp_world=world)
@@ -313,8 +326,11 @@ def wave_sweep(stream, steps):
     sm = g.device_sm_count()
     res = {}
     for B, S in ((4, 32768), (4, 65536), (4, 131072), (8, 16384), (16, 16384)):
-        inp = w.mla_inputs(B=B, q_len=1, H=16, seq_lens=[S] * B, pool_rows=B * S, seed=5000,
-                           device="cuda", name="h16")
+        with torch.cuda.stream(stream):
+            inp = w.mla_inputs(B=B, q_len=1, H=16, seq_lens=[S] * B, pool_rows=B * S, seed=5000,
+                               device="cuda", name="h16")
+        torch.cuda.synchronize()   # the inputs exist before any kernel on `stream` reads them
+        check_slots(inp)
         p = g.mla_problem(inp.q_lat, inp.q_pe, inp.pool, inp.kv_indices, inp.kv_indptr,
                           inp.seq_lens, batch=B, q_len=1, num_heads=16, max_num_keys=S,
                           scale=inp.scale, kv_scale=inp.kv_scale, d_v=512)
@@ -337,6 +353,49 @@ def wave_sweep(stream, steps):
             row[name] = {"np": n, "us_per_call": round(ms * 1e3, 2)}
         row["two_wave_speedup"] = round(row["one_wave"]["us_per_call"] / row["two_wave"]["us_per_call"], 3)
         res["mla_h16_b%d_s%d" % (B, S)] = row
+        del inp, p
+        torch.cuda.empty_cache()
+    return res
+
+
+def sparse_sweep(stream, steps):
+    """Sparse top-k MLA (64 heads, 2048 candidates per query) at every split count from 1 to 32
+    per query count, beside the choices of the two planners: the wave-aligned one decode uses
+    and the sparse page's rules (plan_sparse_splits, CTAs of 64 heads = head_tiles 4)."""
+    import torch
+    import gqa_plan_splits_amd as g
+    import workloads as w
+    sm = g.device_sm_count()
+    res = {}
+    for nq in (1, 2, 4, 8, 16, 24, 32, 64, 128, 256):
+        with torch.cuda.stream(stream):
+            inp = w.sparse_topk(nq, "cuda")
+        torch.cuda.synchronize()   # the inputs exist before any kernel on `stream` reads them
+        check_slots(inp)
+        p = g.mla_problem(inp.q_lat, inp.q_pe, inp.pool, inp.kv_indices, inp.kv_indptr,
+                          inp.seq_lens, batch=inp.B, q_len=1, num_heads=inp.H,
+                          max_num_keys=inp.max_num_keys, scale=inp.scale, kv_scale=inp.kv_scale,
+                          d_v=inp.d_v)
+        out = torch.empty((p.rows, inp.d_v), dtype=torch.bfloat16, device="cuda")
+        lse = torch.empty((p.rows,), dtype=torch.float32, device="cuda")
+        times = {}
+        for n in (1, 2, 4, 8, 16, 32):
+            bk = g.block_k_for(nq * n, sm)
+            ws = torch.empty((g.decode_workspace_bytes(p, n) // 4 + 64,), dtype=torch.float32, device="cuda")
+            fn = (lambda n=n, bk=bk, ws=ws:
+                  g.decode(p, out, lse, np=n, block_k=bk, workspace=ws, stream=stream))
+            for _ in range(3):
+                fn()
+            ms = time_graph(fn, steps, stream) or time_events(fn, steps, stream)
+            times[n] = round(ms * 1e3, 2)
+        best = min(times, key=times.get)
+        wave_np = g.decode_plan(p)[0]
+        page_np, cpb = g.plan_sparse_splits(nq, inp.H, int(inp.max_num_keys), num_sms=sm, head_tiles=4)
+        res["nq%d" % nq] = {"us_by_np": times, "best_np": best, "wave_planner_np": wave_np,
+                            "sparse_planner_np": page_np, "sparse_chunks_per_block": cpb,
+                            "wave_planner_vs_best": round(times[wave_np] / times[best], 3),
+                            "sparse_planner_vs_best": round(times[page_np] / times[best], 3)}
+        print("# sparse nq%d %s" % (nq, json.dumps(res["nq%d" % nq])), file=sys.stderr, flush=True)
         del inp, p
         torch.cuda.empty_cache()
     return res
@@ -403,6 +462,9 @@ def main():
         return
     stream = torch.cuda.Stream()
     sm = g.device_sm_count()
+    if args.sparse_sweep:
+        print(json.dumps({"sparse_planner": sparse_sweep(stream, args.table_steps)}), flush=True)
+        return
     flush = torch.empty((512 << 20) // 4, dtype=torch.float32, device="cuda")
 
     table = {}
@@ -413,6 +475,8 @@ def main():
         with torch.cuda.stream(stream):
             inp = make("cuda")
         torch.cuda.synchronize()
+        if hasattr(inp, "pool"):
+            check_slots(inp)
         case = Case(inp, np_fixed, stream, args.block_k)
         is_head = name == args.workload
         steps = args.steps if is_head else args.table_steps
@@ -497,6 +561,8 @@ def main():
         print("# dcp %s" % json.dumps(result["dcp"]), file=sys.stderr, flush=True)
         result["planner_waves"] = wave_sweep(stream, args.table_steps)
         print("# planner_waves %s" % json.dumps(result["planner_waves"]), file=sys.stderr, flush=True)
+        result["sparse_planner"] = sparse_sweep(stream, args.table_steps)
+        print("# sparse_planner %s" % json.dumps(result["sparse_planner"]), file=sys.stderr, flush=True)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)
     print(json.dumps(result), flush=True)

@@ -293,6 +293,7 @@ def test_mla_graph_replay_matches_eager():
     out = torch.empty((rows, 512), dtype=torch.bfloat16, device=DEV)
     lse = torch.empty((rows,), dtype=torch.float32, device=DEV)
     s = torch.cuda.Stream()
+    torch.cuda.synchronize()   # the inputs, built on the default stream, exist before `s` reads them
     with torch.cuda.stream(s):
         g.decode(p, out, lse, np=8, block_k=32, workspace=ws, stream=s)
     torch.cuda.synchronize()
@@ -329,6 +330,7 @@ def test_graph_replay_with_new_lengths():
     out = torch.empty((inp.rows, 512), dtype=torch.bfloat16, device=DEV)
     lse = torch.empty((inp.rows,), dtype=torch.float32, device=DEV)
     s = torch.cuda.Stream()
+    torch.cuda.synchronize()   # the inputs, built on the default stream, exist before `s` reads them
     with torch.cuda.stream(s):
         g.decode(p, out, lse, np=np_, block_k=bk, workspace=ws, stream=s)
     torch.cuda.synchronize()
