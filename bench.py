@@ -391,10 +391,13 @@ def sparse_sweep(stream, steps):
         best = min(times, key=times.get)
         wave_np = g.decode_plan(p)[0]
         page_np, cpb = g.plan_sparse_splits(nq, inp.H, int(inp.max_num_keys), num_sms=sm, head_tiles=4)
+        meas_np = g.plan_sparse_splits_measured(nq, inp.H, int(inp.max_num_keys), sm_count=sm, max_splits=32)
         res["nq%d" % nq] = {"us_by_np": times, "best_np": best, "wave_planner_np": wave_np,
                             "sparse_planner_np": page_np, "sparse_chunks_per_block": cpb,
+                            "measured_rule_np": meas_np,
                             "wave_planner_vs_best": round(times[wave_np] / times[best], 3),
-                            "sparse_planner_vs_best": round(times[page_np] / times[best], 3)}
+                            "sparse_planner_vs_best": round(times[page_np] / times[best], 3),
+                            "measured_rule_vs_best": round(times[meas_np] / times[best], 3)}
         print("# sparse nq%d %s" % (nq, json.dumps(res["nq%d" % nq])), file=sys.stderr, flush=True)
         del inp, p
         torch.cuda.empty_cache()

@@ -28,6 +28,7 @@ from ._lib import (  # noqa: F401
     merge_ranks,
     mla_problem,
     plan_sparse_splits,
+    plan_sparse_splits_measured,
     plan_splits,
     splitk_reduce,
     splitk_reduce_f32,

@@ -13,7 +13,7 @@ FP8_E4M3FN = 0
 FP8_E4M3FNUZ = 1
 
 # Every function include/gqa_splits.h declares.
-_SYMBOLS = ("plan_splits", "plan_sparse_splits", "block_k_for", "device_sm_count", "decode_plan", "decode_split",
+_SYMBOLS = ("plan_splits", "plan_sparse_splits", "plan_sparse_splits_measured", "block_k_for", "device_sm_count", "decode_plan", "decode_split",
             "splitk_reduce", "splitk_reduce_f32", "merge_ranks", "decode_workspace_bytes", "decode", "fp8_e4m3_to_bf16",
             "status_string", "last_error_detail")
 
@@ -95,6 +95,7 @@ def _load():
     lib.block_k_for.argtypes = [i64, i64]
     lib.plan_sparse_splits.argtypes = [i64, i64, i64, i64, i64, i64, i64, ctypes.POINTER(i64),
                                        ctypes.POINTER(i64)]
+    lib.plan_sparse_splits_measured.argtypes = [i64, i64, i64, i64, i64, i64, i64, ctypes.POINTER(i64)]
     lib.device_sm_count.argtypes = [ctypes.POINTER(i64)]
     lib.decode_plan.argtypes = [pp, i64, i32, i64, ctypes.POINTER(i64), ctypes.POINTER(i32)]
     lib.decode_split.argtypes = [pp, i64, i32, vp, vp, vp]
@@ -177,6 +178,16 @@ def plan_sparse_splits(num_tokens: int, num_heads: int, topk: int, extra_topk: i
                                       head_tiles, ctypes.byref(ns), ctypes.byref(cpb)),
            "plan_sparse_splits")
     return int(ns.value), int(cpb.value)
+
+
+def plan_sparse_splits_measured(num_tokens: int, num_heads: int, topk: int, extra_topk: int = 0, *,
+                                sm_count: int = 0, max_splits: int = 256, rows_per_cta: int = 64) -> int:
+    """Split count of the sparse planner with thresholds measured on MI355X (not the page's)."""
+    out = ctypes.c_int64(0)
+    _check(_load().plan_sparse_splits_measured(num_tokens, num_heads, topk, extra_topk, sm_count,
+                                               max_splits, rows_per_cta, ctypes.byref(out)),
+           "plan_sparse_splits_measured")
+    return int(out.value)
 
 
 def block_k_for(ctas: int, sm_count: int) -> int:

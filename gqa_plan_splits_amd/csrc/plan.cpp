@@ -201,3 +201,27 @@ extern "C" int plan_sparse_splits(int64_t num_tokens, int64_t num_heads, int64_t
     *chunks_per_block_out = chunks > 0 ? div_up(chunks, splits) : 0;
     return GQA_OK;
 }
+
+// The same decision with MI355X's own thresholds, from a sweep of this library's sparse MLA
+// kernel (64 heads, 2048 candidates, 1..256 queries, every power-of-two split from 1 to 32): the
+// fastest split keeps the grid within one wave of CUs (the page's 40 % entry and 80 % bound
+// split too little below one wave), leaves at least two chunks per CTA (one for a lone CTA), and
+// needs no forced split (this kernel walks any number of chunks; the 1024-candidate index table
+// is the other kernel's limit, and forcing two splits at 256 queries costs 1.7x).
+extern "C" int plan_sparse_splits_measured(int64_t num_tokens, int64_t num_heads, int64_t topk,
+                                           int64_t extra_topk, int64_t sm_count, int64_t max_splits,
+                                           int64_t rows_per_cta, int64_t *num_splits_out) {
+    if (!num_splits_out || num_tokens < 1 || num_heads < 1 || max_splits < 1 || rows_per_cta < 1 ||
+        topk < 0 || extra_topk < 0)
+        return GQA_ERR_INVALID_ARGUMENT;
+    if (sm_count <= 0) {
+        const int rc = device_sm_count(&sm_count);
+        if (rc != GQA_OK) return rc;
+    }
+    const int64_t chunks = div_up(topk, kSparseChunk) + div_up(extra_topk, kSparseChunk);
+    const int64_t ctas = num_tokens * div_up(num_heads, rows_per_cta);
+    int64_t cap = std::min(max_splits, sm_count / ctas);
+    cap = std::min(cap, ctas == 1 ? chunks : chunks / 2);
+    *num_splits_out = chunks > 2 && cap >= 1 ? floor_pow2(cap) : 1;
+    return GQA_OK;
+}

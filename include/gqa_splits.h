@@ -171,6 +171,18 @@ int plan_sparse_splits(int64_t num_tokens, int64_t num_heads, int64_t topk, int6
                        int64_t num_sms, int64_t max_splits, int64_t head_tiles,
                        int64_t *num_splits_out, int64_t *chunks_per_block_out);
 
+/* The sparse planner's decision with thresholds measured on MI355X for this library's MLA
+ * kernel rather than the page's (which were measured for a Blackwell kernel): the largest power
+ * of two (<= max_splits) that keeps num_tokens * ceil(num_heads / rows_per_cta) * splits within
+ * sm_count CTAs and leaves every CTA at least two 64-candidate chunks (one when a single CTA runs
+ * unsplit); 1 for two chunks or fewer.  No split is forced by the chunk count.  rows_per_cta is
+ * the query rows one CTA runs (64 for this library's MLA kernel); sm_count <= 0 queries the
+ * current device.  Not a rule of the pages: a measured tuning, checked by the benchmark's sparse
+ * sweep.  Errors: INVALID_ARGUMENT (NULL output, a size below its bound), DEVICE. */
+int plan_sparse_splits_measured(int64_t num_tokens, int64_t num_heads, int64_t topk,
+                                int64_t extra_topk, int64_t sm_count, int64_t max_splits,
+                                int64_t rows_per_cta, int64_t *num_splits_out);
+
 /* CU count of the current HIP device, cached per device after the first query. */
 int device_sm_count(int64_t *sm_out);
 

@@ -92,6 +92,28 @@ def test_sparse_planner_rejections():
         g.plan_sparse_splits(1, 64, 2048, num_sms=256, max_splits=1)
 
 
+def test_sparse_measured_rule_properties():
+    # the MI355X-measured variant: a power of two within max_splits whose grid stays within one
+    # wave of CUs and leaves two chunks per CTA (one for a lone CTA); two chunks never split
+    for nt, nh, topk, extra, sm, mx in itertools.product([1, 2, 3, 8, 24, 64, 256, 300], [16, 64, 128],
+                                                         [0, 64, 128, 192, 1024, 2048, 4096], [0, 256],
+                                                         [80, 256], [1, 16, 32, 256]):
+        ns = g.plan_sparse_splits_measured(nt, nh, topk, extra, sm_count=sm, max_splits=mx)
+        chunks = -(-topk // 64) + -(-extra // 64)
+        ctas = nt * -(-nh // 64)
+        assert ns >= 1 and ns & (ns - 1) == 0 and ns <= mx
+        if chunks <= 2:
+            assert ns == 1
+        elif ns > 1:
+            assert ctas * ns <= sm
+            assert chunks >= (ns if ctas == 1 else 2 * ns)
+            # and the next power of two breaks one of the bounds
+            n2 = 2 * ns
+            assert n2 > mx or ctas * n2 > sm or chunks < (n2 if ctas == 1 else 2 * n2)
+    with pytest.raises(g.GqaError):
+        g.plan_sparse_splits_measured(0, 64, 2048, sm_count=256)
+
+
 def test_planner_rejections():
     for args in [(0, 1, 1, 256), (1, -1, 1, 256), (1, 1, 0, 256)]:
         with pytest.raises(g.GqaError) as e:
