@@ -17,6 +17,10 @@
  *  - Skipped keys: AITER issue "[Perf] pa_decode_sparse ...", section "Measurements" (the
  *    has_invalid flag of the top-k index lists): a negative slot id in an MLA index list is a
  *    key that is not attended.
+ *  - Second cache: FlashInfer API page "cake_sparse_mla_sm120_dsv4_nvfp4_plan_splits", Parameters
+ *    (extra_topk: candidate slots per token in a second cache).  Read as a second pool of rows of
+ *    the same format and scale whose candidates a query attends together with its main-cache
+ *    candidates, in one softmax.
  *  - Merge: base-2 log-sum-exp combination of partial results, the operation behind
  *    mla_splitk_reduce ("AMD reducer constraint") and mla_dcp_lse_merge_ranks.
  *
@@ -228,6 +232,8 @@ typedef struct {
     const uint8_t *pool;
     const int32_t *kv_indices;
     double kv_scale;
+    const uint8_t *pool2;            /* a second cache, or NULL */
+    const int32_t *kv2_indices, *kv2_indptr;
     const double *fp8_table; /* 256 decoded values */
     /* GQA */
     int64_t Hkv, D, page_size;
@@ -238,10 +244,29 @@ typedef struct {
     int error;
 } attn_job;
 
-/* Keys row (b, t) sees: the end-aligned draft window. */
+/* Keys row (b, t) sees: the end-aligned draft window, then (q_len 1 only) every candidate of
+ * the second cache. */
 static int64_t keys_seen(const attn_job *j, int64_t b, int64_t t) {
     int64_t L = (int64_t)j->seq_lens[b] - j->q_len + t + 1;
-    return L > 0 ? L : 0;
+    if (L < 0) L = 0;
+    if (j->pool2) L += j->kv2_indptr[b + 1] - j->kv2_indptr[b];
+    return L;
+}
+
+/* Row of key k of request b: main-cache keys first, then the second cache's; NULL for a
+ * skipped key (a negative slot id). */
+static const uint8_t *mla_row(const attn_job *j, int64_t b, int64_t k) {
+    const int64_t dqk = j->d_lat + j->d_rope;
+    int64_t slot;
+    const uint8_t *pool;
+    if (!j->pool2 || k < j->seq_lens[b]) {
+        slot = j->kv_indices[j->kv_indptr[b] + k];
+        pool = j->pool;
+    } else {
+        slot = j->kv2_indices[j->kv2_indptr[b] + (k - j->seq_lens[b])];
+        pool = j->pool2;
+    }
+    return slot < 0 ? NULL : pool + slot * dqk;
 }
 
 /* Scores s[0..L) of one MLA row against its keys. */
@@ -252,12 +277,11 @@ static void mla_scores(const attn_job *j, int64_t r, int64_t b, int64_t L, doubl
     for (int64_t d = 0; d < j->d_rope; ++d)
         qv[j->d_lat + d] = oracle_bf16_value(j->q_pe[r * j->d_rope + d]);
     for (int64_t k = 0; k < L; ++k) {
-        const int64_t slot = j->kv_indices[j->kv_indptr[b] + k];
-        if (slot < 0) {   /* a skipped key: no weight */
+        const uint8_t *row = mla_row(j, b, k);
+        if (!row) {   /* a skipped key: no weight */
             s[k] = -INFINITY;
             continue;
         }
-        const uint8_t *row = j->pool + slot * dqk;
         double dot = 0.0;
         for (int64_t d = 0; d < dqk; ++d) dot += qv[d] * (j->fp8_table[row[d]] * j->kv_scale);
         s[k] = j->scale * dot;
@@ -265,9 +289,7 @@ static void mla_scores(const attn_job *j, int64_t r, int64_t b, int64_t L, doubl
 }
 
 static double mla_value(const attn_job *j, int64_t b, int64_t k, int64_t d) {
-    const int64_t dqk = j->d_lat + j->d_rope;
-    const int64_t slot = j->kv_indices[j->kv_indptr[b] + k];
-    return j->fp8_table[j->pool[slot * dqk + d]] * j->kv_scale;
+    return j->fp8_table[mla_row(j, b, k)[d]] * j->kv_scale;
 }
 
 static const uint16_t *gqa_row(const attn_job *j, const uint16_t *cache, int64_t b, int64_t k,
@@ -399,13 +421,23 @@ static int check_rows(const int64_t *rows, int64_t n_rows, int64_t total_rows) {
     return 0;
 }
 
-int oracle_mla_decode(int64_t B, int64_t q_len, int64_t H, int64_t d_lat, int64_t d_rope,
+static int mla_decode(int64_t B, int64_t q_len, int64_t H, int64_t d_lat, int64_t d_rope,
                       int64_t d_v, const uint16_t *q_lat, const uint16_t *q_pe,
                       const uint8_t *pool, int64_t pool_rows, const int32_t *kv_indices,
-                      const int32_t *kv_indptr, const int32_t *seq_lens, double scale,
+                      const int32_t *kv_indptr, const int32_t *seq_lens,
+                      const uint8_t *pool2, int64_t pool2_rows, const int32_t *kv2_indices,
+                      const int32_t *kv2_indptr, double scale,
                       double kv_scale, int fnuz, const int64_t *rows, int64_t n_rows,
                       double *o_out, double *lse2_out, int n_threads) {
     if (B <= 0 || q_len <= 0 || H <= 0 || d_lat <= 0 || d_rope < 0 || d_v <= 0) return -1;
+    if (pool2) {
+        if (q_len != 1 || !kv2_indices || !kv2_indptr) return -1;
+        for (int64_t b = 0; b < B; ++b) {
+            if (kv2_indptr[b + 1] < kv2_indptr[b]) return -1;
+            for (int64_t k = kv2_indptr[b]; k < kv2_indptr[b + 1]; ++k)
+                if (kv2_indices[k] >= pool2_rows) return -1;   /* negative: a skipped key */
+        }
+    }
     if (d_v > d_lat + d_rope) return -1;
     if (!q_lat || (d_rope > 0 && !q_pe) || !pool || !kv_indices || !kv_indptr || !seq_lens ||
         !o_out || !lse2_out)
@@ -430,9 +462,36 @@ int oracle_mla_decode(int64_t B, int64_t q_len, int64_t H, int64_t d_lat, int64_
     proto.o_out = o_out; proto.lse2_out = lse2_out;
     proto.d_lat = d_lat; proto.d_rope = d_rope; proto.q_lat = q_lat; proto.q_pe = q_pe;
     proto.pool = pool; proto.kv_indices = kv_indices; proto.kv_scale = kv_scale;
+    proto.pool2 = pool2; proto.kv2_indices = kv2_indices; proto.kv2_indptr = kv2_indptr;
     proto.fp8_table = table;
     if (n_rows == 0) return 0;
     return run_jobs(&proto, n_threads);
+}
+
+int oracle_mla_decode(int64_t B, int64_t q_len, int64_t H, int64_t d_lat, int64_t d_rope,
+                      int64_t d_v, const uint16_t *q_lat, const uint16_t *q_pe,
+                      const uint8_t *pool, int64_t pool_rows, const int32_t *kv_indices,
+                      const int32_t *kv_indptr, const int32_t *seq_lens, double scale,
+                      double kv_scale, int fnuz, const int64_t *rows, int64_t n_rows,
+                      double *o_out, double *lse2_out, int n_threads) {
+    return mla_decode(B, q_len, H, d_lat, d_rope, d_v, q_lat, q_pe, pool, pool_rows, kv_indices,
+                      kv_indptr, seq_lens, NULL, 0, NULL, NULL, scale, kv_scale, fnuz, rows,
+                      n_rows, o_out, lse2_out, n_threads);
+}
+
+int oracle_mla_decode_two_caches(int64_t B, int64_t H, int64_t d_lat, int64_t d_rope,
+                                 int64_t d_v, const uint16_t *q_lat, const uint16_t *q_pe,
+                                 const uint8_t *pool, int64_t pool_rows,
+                                 const int32_t *kv_indices, const int32_t *kv_indptr,
+                                 const int32_t *seq_lens, const uint8_t *pool2,
+                                 int64_t pool2_rows, const int32_t *kv2_indices,
+                                 const int32_t *kv2_indptr, double scale, double kv_scale,
+                                 const int64_t *rows, int64_t n_rows, double *o_out,
+                                 double *lse2_out, int n_threads) {
+    if (!pool2) return -1;
+    return mla_decode(B, 1, H, d_lat, d_rope, d_v, q_lat, q_pe, pool, pool_rows, kv_indices,
+                      kv_indptr, seq_lens, pool2, pool2_rows, kv2_indices, kv2_indptr, scale,
+                      kv_scale, 0, rows, n_rows, o_out, lse2_out, n_threads);
 }
 
 int oracle_gqa_decode(int64_t B, int64_t q_len, int64_t Hq, int64_t Hkv, int64_t D,

@@ -384,3 +384,103 @@ def test_invalid_index_is_rejected():
     inp.kv_indices[0] = inp.pool.shape[0]
     with pytest.raises(ValueError):
         run_mla(inp)
+
+
+# ---- second cache (the sparse planner page's extra_topk: candidates in a second cache)
+
+def run_mla2(inp, rows=None):
+    return oracle.mla_decode(bits16(inp.q_lat), bits16(inp.q_pe), u8(inp.pool),
+                             inp.kv_indices.numpy(), inp.kv_indptr.numpy(), inp.seq_lens.numpy(),
+                             B=inp.B, q_len=1, H=inp.H, d_v=inp.d_v, scale=inp.scale,
+                             kv_scale=inp.kv_scale, rows=rows, pool2=u8(inp.pool2),
+                             kv2_indices=inp.kv2_indices.numpy(), kv2_indptr=inp.kv2_indptr.numpy())
+
+
+def two_cache_case(seed=21, d_qk=512, d_rope=64, d_v=448, lens=(9, 0, 30), extra=(5, 7, 0), skip=()):
+    inp = workloads.mla_inputs(B=len(lens), q_len=1, H=3, seq_lens=list(lens), pool_rows=48,
+                               d_qk=d_qk, d_rope=d_rope, d_v=d_v, seed=seed)
+    return workloads.with_second_cache(inp, pool2_rows=20, extra_lens=list(extra), seed=seed + 50,
+                                       skip=skip)
+
+
+@pytest.mark.parametrize("shape", [dict(), dict(d_qk=576, d_rope=64, d_v=512, lens=(4, 17), extra=(12, 1))])
+def test_two_caches_match_torch_textbook(shape):
+    # textbook softmax attention over the main-cache keys followed by the second cache's, in
+    # torch float64, against the oracle's two-cache entry
+    inp = two_cache_case(**shape)
+    q = torch.cat([inp.q_lat, inp.q_pe], dim=-1).to(torch.float64)
+    pool = inp.pool.view(torch.float8_e4m3fn).to(torch.float64) * inp.kv_scale
+    pool2 = inp.pool2.view(torch.float8_e4m3fn).to(torch.float64) * inp.kv_scale
+    outs, lses = [], []
+    for b in range(inp.B):
+        i1 = inp.kv_indices[int(inp.kv_indptr[b]):int(inp.kv_indptr[b]) + int(inp.seq_lens[b])].long()
+        i2 = inp.kv2_indices[int(inp.kv2_indptr[b]):int(inp.kv2_indptr[b + 1])].long()
+        K = torch.cat([pool[i1], pool2[i2]])
+        if K.shape[0] == 0:
+            outs.append(torch.zeros(inp.H, inp.d_v, dtype=torch.float64))
+            lses.append(torch.full((inp.H,), -math.inf, dtype=torch.float64))
+            continue
+        s = inp.scale * (q[b] @ K.T)
+        outs.append(torch.softmax(s, dim=-1) @ K[:, :inp.d_v])
+        lses.append(torch.logsumexp(s, dim=-1) / LN2)
+    o, l = run_mla2(inp)
+    np.testing.assert_allclose(o, torch.cat(outs).numpy(), rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(l, torch.cat(lses).numpy(), rtol=1e-12, atol=1e-12)
+
+
+def test_two_caches_equal_one_merged_pool():
+    # the second cache appended to the pool, its slot ids shifted by the pool's rows and each
+    # request's list extended by them, is the same attention, bit for bit
+    inp = two_cache_case(lens=(9, 3, 30), extra=(5, 7, 2))
+    n1 = inp.pool.shape[0]
+    merged_pool = torch.cat([inp.pool, inp.pool2])
+    idx, indptr, lens = [], [0], []
+    for b in range(inp.B):
+        a = inp.kv_indices[int(inp.kv_indptr[b]):int(inp.kv_indptr[b]) + int(inp.seq_lens[b])]
+        e = inp.kv2_indices[int(inp.kv2_indptr[b]):int(inp.kv2_indptr[b + 1])] + n1
+        idx.append(torch.cat([a, e]))
+        lens.append(len(a) + len(e))
+        indptr.append(indptr[-1] + lens[-1])
+    o2, l2 = run_mla2(inp)
+    o1, l1 = oracle.mla_decode(bits16(inp.q_lat), bits16(inp.q_pe), u8(merged_pool),
+                               torch.cat(idx).numpy(), np.array(indptr, np.int32),
+                               np.array(lens, np.int32), B=inp.B, q_len=1, H=inp.H, d_v=inp.d_v,
+                               scale=inp.scale, kv_scale=inp.kv_scale)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+def test_second_cache_only_equals_single_cache_on_it():
+    inp = two_cache_case(lens=(0, 0, 0), extra=(5, 7, 1))
+    o2, l2 = run_mla2(inp)
+    lens = (inp.kv2_indptr[1:] - inp.kv2_indptr[:-1]).numpy()
+    o1, l1 = oracle.mla_decode(bits16(inp.q_lat), bits16(inp.q_pe), u8(inp.pool2),
+                               inp.kv2_indices.numpy(), inp.kv2_indptr.numpy(), lens,
+                               B=inp.B, q_len=1, H=inp.H, d_v=inp.d_v, scale=inp.scale,
+                               kv_scale=inp.kv_scale)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+def test_skipped_second_cache_keys_equal_their_removal():
+    inp = two_cache_case(lens=(9, 3, 30), extra=(5, 7, 2), skip=(1, 4, 6))
+    o2, l2 = run_mla2(inp)
+    keep = inp.kv2_indices >= 0
+    counts = [int(keep[int(inp.kv2_indptr[b]):int(inp.kv2_indptr[b + 1])].sum()) for b in range(inp.B)]
+    ptr = [0]
+    for c in counts:
+        ptr.append(ptr[-1] + c)
+    import dataclasses
+    inp_r = dataclasses.replace(inp, kv2_indices=inp.kv2_indices[keep],
+                                kv2_indptr=torch.tensor(ptr, dtype=torch.int32))
+    o1, l1 = run_mla2(inp_r)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+def test_second_cache_rejections():
+    inp = two_cache_case()
+    bad = inp.kv2_indices.clone()
+    bad[0] = 20   # the second pool has 20 rows
+    with pytest.raises(ValueError):
+        oracle.mla_decode(bits16(inp.q_lat), bits16(inp.q_pe), u8(inp.pool), inp.kv_indices.numpy(),
+                          inp.kv_indptr.numpy(), inp.seq_lens.numpy(), B=inp.B, q_len=1, H=inp.H,
+                          d_v=inp.d_v, scale=inp.scale, kv_scale=inp.kv_scale, pool2=u8(inp.pool2),
+                          kv2_indices=bad.numpy(), kv2_indptr=inp.kv2_indptr.numpy())

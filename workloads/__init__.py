@@ -77,6 +77,11 @@ class MlaInputs:
     scale: float
     kv_scale: float = KV_SCALE
     name: str = ""
+    # a second cache (sparse top-k with extra candidates, q_len 1): rows of the same format;
+    # request b also attends pool2 rows kv2_indices[kv2_indptr[b]:kv2_indptr[b+1]]
+    pool2: Optional[torch.Tensor] = None
+    kv2_indices: Optional[torch.Tensor] = None
+    kv2_indptr: Optional[torch.Tensor] = None
 
     @property
     def rows(self) -> int:
@@ -85,7 +90,10 @@ class MlaInputs:
     @property
     def kv_bytes(self) -> int:
         """KV payload bytes one decode reads: every key of every request once (576 or 512 B)."""
-        return int(self.seq_lens.sum().item()) * self.d_qk
+        n = int(self.seq_lens.sum().item())
+        if self.kv2_indices is not None:
+            n += int(self.kv2_indices.numel())
+        return n * self.d_qk
 
 
 @dataclasses.dataclass
@@ -156,11 +164,13 @@ def mla_inputs(*, B: int, q_len: int, H: int, seq_lens: Sequence[int], pool_rows
 
 def sparse_mla_inputs(*, num_queries: int, topk: int = 2048, cache_rows: int = 262144, H: int = 64,
                       seed: int = 4000, device="cpu", name: str = "", invalid_frac: float = 0.0,
-                      all_invalid: Sequence[int] = ()) -> MlaInputs:
+                      all_invalid: Sequence[int] = (), extra_topk: int = 0,
+                      extra_rows: int = 65536) -> MlaInputs:
     """Sparse top-k MLA decode: each query is its own request whose keys are `topk` cache rows
     drawn without replacement; rows are 512 fp8 bytes (448 NoPE + 64 RoPE), value = NoPE part.
     invalid_frac: that fraction of the index entries (seeded positions) is -1, a skipped key;
-    all_invalid: queries whose whole list is -1."""
+    all_invalid: queries whose whole list is -1.  extra_topk > 0: a second cache of extra_rows
+    rows of the same format, from which each query draws extra_topk more candidates."""
     nq = num_queries
     q = _randn((nq, H, 512), seed + 1, device, torch.bfloat16)
     pool = _fp8_pool(cache_rows, 512, seed + 3, device)
@@ -176,9 +186,37 @@ def sparse_mla_inputs(*, num_queries: int, topk: int = 2048, cache_rows: int = 2
         kv_indices[qi * topk:(qi + 1) * topk] = -1
     kv_indptr = (torch.arange(nq + 1, device=device, dtype=torch.int32) * topk)
     sl = torch.full((nq,), topk, dtype=torch.int32, device=device)
+    pool2 = kv2_indices = kv2_indptr = None
+    if extra_topk > 0:
+        pool2 = _fp8_pool(extra_rows, 512, seed + 7, device)
+        g2 = _gen(device, seed + 8)
+        kv2_indices = torch.cat([torch.randperm(extra_rows, generator=g2, device=device)[:extra_topk]
+                                 for _ in range(nq)]).to(torch.int32)
+        kv2_indptr = torch.arange(nq + 1, device=device, dtype=torch.int32) * extra_topk
     return MlaInputs(B=nq, q_len=1, H=H, d_qk=512, d_rope=64, d_v=448, q_lat=q[..., :448],
                      q_pe=q[..., 448:], pool=pool, kv_indices=kv_indices, kv_indptr=kv_indptr,
-                     seq_lens=sl, max_num_keys=topk, scale=512.0 ** -0.5, name=name)
+                     seq_lens=sl, max_num_keys=topk + extra_topk, scale=512.0 ** -0.5, name=name,
+                     pool2=pool2, kv2_indices=kv2_indices, kv2_indptr=kv2_indptr)
+
+
+def with_second_cache(inp: MlaInputs, *, pool2_rows: int, extra_lens: Sequence[int], seed: int,
+                      skip: Sequence[int] = ()) -> MlaInputs:
+    """The same q_len-1 requests with a second cache of pool2_rows rows (the pool's format) from
+    which request b draws extra_lens[b] candidates (with replacement allowed across requests);
+    `skip` lists flat positions of the second-cache list set to -1 (skipped keys)."""
+    assert inp.q_len == 1 and len(extra_lens) == inp.B
+    device = inp.pool.device
+    pool2 = _fp8_pool(pool2_rows, inp.d_qk, seed, device)
+    g = _gen("cpu", seed + 1)
+    idx = torch.cat([torch.randperm(pool2_rows, generator=g)[:n] for n in extra_lens]).to(torch.int32)
+    for k in skip:
+        idx[k] = -1
+    indptr = [0]
+    for n in extra_lens:
+        indptr.append(indptr[-1] + int(n))
+    return dataclasses.replace(inp, pool2=pool2, kv2_indices=idx.to(device),
+                               kv2_indptr=torch.tensor(indptr, dtype=torch.int32, device=device),
+                               max_num_keys=int(inp.max_num_keys) + max(extra_lens))
 
 
 def gqa_inputs(*, B: int, Hq: int, Hkv: int, D: int = 128, page_size: int = 16,
