@@ -58,6 +58,10 @@ class DecodeProblem(ctypes.Structure):
         ("glen", ctypes.c_void_p),
         ("cp_rank", ctypes.c_int32),
         ("cp_world", ctypes.c_int32),
+        ("kv2", ctypes.c_void_p),
+        ("kv2_stride_row", ctypes.c_int64),
+        ("kv2_indices", ctypes.c_void_p),
+        ("kv2_indptr", ctypes.c_void_p),
     ]
 
     # tensors whose memory the struct points at (kept alive with it)
@@ -224,11 +228,13 @@ def _strides(t):
 
 def mla_problem(q_lat, q_pe, pool, kv_indices, kv_indptr, seq_lens, *, batch, q_len, num_heads,
                 max_num_keys, scale, kv_scale, d_v=None, fp8_format=FP8_E4M3FN, glen=None,
-                cp_rank=0, cp_world=1) -> DecodeProblem:
+                cp_rank=0, cp_world=1, pool2=None, kv2_indices=None, kv2_indptr=None) -> DecodeProblem:
     """Absorbed-MLA (or sparse top-k) problem: q_lat [B*q_len, H, d_lat], q_pe [.., H, d_rope]
     bf16 views; pool [N, d_qk] fp8 bytes (uint8 or float8); int32 index tensors.  With glen
     (int32 [B] global lengths), the call is rank cp_rank of cp_world decode-context-parallel
-    ranks: seq_lens and the index lists hold that rank's positions."""
+    ranks: seq_lens and the index lists hold that rank's positions.  With pool2 (sparse rows,
+    q_len 1; the pool's row stride), request b also attends the second-cache rows
+    kv2_indices[kv2_indptr[b]:kv2_indptr[b+1]]; max_num_keys covers both lists."""
     p = DecodeProblem()
     p.kind = KIND_MLA_FUSED
     p.fp8_format = fp8_format
@@ -252,7 +258,12 @@ def mla_problem(q_lat, q_pe, pool, kv_indices, kv_indptr, seq_lens, *, batch, q_
     if glen is not None:
         p.glen = glen.data_ptr()
         p.cp_rank, p.cp_world = cp_rank, cp_world
-    p._keep = (q_lat, q_pe, pool, kv_indices, kv_indptr, seq_lens, glen)
+    if pool2 is not None:
+        p.kv2 = pool2.data_ptr()
+        p.kv2_stride_row = pool2.stride(0) * pool2.element_size()
+        p.kv2_indices = kv2_indices.data_ptr()
+        p.kv2_indptr = kv2_indptr.data_ptr()
+    p._keep = (q_lat, q_pe, pool, kv_indices, kv_indptr, seq_lens, glen, pool2, kv2_indices, kv2_indptr)
     return p
 
 

@@ -76,12 +76,21 @@ int check_problem(const gqa_decode_problem *p, Derived *d) {
         } else if (p->cp_rank != 0 || p->cp_world < 0) {
             return GQA_ERR_INVALID_ARGUMENT;
         }
+        // a second cache: q_len 1 without context parallelism, rows of the pool's format
+        if (p->kv2 || p->kv2_indices || p->kv2_indptr) {
+            if (!p->kv2 || !p->kv2_indices || !p->kv2_indptr) return GQA_ERR_INVALID_ARGUMENT;
+            if (p->q_len != 1 || p->cp_world > 1 || p->glen || !sparse) return GQA_ERR_UNSUPPORTED;
+            // the kernel addresses both caches with the pool's row stride
+            if (p->kv2_stride_row != 0 && p->kv2_stride_row != p->kv_stride_row) return GQA_ERR_UNSUPPORTED;
+            if (!aligned16(p->kv2)) return GQA_ERR_UNSUPPORTED;
+        }
         d->is_mla = true;
         d->cta_rows = (rows_per_req + kMlaRowsPerCta - 1) / kMlaRowsPerCta;
         d->hpg = rows_per_req;
     } else if (p->kind == GQA_KIND_GQA_PAGED) {
         if (!p->k_cache || !p->v_cache || p->num_kv_heads < 1) return GQA_ERR_INVALID_ARGUMENT;
         if (p->cp_world > 1 || p->glen) return GQA_ERR_UNSUPPORTED;
+        if (p->kv2 || p->kv2_indices || p->kv2_indptr) return GQA_ERR_UNSUPPORTED;
         if (p->cp_rank != 0 || p->cp_world < 0) return GQA_ERR_INVALID_ARGUMENT;
         if (p->num_heads % p->num_kv_heads) return GQA_ERR_INVALID_ARGUMENT;
         if (p->d_qk != kGqaHeadDim || p->d_v != kGqaHeadDim || p->d_rope != 0)
@@ -145,6 +154,10 @@ int launch_split(const gqa_decode_problem *p, const Derived &d, int64_t np, int 
         a.kv_indices = p->kv_indices;
         a.kv_indptr = p->kv_indptr;
         a.seq_lens = p->seq_lens;
+        a.kv2 = static_cast<const uint8_t *>(p->kv2);
+        a.kv2_stride = p->kv_stride_row;
+        a.kv2_indices = p->kv2_indices;
+        a.kv2_indptr = p->kv2_indptr;
         const bool cp = p->cp_world > 1 || p->glen;
         a.glen = cp ? p->glen : nullptr;
         a.cp_rank = cp ? p->cp_rank : 0;

@@ -17,6 +17,9 @@ struct MlaSplitArgs {
     const uint8_t *kv;            // fp8 rows
     int64_t kv_stride;            // bytes between rows
     const int32_t *kv_indices, *kv_indptr, *seq_lens;
+    const uint8_t *kv2;           // second cache (fp8 rows of the pool's format), or null
+    int64_t kv2_stride;
+    const int32_t *kv2_indices, *kv2_indptr;   // request b's second-cache rows, after its pool keys
     const int32_t *glen;          // global lengths under context parallelism (cp_world > 1)
     int32_t cp_rank, cp_world;    // key j is global position j * cp_world + cp_rank
     int32_t q_len, H, np, rows_per_req, row_blocks, total_ctas;
@@ -58,6 +61,7 @@ struct ReduceArgs {
 // Query rows one MLA split CTA covers (row_blocks = ceil(rows per request / this)).
 int mla_rows_per_cta();
 hipError_t launch_mla_split(const MlaSplitArgs &a, int d_qk, int d_v, bool direct, hipStream_t s);
+// (with a.kv2 set: the second-cache variant of the same kernel)
 hipError_t launch_gqa_split(const GqaSplitArgs &a, bool direct, hipStream_t s);
 hipError_t launch_splitk_reduce(const ReduceArgs &a, hipStream_t s);
 hipError_t launch_fp8_to_bf16(const uint8_t *in, int64_t n, uint16_t *out, hipStream_t s);

@@ -8,7 +8,9 @@
 // decode context parallelism (same README section) the call holds one rank's share of each
 // request's positions, and the draft window is taken on the global positions.  A negative slot
 // id is a skipped key (the top-k lists' has_invalid case, AITER issue "[Perf]
-// pa_decode_sparse", Measurements): its position counts, its weight is zero.
+// pa_decode_sparse", Measurements): its position counts, its weight is zero.  With a second
+// cache (FlashInfer sparse planner page, Parameters: extra_topk) a request's key list continues
+// past its pool keys with its second-cache rows, of the same format and scale.
 //
 // Work split (512 threads = 8 waves, one CTA per CU; waves w and w + 4 share SIMD w):
 //   - Score waves 0-3: wave w computes S^T = K Q^T for query rows 16 w .. 16 w + 15 against the 64
@@ -158,7 +160,9 @@ __device__ __forceinline__ float rows4_sum(float x) {
     return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
-template <int DQK, int DV, bool DIRECT>
+// EXTRA: a second cache (the sparse planner page's extra_topk): request b's keys are its
+// seq_lens[b] pool keys and then its second-cache rows; a key's list position picks the cache.
+template <int DQK, int DV, bool DIRECT, bool EXTRA>
 __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const MlaSplitArgs a) {
     using T = MlaLayout<DQK>;
     constexpr int DLAT = DQK - 64;
@@ -173,8 +177,14 @@ __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const MlaSplitAr
 
     // Keys of this partition: ceil(S / np) rounded up to block_k, the last ones possibly empty;
     // no row of the block sees past the block's latest draft token.
-    const int S = a.seq_lens[b];
+    const int S1 = a.seq_lens[b];   // keys in the pool
     const int base = a.kv_indptr[b];
+    const int base2 = EXTRA ? a.kv2_indptr[b] : 0;
+    const int S = EXTRA ? S1 + (a.kv2_indptr[b + 1] - base2) : S1;
+    // slot-id address of list position pos (< S) and whether the key is the second cache's
+    auto id_ptr = [&](int pos) -> const int32_t * {
+        return EXTRA && pos >= S1 ? a.kv2_indices + base2 + (pos - S1) : a.kv_indices + base + pos;
+    };
     // Keys draft position t sees: 0 .. S - q_len + t, or under context parallelism the local keys
     // whose global positions j * cp_world + cp_rank are at most glen - q_len + t.
     const int G = a.cp_world > 1 ? a.glen[b] : S;
@@ -451,20 +461,26 @@ __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const MlaSplitAr
     const int tail_pos = 16 * v + (lane >> 2);
     const int tail_chunk = 512 + 16 * ((lane & 3) ^ swz_tail(tail_pos));
     const int tail_key = key_of_pos(tail_pos);
-    const int32_t *const ibase = a.kv_indices + base;
     const uint64_t kv_stride = uint64_t(a.kv_stride);
-    const uint8_t *const kv_line = a.kv + 128 * v;
     const bool id_loader = v == 0;
 
     auto issue_ids = [&](int tile) {
         if (id_loader && tile < ntiles)
-            copy4(ibase + min(k0 + tile * kBK + lane, k1 - 1),
+            copy4(id_ptr(min(k0 + tile * kBK + lane, k1 - 1)),
                   lds_addr + T::kIdOff + (tile % kIdSlots) * 256);
     };
     // A negative slot id marks a key to skip: its copies read row 0 instead, and value wave 0
     // publishes the tile's mask of such keys for the score waves.
     // The copies of one tile given its slot ids: this lane's eight line keys 8 jgrp + i, its rope
     // tail key, and (value wave 0) the key numbered by the lane, whose sign makes the mask.
+    // (a key's cache follows its list position, clamped like the id loads; both caches share the
+    // row stride, so the second cache is the pool's address plus one offset)
+    const int64_t kv2_delta = EXTRA ? int64_t(a.kv2 - a.kv) : 0;
+    auto row_of = [&](int tile, int idx, int32_t id) -> const uint8_t * {
+        const uint8_t *p = a.kv + uint64_t(uint32_t(max(id, 0))) * kv_stride;
+        if (EXTRA && min(k0 + tile * kBK + idx, k1 - 1) >= S1) p += kv2_delta;
+        return p;
+    };
     auto copy_rows = [&](int tile, const int32_t (&kid)[8], int32_t tid, int32_t mid) {
         const uint32_t lslot = lds_addr + (tile % kLineSlots) * 32768 + v * 8192;
         if (id_loader) {
@@ -475,10 +491,10 @@ __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const MlaSplitAr
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const int gc = (lane & 7) ^ swz_line(8 * i + jgrp);
-            copy16(kv_line + uint64_t(uint32_t(max(kid[i], 0))) * kv_stride + 16 * gc, lslot + 1024 * i);
+            copy16(row_of(tile, 8 * jgrp + i, kid[i]) + 128 * v + 16 * gc, lslot + 1024 * i);
         }
         if (T::kTail)
-            copy16(a.kv + uint64_t(uint32_t(max(tid, 0))) * kv_stride + tail_chunk,
+            copy16(row_of(tile, tail_key, tid) + tail_chunk,
                    lds_addr + T::kTailOff + (tile % kTailSlots) * 4096 + 1024 * v);
     };
     // ... with the ids taken from the shared ring
@@ -501,11 +517,10 @@ __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const MlaSplitAr
         for (int i = 0; i < 8; ++i) pre_kid[j][i] = 0;
         pre_tid[j] = pre_mid[j] = 0;
         if (j < ntiles) {
-            const int32_t *src = a.kv_indices + base;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) pre_kid[j][i] = src[min(kb + 8 * jgrp + i, last)];
-            pre_tid[j] = src[min(kb + tail_key, last)];
-            pre_mid[j] = src[min(kb + lane, last)];
+            for (int i = 0; i < 8; ++i) pre_kid[j][i] = *id_ptr(min(kb + 8 * jgrp + i, last));
+            pre_tid[j] = *id_ptr(min(kb + tail_key, last));
+            pre_mid[j] = *id_ptr(min(kb + lane, last));
         }
     }
     // Issue order: ids(3), rows(0), rows(1), rows(2), ids(4), ids(5), then rows(j), ids(j + 3)
@@ -665,13 +680,13 @@ __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const MlaSplitAr
     }
 }
 
-template <int DQK, int DV>
+template <int DQK, int DV, bool EXTRA>
 hipError_t launch_shape(const MlaSplitArgs &a, bool direct, hipStream_t s) {
     const dim3 grid(xcd_grid_size(a.total_ctas)), block(kThreads);
     if (direct)
-        hipLaunchKernelGGL((mla_split_kernel<DQK, DV, true>), grid, block, 0, s, a);
+        hipLaunchKernelGGL((mla_split_kernel<DQK, DV, true, EXTRA>), grid, block, 0, s, a);
     else
-        hipLaunchKernelGGL((mla_split_kernel<DQK, DV, false>), grid, block, 0, s, a);
+        hipLaunchKernelGGL((mla_split_kernel<DQK, DV, false, EXTRA>), grid, block, 0, s, a);
     return hipGetLastError();
 }
 
@@ -681,8 +696,11 @@ int mla_rows_per_cta() { return kBM; }
 
 hipError_t launch_mla_split(const MlaSplitArgs &a, int d_qk, int d_v, bool direct, hipStream_t s) {
     if (a.block_k != 32 && a.block_k != 64) return hipErrorInvalidValue;
-    if (d_qk == 576 && d_v == 512) return launch_shape<576, 512>(a, direct, s);
-    if (d_qk == 512 && d_v == 448) return launch_shape<512, 448>(a, direct, s);
+    const bool extra = a.kv2 != nullptr;
+    if (d_qk == 576 && d_v == 512)   // (the second cache is a sparse top-k feature: 512-byte rows)
+        return extra ? hipErrorInvalidValue : launch_shape<576, 512, false>(a, direct, s);
+    if (d_qk == 512 && d_v == 448)
+        return extra ? launch_shape<512, 448, true>(a, direct, s) : launch_shape<512, 448, false>(a, direct, s);
     return hipErrorInvalidValue;
 }
 

@@ -128,6 +128,21 @@ typedef struct gqa_decode_problem {
     const int32_t *glen;
     int32_t cp_rank;
     int32_t cp_world;
+
+    /* A second cache [FI, Parameters: extra_topk, candidate slots per token in a second cache]
+     * (sparse MLA rows, d_qk 512, with q_len 1 and no context parallelism; kv2 NULL: off).
+     * kv2: fp8 rows of the pool's format [N2, d_qk] at the pool's row stride (kv2_stride_row 0
+     * or equal to kv_stride_row; pointer 16-byte aligned), dequantized with kv_scale.  Request b
+     * attends its seq_lens[b] pool keys and then the second-cache rows
+     * kv2_indices[kv2_indptr[b] .. kv2_indptr[b + 1]) (negative: skipped), all in one softmax;
+     * partitions cut the concatenated list.  kv2_indptr: int32 [B + 1].  max_num_keys must cover
+     * seq_lens[b] plus the request's second-cache count.  Errors: kv2 without both index lists
+     * (or the reverse) GQA_ERR_INVALID_ARGUMENT; with the GQA kind, wide rows, q_len > 1,
+     * context parallelism or another row stride GQA_ERR_UNSUPPORTED. */
+    const void *kv2;
+    int64_t kv2_stride_row;
+    const int32_t *kv2_indices;
+    const int32_t *kv2_indptr;
 } gqa_decode_problem;
 
 /* ---------------------------------------------------------------------------------------- */

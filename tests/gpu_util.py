@@ -30,7 +30,8 @@ def mla_problem(inp):
     return g.mla_problem(inp.q_lat, inp.q_pe, inp.pool, inp.kv_indices, inp.kv_indptr, inp.seq_lens,
                          batch=inp.B, q_len=inp.q_len, num_heads=inp.H,
                          max_num_keys=inp.max_num_keys, scale=inp.scale, kv_scale=inp.kv_scale,
-                         d_v=inp.d_v)
+                         d_v=inp.d_v, pool2=inp.pool2, kv2_indices=inp.kv2_indices,
+                         kv2_indptr=inp.kv2_indptr)
 
 
 def gqa_problem(inp):
@@ -57,11 +58,16 @@ def oracle_mla(inp, rows=None, n_threads=0):
     attention)."""
     H, q_len = inp.H, inp.q_len
     if rows is None:
+        second = {}
+        if inp.pool2 is not None:
+            second = dict(pool2=inp.pool2.cpu().numpy(), kv2_indices=inp.kv2_indices.cpu().numpy(),
+                          kv2_indptr=inp.kv2_indptr.cpu().numpy())
         return oracle.mla_decode(bits16(inp.q_lat), bits16(inp.q_pe), inp.pool.cpu().numpy(),
                                  inp.kv_indices.cpu().numpy(), inp.kv_indptr.cpu().numpy(),
                                  inp.seq_lens.cpu().numpy(), B=inp.B, q_len=q_len, H=H,
                                  d_v=inp.d_v, scale=inp.scale, kv_scale=inp.kv_scale,
-                                 n_threads=n_threads)
+                                 n_threads=n_threads, **second)
+    assert inp.pool2 is None, "sampled rows: one cache only"
     rows = list(rows)
     reqs = sorted({r // (q_len * H) for r in rows})
     indptr = inp.kv_indptr.cpu()

@@ -255,6 +255,37 @@ def test_context_parallel_rejections():
     expect_status(lambda: g.decode_split(p, 4, 32, FAKE, FAKE), -2)
 
 
+def test_second_cache_rejections():
+    # a second cache needs its index lists, sparse rows, q_len 1, no context parallelism and the
+    # pool's row stride
+    def sparse():
+        p = mla_fake(d_qk=512, d_v=448, max_keys=4096)
+        p.kv2, p.kv2_indices, p.kv2_indptr = FAKE, FAKE, FAKE
+        return p
+    assert g.decode_workspace_bytes(sparse(), 4) > 0
+    p = sparse()
+    p.kv2_indices = None
+    expect_status(lambda: g.decode_split(p, 4, 32, FAKE, FAKE), -1)
+    p = sparse()
+    p.kv2 = None
+    expect_status(lambda: g.decode_split(p, 4, 32, FAKE, FAKE), -1)
+    p = sparse()
+    p.q_len = 2
+    expect_status(lambda: g.decode_split(p, 4, 32, FAKE, FAKE), -2)
+    p = mla_fake()   # wide rows
+    p.kv2, p.kv2_indices, p.kv2_indptr = FAKE, FAKE, FAKE
+    expect_status(lambda: g.decode_split(p, 4, 32, FAKE, FAKE), -2)
+    p = sparse()
+    p.kv2_stride_row = 1024   # not the pool's stride
+    expect_status(lambda: g.decode_split(p, 4, 32, FAKE, FAKE), -2)
+    p = sparse()
+    p.glen, p.cp_world, p.cp_rank = FAKE, 2, 0
+    expect_status(lambda: g.decode_split(p, 4, 32, FAKE, FAKE), -2)
+    p = gqa_fake()
+    p.kv2, p.kv2_indices, p.kv2_indptr = FAKE, FAKE, FAKE
+    expect_status(lambda: g.decode_split(p, 4, 32, FAKE, FAKE), -2)
+
+
 def test_merge_ranks_argument_rejections():
     expect_status(lambda: g.merge_ranks(4, -1, 512, FAKE, FAKE, FAKE), -1)
     expect_status(lambda: g.merge_ranks(0, 8, 512, FAKE, FAKE, FAKE), -2)

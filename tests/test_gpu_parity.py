@@ -197,6 +197,52 @@ def test_sparse_skipped_keys_match_oracle():
     assert torch.all(lse[5 * 64:6 * 64] == -float("inf"))
 
 
+@pytest.mark.parametrize("np_,bk", [(1, 64), (3, 32), (5, 64), (0, 0)])
+def test_sparse_second_cache_matches_oracle(np_, bk):
+    # ragged second-cache counts: none, fewer than a tile, tiles that straddle the boundary
+    # between the caches, a whole list skipped, an extra list longer than the main one
+    base = workloads.sparse_mla_inputs(num_queries=8, topk=200, cache_rows=4096, seed=4300,
+                                       invalid_frac=0.1, device=DEV)
+    extra = [0, 7, 64, 100, 33, 1, 300, 129]
+    skip = list(range(7, 7 + 64)) + [200, 201, 500]
+    inp = workloads.with_second_cache(base, pool2_rows=2048, extra_lens=extra, seed=4310, skip=skip)
+    torch.cuda.synchronize()
+    log("sparse second cache np=%d bk=%d" % (np_, bk))
+    out, lse = run_decode(mla_problem(inp), 448, np_, bk)
+    torch.cuda.synchronize()
+    ref_o, ref_l = oracle_mla(inp)
+    compare(out, lse, ref_o, ref_l, "sparse second cache np=%d bk=%d" % (np_, bk))
+
+
+def test_sparse_second_cache_only():
+    # every main key skipped: the second cache alone decides the output; a request with both
+    # lists skipped stays empty
+    base = workloads.sparse_mla_inputs(num_queries=4, topk=96, cache_rows=1024, seed=4400,
+                                       all_invalid=(0, 1, 2, 3), device=DEV)
+    inp = workloads.with_second_cache(base, pool2_rows=1024, extra_lens=[150, 64, 0, 5], seed=4410,
+                                      skip=list(range(214, 219)))
+    torch.cuda.synchronize()
+    log("sparse second cache only")
+    out, lse = run_decode(mla_problem(inp), 448, 2, 64)
+    torch.cuda.synchronize()
+    ref_o, ref_l = oracle_mla(inp)
+    compare(out, lse, ref_o, ref_l, "sparse second cache only")
+    assert torch.all(lse[2 * 64:4 * 64] == -float("inf"))
+
+
+def test_sparse_second_cache_full_size():
+    # the sparse workload at 32 queries with 512 extra candidates per query, planner launch
+    inp = workloads.sparse_mla_inputs(num_queries=32, seed=4500, extra_topk=512, device=DEV)
+    torch.cuda.synchronize()
+    p = mla_problem(inp)
+    np_, bk = g.decode_plan(p)
+    log("sparse second cache full size np=%d bk=%d" % (np_, bk))
+    out, lse = run_decode(p, 448, np_, bk)
+    torch.cuda.synchronize()
+    ref_o, ref_l = oracle_mla(inp, n_threads=8)
+    compare(out, lse, ref_o, ref_l, "sparse second cache full size")
+
+
 def dcp_rank_problem(inp, world, rank, glen):
     """Rank `rank` of `world` decode-context-parallel ranks: the positions p % world == rank of
     every request (in position order), with the global lengths in glen."""
