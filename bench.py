@@ -62,6 +62,9 @@ def make_workloads():
         ("mla_h64_b8_s131072_q4", lambda d: w.mla_long(8, 4, d), 0),
         ("mla_h64_b16_s131072_q4", lambda d: w.mla_long(16, 4, d), 0),
         ("gqa_b32_hq64_hkv8_d128_p16", lambda d: w.gqa_paged(d), 0),
+        # not one of the quoted configurations: a skewed batch, where the equal split leaves the
+        # long request's few partitions to carry most of the keys
+        ("mla_h64_b32_skewed_1x131072_31x2048", lambda d: w.mla_skewed(d), 0),
     ]
     for nq in w.SPARSE_QUERY_COUNTS:
         items.append(("sparse_mla_h64_topk2048_nq%d" % nq, (lambda n: lambda d: w.sparse_topk(n, d))(nq), 0))
@@ -109,6 +112,16 @@ class Case:
 
     def split_only(self):
         self.g.decode_split(self.p, self.np, self.bk, self.po, self.pl, stream=self.stream)
+
+    def proportional_step(self):
+        # the same budget of np partitions per request, planned on the device in proportion to
+        # the lengths (at most 4 np per request)
+        import torch
+        if not hasattr(self, "ws_prop"):
+            n = self.g.decode_proportional_workspace_bytes(self.p, self.np)
+            self.ws_prop = torch.empty((n // 4 + 64,), dtype=torch.float32, device="cuda")
+        self.g.decode_proportional(self.p, self.out, self.lse, np=self.np, block_k=self.bk,
+                                   workspace=self.ws_prop, stream=self.stream)
 
     def reduce_only(self):
         self.g.splitk_reduce(self.rows, self.np, self.d_v, self.po, self.pl, self.out, self.lse,
@@ -492,6 +505,11 @@ def main():
             [case.step, case.split_only, case.reduce_only if case.np > 1 else None], steps, stream)
         ms_cold = time_cold(case.step, max(5, steps // 4), stream, flush)
         ms_graph = time_graph(case.step, steps, stream)
+        ms_eq = ms_prop = None
+        if not args.headline_only:   # keeps a profiled headline run to the headline's launches
+            case.proportional_step()
+            ms_eq, ms_prop = time_interleaved([case.step, case.proportional_step],
+                                              max(5, steps // 10 * 5), stream)
         case.step()
         torch.cuda.synchronize()
         entry = {
@@ -504,6 +522,9 @@ def main():
             "split_us": round(ms_split * 1e3, 2),
             "reduce_us": round(ms_red * 1e3, 2),
             "np": case.np, "block_k": case.bk, "kv_bytes": case.kv_bytes(),
+            # decode_proportional with the same budget, timed against decode in one interleave
+            "us_per_call_proportional": round(ms_prop * 1e3, 2) if ms_prop else None,
+            "proportional_vs_equal": round(ms_prop / ms_eq, 3) if ms_prop else None,
         }
         table[name] = entry
         print("# %-36s %s" % (name, json.dumps(entry)), file=sys.stderr, flush=True)

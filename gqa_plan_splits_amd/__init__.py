@@ -19,6 +19,9 @@ from ._lib import (  # noqa: F401
     decode_plan,
     decode_split,
     decode_workspace_bytes,
+    decode_proportional,
+    decode_proportional_workspace_bytes,
+    plan_proportional_device,
     device_sm_count,
     exported_symbols,
     fp8_e4m3_to_bf16,

@@ -14,7 +14,9 @@ FP8_E4M3FNUZ = 1
 
 # Every function include/gqa_splits.h declares.
 _SYMBOLS = ("plan_splits", "plan_sparse_splits", "plan_sparse_splits_measured", "block_k_for", "device_sm_count", "decode_plan", "decode_split",
-            "splitk_reduce", "splitk_reduce_f32", "merge_ranks", "decode_workspace_bytes", "decode", "fp8_e4m3_to_bf16",
+            "splitk_reduce", "splitk_reduce_f32", "merge_ranks", "decode_workspace_bytes", "decode",
+            "plan_proportional_device", "decode_proportional_workspace_bytes", "decode_proportional",
+            "fp8_e4m3_to_bf16",
             "status_string", "last_error_detail")
 
 
@@ -108,6 +110,9 @@ def _load():
     lib.merge_ranks.argtypes = [i64, i64, i64, vp, vp, vp, vp, vp]
     lib.decode_workspace_bytes.argtypes = [pp, i64, ctypes.POINTER(ctypes.c_size_t)]
     lib.decode.argtypes = [pp, i64, i32, vp, ctypes.c_size_t, vp, vp, vp]
+    lib.plan_proportional_device.argtypes = [vp, vp, i64, i64, i64, i32, vp, vp, vp]
+    lib.decode_proportional_workspace_bytes.argtypes = [pp, i64, i64, ctypes.POINTER(ctypes.c_size_t)]
+    lib.decode_proportional.argtypes = [pp, i64, i64, i32, vp, ctypes.c_size_t, vp, vp, vp]
     lib.fp8_e4m3_to_bf16.argtypes = [vp, i64, vp, vp]
     lib.status_string.argtypes = [i32]
     lib.status_string.restype = ctypes.c_char_p
@@ -337,6 +342,31 @@ def decode(problem: DecodeProblem, out, lse2_out=None, *, np: int = 0, block_k: 
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(_load().decode(ctypes.byref(problem), np, block_k, _ptr(workspace), ws_bytes, _ptr(out),
                           _ptr(lse2_out), _stream(stream)), "decode")
+
+
+def plan_proportional_device(seq_lens, extra_indptr, batch: int, budget: int, cap: int,
+                             block_k: int, part_start, part_chunk, stream=None):
+    """Device-side length-proportional plan into part_start [batch + 1] and part_chunk [batch]
+    (int32 device tensors)."""
+    _check(_load().plan_proportional_device(_ptr(seq_lens), _ptr(extra_indptr), batch, budget, cap,
+                                            block_k, _ptr(part_start), _ptr(part_chunk),
+                                            _stream(stream)), "plan_proportional_device")
+
+
+def decode_proportional_workspace_bytes(problem: DecodeProblem, np: int = 0, cap: int = 0) -> int:
+    out = ctypes.c_size_t(0)
+    _check(_load().decode_proportional_workspace_bytes(ctypes.byref(problem), np, cap,
+                                                       ctypes.byref(out)),
+           "decode_proportional_workspace_bytes")
+    return out.value
+
+
+def decode_proportional(problem: DecodeProblem, out, lse2_out=None, *, np: int = 0, cap: int = 0,
+                        block_k: int = 0, workspace=None, stream=None):
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(_load().decode_proportional(ctypes.byref(problem), np, cap, block_k, _ptr(workspace),
+                                       ws_bytes, _ptr(out), _ptr(lse2_out), _stream(stream)),
+           "decode_proportional")
 
 
 def fp8_e4m3_to_bf16(inp, n: int, out, stream=None):

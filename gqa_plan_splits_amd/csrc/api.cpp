@@ -133,14 +133,19 @@ int resolve_plan(const gqa_decode_problem *p, const Derived &d, int64_t np_or_0,
     return GQA_OK;
 }
 
+// np equal partitions per request, or with part_start set the planned length-proportional
+// slots: `slots` of them in the grid, np slots per row in the partial buffers.
 int launch_split(const gqa_decode_problem *p, const Derived &d, int64_t np, int bk,
-                 float *part_o, float *part_lse2, void *out, float *lse2_out, hipStream_t s) {
+                 float *part_o, float *part_lse2, void *out, float *lse2_out, hipStream_t s,
+                 const int32_t *part_start = nullptr, const int32_t *part_chunk = nullptr,
+                 int64_t slots = 0) {
     const bool direct = out != nullptr;
+    const int64_t grid_parts = part_start ? slots : p->batch * np;
     if (d.is_mla) {
         // the kernel's own row blocks (the planner's 32-row CTA count only sizes the split)
         const int64_t rpc = gqa::mla_rows_per_cta();
         const int64_t row_blocks = (d.rows_per_req + rpc - 1) / rpc;
-        const int64_t total = p->batch * np * row_blocks;
+        const int64_t total = grid_parts * row_blocks;
         if (total > (int64_t(1) << 30)) return GQA_ERR_UNSUPPORTED;
         gqa::MlaSplitArgs a;
         a.q = static_cast<const uint16_t *>(p->q);
@@ -169,6 +174,9 @@ int launch_split(const gqa_decode_problem *p, const Derived &d, int64_t np, int 
         a.row_blocks = int32_t(row_blocks);
         a.total_ctas = int32_t(total);
         a.block_k = bk;
+        a.part_start = part_start;
+        a.part_chunk = part_chunk;
+        a.batch = int32_t(p->batch);
         a.score_scale = p->scale * p->kv_scale * kLog2e;
         a.out_scale = p->kv_scale;
         a.part_o = part_o;
@@ -178,7 +186,7 @@ int launch_split(const gqa_decode_problem *p, const Derived &d, int64_t np, int 
         const hipError_t err = gqa::launch_mla_split(a, int(p->d_qk), int(p->d_v), direct, s);
         return launch_status(err, "mla split");
     } else {
-        const int64_t total = p->batch * np * d.cta_rows;
+        const int64_t total = grid_parts * d.cta_rows;
         if (total > (int64_t(1) << 30)) return GQA_ERR_UNSUPPORTED;
         gqa::GqaSplitArgs a;
         a.q = static_cast<const uint16_t *>(p->q);
@@ -203,6 +211,8 @@ int launch_split(const gqa_decode_problem *p, const Derived &d, int64_t np, int 
         a.out = static_cast<uint16_t *>(out);
         a.lse2_out = lse2_out;
         a.block_k = bk;
+        a.part_start = part_start;
+        a.part_chunk = part_chunk;
         const hipError_t err = gqa::launch_gqa_split(a, direct, s);
         return launch_status(err, "gqa split");
     }
@@ -261,6 +271,8 @@ int launch_merge(int64_t rows, int64_t np, int64_t d_v, const float *po, const f
     a.o_part = o_part;
     a.l_row = l_row;
     a.l_part = l_part;
+    a.part_start = nullptr;
+    a.rows_per_req = 0;
     return launch_status(gqa::launch_splitk_reduce(a, reinterpret_cast<hipStream_t>(s)), what);
 }
 
@@ -356,4 +368,125 @@ extern "C" const char *status_string(int status) {
         case GQA_ERR_DEVICE: return "no usable HIP device";
         default: return "unknown status";
     }
+}
+
+namespace {
+
+// Proportional plan: the budget of partition slots (np per request), the most one request may
+// take, and the workspace layout: slot-major partials ([budget, rows_per_req, d_v] and
+// [budget, rows_per_req] fp32), then part_start and part_chunk.
+struct PropLayout {
+    int64_t budget, cap;
+    size_t o_bytes, l_bytes, start_bytes, chunk_bytes;
+    size_t total() const { return o_bytes + l_bytes + start_bytes + chunk_bytes; }
+};
+
+int prop_layout(const gqa_decode_problem *p, const Derived &d, int64_t np, int64_t cap_or_0,
+                PropLayout *L) {
+    if (p->cp_world > 1 || p->glen) return GQA_ERR_UNSUPPORTED;
+    if (np < 1 || np > kMaxPartitions || cap_or_0 < 0 || cap_or_0 > kMaxPartitions)
+        return GQA_ERR_UNSUPPORTED;
+    L->budget = p->batch * np;
+    if (L->budget > (int64_t(1) << 30)) return GQA_ERR_UNSUPPORTED;
+    L->cap = cap_or_0 ? cap_or_0 : kMaxPartitions;
+    // the same bytes as np partitions per row
+    partial_bytes(d, np, p->d_v, &L->o_bytes, &L->l_bytes);
+    L->start_bytes = align256(size_t(p->batch + 1) * sizeof(int32_t));
+    L->chunk_bytes = align256(size_t(p->batch) * sizeof(int32_t));
+    return GQA_OK;
+}
+
+}  // namespace
+
+extern "C" int plan_proportional_device(const int32_t *seq_lens, const int32_t *extra_indptr,
+                                        int64_t batch, int64_t budget, int64_t cap, int block_k,
+                                        int32_t *part_start, int32_t *part_chunk, gqa_stream_t s) {
+    if (!seq_lens || !part_start || !part_chunk) return GQA_ERR_INVALID_ARGUMENT;
+    if (batch < 1 || budget < 1 || cap < 1) return GQA_ERR_INVALID_ARGUMENT;
+    if (batch > (int64_t(1) << 24) || budget > (int64_t(1) << 30) || cap > kMaxPartitions ||
+        (block_k != 32 && block_k != 64))
+        return GQA_ERR_UNSUPPORTED;
+    gqa::PlanArgs a;
+    a.seq_lens = seq_lens;
+    a.extra_indptr = extra_indptr;
+    a.batch = int32_t(batch);
+    a.budget = int32_t(budget);
+    a.cap = int32_t(cap);
+    a.block_k = block_k;
+    a.part_start = part_start;
+    a.part_chunk = part_chunk;
+    return launch_status(gqa::launch_plan_proportional(a, reinterpret_cast<hipStream_t>(s)),
+                         "plan_proportional_device");
+}
+
+extern "C" int decode_proportional_workspace_bytes(const gqa_decode_problem *p, int64_t np,
+                                                   int64_t cap_or_0, size_t *bytes) {
+    if (!bytes) return GQA_ERR_INVALID_ARGUMENT;
+    Derived d;
+    int rc = check_problem(p, &d);
+    if (rc != GQA_OK) return rc;
+    if (np == 0) {
+        int bk;
+        rc = resolve_plan(p, d, 0, 64, 0, &np, &bk);
+        if (rc != GQA_OK) return rc;
+    }
+    PropLayout L;
+    rc = prop_layout(p, d, np, cap_or_0, &L);
+    if (rc != GQA_OK) return rc;
+    *bytes = L.total();
+    return GQA_OK;
+}
+
+extern "C" int decode_proportional(const gqa_decode_problem *p, int64_t np_or_0, int64_t cap_or_0,
+                                   int block_k_or_0, void *workspace, size_t ws_bytes, void *out,
+                                   float *lse2_out, gqa_stream_t s) {
+    Derived d;
+    int rc = check_problem(p, &d);
+    if (rc != GQA_OK) return rc;
+    if (!out || !workspace) return GQA_ERR_INVALID_ARGUMENT;
+    int64_t np;
+    int bk;
+    rc = resolve_plan(p, d, np_or_0, block_k_or_0, 0, &np, &bk);
+    if (rc != GQA_OK) return rc;
+    PropLayout L;
+    rc = prop_layout(p, d, np, cap_or_0, &L);
+    if (rc != GQA_OK) return rc;
+    if (ws_bytes < L.total()) return GQA_ERR_WORKSPACE_TOO_SMALL;
+    if (reinterpret_cast<uintptr_t>(workspace) & 255u) return GQA_ERR_INVALID_ARGUMENT;
+    if (reinterpret_cast<uintptr_t>(out) % 8) return GQA_ERR_UNSUPPORTED;
+    char *w = static_cast<char *>(workspace);
+    float *part_o = reinterpret_cast<float *>(w);
+    float *part_l = reinterpret_cast<float *>(w + L.o_bytes);
+    int32_t *start = reinterpret_cast<int32_t *>(w + L.o_bytes + L.l_bytes);
+    int32_t *chunk = reinterpret_cast<int32_t *>(w + L.o_bytes + L.l_bytes + L.start_bytes);
+    const hipStream_t st = reinterpret_cast<hipStream_t>(s);
+    gqa::PlanArgs a;
+    a.seq_lens = p->seq_lens;
+    a.extra_indptr = p->kv2 ? p->kv2_indptr : nullptr;
+    a.batch = int32_t(p->batch);
+    a.budget = int32_t(L.budget);
+    a.cap = int32_t(L.cap);
+    a.block_k = bk;
+    a.part_start = start;
+    a.part_chunk = chunk;
+    rc = launch_status(gqa::launch_plan_proportional(a, st), "proportional plan");
+    if (rc != GQA_OK) return rc;
+    // at most budget slots (budget >= batch, so the plan always fits it)
+    rc = launch_split(p, d, np, bk, part_o, part_l, nullptr, nullptr, st, start, chunk, L.budget);
+    if (rc != GQA_OK) return rc;
+    gqa::ReduceArgs r;
+    r.part_o = part_o;
+    r.part_lse2 = part_l;
+    r.out = static_cast<uint16_t *>(out);
+    r.out_f32 = nullptr;
+    r.lse2_out = lse2_out;
+    r.rows = d.rows;
+    r.np = int32_t(L.cap);
+    r.dv = int32_t(p->d_v);
+    r.o_row = r.l_row = 0;   // rows are placed through the plan
+    r.o_part = d.rows_per_req * p->d_v;
+    r.l_part = d.rows_per_req;
+    r.part_start = start;
+    r.rows_per_req = d.rows_per_req;
+    return launch_status(gqa::launch_splitk_reduce(r, st), "proportional reduce");
 }

@@ -76,4 +76,19 @@ __device__ __forceinline__ int xcd_logical_block(int hw_id, int total) {
 
 inline int xcd_grid_size(int total) { return ((total + 7) >> 3) << 3; }
 
+// Length-proportional partitions: request b owns partition slots part_start[b] ..
+// part_start[b + 1] - 1 (part_start non-decreasing, part_start[0] = 0).  Returns the request
+// owning slot i, or batch when i lies past the last slot.  Every lane of the wave takes part
+// (one load per 64 requests) and gets the same, wave-uniform, answer.
+__device__ __forceinline__ int request_of_slot(const int32_t *part_start, int batch, int i) {
+    const int lane = threadIdx.x & 63;
+    int b = 0;
+    for (int j0 = 1; j0 <= batch; j0 += 64) {
+        const int j = j0 + lane;
+        const bool le = j <= batch && part_start[j] <= i;
+        b += __builtin_popcountll(__builtin_amdgcn_ballot_w64(le));
+    }
+    return __builtin_amdgcn_readfirstlane(b);
+}
+
 }  // namespace gqa

@@ -97,8 +97,12 @@ __global__ void __launch_bounds__(64) gqa_split_kernel(const GqaSplitArgs a) {
     const int lane = threadIdx.x, g = lane >> 4, col = lane & 15;
     const int kvh = logical % a.Hkv;
     const int rest = logical / a.Hkv;
-    const int part = rest % a.np;
-    const int b = request_by_length(a.seq_lens, a.batch, rest / a.np, lane);
+    // np equal partitions per request (longest requests first), or the planned
+    // length-proportional slots
+    const int b = a.part_start ? request_of_slot(a.part_start, a.batch, rest)
+                               : request_by_length(a.seq_lens, a.batch, rest / a.np, lane);
+    if (b >= a.batch) return;
+    const int part = a.part_start ? rest - a.part_start[b] : rest % a.np;
     const int rows_cta = a.q_len * a.group;
     const int page_mask = (1 << a.page_shift) - 1;
 
@@ -106,7 +110,8 @@ __global__ void __launch_bounds__(64) gqa_split_kernel(const GqaSplitArgs a) {
     // last ones possibly empty; no row sees past the latest draft token.
     const int S = a.seq_lens[b];
     const int pbase = a.kv_indptr[b];
-    const int chunk = ((S + a.np - 1) / a.np + a.block_k - 1) / a.block_k * a.block_k;
+    const int chunk = a.part_start ? a.part_chunk[b]
+                                   : ((S + a.np - 1) / a.np + a.block_k - 1) / a.block_k * a.block_k;
     const int k0 = part * chunk;
     const int k1 = min(max(0, S - a.q_len + (rows_cta - 1) / a.group + 1), k0 + chunk);
     const int kfull = min(k1, max(0, S - a.q_len + 1));   // tokens every row sees
@@ -242,10 +247,13 @@ __global__ void __launch_bounds__(64) gqa_split_kernel(const GqaSplitArgs a) {
                            pack_bf16x2(oacc[j][2] * inv, oacc[j][3] * inv));
         if (g == 0 && a.lse2_out) a.lse2_out[row] = lse2;
     } else {
-        float *o = a.part_o + (row * a.np + part) * kD + 4 * g;
+        // partial row: [row, np] or, with planned slots, [slot, q_len * Hq]
+        const int64_t prow = a.part_start ? (int64_t(rest) * a.q_len + t) * a.Hq + head
+                                          : row * a.np + part;
+        float *o = a.part_o + prow * kD + 4 * g;
 #pragma unroll
         for (int j = 0; j < 8; ++j) *reinterpret_cast<f32x4 *>(o + 16 * j) = oacc[j] * inv;
-        if (g == 0) a.part_lse2[row * a.np + part] = lse2;
+        if (g == 0) a.part_lse2[prow] = lse2;
     }
 }
 

@@ -24,6 +24,11 @@ struct MlaSplitArgs {
     int32_t cp_rank, cp_world;    // key j is global position j * cp_world + cp_rank
     int32_t q_len, H, np, rows_per_req, row_blocks, total_ctas;
     int32_t block_k;              // partition lengths are rounded up to a multiple of this
+    // length-proportional partitions (null: np equal partitions per request): request b owns
+    // slots part_start[b] .. part_start[b + 1] - 1 of part_chunk[b] keys each, and the partials
+    // are then slot-major: [slot, rows_per_req, DV] and [slot, rows_per_req]
+    const int32_t *part_start, *part_chunk;
+    int32_t batch;
     float score_scale;            // scale * kv_scale * log2(e): scores in base-2 units
     float out_scale;              // kv_scale: the raw fp8 values are accumulated unscaled
     float *part_o;                // [rows, np, DV]
@@ -40,6 +45,7 @@ struct GqaSplitArgs {
     const int32_t *page_indices, *kv_indptr, *seq_lens;
     int32_t batch, q_len, Hq, Hkv, group, page_shift, np, total_ctas;
     int32_t block_k;              // partition lengths are rounded up to a multiple of this
+    const int32_t *part_start, *part_chunk;   // as in MlaSplitArgs
     float score_scale;            // scale * log2(e)
     float *part_o, *part_lse2;
     uint16_t *out;
@@ -55,6 +61,23 @@ struct ReduceArgs {
     int32_t np, dv;
     // element strides: partial output (row, partition) and partial lse2 (row, partition)
     int64_t o_row, o_part, l_row, l_part;
+    // planned slots (null: np partitions per row): the partitions of row r of request b are
+    // slots part_start[b] .. part_start[b + 1] - 1, slot-major ([slot, rows_per_req, dv]);
+    // np is then only the most any request has
+    const int32_t *part_start;
+    int64_t rows_per_req;
+};
+
+// Device-side planner of length-proportional partitions.  Keys of request b: seq_lens[b] plus
+// extra_indptr[b + 1] - extra_indptr[b] when extra_indptr is set.  Under a common length c,
+// request b takes ceil(L_b / c) slots of c keys, or, beyond cap, cap slots' worth at the
+// smallest multiple of block_k that fits; c is the smallest multiple of block_k whose slots
+// sum to at most budget (at most one slot per request if none does).  Writes part_start
+// [batch + 1] and part_chunk [batch].
+struct PlanArgs {
+    const int32_t *seq_lens, *extra_indptr;
+    int32_t batch, budget, cap, block_k;
+    int32_t *part_start, *part_chunk;
 };
 
 // Launchers: return hipSuccess or the launch error.  All enqueue on `s` only.
@@ -64,6 +87,7 @@ hipError_t launch_mla_split(const MlaSplitArgs &a, int d_qk, int d_v, bool direc
 // (with a.kv2 set: the second-cache variant of the same kernel)
 hipError_t launch_gqa_split(const GqaSplitArgs &a, bool direct, hipStream_t s);
 hipError_t launch_splitk_reduce(const ReduceArgs &a, hipStream_t s);
+hipError_t launch_plan_proportional(const PlanArgs &a, hipStream_t s);
 hipError_t launch_fp8_to_bf16(const uint8_t *in, int64_t n, uint16_t *out, hipStream_t s);
 
 }  // namespace gqa

@@ -172,8 +172,10 @@ __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const MlaSplitAr
     if (logical < 0) return;
     const int rblk = logical % a.row_blocks;
     const int rest = logical / a.row_blocks;
-    const int part = rest % a.np;
-    const int b = rest / a.np;
+    // np equal partitions per request, or the planned length-proportional slots
+    const int b = a.part_start ? request_of_slot(a.part_start, a.batch, rest) : rest / a.np;
+    if (b >= a.batch) return;
+    const int part = a.part_start ? rest - a.part_start[b] : rest % a.np;
 
     // Keys of this partition: ceil(S / np) rounded up to block_k, the last ones possibly empty;
     // no row of the block sees past the block's latest draft token.
@@ -193,7 +195,8 @@ __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const MlaSplitAr
         if (a.cp_world == 1) return max(0, last + 1);
         return last >= a.cp_rank ? min(S, (last - a.cp_rank) / a.cp_world + 1) : 0;
     };
-    const int chunk = ((S + a.np - 1) / a.np + a.block_k - 1) / a.block_k * a.block_k;
+    const int chunk = a.part_start ? a.part_chunk[b]
+                                   : ((S + a.np - 1) / a.np + a.block_k - 1) / a.block_k * a.block_k;
     const int k0 = part * chunk;
     const int row0 = rblk * kBM;
     const int nrows = min(kBM, a.rows_per_req - row0);
@@ -652,6 +655,9 @@ __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const MlaSplitAr
         const int rl = 32 * rb + n;
         if (rl >= nrows) continue;
         const int64_t row = int64_t(b) * a.rows_per_req + row0 + rl;
+        // partial row: [row, np] or, with planned slots, [slot, rows_per_req]
+        const int64_t prow = a.part_start ? int64_t(rest) * a.rows_per_req + row0 + rl
+                                          : row * a.np + part;
         const float inv = lq[rb] > 0.f ? a.out_scale / lq[rb] : 0.f;
         const float lse2 = le[rb] > 0.f ? float(mc[rb]) + __log2f(le[rb]) : kNegInf;
 #pragma unroll
@@ -666,7 +672,7 @@ __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const MlaSplitAr
                     *reinterpret_cast<uint2 *>(a.out + row * DV + col) =
                         make_uint2(pack_bf16x2(v0, v1), pack_bf16x2(v2, v3));
                 } else {
-                    *reinterpret_cast<f32x4 *>(a.part_o + (row * a.np + part) * DV + col) =
+                    *reinterpret_cast<f32x4 *>(a.part_o + prow * DV + col) =
                         f32x4{v0, v1, v2, v3};
                 }
             }
@@ -674,7 +680,7 @@ __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const MlaSplitAr
             if (DIRECT) {
                 if (a.lse2_out) a.lse2_out[row] = lse2;
             } else {
-                a.part_lse2[row * a.np + part] = lse2;
+                a.part_lse2[prow] = lse2;
             }
         }
     }

@@ -68,13 +68,24 @@ __global__ void __launch_bounds__(256) splitk_reduce_kernel(const ReduceArgs a, 
         const int c_end = min(nvec, (chunk + 1) * chunk_vec);
         const bool lead = !SPLIT || w == 0;   // the wave that writes the item's output
 
-        const float *lp = a.part_lse2 + row * a.l_row;
+        // the row's partitions: np of them at row * o_row (l_row), or with a plan the slots of
+        // the row's request, slot-major
+        int np = a.np;
+        int64_t obase = row * a.o_row, lbase = row * a.l_row;
+        if (a.part_start) {
+            const int64_t b = row / a.rows_per_req, r = row - b * a.rows_per_req;
+            const int s0 = a.part_start[b];
+            np = a.part_start[b + 1] - s0;
+            lbase = int64_t(s0) * a.rows_per_req + r;
+            obase = lbase * a.dv;
+        }
+        const float *lp = a.part_lse2 + lbase;
         float l4[4];
         float mx = kNegInf;
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
             const int p = lane + 64 * k;
-            l4[k] = p < a.np ? lp[p * a.l_part] : kNegInf;
+            l4[k] = p < np ? lp[p * a.l_part] : kNegInf;
             mx = fmaxf(mx, l4[k]);
         }
         mx = wave_max(mx);   // with SPLIT identical in the four waves: the branch is block-uniform
@@ -90,7 +101,7 @@ __global__ void __launch_bounds__(256) splitk_reduce_kernel(const ReduceArgs a, 
         for (int k = 0; k < 4; ++k) {
             const int p = lane + 64 * k;
             const float wgt = fast_exp2(l4[k] - mx);   // -inf -> 0
-            if (p < a.np) wbuf[w][p] = wgt;
+            if (p < np) wbuf[w][p] = wgt;
             wsum += wgt;
         }
         wsum = wave_sum(wsum);
@@ -109,23 +120,27 @@ __global__ void __launch_bounds__(256) splitk_reduce_kernel(const ReduceArgs a, 
 #pragma unroll
             for (int j = 0; j < 4; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
             if (col_ok) {
-                const float *po = a.part_o + row * a.o_row + 4 * c4;
+                const float *po = a.part_o + obase + 4 * c4;
                 int p = SPLIT ? w : 0;
-                for (; p + 3 * pstep < a.np; p += 4 * pstep) {
+                for (; p + 3 * pstep < np; p += 4 * pstep) {
+                    // weights are the row's, the same in every lane: a partition without weight
+                    // is not loaded at all
                     f32x4 x[4];
-#pragma unroll
-                    for (int j = 0; j < 4; ++j)
-                        x[j] = load4(po + int64_t(p + pstep * j) * a.o_part);
+                    float wg[4];
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
-                        const float wgt = wbuf[w][p + pstep * j];
-                        if (wgt != 0.f) acc[j] += wgt * x[j];
+                        wg[j] = wbuf[w][p + pstep * j];
+                        x[j] = wg[j] != 0.f ? load4(po + int64_t(p + pstep * j) * a.o_part)
+                                            : f32x4{0.f, 0.f, 0.f, 0.f};
                     }
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        if (wg[j] != 0.f) acc[j] += wg[j] * x[j];
                 }
 #pragma unroll
                 for (int j = 0; j < 3; ++j) {   // at most three left
                     const int q = p + pstep * j;
-                    if (q < a.np) {
+                    if (q < np) {
                         const float wgt = wbuf[w][q];
                         if (wgt != 0.f) acc[j] += wgt * load4(po + int64_t(q) * a.o_part);
                     }

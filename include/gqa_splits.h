@@ -268,6 +268,45 @@ int decode_workspace_bytes(const gqa_decode_problem *p, int64_t np, size_t *byte
 int decode(const gqa_decode_problem *p, int64_t np_or_0, int block_k_or_0, void *workspace,
            size_t ws_bytes, void *out, float *lse2_out, gqa_stream_t s);
 
+/* Device-side plan of length-proportional partitions [MM, "VarlenPlan": a plan made on the GPU
+ * from device-side lengths, so a captured decode replays with new lengths; the rule is this
+ * library's reading].  Request b has L_b = seq_lens[b] keys, plus extra_indptr[b + 1] -
+ * extra_indptr[b] when extra_indptr is not NULL (a second cache).  Under a common length c,
+ * request b takes n_b = ceil(L_b / c) partitions of c keys, or, when that exceeds cap,
+ * chunk_b = the smallest multiple of block_k with ceil(L_b / chunk_b) <= cap and as many
+ * partitions of chunk_b keys as that needs.  c is the smallest multiple of block_k for which
+ * the sum of n_b is at most budget; if none is (budget below the number of non-empty requests),
+ * c is the longest L_b rounded up to block_k.  Partition j of request b covers its keys
+ * [j * chunk_b, (j + 1) * chunk_b).
+ *   seq_lens [batch], extra_indptr [batch + 1] or NULL: int32 device (inputs)
+ *   part_start [batch + 1] int32 device (output): exclusive prefix sum of n_b
+ *   part_chunk [batch] int32 device (output): chunk_b
+ * batch 1..2^24, budget 1..2^30, cap 1..256, block_k 32 or 64.  Enqueued on s, no host sync.
+ * Errors: INVALID_ARGUMENT (NULL pointer, batch, budget or cap below 1), UNSUPPORTED (out of
+ * range), LAUNCH_FAILED. */
+int plan_proportional_device(const int32_t *seq_lens, const int32_t *extra_indptr, int64_t batch,
+                             int64_t budget, int64_t cap, int block_k, int32_t *part_start,
+                             int32_t *part_chunk, gqa_stream_t s);
+
+/* Workspace decode_proportional() needs: the partials of batch * np slots, slot-major
+ * ([slot, q_len * H, d_v] and [slot, q_len * H] fp32: as many bytes as decode's np partitions
+ * per row), then the plan's two tables, each part 256-byte aligned.  np = 0: the planner's
+ * choice on the current device; cap_or_0 (0 or 1..256) does not change the size. */
+int decode_proportional_workspace_bytes(const gqa_decode_problem *p, int64_t np, int64_t cap_or_0,
+                                        size_t *bytes);
+
+/* Whole decode with length-proportional partitions planned on the device: the budget is
+ * batch * np slots, the grid of the equal split (np_or_0 = 0: the planner's np), split by
+ * plan_proportional_device over the problem's lengths (and second-cache counts) with at most
+ * cap_or_0 (0: 256) slots per request; then the split kernel over the planned slots and the
+ * reducer over each row's slots, both placed through the plan's tables.  No host sync: a
+ * captured call re-plans on every replay.  Output as decode (out 8-byte aligned).  Without
+ * context parallelism (else UNSUPPORTED).  Errors: as decode, WORKSPACE_TOO_SMALL below
+ * decode_proportional_workspace_bytes. */
+int decode_proportional(const gqa_decode_problem *p, int64_t np_or_0, int64_t cap_or_0,
+                        int block_k_or_0, void *workspace, size_t ws_bytes, void *out,
+                        float *lse2_out, gqa_stream_t s);
+
 /* Utility: decode n OCP e4m3fn bytes to bf16 with the same conversion the MLA split kernel
  * applies to the pool (exact; unit scale).  in, out 16-byte aligned device buffers; out holds
  * n bf16 values.  Lets callers and tests check the device's fp8 decoding byte by byte. */

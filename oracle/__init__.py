@@ -13,7 +13,10 @@ Sources (cited by page title and section):
   count" ("Why it is not monotonic in num_queries");
 * attention -- moonmath-amd README ("MLA decode" usage and constraints; gfx950 "forward_paged");
   "Numerics" fixes the target as attention over the same dequantized KV;
-* merge -- base-2 log-sum-exp combination of partials (mla_splitk_reduce, mla_dcp_lse_merge_ranks).
+* merge -- base-2 log-sum-exp combination of partials (mla_splitk_reduce, mla_dcp_lse_merge_ranks);
+* proportional plan -- moonmath-amd README ("VarlenPlan": a plan made on the GPU from device-side
+  lengths); the length-proportional rule is a reading of that section, written here in plain
+  integer Python (the one function whose arithmetic is not in ``oracle.c``).
 
 Parity pins: every function here is pinned by ``tests/test_oracle_*.py`` against page values,
 closed forms, invariants and torch-CPU library routines; none is "parity unpinned" except the
@@ -139,6 +142,37 @@ def plan_sparse_splits(num_tokens: int, num_heads: int, topk: int, extra_topk: i
     rc = _load().oracle_plan_sparse_splits(num_tokens, num_heads, topk, extra_topk, num_sms,
                                            max_splits, head_tiles, ctypes.byref(ns), ctypes.byref(cpb))
     return None if rc != 0 else (int(ns.value), int(cpb.value))
+
+
+def proportional_plan(lengths, budget: int, cap: int, block_k: int):
+    """Length-proportional partitions for a batch with lengths[b] keys per request.
+
+    Under a common partition length c a request takes as many partitions of c keys as cover its
+    keys, except that no request takes more than `cap`: one that would gets the fewest
+    partitions of the smallest block_k multiple that covers it in cap.  c is the smallest
+    multiple of block_k for which the partitions of the whole batch number at most `budget`
+    (the longest request rounded up to block_k when no c does).  Returns (part_start,
+    part_chunk): the exclusive prefix sum of the counts ([batch + 1]) and each request's
+    partition length ([batch])."""
+    lengths = [max(0, int(x)) for x in lengths]
+
+    def split(n, c):
+        k = -(-n // c)
+        if k > cap:
+            c = -(-(-(-n // cap)) // block_k) * block_k
+            k = -(-n // c)
+        return k, c
+
+    longest_c = max(block_k, -(-max(lengths + [0]) // block_k) * block_k)
+    c = block_k
+    while c < longest_c and sum(split(n, c)[0] for n in lengths) > budget:
+        c += block_k
+    start, chunk = [0], []
+    for n in lengths:
+        k, cb = split(n, c)
+        start.append(start[-1] + k)
+        chunk.append(cb)
+    return start, chunk
 
 
 def block_k(ctas: int, sm_count: int) -> int:

@@ -286,6 +286,47 @@ def test_second_cache_rejections():
     expect_status(lambda: g.decode_split(p, 4, 32, FAKE, FAKE), -2)
 
 
+def test_proportional_plan_argument_rejections():
+    def plan(seq=FAKE, batch=4, budget=16, cap=8, bk=32, start=FAKE, chunk=FAKE):
+        return lambda: g.plan_proportional_device(seq, None, batch, budget, cap, bk, start, chunk)
+    expect_status(plan(seq=None), -1)
+    expect_status(plan(start=None), -1)
+    expect_status(plan(chunk=None), -1)
+    expect_status(plan(batch=0), -1)
+    expect_status(plan(budget=0), -1)
+    expect_status(plan(cap=0), -1)
+    expect_status(plan(cap=257), -2)
+    expect_status(plan(bk=16), -2)
+    expect_status(plan(budget=(1 << 30) + 1), -2)
+
+
+def test_decode_proportional_layout_and_rejections():
+    lib = g._lib._load()
+
+    def call(p, np_, cap, ws_bytes, out=FAKE, ws=0x100000):
+        return lib.decode_proportional(ctypes.byref(p), np_, cap, 32, ws, ws_bytes, out, None, None)
+
+    # workspace: slot-major partials of batch * np slots (decode's bytes for np), then the two
+    # plan tables, each 256-byte aligned; cap does not change it
+    p = mla_fake(B=3, H=64)
+    rows, dv = 3 * 64, 512
+    want = rows * 8 * dv * 4 + rows * 8 * 4 + 256 + 256
+    assert g.decode_proportional_workspace_bytes(p, 8) == want
+    assert g.decode_proportional_workspace_bytes(p, 8, 5) == want
+    assert g.decode_proportional_workspace_bytes(p, 8) == g.decode_workspace_bytes(p, 8) + 512
+    assert call(p, 8, 0, want - 1) == -3
+    assert call(p, 8, 0, want, out=None) == -1
+    assert call(p, 8, 0, want, ws=0x100010) == -1     # workspace not 256-byte aligned
+    assert call(p, 8, 257, 1 << 40) == -2
+    assert call(p, 257, 0, 1 << 40) == -2
+    p.glen, p.cp_world, p.cp_rank = FAKE, 2, 0
+    assert call(p, 8, 0, 1 << 40) == -2
+    assert call(p, 8, 0, want, out=FAKE + 4) == -2   # output not 8-byte aligned
+    q = gqa_fake(B=5)
+    rows = 5 * 64
+    assert g.decode_proportional_workspace_bytes(q, 3) == rows * 3 * 128 * 4 + 3840 + 512
+
+
 def test_merge_ranks_argument_rejections():
     expect_status(lambda: g.merge_ranks(4, -1, 512, FAKE, FAKE, FAKE), -1)
     expect_status(lambda: g.merge_ranks(0, 8, 512, FAKE, FAKE, FAKE), -2)

@@ -4,6 +4,8 @@ Planner: Modular MAX API page "hip_mha_decoding_num_partitions".  Tile rule: AIT
 "[Perf] pa_decode_sparse: BLOCK_K=64 is suboptimal above the CU count"."""
 import itertools
 
+import numpy as np
+
 import pytest
 
 import oracle
@@ -159,3 +161,98 @@ def test_sparse_planner_split_is_largest_admissible():
                         if room and enough and chunks > 2:
                             best = s
                     assert ns == best, (sms, nt, nh, topk, ns, best)
+
+
+# ---------------------------------------------------------------------------------------------
+# Length-proportional partitions (moonmath-amd README, "VarlenPlan": planning on the GPU from
+# device-side lengths; the proportional rule is this library's reading)
+# ---------------------------------------------------------------------------------------------
+
+def test_proportional_plan_worked_example():
+    # lengths 1000, 0, 31, 5000 over 8 partitions, at most 4 per request, 32-key tiles, by hand.
+    # 5000 keys need more than 4 partitions below 1250 keys each, so they take 4 of 1280 keys
+    # whatever the common length c; 31 keys take 1 and 0 keys none.  1000 keys take 4 partitions
+    # for c < 334 (capped at 4 of 256 below 250) -- 9 in all, over the budget -- and 3 for
+    # 334 <= c < 500, 8 in all.  The smallest multiple of 32 from 334 on is 352.
+    start, chunk = oracle.proportional_plan([1000, 0, 31, 5000], budget=8, cap=4, block_k=32)
+    assert start == [0, 3, 3, 4, 8]
+    assert chunk == [352, 352, 352, 1280]
+
+
+def _check_plan(lengths, budget, cap, bk):
+    start, chunk = oracle.proportional_plan(lengths, budget, cap, bk)
+    B = len(lengths)
+    assert len(start) == B + 1 and start[0] == 0
+
+    def count(c):   # partitions of the batch under common length c, by the rule's definition
+        n = 0
+        for L in lengths:
+            k = -(-L // c)
+            if k > cap:
+                cb = bk
+                while -(-L // cb) > cap:   # brute force: smallest bk multiple within cap
+                    cb += bk
+                k = -(-L // cb)
+            n += k
+        return n
+
+    common = [chunk[b] for b in range(B) if -(-lengths[b] // chunk[b]) <= cap or lengths[b] == 0]
+    nonempty = sum(1 for L in lengths if L > 0)
+    for b, L in enumerate(lengths):
+        k = start[b + 1] - start[b]
+        assert chunk[b] % bk == 0 and chunk[b] >= bk
+        assert 0 <= k <= cap
+        # the partitions cover the request's keys and none of them is empty
+        assert k * chunk[b] >= L and (k - 1) * chunk[b] < max(L, 1)
+    if budget >= nonempty:
+        assert start[-1] <= budget
+        # minimality of the common length: one block_k shorter overflows the budget
+        c = min(common) if common else None
+        if c is not None and c > bk:
+            assert count(c - bk) > budget
+            assert count(c) == start[-1]
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_proportional_plan_invariants_random(seed):
+    rng = np.random.default_rng(seed)
+    B = int(rng.integers(1, 40))
+    kind = seed % 4
+    if kind == 0:
+        lengths = rng.integers(0, 5000, B).tolist()
+    elif kind == 1:
+        lengths = rng.integers(1024, 32769, B).tolist()
+    elif kind == 2:   # one long request among short ones
+        lengths = [int(rng.integers(1, 200)) for _ in range(B)]
+        lengths[int(rng.integers(B))] = int(rng.integers(50000, 200000))
+    else:
+        lengths = [0] * B
+    budget = int(rng.integers(1, 8 * B + 2))
+    cap = int(rng.integers(1, 257))
+    bk = (32, 64)[seed % 2]
+    _check_plan(lengths, budget, cap, bk)
+
+
+@pytest.mark.parametrize("S,B,np_,bk", [(65536, 2, 64, 32), (131072, 16, 16, 32), (1000, 3, 7, 64),
+                                        (33, 5, 4, 32), (1, 1, 1, 64)])
+def test_proportional_plan_uniform_lengths_is_the_equal_split(S, B, np_, bk):
+    # equal lengths with a budget of np per request: every request gets the equal split's
+    # partition length ceil(S / np) rounded up to bk, and as many partitions as that split fills
+    start, chunk = oracle.proportional_plan([S] * B, budget=B * np_, cap=256, block_k=bk)
+    eq = -(-(-(-S // np_)) // bk) * bk
+    assert chunk == [eq] * B
+    assert [start[b + 1] - start[b] for b in range(B)] == [-(-S // eq)] * B
+
+
+def test_proportional_plan_empty_batch_and_cap_one():
+    start, chunk = oracle.proportional_plan([0, 0, 0], budget=5, cap=8, block_k=64)
+    assert start == [0, 0, 0, 0] and chunk == [64, 64, 64]
+    # cap 1: every non-empty request is one partition covering all its keys, so 3 partitions fit
+    # 100 at any common length and the common length is the smallest, 32: 7 keys fit one such
+    # partition, 100 and 4096 keys take one partition of 128 and 4096 keys
+    start, chunk = oracle.proportional_plan([100, 7, 0, 4096], budget=100, cap=1, block_k=32)
+    assert start == [0, 1, 2, 2, 3]
+    assert chunk == [128, 32, 32, 4096]
+    # a budget below the non-empty requests: each takes one partition of the longest, rounded up
+    start, chunk = oracle.proportional_plan([100, 7, 0, 4096], budget=2, cap=8, block_k=32)
+    assert start == [0, 1, 2, 2, 3] and chunk == [4096] * 4

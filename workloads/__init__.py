@@ -271,6 +271,14 @@ def mla_long(B: int, q_len: int = 1, device="cpu"):
                       seed=2000, device=device, name="mla_h64_b%d_s131072_q%d" % (B, q_len))
 
 
+def mla_skewed(device="cpu"):
+    """A skewed serving batch: H=64, one request of 131072 keys among 31 of 2048 (the same
+    fp8 pool as the long-context workloads)."""
+    lens = [131072] + [2048] * 31
+    return mla_inputs(B=32, q_len=1, H=64, seq_lens=lens, pool_rows=sum(lens), seed=2100,
+                      device=device, name="mla_h64_b32_skewed_1x131072_31x2048")
+
+
 GQA_LEN_SEED = 3000 + 5
 
 
