@@ -37,6 +37,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sparse-sweep", action="store_true",
                     help="only time the sparse top-k split sweep and print it")
+    ap.add_argument("--branch-sweep", action="store_true",
+                    help="only the planner-branch sweep (MLA 32/128 heads, GQA one kv head)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle sample")
     ap.add_argument("--table-steps", type=int, default=20)
@@ -371,6 +373,59 @@ def wave_sweep(stream, steps):
     return res
 
 
+def branch_sweep(stream, steps):
+    """The planner's other branches on this library's kernels: MLA with 32 and 128 heads, and
+    GQA with one kv head (16 query heads) and with 4 query heads per kv head, each timed at every
+    power-of-two partition count up to 256 (graph-replayed decode calls) beside the planner's
+    choice."""
+    import torch
+    import gqa_plan_splits_amd as g
+    import workloads as w
+    cases = [("mla_h32_b4_s65536", "mla", 4, 32, 1, 65536), ("mla_h32_b16_s16384", "mla", 16, 32, 1, 16384),
+             ("mla_h128_b4_s65536", "mla", 4, 128, 1, 65536), ("mla_h128_b16_s16384", "mla", 16, 128, 1, 16384),
+             ("gqa_hq16_hkv1_b8_s32768", "gqa", 8, 16, 1, 32768), ("gqa_hq16_hkv1_b64_s8192", "gqa", 64, 16, 1, 8192),
+             ("gqa_hq32_hkv8_b8_s32768", "gqa", 8, 32, 8, 32768), ("gqa_hq32_hkv8_b64_s8192", "gqa", 64, 32, 8, 8192)]
+    res = {}
+    for name, kind, B, H, Hkv, S in cases:
+        with torch.cuda.stream(stream):
+            if kind == "mla":
+                inp = w.mla_inputs(B=B, q_len=1, H=H, seq_lens=[S] * B, pool_rows=B * S, seed=5100,
+                                   device="cuda", name=name)
+            else:
+                inp = w.gqa_inputs(B=B, Hq=H, Hkv=Hkv, D=128, page_size=16, seq_lens=[S] * B,
+                                   num_pages=B * S // 16, seed=5200, device="cuda", name=name)
+        torch.cuda.synchronize()   # the inputs exist before any kernel on `stream` reads them
+        if kind == "mla":
+            check_slots(inp)
+            p = g.mla_problem(inp.q_lat, inp.q_pe, inp.pool, inp.kv_indices, inp.kv_indptr,
+                              inp.seq_lens, batch=B, q_len=1, num_heads=H, max_num_keys=S,
+                              scale=inp.scale, kv_scale=inp.kv_scale, d_v=512)
+            d_v = 512
+        else:
+            p = g.gqa_problem(inp.q, inp.k_cache, inp.v_cache, inp.kv_page_indices, inp.kv_indptr,
+                              inp.seq_lens, batch=B, q_len=1, max_num_keys=S, scale=inp.scale)
+            d_v = 128
+        planner = g.decode_plan(p)[0]
+        out = torch.empty((p.rows, d_v), dtype=torch.bfloat16, device="cuda")
+        lse = torch.empty((p.rows,), dtype=torch.float32, device="cuda")
+        times = {}
+        for n in sorted({1, 2, 4, 8, 16, 32, 64, 128, 256, planner}):
+            ws = torch.empty((g.decode_workspace_bytes(p, n) // 4 + 64,), dtype=torch.float32,
+                             device="cuda")
+            fn = (lambda n=n, ws=ws: g.decode(p, out, lse, np=n, workspace=ws, stream=stream))
+            for _ in range(3):
+                fn()
+            times[n] = (time_graph(fn, steps, stream) or time_events(fn, steps, stream)) * 1e3
+            del ws
+        best = min(times, key=times.get)
+        res[name] = {"us_by_np": {str(k): round(v, 2) for k, v in times.items()}, "best_np": best,
+                     "planner_np": planner, "planner_vs_best": round(times[planner] / times[best], 3)}
+        print("# branch %s %s" % (name, json.dumps(res[name])), file=sys.stderr, flush=True)
+        del inp, p, out, lse
+        torch.cuda.empty_cache()
+    return res
+
+
 def sparse_sweep(stream, steps):
     """Sparse top-k MLA (64 heads, 2048 candidates per query) at every split count from 1 to 32
     per query count, beside the choices of the two planners: the wave-aligned one decode uses
@@ -481,6 +536,9 @@ def main():
     if args.sparse_sweep:
         print(json.dumps({"sparse_planner": sparse_sweep(stream, args.table_steps)}), flush=True)
         return
+    if args.branch_sweep:
+        print(json.dumps({"planner_branches": branch_sweep(stream, args.table_steps)}), flush=True)
+        return
     flush = torch.empty((512 << 20) // 4, dtype=torch.float32, device="cuda")
 
     table = {}
@@ -587,6 +645,7 @@ def main():
         print("# planner_waves %s" % json.dumps(result["planner_waves"]), file=sys.stderr, flush=True)
         result["sparse_planner"] = sparse_sweep(stream, args.table_steps)
         print("# sparse_planner %s" % json.dumps(result["sparse_planner"]), file=sys.stderr, flush=True)
+        result["planner_branches"] = branch_sweep(stream, args.table_steps)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)
     print(json.dumps(result), flush=True)

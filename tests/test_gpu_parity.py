@@ -186,6 +186,20 @@ def test_mla_skipped_keys_match_oracle(q_len):
         compare(out, lse, ref_o, ref_l, "mla skipped keys q_len=%d np=%d" % (q_len, np_))
 
 
+@pytest.mark.parametrize("H,q_len", [(128, 1), (128, 2), (96, 1)])
+@pytest.mark.parametrize("np_", [1, 3])
+def test_mla_wide_head_counts_match_oracle(H, q_len, np_):
+    # more than one 64-row block per request from the heads alone (and a half block at 96)
+    inp = workloads.mla_inputs(B=3, q_len=q_len, H=H, seq_lens=[2000, 65, 0], pool_rows=2100,
+                               seed=66, device=DEV)
+    torch.cuda.synchronize()
+    log("mla H=%d q_len=%d np=%d" % (H, q_len, np_))
+    out, lse = run_decode(mla_problem(inp), 512, np_, 32)
+    torch.cuda.synchronize()
+    ref_o, ref_l = oracle_mla(inp)
+    compare(out, lse, ref_o, ref_l, "mla H=%d q_len=%d np=%d" % (H, q_len, np_))
+
+
 def test_sparse_skipped_keys_match_oracle():
     inp = workloads.sparse_mla_inputs(num_queries=24, invalid_frac=0.25, all_invalid=(5,), seed=4100,
                                       device=DEV)
