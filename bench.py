@@ -420,6 +420,10 @@ def branch_sweep(stream, steps):
         best = min(times, key=times.get)
         res[name] = {"us_by_np": {str(k): round(v, 2) for k, v in times.items()}, "best_np": best,
                      "planner_np": planner, "planner_vs_best": round(times[planner] / times[best], 3)}
+        if kind == "gqa":   # the MI355X-measured GQA variant (a power of two, or the planner's np)
+            m = g.plan_gqa_splits_measured(B, S, Hkv)
+            if m in times:
+                res[name].update(measured_np=m, measured_vs_best=round(times[m] / times[best], 3))
         print("# branch %s %s" % (name, json.dumps(res[name])), file=sys.stderr, flush=True)
         del inp, p, out, lse
         torch.cuda.empty_cache()

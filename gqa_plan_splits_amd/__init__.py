@@ -30,6 +30,7 @@ from ._lib import (  # noqa: F401
     library_path,
     merge_ranks,
     mla_problem,
+    plan_gqa_splits_measured,
     plan_sparse_splits,
     plan_sparse_splits_measured,
     plan_splits,

@@ -13,7 +13,7 @@ FP8_E4M3FN = 0
 FP8_E4M3FNUZ = 1
 
 # Every function include/gqa_splits.h declares.
-_SYMBOLS = ("plan_splits", "plan_sparse_splits", "plan_sparse_splits_measured", "block_k_for", "device_sm_count", "decode_plan", "decode_split",
+_SYMBOLS = ("plan_splits", "plan_sparse_splits", "plan_sparse_splits_measured", "plan_gqa_splits_measured", "block_k_for", "device_sm_count", "decode_plan", "decode_split",
             "splitk_reduce", "splitk_reduce_f32", "merge_ranks", "decode_workspace_bytes", "decode",
             "plan_proportional_device", "decode_proportional_workspace_bytes", "decode_proportional",
             "fp8_e4m3_to_bf16",
@@ -102,6 +102,7 @@ def _load():
     lib.plan_sparse_splits.argtypes = [i64, i64, i64, i64, i64, i64, i64, ctypes.POINTER(i64),
                                        ctypes.POINTER(i64)]
     lib.plan_sparse_splits_measured.argtypes = [i64, i64, i64, i64, i64, i64, i64, ctypes.POINTER(i64)]
+    lib.plan_gqa_splits_measured.argtypes = [i64, i64, i64, i64, ctypes.POINTER(i64)]
     lib.device_sm_count.argtypes = [ctypes.POINTER(i64)]
     lib.decode_plan.argtypes = [pp, i64, i32, i64, ctypes.POINTER(i64), ctypes.POINTER(i32)]
     lib.decode_split.argtypes = [pp, i64, i32, vp, vp, vp]
@@ -175,6 +176,14 @@ def plan_splits(batch_size: int, num_keys: int, heads_per_group: int, sm_count: 
     out = ctypes.c_int64(0)
     _check(_load().plan_splits(batch_size, num_keys, heads_per_group, sm_count, int(bool(is_mla)),
                                ctypes.byref(out)), "plan_splits")
+    return out.value
+
+
+def plan_gqa_splits_measured(batch_size: int, max_num_keys: int, num_kv_heads: int,
+                             sm_count: int = 0) -> int:
+    out = ctypes.c_int64(0)
+    _check(_load().plan_gqa_splits_measured(batch_size, max_num_keys, num_kv_heads, sm_count,
+                                            ctypes.byref(out)), "plan_gqa_splits_measured")
     return out.value
 
 

@@ -225,3 +225,26 @@ extern "C" int plan_sparse_splits_measured(int64_t num_tokens, int64_t num_heads
     *num_splits_out = chunks > 2 && cap >= 1 ? floor_pow2(cap) : 1;
     return GQA_OK;
 }
+
+extern "C" int plan_gqa_splits_measured(int64_t batch_size, int64_t max_num_keys,
+                                        int64_t num_kv_heads, int64_t sm_count, int64_t *np_out) {
+    if (!np_out || batch_size < 1 || max_num_keys < 0 || num_kv_heads < 1)
+        return GQA_ERR_INVALID_ARGUMENT;
+    if (sm_count <= 0) {
+        const int rc = device_sm_count(&sm_count);
+        if (rc != GQA_OK) return rc;
+    }
+    int64_t base;
+    int rc = plan_splits(batch_size, max_num_keys, num_kv_heads, sm_count, 0, &base);
+    if (rc != GQA_OK) return rc;
+    // the split kernel's CTAs are one wave: the chip is full from four of them per CU on,
+    // as long as a partition keeps at least kGqaMinKeys keys
+    constexpr int64_t kCtasPerCu = 4, kGqaMinKeys = 256, kMax = 256;
+    const int64_t ctas = batch_size * num_kv_heads;
+    const int64_t key_cap = std::max<int64_t>(1, std::min(kMax, max_num_keys / kGqaMinKeys));
+    int64_t fill = 1;
+    while (fill < key_cap && ctas * fill < kCtasPerCu * sm_count) fill *= 2;
+    fill = std::min(fill, floor_pow2(key_cap));
+    *np_out = std::max(base, fill);
+    return GQA_OK;
+}

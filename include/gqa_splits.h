@@ -186,6 +186,18 @@ int plan_sparse_splits(int64_t num_tokens, int64_t num_heads, int64_t topk, int6
                        int64_t num_sms, int64_t max_splits, int64_t head_tiles,
                        int64_t *num_splits_out, int64_t *chunks_per_block_out);
 
+/* The wave-aligned planner's choice for paged GQA, raised where this library's GQA split kernel
+ * measured better on MI355X: max(plan_splits(batch_size, max_num_keys, num_kv_heads, sm_count,
+ * 0), the smallest power of two np with batch_size * num_kv_heads * np >= 4 * sm_count), the
+ * latter held to at least 256 keys per partition (the largest power of two <= max_num_keys / 256,
+ * at least 1) and to 256.  The kernel's CTAs are one wave and several run per CU, so the pages'
+ * count of one CTA per CU under-splits batches with few kv-head CTAs.  sm_count <= 0 queries the
+ * current device.  Not a rule of the pages: a measured tuning, checked by the benchmark's
+ * planner-branch sweep.  Errors: INVALID_ARGUMENT (NULL output, a size below its bound), DEVICE,
+ * and those of plan_splits. */
+int plan_gqa_splits_measured(int64_t batch_size, int64_t max_num_keys, int64_t num_kv_heads,
+                             int64_t sm_count, int64_t *np_out);
+
 /* The sparse planner's decision with thresholds measured on MI355X for this library's MLA
  * kernel rather than the page's (which were measured for a Blackwell kernel): the largest power
  * of two (<= max_splits) that keeps num_tokens * ceil(num_heads / rows_per_cta) * splits within
