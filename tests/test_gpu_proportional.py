@@ -155,3 +155,23 @@ def test_skewed_batch_full_size_sampled():
     rows = sorted(set(rows))
     ref_o, ref_l = oracle_mla(inp, rows)
     compare(out[rows], lse[rows], ref_o, ref_l, "skewed batch proportional")
+
+
+@pytest.mark.parametrize("kind", ["mla", "gqa"])
+def test_proportional_with_planner_choices(kind):
+    # np = 0 and block_k = 0: the wave-aligned planner's budget and the tile rule, as decode
+    lens = [5000, 17, 0, 1200, 64]
+    if kind == "mla":
+        inp = workloads.mla_inputs(B=5, q_len=1, H=64, seq_lens=lens, pool_rows=6400, seed=83,
+                                   device=DEV)
+        p, d_v, ref = mla_problem(inp), 512, oracle_mla
+    else:
+        inp = workloads.gqa_inputs(B=5, Hq=32, Hkv=4, D=128, page_size=16, seq_lens=lens,
+                                   num_pages=420, q_len=1, seed=93, device=DEV)
+        p, d_v, ref = gqa_problem(inp), 128, oracle_gqa
+    torch.cuda.synchronize()
+    log("proportional %s with planner choices np=%d bk=%d" % ((kind,) + tuple(g.decode_plan(p))))
+    out, lse = run_prop(p, d_v)
+    torch.cuda.synchronize()
+    ref_o, ref_l = ref(inp)
+    compare(out, lse, ref_o, ref_l, "proportional %s planner choices" % kind)
