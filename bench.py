@@ -37,6 +37,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sparse-sweep", action="store_true",
                     help="only time the sparse top-k split sweep and print it")
+    ap.add_argument("--proportional-sweep", action="store_true",
+                    help="only the equal-split vs length-proportional sweep over skewed batches")
     ap.add_argument("--branch-sweep", action="store_true",
                     help="only the planner-branch sweep (MLA 32/128 heads, GQA one kv head)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -430,6 +432,62 @@ def branch_sweep(stream, steps):
     return res
 
 
+def proportional_sweep(stream, steps):
+    """decode (np equal partitions per request) against decode_proportional (the same budget
+    spread by length on the device) as one long request of 131072 keys stands among shorter
+    ones: MLA, H = 64, batches of 8 and 32, graph-replayed calls."""
+    import torch
+    import gqa_plan_splits_amd as g
+    import workloads as w
+    res = {}
+    for B in (8, 32):
+        for short in (131072, 32768, 8192, 2048, 256):
+            lens = [131072] + [short] * (B - 1)
+            name = "mla_h64_b%d_1x131072_%dx%d" % (B, B - 1, short)
+            with torch.cuda.stream(stream):
+                inp = w.mla_inputs(B=B, q_len=1, H=64, seq_lens=lens, pool_rows=sum(lens), seed=5300,
+                                   device="cuda", name=name)
+            torch.cuda.synchronize()   # the inputs exist before any kernel on `stream` reads them
+            check_slots(inp)
+            p = g.mla_problem(inp.q_lat, inp.q_pe, inp.pool, inp.kv_indices, inp.kv_indptr,
+                              inp.seq_lens, batch=B, q_len=1, num_heads=64, max_num_keys=131072,
+                              scale=inp.scale, kv_scale=inp.kv_scale, d_v=512)
+            np_, bk = g.decode_plan(p)
+            out = torch.empty((p.rows, 512), dtype=torch.bfloat16, device="cuda")
+            lse = torch.empty((p.rows,), dtype=torch.float32, device="cuda")
+            ws = torch.empty((g.decode_workspace_bytes(p, np_) // 4 + 64,), dtype=torch.float32,
+                             device="cuda")
+            wsp = torch.empty((g.decode_proportional_workspace_bytes(p, np_) // 4 + 64,),
+                              dtype=torch.float32, device="cuda")
+            eq = lambda: g.decode(p, out, lse, np=np_, block_k=bk, workspace=ws, stream=stream)
+            prop = lambda: g.decode_proportional(p, out, lse, np=np_, block_k=bk, workspace=wsp,
+                                                 stream=stream)
+            # both captured, then replayed in five alternating rounds after a settling phase, so
+            # that clock drift weighs on both alike
+            graphs = []
+            for fn in (eq, prop):
+                for _ in range(3):
+                    fn()
+                torch.cuda.synchronize()
+                gr = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(gr, stream=stream):
+                    fn()
+                torch.cuda.synchronize()
+                graphs.append(gr)
+            with torch.cuda.stream(stream):
+                settle(graphs[0].replay, 150.0)
+                t_eq, t_prop = time_interleaved([graphs[0].replay, graphs[1].replay],
+                                                max(5, steps // 5 * 5), stream)
+            times = {"equal": t_eq * 1e3, "proportional": t_prop * 1e3}
+            res[name] = {"np": np_, "equal_us": round(times["equal"], 2),
+                         "proportional_us": round(times["proportional"], 2),
+                         "proportional_vs_equal": round(times["proportional"] / times["equal"], 3)}
+            print("# proportional %s %s" % (name, json.dumps(res[name])), file=sys.stderr, flush=True)
+            del inp, p, out, lse, ws, wsp, graphs
+            torch.cuda.empty_cache()
+    return res
+
+
 def sparse_sweep(stream, steps):
     """Sparse top-k MLA (64 heads, 2048 candidates per query) at every split count from 1 to 32
     per query count, beside the choices of the two planners: the wave-aligned one decode uses
@@ -539,6 +597,9 @@ def main():
     sm = g.device_sm_count()
     if args.sparse_sweep:
         print(json.dumps({"sparse_planner": sparse_sweep(stream, args.table_steps)}), flush=True)
+        return
+    if args.proportional_sweep:
+        print(json.dumps({"proportional": proportional_sweep(stream, args.table_steps)}), flush=True)
         return
     if args.branch_sweep:
         print(json.dumps({"planner_branches": branch_sweep(stream, args.table_steps)}), flush=True)
