@@ -12,20 +12,22 @@ constexpr int kPlanThreads = 256;
 constexpr int kPlanWaves = kPlanThreads / 64;
 constexpr int kPlanCached = 8192;   // requests whose key counts the search reads from LDS
 
-__device__ __forceinline__ int64_t keys_in_memory(const PlanArgs &a, int b) {
+// Keys of request b (negative counts as none), held to 2^31 - 1 so that the search below runs
+// in 32-bit arithmetic.
+__device__ __forceinline__ uint32_t keys_in_memory(const PlanArgs &a, int b) {
     int64_t n = a.seq_lens[b];
     if (a.extra_indptr) n += int64_t(a.extra_indptr[b + 1]) - a.extra_indptr[b];
-    return n > 0 ? n : 0;
+    return uint32_t(min(max(n, int64_t(0)), int64_t(INT32_MAX)));
 }
 
-__device__ __forceinline__ int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
-
-// Slots of a request with n keys under the common chunk c, and the chunk it uses.
-__device__ __forceinline__ void slots_of(const PlanArgs &a, int64_t n, int64_t c, int *slots,
+// Slots of a request with n keys under the common chunk c, and the chunk it uses (n, c < 2^31,
+// so n + c - 1 fits 32 bits).
+__device__ __forceinline__ void slots_of(const PlanArgs &a, uint32_t n, uint32_t c, int *slots,
                                          int *chunk) {
-    int64_t k = (n + c - 1) / c;
-    if (k > a.cap) {
-        c = round_up((n + a.cap - 1) / a.cap, a.block_k);
+    uint32_t k = (n + c - 1) / c;
+    if (k > uint32_t(a.cap)) {
+        const uint32_t bk = uint32_t(a.block_k), per = (n + a.cap - 1) / uint32_t(a.cap);
+        c = (per + bk - 1) / bk * bk;
         k = (n + c - 1) / c;
     }
     *slots = int(k);
@@ -46,19 +48,19 @@ __device__ __forceinline__ int64_t block_sum(int64_t v, int64_t *slot) {
 __global__ void __launch_bounds__(kPlanThreads) plan_proportional_kernel(const PlanArgs a) {
     __shared__ int64_t wave_sum[kPlanWaves];
     __shared__ int32_t wave_scan[kPlanWaves];
-    __shared__ int32_t cached[kPlanCached];
+    __shared__ uint32_t cached[kPlanCached];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const bool use_lds = a.batch <= kPlanCached;
     for (int b = threadIdx.x; use_lds && b < a.batch; b += kPlanThreads)
-        cached[b] = int32_t(min(keys_in_memory(a, b), int64_t(INT32_MAX)));
+        cached[b] = keys_in_memory(a, b);
     __syncthreads();
-    auto keys_of = [&](int b) -> int64_t { return use_lds ? cached[b] : keys_in_memory(a, b); };
+    auto keys_of = [&](int b) -> uint32_t { return use_lds ? cached[b] : keys_in_memory(a, b); };
 
     // The common partition length: the smallest multiple of block_k whose slots, summed over
     // the batch, fit the budget (slot counts only fall as it grows, so a binary search finds it;
     // at the longest request rounded up every request takes at most one slot).
     int64_t longest = 0;
-    for (int b = threadIdx.x; b < a.batch; b += kPlanThreads) longest = max(longest, keys_of(b));
+    for (int b = threadIdx.x; b < a.batch; b += kPlanThreads) longest = max(longest, int64_t(keys_of(b)));
     for (int m = 32; m; m >>= 1) longest = max(longest, __shfl_xor(longest, m, 64));
     if (lane == 0) wave_sum[wave] = longest;
     __syncthreads();
@@ -69,7 +71,7 @@ __global__ void __launch_bounds__(kPlanThreads) plan_proportional_kernel(const P
         int64_t n = 0;
         for (int b = threadIdx.x; b < a.batch; b += kPlanThreads) {
             int slots, chunk;
-            slots_of(a, keys_of(b), mid * a.block_k, &slots, &chunk);
+            slots_of(a, keys_of(b), uint32_t(mid * a.block_k), &slots, &chunk);
             n += slots;
         }
         if (block_sum(n, wave_sum) <= a.budget) hi = mid;
@@ -83,7 +85,7 @@ __global__ void __launch_bounds__(kPlanThreads) plan_proportional_kernel(const P
     for (int b0 = 0; b0 < a.batch; b0 += kPlanThreads) {
         const int b = b0 + threadIdx.x;
         int slots = 0, chunk = 0;
-        if (b < a.batch) slots_of(a, keys_of(b), common, &slots, &chunk);
+        if (b < a.batch) slots_of(a, keys_of(b), uint32_t(common), &slots, &chunk);
         int x = slots;   // inclusive scan within the wave
         for (int d = 1; d < 64; d <<= 1) {
             const int y = __shfl_up(x, d, 64);
