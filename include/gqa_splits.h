@@ -289,7 +289,8 @@ int decode(const gqa_decode_problem *p, int64_t np_or_0, int block_k_or_0, void 
  * partitions of chunk_b keys as that needs.  c is the smallest multiple of block_k for which
  * the sum of n_b is at most budget; if none is (budget below the number of non-empty requests),
  * c is the longest L_b rounded up to block_k.  Partition j of request b covers its keys
- * [j * chunk_b, (j + 1) * chunk_b).
+ * [j * chunk_b, (j + 1) * chunk_b).  A negative L_b counts as 0, and one above 2^31 - 1 as
+ * 2^31 - 1.
  *   seq_lens [batch], extra_indptr [batch + 1] or NULL: int32 device (inputs)
  *   part_start [batch + 1] int32 device (output): exclusive prefix sum of n_b
  *   part_chunk [batch] int32 device (output): chunk_b
