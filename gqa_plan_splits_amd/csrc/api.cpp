@@ -59,7 +59,7 @@ int check_problem(const gqa_decode_problem *p, Derived *d) {
             return GQA_ERR_INVALID_ARGUMENT;
         if (!p->kv || !p->q_pe || p->num_kv_heads != 1) return GQA_ERR_INVALID_ARGUMENT;
         if (!(p->kv_scale > 0.f) || !std::isfinite(p->kv_scale)) return GQA_ERR_INVALID_ARGUMENT;
-        // gfx950 converts OCP e4m3fn natively; the fnuz encoding has no kernel in this build.
+        // gfx950 converts OCP e4m3fn natively; the fnuz encoding has no kernel in this library.
         if (p->fp8_format == GQA_FP8_E4M3FNUZ) return GQA_ERR_UNSUPPORTED;
         const bool wide = p->d_qk == 576 && p->d_rope == 64 && p->d_v == 512;
         const bool sparse = p->d_qk == 512 && p->d_rope == 64 && p->d_v == 448;
@@ -362,7 +362,7 @@ extern "C" const char *status_string(int status) {
     switch (status) {
         case GQA_OK: return "ok";
         case GQA_ERR_INVALID_ARGUMENT: return "invalid argument";
-        case GQA_ERR_UNSUPPORTED: return "unsupported problem for this build";
+        case GQA_ERR_UNSUPPORTED: return "unsupported problem for this library";
         case GQA_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
         case GQA_ERR_LAUNCH_FAILED: return "kernel launch failed";
         case GQA_ERR_DEVICE: return "no usable HIP device";

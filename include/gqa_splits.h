@@ -55,7 +55,7 @@ typedef struct ihipStream_t *gqa_stream_t;
 typedef enum gqa_status {
     GQA_OK = 0,
     GQA_ERR_INVALID_ARGUMENT = -1,   /* null pointer, non-positive size, inconsistent sizes */
-    GQA_ERR_UNSUPPORTED = -2,        /* a valid problem this build has no kernel for */
+    GQA_ERR_UNSUPPORTED = -2,        /* a valid problem this library has no kernel for */
     GQA_ERR_WORKSPACE_TOO_SMALL = -3,
     GQA_ERR_LAUNCH_FAILED = -4,      /* the HIP runtime refused a launch */
     GQA_ERR_DEVICE = -5              /* no usable HIP device / device query failed */
