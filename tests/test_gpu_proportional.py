@@ -36,6 +36,7 @@ PLAN_CASES = [
     ("all empty", [0, 0, 0], 9, 8, 32, None),
     ("wide batch", None, 600 * 2, 8, 32, None),          # 600 requests: three scan rounds
     ("second cache", [100, 2048, 0, 7], 16, 16, 64, [0, 64, 64, 1000, 1001]),
+    ("past the LDS cache", "big", 9000 * 2, 16, 32, None),   # 9000 requests: counts read from memory
 ]
 
 
@@ -43,6 +44,8 @@ PLAN_CASES = [
 def test_plan_tables_match_oracle(name, lens, budget, cap, bk, extra):
     if lens is None:
         lens = np.random.default_rng(5).integers(0, 40000, 600).tolist()
+    elif lens == "big":
+        lens = np.random.default_rng(6).integers(0, 3000, 9000).tolist()
     B = len(lens)
     log("proportional plan %s B=%d budget=%d cap=%d bk=%d" % (name, B, budget, cap, bk))
     seq = torch.tensor(lens, dtype=torch.int32, device=DEV)
