@@ -178,3 +178,16 @@ def test_proportional_with_planner_choices(kind):
     torch.cuda.synchronize()
     ref_o, ref_l = ref(inp)
     compare(out, lse, ref_o, ref_l, "proportional %s planner choices" % kind)
+
+
+def test_sparse_proportional_many_queries():
+    # 100 queries: the slot lookup in the MLA kernel walks the prefix table 64 requests at a time
+    inp = workloads.sparse_mla_inputs(num_queries=100, topk=256, cache_rows=8192, seed=4700,
+                                      invalid_frac=0.05, all_invalid=(70,), device=DEV)
+    torch.cuda.synchronize()
+    log("sparse proportional 100 queries")
+    out, lse = run_prop(mla_problem(inp), 448, 2, 0, 32)
+    torch.cuda.synchronize()
+    ref_o, ref_l = oracle_mla(inp)
+    compare(out, lse, ref_o, ref_l, "sparse proportional 100 queries")
+    assert torch.all(lse[70 * 64:71 * 64] == -float("inf"))
