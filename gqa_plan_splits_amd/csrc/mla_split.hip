@@ -12,22 +12,26 @@
 // cache (FlashInfer sparse planner page, Parameters: extra_topk) a request's key list continues
 // past its pool keys with its second-cache rows, of the same format and scale.
 //
+// Arithmetic.  QK^T multiplies the bf16 query by the stored fp8 K decoded exactly to bf16, on
+// the bf16 MFMA: every product is exact and the sums are fp32.  (gfx950's block-scaled fp8 MFMA
+// would run an exact fp8 hi/lo split of the query at the same speed, but it aligns its 128
+// products to about 15 bits below the largest one, an error of order 2^-15 max|q k| on every
+// score, which the base-2 LSE of a row with few keys or a peaky softmax shows directly.)  The
+// softmax weights p = 2^(score - m + 8), m the ceiling of the row's largest base-2 score so far,
+// are stored as fp16 (11 significant bits); PV multiplies them by V decoded exactly to fp16 on
+// the fp16 MFMA.  The output is normalized by the sum of the stored weights, so a dominant key
+// carries no rounding of its own weight into it; the LSE comes from the sum of the exact ones.
+//
 // Work split (512 threads = 8 waves, one CTA per CU; waves w and w + 4 share SIMD w):
 //   - Score waves 0-3: wave w computes S^T = K Q^T for query rows 16 w .. 16 w + 15 against the 64
-//     keys of a tile on the block-scaled fp8 MFMA v_mfma_scale_f32_16x16x128_f8f6f4 (unit scales),
-//     one accumulator per 16-key block, then the rows' softmax.  K is used as stored.  A bf16 query
-//     row, scaled by a power of two so its largest element lies in [128, 256), is the exact sum of
-//     two e4m3 vectors (hi = nearest, lo = remainder) except below e4m3's subnormal step; each
-//     product runs twice.  The row maximum of a tile is kept as an integer (the ceiling of the
-//     base-2 score), so probabilities of different tiles differ by exact powers of two; they go to
-//     LDS as fp8 hi/lo pairs of p * 2^8 (p <= 1), with the maximum and two row sums: of the
-//     quantized probabilities (the weights PV applies, which normalize the output, so that a
-//     dominant key carries no quantization error into it) and of the exact ones (which give the
-//     log-sum-exp).
+//     keys of a tile on v_mfma_f32_16x16x32_bf16, one accumulator per 16-key block, then the
+//     rows' online softmax.  It keeps each row's running maximum and both sums, and hands the
+//     value waves P(t) (64 rows x 64 keys, fp16) and the rows' maxima and sums through LDS.
 //   - Value waves 4-7: wave 4 + v accumulates output columns 128 v .. +127 (line v of the key rows)
-//     for all 64 rows on the same MFMA: V^T comes from the fp8 tile through ds_read_b64_tr_b8, P^T
-//     from LDS, and the power of two that aligns the tile's row maximum with the row's running
-//     maximum is the MFMA's per-lane B scale.  The value waves also move the data: wave 4 + v copies line v
+//     for all 64 rows on v_mfma_f32_32x32x16_f16: V^T comes from the fp8 tile through
+//     ds_read_b64_tr_b8 (decoded to fp16), P^T from LDS; when a row's maximum moved, its
+//     accumulators are first scaled by the exact power of two 2^(m_old - m_new).  The value
+//     waves also move the data: wave 4 + v copies line v
 //     of every key of a tile (and a quarter of the 64-byte rope tails of 576-byte rows) straight
 //     from HBM into LDS with global_load_lds_dwordx4, two tiles ahead, after loading the tile's
 //     slot ids the same way two tiles before that.  The copies are issued from inline assembly and
@@ -83,8 +87,8 @@ struct MlaLayout {
     static constexpr bool kTail = DQK == 576;               // rope tails in their own ring
     static constexpr int kTailOff = kLineSlots * 32768;
     static constexpr int kPOff = kTailOff + (kTail ? kTailSlots * 4096 : 0);
-    static constexpr int kMlOff = kPOff + 2 * 8192;         // P [2][hi, lo][64 rows][64 keys]
-    static constexpr int kMlBytes = 3 * 256;                // M, Q, E [64 rows]
+    static constexpr int kMlOff = kPOff + 2 * 8192;         // P [2][64 rows][64 keys] fp16
+    static constexpr int kMlBytes = 3 * 256;                // m, lq, le [64 rows]
     static constexpr int kIdOff = kMlOff + 2 * kMlBytes;
     static constexpr int kBadOff = kIdOff + kIdSlots * 256;   // per tile: 64-bit mask of skipped keys
     static constexpr int kLdsBytes = kBadOff + kIdSlots * 8;
@@ -103,6 +107,30 @@ __device__ __forceinline__ int line_off(int line, int pos, int c) {
 __device__ __forceinline__ int tail_off(int pos, int c) { return pos * 64 + ((c ^ swz_tail(pos)) << 4); }
 // Slot-list index (0..63, relative to the tile) of the key at tile position pos.
 __device__ __forceinline__ int key_of_pos(int pos) { return 8 * (pos & 7) + (pos >> 3); }
+
+// P rows of a tile: 128 bytes per query row (64 fp16 weights in tile-position order), the
+// 16-byte slot q (weights 8 q .. 8 q + 7) stored at slot q ^ ((row >> 1) & 7).  The value waves'
+// reads of one slot by 16 rows whose bits 1-3 differ (with either bit 0) then touch 16 distinct
+// 16-byte slots of a 256-byte bank row.
+__device__ __forceinline__ int p_slot(int row, int q) { return row * 128 + ((q ^ ((row >> 1) & 7)) << 4); }
+
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+// Two fp32 to packed fp16, round to nearest even (v_cvt_pk_f16_f32).
+__device__ __forceinline__ f16x2 pack_f16x2(float a, float b) {
+    f16x2 r;
+    r.x = static_cast<_Float16>(a);
+    r.y = static_cast<_Float16>(b);
+    return r;
+}
+// Eight OCP e4m3fn bytes to fp16, exactly (every e4m3fn value is an fp16 value).
+__device__ __forceinline__ f16x8 fp8x8_to_f16x8(uint32_t lo, uint32_t hi) {
+    const f16x2 a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 1.0f, false);
+    const f16x2 b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 1.0f, true);
+    const f16x2 c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 1.0f, false);
+    const f16x2 d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 1.0f, true);
+    return f16x8{a.x, a.y, b.x, b.y, c.x, c.y, d.x, d.y};
+}
 
 // Direct HBM -> LDS copies: lane L's bytes land at m0 + 16 L (or 4 L).  Every pool row is read
 // once, so the copies are non-temporal (nt): on gfx950 that streaming hint lifts the bandwidth of
@@ -132,16 +160,6 @@ template <int DLAT>
 __device__ __forceinline__ u32x4 load_q8(const uint16_t *ql, const uint16_t *qp, int d) {
     return d < DLAT ? *reinterpret_cast<const u32x4 *>(ql + d)
                     : *reinterpret_cast<const u32x4 *>(qp + (d - DLAT));
-}
-
-// x (|x| < 448) -> (hi, lo) e4m3 quads: hi = nearest, lo = nearest to the remainder.
-__device__ __forceinline__ void split_fp8x4(float x0, float x1, float x2, float x3, int &hi, int &lo) {
-    hi = __builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, 0, false);
-    hi = __builtin_amdgcn_cvt_pk_fp8_f32(x2, x3, hi, true);
-    const f32x2 h01 = __builtin_amdgcn_cvt_pk_f32_fp8(hi, false);
-    const f32x2 h23 = __builtin_amdgcn_cvt_pk_f32_fp8(hi, true);
-    lo = __builtin_amdgcn_cvt_pk_fp8_f32(x0 - h01.x, x1 - h01.y, 0, false);
-    lo = __builtin_amdgcn_cvt_pk_fp8_f32(x2 - h23.x, x3 - h23.y, lo, true);
 }
 
 // Max / sum over the four lanes l, l ^ 16, l ^ 32, l ^ 48 (one per 16-lane row of a 16x16 MFMA
@@ -217,21 +235,24 @@ __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const MlaSplitAr
 
     if (wave < 4) {
         // ================================ score wave ================================
-        // Score wave w: query rows 16 w .. 16 w + 15 against all 64 keys of a tile, on the 16x16x128
-        // block-scaled fp8 MFMA (unit scales), one accumulator per 16-key block.  Lane (n16, g)
-        // holds bytes 32 g .. 32 g + 31 of each 128-byte contraction step; the 64-byte rope tail of
-        // 576-byte rows is one more step whose upper half is zero.
+        // Score wave w: query rows 16 w .. 16 w + 15 against all 64 keys of a tile, on the
+        // 16x16x32 bf16 MFMA, one accumulator per 16-key block.  The stored fp8 K bytes are
+        // converted exactly to bf16 in registers, so every product q * k is exact and the sums
+        // are plain fp32 (the block-scaled fp8 MFMA aligns its 128 products with about 15 bits
+        // below the largest, which puts an error of order 2^-15 max|q k| on every score).
+        // Lane (n16, g) reads bytes 32 g .. 32 g + 31 of each 128-byte line of its key: the four
+        // 8-byte pieces feed four MFMAs, whose k slots 8 g .. 8 g + 7 are dims 128 s + 32 g + 8 i
+        // + 0..7 (the query operand takes the same dims).  The 64-byte rope tail of 576-byte rows
+        // is two more MFMAs: lane g takes dims 32 (g & 1) + 8 (g >> 1) + 0..7 of the tail in the
+        // first and 16 more in the second.
         const int n16 = lane & 15, g = lane >> 4;
         const int rl = 16 * wave + n16;         // row within the block
         const bool row_ok = rl < nrows;
-        constexpr int NS = (DQK + 127) / 128;   // contraction steps
-        // MFMAs per 16-key block: hi and lo products of every step, except that the rope tail of
-        // 576-byte rows needs one: lanes g >= 2, whose K bytes repeat those of lanes g - 2, hold the
-        // lo part of the query tail where the hi part of the other lanes is, so one product sums
-        // K (Q_hi + Q_lo) over the 64 tail bytes.
+        constexpr int NL = DQK / 128;           // full 128-byte lines per row
+        constexpr int NQ = 4 * NL + (T::kTail ? 2 : 0);   // MFMAs per 16-key block
         int p_end;                              // keys visible to this row
-        float c_row;                            // base-2 score per unit of the raw product
-        i32x8 qhi[NS], qlo[NS];
+        const float c_row = a.score_scale;      // base-2 score per unit of the raw product
+        bf16x8 qv[NQ];                          // B operands: this lane's query dims per MFMA
         {
             const int r = row0 + rl;
             const int t = row_ok ? r / a.H : 0;
@@ -240,97 +261,72 @@ __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const MlaSplitAr
             const int64_t tok = int64_t(b) * a.q_len + t;
             const uint16_t *ql = a.q + tok * a.q_st_tok + int64_t(hh) * a.q_st_head;
             const uint16_t *qp = a.q_pe + tok * a.qpe_st_tok + int64_t(hh) * a.qpe_st_head;
-            // piece pc (0..3) of step s: 8 values at d = 128 s + 32 g + 8 pc (none past DQK; in the
-            // rope tail lanes g >= 2 load those of lanes g - 2); all loaded at once (one memory
-            // round trip), kept in registers for the split
-            auto gq = [&](int s) { return T::kTail && s == NS - 1 ? (g & 1) : g; };
-            auto piece_ok = [&](int s, int pc) { return row_ok && 128 * s + 32 * gq(s) + 8 * pc < DQK; };
-            u32x4 qraw[NS][4];
+            auto piece = [&](int d) {
+                return as_bf16x8(row_ok ? load_q8<DLAT>(ql, qp, d) : u32x4{0u, 0u, 0u, 0u});
+            };
 #pragma unroll
-            for (int s = 0; s < NS; ++s)
+            for (int s = 0; s < NL; ++s)
 #pragma unroll
-                for (int pc = 0; pc < 4; ++pc)
-                    qraw[s][pc] = piece_ok(s, pc) ? load_q8<DLAT>(ql, qp, 128 * s + 32 * gq(s) + 8 * pc)
-                                                  : u32x4{0u, 0u, 0u, 0u};
-            float mx = 0.f;
-#pragma unroll
-            for (int s = 0; s < NS; ++s)
-#pragma unroll
-                for (int pc = 0; pc < 4; ++pc)
-#pragma unroll
-                    for (int w = 0; w < 4; ++w)
-                        mx = fmaxf(mx, fmaxf(fabsf(bf16_lo(qraw[s][pc][w])), fabsf(bf16_hi(qraw[s][pc][w]))));
-            mx = rows4_max(mx);
-            int ex = 0;
-            if (mx > 0.f) frexpf(mx, &ex);            // mx = f * 2^ex, f in [0.5, 1)
-            const float qs = ldexpf(1.f, 8 - ex);     // row maximum scaled into [128, 256)
-            c_row = a.score_scale * ldexpf(1.f, ex - 8);
-#pragma unroll
-            for (int s = 0; s < NS; ++s)
-#pragma unroll
-                for (int pc = 0; pc < 4; ++pc) {
-                    const u32x4 w4 = qraw[s][pc];
-#pragma unroll
-                    for (int w = 0; w < 4; w += 2) {
-                        int hi, lo;
-                        split_fp8x4(bf16_lo(w4[w]) * qs, bf16_hi(w4[w]) * qs,
-                                    bf16_lo(w4[w + 1]) * qs, bf16_hi(w4[w + 1]) * qs, hi, lo);
-                        qhi[s][2 * pc + w / 2] = hi;
-                        qlo[s][2 * pc + w / 2] = lo;
-                    }
-                }
-            if (T::kTail && g >= 2) qhi[NS - 1] = qlo[NS - 1];
+                for (int i = 0; i < 4; ++i) qv[4 * s + i] = piece(128 * s + 32 * g + 8 * i);
+            if constexpr (T::kTail) {
+                qv[4 * NL] = piece(512 + 32 * (g & 1) + 8 * (g >> 1));
+                qv[4 * NL + 1] = piece(512 + 32 * (g & 1) + 16 + 8 * (g >> 1));
+            }
         }
 
         // Loop-invariant LDS offsets of this lane's K operand (key at tile position 16 kbk + n16,
         // chunks 2 g and 2 g + 1 of line s; the swizzle does not depend on kbk, so 16-key block kbk
-        // adds 2048 bytes, line s 8192).  Rope tails: chunks 2 g, 2 g + 1 (g < 2), block kbk
-        // adds 1024 bytes.
+        // adds 2048 bytes, line s 8192).  Rope tails: 8 bytes at 8 (g >> 1) of tail chunks
+        // 2 (g & 1) and 2 (g & 1) + 1; block kbk adds 1024 bytes.
         const int k_off0 = line_off(0, n16, 2 * g), k_off1 = line_off(0, n16, 2 * g + 1);
-        const int k_tail0 = T::kTailOff + tail_off(n16, (2 * g) & 3);
-        const int k_tail1 = T::kTailOff + tail_off(n16, (2 * g + 1) & 3);
-        // P words of this lane: keys 16 kbk + 4 g .. + 3 of row rl, 16-byte chunk kbk of the 64-byte
-        // row, chunks swizzled by the row
-        const int p_sw = (rl >> 2) & 3;
+        const int k_tail0 = T::kTailOff + tail_off(n16, 2 * (g & 1)) + 8 * (g >> 1);
+        const int k_tail1 = T::kTailOff + tail_off(n16, 2 * (g & 1) + 1) + 8 * (g >> 1);
+        // P of this lane: the fp16 weights of tile positions 16 kbk + 4 g .. + 3 of row rl, the
+        // 8 bytes at 8 (g & 1) of 16-byte slot 2 kbk + (g >> 1) of the row's 128 bytes (p_slot).
         int p_wr[4];
 #pragma unroll
-        for (int kbk = 0; kbk < 4; ++kbk) p_wr[kbk] = rl * 64 + ((kbk ^ p_sw) << 4) + 4 * g;
+        for (int kbk = 0; kbk < 4; ++kbk) p_wr[kbk] = p_slot(rl, 2 * kbk + (g >> 1)) + 8 * (g & 1);
         // Score i of block kbk of this lane is tile position 16 kbk + 4 g + i, slot-list index
         // 32 (g & 1) + (g >> 1) + 8 i + 2 kbk (key_of_pos).
         const int kidx_base = 32 * (g & 1) + (g >> 1);
 
-        // K operand reads and the MFMAs of 16-key block kbk of the scores of tile t (9 for
-        // 576-byte rows, 8 for 512-byte rows).
+        // K operand reads, their exact conversion to bf16 and the MFMAs of 16-key block kbk of
+        // the scores of tile t (18 for 576-byte rows, 16 for 512-byte rows), in two accumulator
+        // chains so that no MFMA waits on the one just before it.
         auto qk_block = [&](int t, int kbk, f32x4 &sacc) {
             const uint8_t *lb = lds + (t % kLineSlots) * 32768 + 2048 * kbk;
             const uint8_t *tlb = lds + (t % kTailSlots) * 4096 + 1024 * kbk;
-            sacc = f32x4{0.f, 0.f, 0.f, 0.f};
-            f32x4 slo = f32x4{0.f, 0.f, 0.f, 0.f};
+            f32x4 acc0 = f32x4{0.f, 0.f, 0.f, 0.f};
+            f32x4 acc1 = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int s = 0; s < NS; ++s) {
-                u32x4 lo16, hi16;
-                if (T::kTail && s == NS - 1) {
-                    // lanes g >= 2 read the chunks of lanes g - 2 (their query operand is the lo tail)
-                    lo16 = *reinterpret_cast<const u32x4 *>(tlb + k_tail0);
-                    hi16 = *reinterpret_cast<const u32x4 *>(tlb + k_tail1);
-                } else {
-                    lo16 = *reinterpret_cast<const u32x4 *>(lb + 8192 * s + k_off0);
-                    hi16 = *reinterpret_cast<const u32x4 *>(lb + 8192 * s + k_off1);
-                }
-                const i32x8 kraw = i32x8{int(lo16.x), int(lo16.y), int(lo16.z), int(lo16.w),
-                                         int(hi16.x), int(hi16.y), int(hi16.z), int(hi16.w)};
-                // hi and lo products in two chains, so consecutive MFMAs do not depend on each other
-                sacc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(kraw, qhi[s], sacc, 0, 0, 0, 127, 0, 127);
-                if (!(T::kTail && s == NS - 1))
-                    slo = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(kraw, qlo[s], slo, 0, 0, 0, 127, 0, 127);
+            for (int s = 0; s < NL; ++s) {
+                const u32x4 lo16 = *reinterpret_cast<const u32x4 *>(lb + 8192 * s + k_off0);
+                const u32x4 hi16 = *reinterpret_cast<const u32x4 *>(lb + 8192 * s + k_off1);
+                acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp8x8_to_bf16x8(lo16.x, lo16.y), qv[4 * s], acc0, 0, 0, 0);
+                acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp8x8_to_bf16x8(lo16.z, lo16.w), qv[4 * s + 1], acc1, 0, 0, 0);
+                acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp8x8_to_bf16x8(hi16.x, hi16.y), qv[4 * s + 2], acc0, 0, 0, 0);
+                acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp8x8_to_bf16x8(hi16.z, hi16.w), qv[4 * s + 3], acc1, 0, 0, 0);
             }
-            sacc += slo;
+            if constexpr (T::kTail) {
+                const u32x2 t0 = *reinterpret_cast<const u32x2 *>(tlb + k_tail0);
+                const u32x2 t1 = *reinterpret_cast<const u32x2 *>(tlb + k_tail1);
+                acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp8x8_to_bf16x8(t0.x, t0.y), qv[4 * NL], acc0, 0, 0, 0);
+                acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp8x8_to_bf16x8(t1.x, t1.y), qv[4 * NL + 1], acc1, 0, 0, 0);
+            }
+            sacc = acc0 + acc1;
         };
 
-        // Softmax of this lane's row over tile t in base 2 with an integer maximum m:
-        // p * 2^8 = 2^(score - m + 8) in (0, 256], written to P(t) with m and the row sums.
+        // Online softmax of this lane's row in base 2 with an integer running maximum m (the
+        // ceiling of the largest base-2 score so far): a key's weight is p = 2^(score - m + 8) in
+        // (0, 256], stored in fp16 (11 significant bits).  The row's sums of the stored weights
+        // (lq, which normalizes the output: a dominant key then carries no rounding of its own
+        // weight into it) and of the exact weights (le, which gives the log-sum-exp) are kept
+        // here, and rescaled by the exact power of two 2^(m_old - m_new) when m moves.  All four
+        // lanes of a row hold the same values.
+        int m_run = kNoMax;
+        float lq_run = 0.f, le_run = 0.f;
         struct Soft {
-            float bias, esum, qsum;
+            float bias, esum, qsum, alpha;
             int m;
         };
         // Masked variant (tiles past some row's window or the partition end, and tiles with
@@ -358,8 +354,10 @@ __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const MlaSplitAr
             for (int kbk = 0; kbk < 4; ++kbk)
                 m4[kbk] = fmaxf(fmaxf(sacc[kbk][0], sacc[kbk][1]), fmaxf(sacc[kbk][2], sacc[kbk][3]));
             const float mx = rows4_max(fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3])));
+            const int mt = mx == kNegInf ? kNoMax : int(ceilf(mx * c_row));
             Soft sf;
-            sf.m = mx == kNegInf ? kNoMax : int(ceilf(mx * c_row));
+            sf.m = max(m_run, mt);
+            sf.alpha = ldexpf(1.f, m_run - sf.m);
             sf.bias = float(8 - sf.m);
             sf.esum = sf.qsum = 0.f;
             return sf;
@@ -369,27 +367,24 @@ __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const MlaSplitAr
             const float p1 = fast_exp2(fmaf(sc[1], c_row, sf.bias));
             const float p2 = fast_exp2(fmaf(sc[2], c_row, sf.bias));
             const float p3 = fast_exp2(fmaf(sc[3], c_row, sf.bias));
-            int whi, wlo;
-            split_fp8x4(p0, p1, p2, p3, whi, wlo);
-            const f32x2 h01 = __builtin_amdgcn_cvt_pk_f32_fp8(whi, false);
-            const f32x2 h23 = __builtin_amdgcn_cvt_pk_f32_fp8(whi, true);
-            const f32x2 l01 = __builtin_amdgcn_cvt_pk_f32_fp8(wlo, false);
-            const f32x2 l23 = __builtin_amdgcn_cvt_pk_f32_fp8(wlo, true);
+            const f16x2 h01 = pack_f16x2(p0, p1), h23 = pack_f16x2(p2, p3);
             sf.esum += (p0 + p1) + (p2 + p3);
-            sf.qsum += ((h01.x + l01.x) + (h01.y + l01.y)) + ((h23.x + l23.x) + (h23.y + l23.y));
-            uint8_t *pb = P + (t & 1) * 8192;
-            *reinterpret_cast<int *>(pb + p_wr[kbk]) = whi;
-            *reinterpret_cast<int *>(pb + 4096 + p_wr[kbk]) = wlo;
+            sf.qsum += (float(h01.x) + float(h01.y)) + (float(h23.x) + float(h23.y));
+            *reinterpret_cast<u32x2 *>(P + (t & 1) * 8192 + p_wr[kbk]) =
+                u32x2{__builtin_bit_cast(uint32_t, h01), __builtin_bit_cast(uint32_t, h23)};
         };
         auto sm_finish = [&](int t, Soft &sf) {
             const float esum = rows4_sum(sf.esum);
             const float qsum = rows4_sum(sf.qsum);
+            lq_run = fmaf(lq_run, sf.alpha, qsum);
+            le_run = fmaf(le_run, sf.alpha, esum);
+            m_run = sf.m;
             // the four lanes of a row hold the same values and all store them (no branch, which
             // would split the step's scheduling region)
             uint8_t *mlb = ML + (t & 1) * T::kMlBytes + rl * 4;
-            *reinterpret_cast<int *>(mlb) = sf.m;
-            *reinterpret_cast<float *>(mlb + 256) = qsum;
-            *reinterpret_cast<float *>(mlb + 512) = esum;
+            *reinterpret_cast<int *>(mlb) = m_run;
+            *reinterpret_cast<float *>(mlb + 256) = lq_run;
+            *reinterpret_cast<float *>(mlb + 512) = le_run;
         };
 
         // Step t: the MFMAs of tile t + 1 (the last tile again at the end; its scores are then
@@ -534,10 +529,13 @@ __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const MlaSplitAr
     auto cnt_rows = [&](int j) { return j >= 0 && j < ntiles ? NC : 0; };
     auto cnt_ids = [&](int j) { return id_loader && j >= 0 && j < ntiles ? 1 : 0; };
 
-    // ---- PV operands.  V^T (A operand) of column block cb: lane (m, h) holds keys 16 h + 0..15
-    // (bytes 0-15) and 32 + 16 h + 0..15 (bytes 16-31) of column m; a transposed read hands a
-    // 16-lane group 8 keys of 16 columns: lane s = 2 k + hh points at key k of the read, bytes
-    // 8 hh.. of the chunk (cb for lanes 0-15 of each half-wave, cb ^ 4 for lanes 16-31).
+    // ---- PV on v_mfma_f32_32x32x16_f16 as O^T = V^T P^T, four MFMAs per 64 keys.  V^T (A
+    // operand) of column block cb: transposed read r hands lane (m, h) 8 fp8 bytes, keys
+    // 16 h + 8 (r & 1) + 32 (r >> 1) + 0..7 of column m (a 16-lane group reads 8 keys of 16
+    // columns: lane s = 2 k + hh points at key k of the read, bytes 8 hh.. of the chunk: cb for
+    // lanes 0-15 of each half-wave, cb ^ 4 for lanes 16-31); converted exactly to fp16, they are
+    // the k slots 8 h .. 8 h + 7 of MFMA r.  P^T (B operand) of MFMA r for row 32 rb + n: the
+    // same keys' fp16 weights, P slot 2 h + (r & 1) + 4 (r >> 1) of the row.
     const int kk = (lane & 15) >> 1, hh = lane & 1, half = (lane >> 4) & 1;
     int v_off[4][4];
 #pragma unroll
@@ -545,18 +543,13 @@ __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const MlaSplitAr
 #pragma unroll
         for (int r = 0; r < 4; ++r)
             v_off[cb][r] = line_off(v, 16 * h + 8 * (r & 1) + 32 * (r >> 1) + kk, half ? (cb ^ 4) : cb) + 8 * hh;
-    //   P^T (B operand) of row 32 rb + n: keys 16 h .. (chunk h) and 32 + 16 h .. (chunk 2 + h)
-    int p_rd[2][2];
+    int p_rd[2][4];
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-        const int row = 32 * rb + n, sw = (row >> 2) & 3;
-        p_rd[rb][0] = row * 64 + ((h ^ sw) << 4);
-        p_rd[rb][1] = row * 64 + (((2 + h) ^ sw) << 4);
-    }
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) p_rd[rb][r] = p_slot(32 * rb + n, 2 * h + (r & 1) + 4 * (r >> 1));
 
-    int mc[2] = {kNoMax, kNoMax};   // running integer maxima of rows n and 32 + n
-    float lq[2] = {0.f, 0.f};       // running sums of the applied (quantized) weights
-    float le[2] = {0.f, 0.f};       // running sums of 2^(score - mc)
+    int mc[2] = {kNoMax, kNoMax};   // the running maxima of rows n and 32 + n the accumulators hold
     f32x16 oacc[2][4];
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb)
@@ -565,58 +558,42 @@ __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const MlaSplitAr
 #pragma unroll
             for (int i = 0; i < 16; ++i) oacc[rb][cb][i] = 0.f;
 
-    // PV of tile t: running maxima and sums, the rescale when a maximum moved, then 16 MFMAs.
+    // PV of tile t: the rescale when a row's running maximum moved, then 32 MFMAs.
     auto pv = [&](int t) {
         const uint8_t *pbuf = P + (t & 1) * 8192;
         const uint8_t *mlb = ML + (t & 1) * T::kMlBytes;
-        int sc[2];
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb) {
-            const int row = 32 * rb + n;
-            const int mt = *reinterpret_cast<const int *>(mlb + row * 4);
-            const float qt = *reinterpret_cast<const float *>(mlb + 256 + row * 4);
-            const float et = *reinterpret_cast<const float *>(mlb + 512 + row * 4);
-            const int m_new = max(mc[rb], mt);
+            const int m_new = *reinterpret_cast<const int *>(mlb + (32 * rb + n) * 4);
             const float alpha = ldexpf(1.f, mc[rb] - m_new);
-            lq[rb] = lq[rb] * alpha + ldexpf(qt, mt - m_new - 8);
-            le[rb] = le[rb] * alpha + ldexpf(et, mt - m_new - 8);
             mc[rb] = m_new;
-            sc[rb] = max(0, 127 - 8 + mt - m_new);
             if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
 #pragma unroll
                 for (int cb = 0; cb < 4; ++cb) oacc[rb][cb] *= alpha;
             }
         }
-        i32x8 ph[2], pl[2];
+        f16x8 pw[2][4];
 #pragma unroll
-        for (int rb = 0; rb < 2; ++rb) {
-            const u32x4 a0 = *reinterpret_cast<const u32x4 *>(pbuf + p_rd[rb][0]);
-            const u32x4 a1 = *reinterpret_cast<const u32x4 *>(pbuf + p_rd[rb][1]);
-            const u32x4 b0 = *reinterpret_cast<const u32x4 *>(pbuf + 4096 + p_rd[rb][0]);
-            const u32x4 b1 = *reinterpret_cast<const u32x4 *>(pbuf + 4096 + p_rd[rb][1]);
-            ph[rb] = i32x8{int(a0.x), int(a0.y), int(a0.z), int(a0.w), int(a1.x), int(a1.y), int(a1.z), int(a1.w)};
-            pl[rb] = i32x8{int(b0.x), int(b0.y), int(b0.z), int(b0.w), int(b1.x), int(b1.y), int(b1.z), int(b1.w)};
-        }
+        for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                pw[rb][r] = __builtin_bit_cast(f16x8, *reinterpret_cast<const u32x4 *>(pbuf + p_rd[rb][r]));
         const uint8_t *lb = lds + (t % kLineSlots) * 32768;
 #pragma unroll
         for (int cb = 0; cb < 4; ++cb) {
-            int2v raw[4];
+            f16x8 vt[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int2v raw = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                    (__attribute__((address_space(3))) int2v *)(lb + v_off[cb][r]));
+                vt[r] = fp8x8_to_f16x8(uint32_t(raw.x), uint32_t(raw.y));
+            }
+            // the two row blocks alternate, so no MFMA waits on the one just before it
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-                raw[r] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-                    (__attribute__((address_space(3))) int2v *)(lb + v_off[cb][r]));
-            const i32x8 vt = i32x8{raw[0].x, raw[0].y, raw[1].x, raw[1].y,
-                                   raw[2].x, raw[2].y, raw[3].x, raw[3].y};
-            // hi products of both row blocks, then the lo products: no MFMA waits on the one
-            // just before it
 #pragma unroll
-            for (int rb = 0; rb < 2; ++rb)
-                oacc[rb][cb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                    vt, ph[rb], oacc[rb][cb], 0, 0, 0, 127, 0, sc[rb]);
-#pragma unroll
-            for (int rb = 0; rb < 2; ++rb)
-                oacc[rb][cb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                    vt, pl[rb], oacc[rb][cb], 0, 0, 0, 127, 0, sc[rb]);
+                for (int rb = 0; rb < 2; ++rb)
+                    oacc[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vt[r], pw[rb][r], oacc[rb][cb], 0, 0, 0);
         }
     };
 
@@ -658,8 +635,15 @@ __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const MlaSplitAr
         // partial row: [row, np] or, with planned slots, [slot, rows_per_req]
         const int64_t prow = a.part_start ? int64_t(rest) * a.rows_per_req + row0 + rl
                                           : row * a.np + part;
-        const float inv = lq[rb] > 0.f ? a.out_scale / lq[rb] : 0.f;
-        const float lse2 = le[rb] > 0.f ? float(mc[rb]) + __log2f(le[rb]) : kNegInf;
+        // the sums of the row over all its tiles, stored with the last tile's maximum
+        float lq = 0.f, le = 0.f;
+        if (ntiles > 0) {
+            const uint8_t *mlb = ML + ((ntiles - 1) & 1) * T::kMlBytes + rl * 4;
+            lq = *reinterpret_cast<const float *>(mlb + 256);
+            le = *reinterpret_cast<const float *>(mlb + 512);
+        }
+        const float inv = lq > 0.f ? a.out_scale / lq : 0.f;
+        const float lse2 = le > 0.f ? float(mc[rb] - 8) + __log2f(le) : kNegInf;
 #pragma unroll
         for (int cb = 0; cb < 4; ++cb)
 #pragma unroll

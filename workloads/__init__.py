@@ -296,3 +296,101 @@ SPARSE_QUERY_COUNTS = (24, 32, 34, 64, 128, 256)
 def sparse_topk(num_queries: int, device="cpu"):
     return sparse_mla_inputs(num_queries=num_queries, seed=4000, device=device,
                              name="sparse_mla_h64_topk2048_nq%d" % num_queries)
+
+
+# --------------------------------------------------------------------------------------------
+# Wide-dynamic-range variants of an MLA input (numerics stress cases).  Each returns a new
+# MlaInputs with the same requests and slot lists; only values change.
+# --------------------------------------------------------------------------------------------
+
+def scaled_queries(inp: MlaInputs, mul: float) -> MlaInputs:
+    """q_lat and q_pe multiplied by `mul` (a power of two keeps the bf16 values exact), so that
+    scores spread over many octaves within and across key tiles."""
+    return dataclasses.replace(inp, q_lat=(inp.q_lat.float() * mul).to(torch.bfloat16),
+                               q_pe=(inp.q_pe.float() * mul).to(torch.bfloat16))
+
+
+def wide_range_queries(inp: MlaInputs, octaves: float = 20.0, mul: float = 1.0,
+                       seed: int = 0) -> MlaInputs:
+    """Query elements of random sign whose magnitudes are log-uniform over `octaves` binary
+    octaves below `mul`: every row holds values from about 2^-octaves to 1 of its maximum."""
+    dev = inp.q_lat.device
+    g = _gen("cpu", seed)
+
+    def draw(shape):
+        mag = torch.exp2(-octaves * torch.rand(shape, generator=g, dtype=torch.float64))
+        sgn = torch.where(torch.rand(shape, generator=g) < 0.5, -1.0, 1.0).double()
+        return (sgn * mag * mul).to(torch.bfloat16).to(dev)
+
+    return dataclasses.replace(inp, q_lat=draw(tuple(inp.q_lat.shape)),
+                               q_pe=draw(tuple(inp.q_pe.shape)))
+
+
+# e4m3fn codes at the edges of the format: the largest magnitudes (448, 416, 384, 352) and the
+# subnormals (m * 2^-9, m = 1..7), both signs.
+E4M3FN_LARGE_CODES = (0x7E, 0x7D, 0x7C, 0x7B, 0xFE, 0xFD, 0xFC, 0xFB)
+E4M3FN_SUBNORMAL_CODES = tuple(range(0x01, 0x08)) + tuple(range(0x81, 0x88))
+
+
+def extreme_pool(inp: MlaInputs, frac_large: float = 0.1, frac_subnormal: float = 0.1,
+                 seed: int = 0) -> MlaInputs:
+    """A copy of the pool in which a seeded fraction of the bytes is replaced by the largest
+    e4m3fn magnitudes and another fraction by subnormal codes."""
+    g = _gen("cpu", seed)
+    pool = inp.pool.cpu().clone()
+    r = torch.rand(pool.shape, generator=g)
+    large = torch.tensor(E4M3FN_LARGE_CODES, dtype=torch.uint8)
+    sub = torch.tensor(E4M3FN_SUBNORMAL_CODES, dtype=torch.uint8)
+    m_large = r < frac_large
+    m_sub = r >= 1.0 - frac_subnormal
+    pool[m_large] = large[torch.randint(0, len(large), (int(m_large.sum()),), generator=g)]
+    pool[m_sub] = sub[torch.randint(0, len(sub), (int(m_sub.sum()),), generator=g)]
+    return dataclasses.replace(inp, pool=pool.to(inp.pool.device))
+
+
+def dominant_keys(inp: MlaInputs, seed: int = 0, noise: float = 0.05, block: int = 64) -> MlaInputs:
+    """Queries that share one direction u (per-head noise of relative size `noise`), and in every
+    run of `block` consecutive positions of each request's slot list one key whose pool row is u
+    encoded in fp8 at a seeded amplitude (row maximum 100..440 before the kv scale).  Each such
+    key dominates its block for every head, and the blocks' maxima differ by many octaves."""
+    dev = inp.pool.device
+    g = _gen("cpu", seed)
+    d_lat = inp.q_lat.shape[-1]
+    d_qk = inp.pool.shape[1]
+    u = torch.randn((d_qk,), generator=g, dtype=torch.float64)
+    ntok, H = inp.q_lat.shape[0], inp.q_lat.shape[1]
+    q = u.view(1, 1, -1) * (1.0 + noise * torch.randn((ntok, H, d_qk), generator=g, dtype=torch.float64))
+    q = q.to(torch.bfloat16)
+    pool = inp.pool.cpu().clone()
+    idx = inp.kv_indices.cpu()
+    indptr = inp.kv_indptr.cpu()
+    lens = inp.seq_lens.cpu()
+    unit = u / u.abs().max()
+    for b in range(inp.B):
+        a, n = int(indptr[b]), int(lens[b])
+        for s0 in range(0, n, block):
+            j = s0 + int(torch.randint(0, min(block, n - s0), (1,), generator=g))
+            slot = int(idx[a + j])
+            if slot < 0:
+                continue
+            amp = 100.0 + 340.0 * float(torch.rand((1,), generator=g))
+            pool[slot] = fp8_e4m3fn_bytes((unit * amp).float())
+    return dataclasses.replace(inp, q_lat=q[..., :d_lat].contiguous().to(dev),
+                               q_pe=q[..., d_lat:].contiguous().to(dev), pool=pool.to(dev))
+
+
+def sorted_slots(inp: MlaInputs, how: str) -> MlaInputs:
+    """The same keys with each request's slot list reordered: "request" sorts it ascending,
+    "contiguous" gives request b the pool rows kv_indptr[b] .. kv_indptr[b + 1] - 1 in order (a
+    plain arange, with the pool unchanged)."""
+    idx = inp.kv_indices.cpu().clone()
+    indptr = inp.kv_indptr.cpu()
+    if how == "contiguous":
+        idx = torch.arange(idx.numel(), dtype=torch.int32) % inp.pool.shape[0]
+    elif how == "request":
+        for b in range(inp.B):
+            a, e = int(indptr[b]), int(indptr[b + 1])
+            idx[a:e] = torch.sort(idx[a:e]).values
+    else:
+        raise ValueError(how)
+    return dataclasses.replace(inp, kv_indices=idx.to(torch.int32).to(inp.kv_indices.device))
