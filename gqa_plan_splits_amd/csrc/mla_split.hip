@@ -88,17 +88,16 @@ struct MlaLayout {
     static constexpr int kTailOff = kLineSlots * 32768;
     static constexpr int kPOff = kTailOff + (kTail ? kTailSlots * 4096 : 0);
     static constexpr int kMlOff = kPOff + 2 * 8192;         // P [2][64 rows][64 keys] fp16
-    static constexpr int kMlBytes = 3 * 256;                // m, lq, le [64 rows]
+    static constexpr int kMlBytes = 2 * 256;                // m [blocks 0, 1][64 rows]
     static constexpr int kIdOff = kMlOff + 2 * kMlBytes;
     static constexpr int kBadOff = kIdOff + kIdSlots * 256;   // per tile: 64-bit mask of skipped keys
     static constexpr int kLdsBytes = kBadOff + kIdSlots * 8;
-    static constexpr int kCopies = 8 + (kTail ? 1 : 0);     // copy instructions per tile per wave
     static_assert(DQK == 576 || DQK == 512, "row width");
     static_assert(kLdsBytes <= 160 * 1024, "LDS");
 };
 
 __device__ __forceinline__ int swz_line(int pos) { return ((pos >> 2) & 1) | (pos & 2) | ((pos >> 1) & 4); }
-__device__ __forceinline__ int swz_tail(int pos) { return (pos >> 2) & 1; }
+__device__ __forceinline__ int swz_tail(int pos) { return (pos >> 2) & 3; }
 // Byte offsets inside a line slot of 16-byte chunk c (< 8) of line `line`, and inside a tail slot
 // of chunk c (< 4) of a rope tail.
 __device__ __forceinline__ int line_off(int line, int pos, int c) {
@@ -141,7 +140,7 @@ __device__ __forceinline__ void copy16(const uint8_t *g, uint32_t m0) {
 __device__ __forceinline__ void copy4(const int32_t *g, uint32_t m0) {
     asm volatile("global_load_lds_dword %0, off nt" ::"v"(g), "{m0}"(m0) : "memory");
 }
-// s_waitcnt vmcnt(n) for a wave-uniform n in [0, 15].
+// s_waitcnt vmcnt(n) for a wave-uniform n in [0, 31] (larger n waits for vmcnt(31)).
 __device__ __forceinline__ void wait_vmem(int n) {
     switch (n) {
 #define GQA_WAIT_CASE(k) \
@@ -149,8 +148,12 @@ __device__ __forceinline__ void wait_vmem(int n) {
         GQA_WAIT_CASE(0) GQA_WAIT_CASE(1) GQA_WAIT_CASE(2) GQA_WAIT_CASE(3) GQA_WAIT_CASE(4)
         GQA_WAIT_CASE(5) GQA_WAIT_CASE(6) GQA_WAIT_CASE(7) GQA_WAIT_CASE(8) GQA_WAIT_CASE(9)
         GQA_WAIT_CASE(10) GQA_WAIT_CASE(11) GQA_WAIT_CASE(12) GQA_WAIT_CASE(13) GQA_WAIT_CASE(14)
+        GQA_WAIT_CASE(15) GQA_WAIT_CASE(16) GQA_WAIT_CASE(17) GQA_WAIT_CASE(18) GQA_WAIT_CASE(19)
+        GQA_WAIT_CASE(20) GQA_WAIT_CASE(21) GQA_WAIT_CASE(22) GQA_WAIT_CASE(23) GQA_WAIT_CASE(24)
+        GQA_WAIT_CASE(25) GQA_WAIT_CASE(26) GQA_WAIT_CASE(27) GQA_WAIT_CASE(28) GQA_WAIT_CASE(29)
+        GQA_WAIT_CASE(30)
 #undef GQA_WAIT_CASE
-        default: asm volatile("s_waitcnt vmcnt(15)" ::: "memory"); break;
+        default: asm volatile("s_waitcnt vmcnt(31)" ::: "memory"); break;
     }
 }
 
@@ -233,28 +236,32 @@ __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const MlaSplitAr
     const int32_t *const id_ring = reinterpret_cast<const int32_t *>(lds + T::kIdOff);
     uint64_t *const bad_ring = reinterpret_cast<uint64_t *>(lds + T::kBadOff);
 
-    if (wave < 4) {
+    // Roles by wave: waves w and w + 4 share a SIMD, and waves 0-3 sit on four different SIMDs.
+    // The score waves 0, 4 (rows 0-31) and 1, 5 (rows 32-63) have two SIMDs to themselves for
+    // their QK^T MFMAs; the value waves 2, 6 and 3, 7 share the other two for PV.
+    if (wave < 2 || wave == 4 || wave == 5) {
         // ================================ score wave ================================
-        // Score wave w: query rows 16 w .. 16 w + 15 against all 64 keys of a tile, on the
-        // 16x16x32 bf16 MFMA, one accumulator per 16-key block.  The stored fp8 K bytes are
-        // converted exactly to bf16 in registers, so every product q * k is exact and the sums
-        // are plain fp32 (the block-scaled fp8 MFMA aligns its 128 products with about 15 bits
-        // below the largest, which puts an error of order 2^-15 max|q k| on every score).
-        // Lane (n16, g) reads bytes 32 g .. 32 g + 31 of each 128-byte line of its key: the four
-        // 8-byte pieces feed four MFMAs, whose k slots 8 g .. 8 g + 7 are dims 128 s + 32 g + 8 i
-        // + 0..7 (the query operand takes the same dims).  The 64-byte rope tail of 576-byte rows
-        // is two more MFMAs: lane g takes dims 32 (g & 1) + 8 (g >> 1) + 0..7 of the tail in the
-        // first and 16 more in the second.
-        const int n16 = lane & 15, g = lane >> 4;
-        const int rl = 16 * wave + n16;         // row within the block
-        const bool row_ok = rl < nrows;
+        // Score wave w: query rows 32 (w & 1) .. + 31 against 32-key block kb = w >> 2 of every
+        // tile, S^T = K Q^T on v_mfma_f32_32x32x16_bf16.  The stored fp8 K bytes are converted
+        // exactly to bf16 in registers, so every product q * k is exact and the sums are fp32.
+        // Lane (n, h) reads the 64 bytes 64 h .. 64 h + 63 of each 128-byte line of key n of the
+        // block: MFMA j (0..7) of line L takes its bytes 8 j .. 8 j + 7 as k slots 8 h .. 8 h + 7,
+        // dims 128 L + 64 h + 8 j + 0..7 (the query operand takes the same dims).  The 64-byte
+        // rope tail of 576-byte rows is four more MFMAs over dims 512 + 32 h + 8 j + 0..7.  The
+        // two score waves of a SIMD run the same rows on alternate blocks, so each keeps its own
+        // online softmax; the value waves align the two, and merge their sums at the end.
+        // In the MFMA output layout lane (n, h) holds row n's scores of block positions
+        // 8 j + 4 h + i (j, i = 0..3).
+        const int kb = wave >> 2;               // this wave's block of every tile
+        const int srow = 32 * (wave & 1) + n;   // row within the CTA
+        const bool row_ok = srow < nrows;
         constexpr int NL = DQK / 128;           // full 128-byte lines per row
-        constexpr int NQ = 4 * NL + (T::kTail ? 2 : 0);   // MFMAs per 16-key block
+        constexpr int NQ = 8 * NL + (T::kTail ? 4 : 0);   // MFMAs per 32-key block
         int p_end;                              // keys visible to this row
         const float c_row = a.score_scale;      // base-2 score per unit of the raw product
         bf16x8 qv[NQ];                          // B operands: this lane's query dims per MFMA
         {
-            const int r = row0 + rl;
+            const int r = row0 + srow;
             const int t = row_ok ? r / a.H : 0;
             const int hh = row_ok ? r - t * a.H : 0;
             p_end = row_ok ? min(visible(t), k1) : k0;
@@ -265,95 +272,86 @@ __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const MlaSplitAr
                 return as_bf16x8(row_ok ? load_q8<DLAT>(ql, qp, d) : u32x4{0u, 0u, 0u, 0u});
             };
 #pragma unroll
-            for (int s = 0; s < NL; ++s)
+            for (int L = 0; L < NL; ++L)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) qv[4 * s + i] = piece(128 * s + 32 * g + 8 * i);
+                for (int j = 0; j < 8; ++j) qv[8 * L + j] = piece(128 * L + 64 * h + 8 * j);
             if constexpr (T::kTail) {
-                qv[4 * NL] = piece(512 + 32 * (g & 1) + 8 * (g >> 1));
-                qv[4 * NL + 1] = piece(512 + 32 * (g & 1) + 16 + 8 * (g >> 1));
+#pragma unroll
+                for (int j = 0; j < 4; ++j) qv[8 * NL + j] = piece(512 + 32 * h + 8 * j);
             }
         }
 
-        // Loop-invariant LDS offsets of this lane's K operand (key at tile position 16 kbk + n16,
-        // chunks 2 g and 2 g + 1 of line s; the swizzle does not depend on kbk, so 16-key block kbk
-        // adds 2048 bytes, line s 8192).  Rope tails: 8 bytes at 8 (g >> 1) of tail chunks
-        // 2 (g & 1) and 2 (g & 1) + 1; block kbk adds 1024 bytes.
-        const int k_off0 = line_off(0, n16, 2 * g), k_off1 = line_off(0, n16, 2 * g + 1);
-        const int k_tail0 = T::kTailOff + tail_off(n16, 2 * (g & 1)) + 8 * (g >> 1);
-        const int k_tail1 = T::kTailOff + tail_off(n16, 2 * (g & 1) + 1) + 8 * (g >> 1);
-        // P of this lane: the fp16 weights of tile positions 16 kbk + 4 g .. + 3 of row rl, the
-        // 8 bytes at 8 (g & 1) of 16-byte slot 2 kbk + (g >> 1) of the row's 128 bytes (p_slot).
-        int p_wr[4];
+        // LDS offsets of this lane's K operand within tile t's slots: key at position 32 kb + n,
+        // chunks 4 h .. 4 h + 3 of each line (line L adds 8192 bytes), rope-tail chunks 2 h and
+        // 2 h + 1.
+        int k_off[4], k_tail[2];
 #pragma unroll
-        for (int kbk = 0; kbk < 4; ++kbk) p_wr[kbk] = p_slot(rl, 2 * kbk + (g >> 1)) + 8 * (g & 1);
-        // Score i of block kbk of this lane is tile position 16 kbk + 4 g + i, slot-list index
-        // 32 (g & 1) + (g >> 1) + 8 i + 2 kbk (key_of_pos).
-        const int kidx_base = 32 * (g & 1) + (g >> 1);
+        for (int c = 0; c < 4; ++c) k_off[c] = line_off(0, 32 * kb + n, 4 * h + c);
+#pragma unroll
+        for (int c = 0; c < 2; ++c) k_tail[c] = T::kTailOff + tail_off(32 * kb + n, 2 * h + c);
+        // Slot-list index of this lane's score (j, i), relative to the tile:
+        // key_of_pos(32 kb + 8 j + 4 h + i) = 32 h + 8 i + 4 kb + j.
+        const int kidx = 32 * h + 4 * kb;
 
-        // K operand reads, their exact conversion to bf16 and the MFMAs of 16-key block kbk of
-        // the scores of tile t (18 for 576-byte rows, 16 for 512-byte rows), in two accumulator
-        // chains so that no MFMA waits on the one just before it.
-        auto qk_block = [&](int t, int kbk, f32x4 &sacc) {
-            const uint8_t *lb = lds + (t % kLineSlots) * 32768 + 2048 * kbk;
-            const uint8_t *tlb = lds + (t % kTailSlots) * 4096 + 1024 * kbk;
-            f32x4 acc0 = f32x4{0.f, 0.f, 0.f, 0.f};
-            f32x4 acc1 = f32x4{0.f, 0.f, 0.f, 0.f};
+        // K operand reads, their exact conversion to bf16 and the MFMAs of this wave's block of
+        // tile t, in one accumulator chain (the matrix core forwards an accumulator to the next
+        // MFMA of the same kind): line L (8 MFMAs), and the rope tail (4 MFMAs).
+        auto qk_line = [&](int t, int L, f32x16 &acc) {
+            const uint8_t *lb = lds + (t % kLineSlots) * 32768 + 8192 * L;
 #pragma unroll
-            for (int s = 0; s < NL; ++s) {
-                const u32x4 lo16 = *reinterpret_cast<const u32x4 *>(lb + 8192 * s + k_off0);
-                const u32x4 hi16 = *reinterpret_cast<const u32x4 *>(lb + 8192 * s + k_off1);
-                acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp8x8_to_bf16x8(lo16.x, lo16.y), qv[4 * s], acc0, 0, 0, 0);
-                acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp8x8_to_bf16x8(lo16.z, lo16.w), qv[4 * s + 1], acc1, 0, 0, 0);
-                acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp8x8_to_bf16x8(hi16.x, hi16.y), qv[4 * s + 2], acc0, 0, 0, 0);
-                acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp8x8_to_bf16x8(hi16.z, hi16.w), qv[4 * s + 3], acc1, 0, 0, 0);
+            for (int c = 0; c < 4; ++c) {
+                const u32x4 k16 = *reinterpret_cast<const u32x4 *>(lb + k_off[c]);
+                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fp8x8_to_bf16x8(k16.x, k16.y), qv[8 * L + 2 * c], acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fp8x8_to_bf16x8(k16.z, k16.w), qv[8 * L + 2 * c + 1], acc, 0, 0, 0);
             }
-            if constexpr (T::kTail) {
-                const u32x2 t0 = *reinterpret_cast<const u32x2 *>(tlb + k_tail0);
-                const u32x2 t1 = *reinterpret_cast<const u32x2 *>(tlb + k_tail1);
-                acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp8x8_to_bf16x8(t0.x, t0.y), qv[4 * NL], acc0, 0, 0, 0);
-                acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp8x8_to_bf16x8(t1.x, t1.y), qv[4 * NL + 1], acc1, 0, 0, 0);
+        };
+        auto qk_tail = [&](int t, f32x16 &acc) {
+            const uint8_t *tlb = lds + (t % kTailSlots) * 4096;
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+                const u32x4 k16 = *reinterpret_cast<const u32x4 *>(tlb + k_tail[c]);
+                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fp8x8_to_bf16x8(k16.x, k16.y), qv[8 * NL + 2 * c], acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fp8x8_to_bf16x8(k16.z, k16.w), qv[8 * NL + 2 * c + 1], acc, 0, 0, 0);
             }
-            sacc = acc0 + acc1;
+        };
+        auto zero16 = [](f32x16 &x) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) x[i] = 0.f;
         };
 
-        // Online softmax of this lane's row in base 2 with an integer running maximum m (the
-        // ceiling of the largest base-2 score so far): a key's weight is p = 2^(score - m + 8) in
-        // (0, 256], stored in fp16 (11 significant bits).  The row's sums of the stored weights
+        // Online softmax over this wave's blocks, in base 2 with an integer running maximum m
+        // (the ceiling of the largest base-2 score so far): a key's weight is p = 2^(score - m + 8)
+        // in (0, 256], stored in fp16 (11 significant bits).  The row's sums of the stored weights
         // (lq, which normalizes the output: a dominant key then carries no rounding of its own
-        // weight into it) and of the exact weights (le, which gives the log-sum-exp) are kept
-        // here, and rescaled by the exact power of two 2^(m_old - m_new) when m moves.  All four
-        // lanes of a row hold the same values.
+        // weight into it) and of the exact weights (le, which gives the log-sum-exp) are rescaled
+        // by the exact power of two 2^(m_old - m_new) when m moves.  Lanes n and n + 32 hold the
+        // same values.  The block's maximum goes to LDS beside P.  The work comes in four stages,
+        // each placed beside the MFMAs of one 128-byte line of the next tile's scores.
         int m_run = kNoMax;
         float lq_run = 0.f, le_run = 0.f;
         struct Soft {
-            float bias, esum, qsum, alpha;
+            float alpha, bias, esum, qsum;
             int m;
         };
-        // Masked variant (tiles past some row's window or the partition end, and tiles with
-        // skipped keys): scores of keys a row does not see become -inf, without branches.
-        auto sm_max = [&](int t, f32x4 (&sacc)[4], auto masked) -> Soft {
+        // stage 0: masks (the masked variant: tiles past some row's window or the partition end,
+        // and tiles with skipped keys, whose scores of keys a row does not see become -inf), the
+        // block maximum and the new running maximum
+        auto sm0 = [&](int t, f32x16 &sc, auto masked) -> Soft {
             if constexpr (decltype(masked)::value) {
                 // keys whose slot id is negative (bit k: slot-list index k of the tile)
-                const uint32_t bad = uint32_t(bad_ring[t % kIdSlots] >> kidx_base);
+                const uint32_t bad = uint32_t(bad_ring[t % kIdSlots] >> kidx);
+                const int thr = p_end - k0 - t * kBK - kidx;   // visible: index < thr
 #pragma unroll
-                for (int kbk = 0; kbk < 4; ++kbk)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        if ((bad >> (8 * i + 2 * kbk)) & 1) sacc[kbk][i] = kNegInf;
-            }
-            if constexpr (decltype(masked)::value) {
-                const int thr = p_end - k0 - t * kBK - kidx_base;   // visible: index - base < thr
-#pragma unroll
-                for (int kbk = 0; kbk < 4; ++kbk)
+                for (int j = 0; j < 4; ++j)
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
-                        if (8 * i + 2 * kbk >= thr) sacc[kbk][i] = kNegInf;
+                        if (((bad >> (8 * i + j)) & 1) || 8 * i + j >= thr) sc[4 * j + i] = kNegInf;
             }
-            float m4[4];
+            float mx = sc[0];
 #pragma unroll
-            for (int kbk = 0; kbk < 4; ++kbk)
-                m4[kbk] = fmaxf(fmaxf(sacc[kbk][0], sacc[kbk][1]), fmaxf(sacc[kbk][2], sacc[kbk][3]));
-            const float mx = rows4_max(fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3])));
+            for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sc[i]);
+            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+            mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
             const int mt = mx == kNegInf ? kNoMax : int(ceilf(mx * c_row));
             Soft sf;
             sf.m = max(m_run, mt);
@@ -362,95 +360,92 @@ __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const MlaSplitAr
             sf.esum = sf.qsum = 0.f;
             return sf;
         };
-        auto sm_block = [&](int t, const f32x4 &sc, int kbk, Soft &sf) {
-            const float p0 = fast_exp2(fmaf(sc[0], c_row, sf.bias));
-            const float p1 = fast_exp2(fmaf(sc[1], c_row, sf.bias));
-            const float p2 = fast_exp2(fmaf(sc[2], c_row, sf.bias));
-            const float p3 = fast_exp2(fmaf(sc[3], c_row, sf.bias));
-            const f16x2 h01 = pack_f16x2(p0, p1), h23 = pack_f16x2(p2, p3);
-            sf.esum += (p0 + p1) + (p2 + p3);
-            sf.qsum += (float(h01.x) + float(h01.y)) + (float(h23.x) + float(h23.y));
-            *reinterpret_cast<u32x2 *>(P + (t & 1) * 8192 + p_wr[kbk]) =
-                u32x2{__builtin_bit_cast(uint32_t, h01), __builtin_bit_cast(uint32_t, h23)};
+        // stages 1 and 2: the weights of score groups j0, j0 + 1 (8 per lane) to P
+        auto sm12 = [&](int t, int j0, const f32x16 &sc, Soft &sf) {
+            uint8_t *pb = P + (t & 1) * 8192;
+#pragma unroll
+            for (int j = j0; j < j0 + 2; ++j) {
+                const float p0 = fast_exp2(fmaf(sc[4 * j], c_row, sf.bias));
+                const float p1 = fast_exp2(fmaf(sc[4 * j + 1], c_row, sf.bias));
+                const float p2 = fast_exp2(fmaf(sc[4 * j + 2], c_row, sf.bias));
+                const float p3 = fast_exp2(fmaf(sc[4 * j + 3], c_row, sf.bias));
+                const f16x2 h01 = pack_f16x2(p0, p1), h23 = pack_f16x2(p2, p3);
+                sf.esum += (p0 + p1) + (p2 + p3);
+                sf.qsum += (float(h01.x) + float(h01.y)) + (float(h23.x) + float(h23.y));
+                *reinterpret_cast<u32x2 *>(pb + p_slot(srow, 4 * kb + j) + 8 * h) =
+                    u32x2{__builtin_bit_cast(uint32_t, h01), __builtin_bit_cast(uint32_t, h23)};
+            }
         };
-        auto sm_finish = [&](int t, Soft &sf) {
-            const float esum = rows4_sum(sf.esum);
-            const float qsum = rows4_sum(sf.qsum);
-            lq_run = fmaf(lq_run, sf.alpha, qsum);
-            le_run = fmaf(le_run, sf.alpha, esum);
+        // stage 3: the row sums, the running state, the block maximum to LDS
+        auto sm3 = [&](int t, Soft &sf) {
+            const auto se = __builtin_amdgcn_permlane32_swap(__float_as_uint(sf.esum), __float_as_uint(sf.esum), false, false);
+            const auto sq = __builtin_amdgcn_permlane32_swap(__float_as_uint(sf.qsum), __float_as_uint(sf.qsum), false, false);
+            lq_run = fmaf(lq_run, sf.alpha, __uint_as_float(sq[0]) + __uint_as_float(sq[1]));
+            le_run = fmaf(le_run, sf.alpha, __uint_as_float(se[0]) + __uint_as_float(se[1]));
             m_run = sf.m;
-            // the four lanes of a row hold the same values and all store them (no branch, which
-            // would split the step's scheduling region)
-            uint8_t *mlb = ML + (t & 1) * T::kMlBytes + rl * 4;
-            *reinterpret_cast<int *>(mlb) = m_run;
-            *reinterpret_cast<float *>(mlb + 256) = lq_run;
-            *reinterpret_cast<float *>(mlb + 512) = le_run;
+            // lanes n and n + 32 hold the same value and both store it (no branch)
+            *reinterpret_cast<int *>(ML + (t & 1) * T::kMlBytes + 256 * kb + srow * 4) = m_run;
         };
+#define GQA_SB __builtin_amdgcn_sched_barrier(0)
 
-        // Step t: the MFMAs of tile t + 1 (the last tile again at the end; its scores are then
-        // unused), one 16-key block per scheduling region, each region also holding a piece of
-        // the softmax of tile t (whose scores `cur` holds), so the MFMAs and the vector work
-        // overlap while only one block's K operands are in registers.
-        // Returns whether tile t + 1 has skipped keys (read here, off the critical path: its mask
-        // was published steps ago), which picks the next step's variant.
-        auto step = [&](int t, f32x4 (&cur)[4], f32x4 (&next)[4], auto masked) -> bool {
+        // Step t: the softmax of tile t (whose scores `cur` holds) in four stages, each beside the
+        // MFMAs of one line of tile t + 1's scores (the last tile again at the end; those scores
+        // are then unused), which accumulate in `nxt`.
+        auto step = [&](int t, f32x16 &cur, f32x16 &nxt, auto masked) {
             const int tq = min(t + 1, ntiles - 1);
-            const bool next_bad = bad_ring[tq % kIdSlots] != 0;
-            qk_block(tq, 0, next[0]);
-            Soft sf = sm_max(t, cur, masked);
-            __builtin_amdgcn_sched_barrier(0);
-            qk_block(tq, 1, next[1]);
-            sm_block(t, cur[0], 0, sf);
-            __builtin_amdgcn_sched_barrier(0);
-            qk_block(tq, 2, next[2]);
-            sm_block(t, cur[1], 1, sf);
-            __builtin_amdgcn_sched_barrier(0);
-            qk_block(tq, 3, next[3]);
-            sm_block(t, cur[2], 2, sf);
-            sm_block(t, cur[3], 3, sf);
-            sm_finish(t, sf);
+            zero16(nxt);
+            if constexpr (T::kTail) qk_tail(tq, nxt);
+            Soft sf = sm0(t, cur, masked);
+            qk_line(tq, 0, nxt);
+            GQA_SB;
+            sm12(t, 0, cur, sf);
+            qk_line(tq, 1, nxt);
+            GQA_SB;
+            sm12(t, 2, cur, sf);
+            qk_line(tq, 2, nxt);
+            GQA_SB;
+            sm3(t, sf);
+            qk_line(tq, 3, nxt);
             __syncthreads();   // P(t) published; tile t + 2 landed
-            return next_bad;
         };
 
         using yes = std::integral_constant<bool, true>;
         using no = std::integral_constant<bool, false>;
         if (ntiles > 0) {
             __syncthreads();   // tiles 0 and 1 landed
-            f32x4 sa[4], sb[4];
+            f32x16 sa, sb;
+            zero16(sa);
+            if constexpr (T::kTail) qk_tail(0, sa);
 #pragma unroll
-            for (int kbk = 0; kbk < 4; ++kbk) {
-                qk_block(0, kbk, sa[kbk]);
-                __builtin_amdgcn_sched_barrier(0);   // one block's K operands in registers at a time
-            }
-            __syncthreads();   // tile 0 read: step 0's copies may refill its tail slot
+            for (int L = 0; L < NL; ++L) qk_line(0, L, sa);
+            __syncthreads();   // tile 0's rope tails read: step 0's copies may refill their slot
+            // tiles with keys past some row's window or the partition end, or with skipped keys
+            // (mask published when the tile's copies were issued), take the masked variant
+            auto masked_tile = [&](int t) {
+                return t >= n_full || __builtin_amdgcn_readfirstlane(uint32_t(bad_ring[t % kIdSlots] != 0));
+            };
             int t = 0;
-            bool bad = bad_ring[0] != 0;
-            for (; t + 1 < n_full; t += 2) {
-                bad = bad ? step(t, sa, sb, yes{}) : step(t, sa, sb, no{});
-                bad = bad ? step(t + 1, sb, sa, yes{}) : step(t + 1, sb, sa, no{});
+            for (; t + 1 < ntiles; t += 2) {
+                if (masked_tile(t)) step(t, sa, sb, yes{}); else step(t, sa, sb, no{});
+                if (masked_tile(t + 1)) step(t + 1, sb, sa, yes{}); else step(t + 1, sb, sa, no{});
             }
-            if (t < n_full) {   // one full tile left: its scores are in sa
-                bad ? step(t, sa, sb, yes{}) : step(t, sa, sb, no{});
-                ++t;
-                for (; t + 1 < ntiles; t += 2) {
-                    step(t, sb, sa, yes{});
-                    step(t + 1, sa, sb, yes{});
-                }
-                if (t < ntiles) step(t, sb, sa, yes{});
-            } else {
-                for (; t + 1 < ntiles; t += 2) {
-                    step(t, sa, sb, yes{});
-                    step(t + 1, sb, sa, yes{});
-                }
-                if (t < ntiles) step(t, sa, sb, yes{});
+            if (t < ntiles) {
+                if (masked_tile(t)) step(t, sa, sb, yes{}); else step(t, sa, sb, no{});
             }
+            // this wave's final state, in the P buffer the value waves no longer read:
+            // [block][row] of {m, lq, le}
+            uint8_t *fin = P + (ntiles & 1) * 8192 + kb * 768 + srow * 4;
+            *reinterpret_cast<int *>(fin) = m_run;
+            *reinterpret_cast<float *>(fin + 256) = lq_run;
+            *reinterpret_cast<float *>(fin + 512) = le_run;
+            __syncthreads();   // final states published
         }
+#undef GQA_SB
         return;
     }
 
     // ================================ value wave ================================
-    const int v = wave - 4;   // output columns 128 v .. 128 v + 127 = line v of the rows
+    const int v = (wave & 1) + ((wave >> 1) & 2);   // waves 2, 3, 6, 7 -> 0, 1, 2, 3: line v
     // ---- copies.  Instruction i writes tile positions 8 i .. 8 i + 7 of line v: lane L carries
     // slot-list key 8 (L >> 3) + i at position 8 i + (L >> 3), chunk position L & 7, i.e. global
     // chunk (L & 7) ^ swz_line(position).  The tail copy writes positions 16 v .. 16 v + 15.
@@ -479,7 +474,7 @@ __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const MlaSplitAr
         if (EXTRA && min(k0 + tile * kBK + idx, k1 - 1) >= S1) p += kv2_delta;
         return p;
     };
-    auto copy_rows = [&](int tile, const int32_t (&kid)[8], int32_t tid, int32_t mid) {
+    auto copy_lines = [&](int tile, const int32_t (&kid)[8], int32_t mid) {
         const uint32_t lslot = lds_addr + (tile % kLineSlots) * 32768 + v * 8192;
         if (id_loader) {
             // every lane stores the same mask (no branch)
@@ -491,18 +486,24 @@ __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const MlaSplitAr
             const int gc = (lane & 7) ^ swz_line(8 * i + jgrp);
             copy16(row_of(tile, 8 * jgrp + i, kid[i]) + 128 * v + 16 * gc, lslot + 1024 * i);
         }
+    };
+    auto copy_tail = [&](int tile, int32_t tid) {
         if (T::kTail)
             copy16(row_of(tile, tail_key, tid) + tail_chunk,
                    lds_addr + T::kTailOff + (tile % kTailSlots) * 4096 + 1024 * v);
     };
     // ... with the ids taken from the shared ring
-    auto issue_rows = [&](int tile) {
+    auto issue_lines = [&](int tile) {
         if (tile >= ntiles) return;
         const int32_t *ids = id_ring + (tile % kIdSlots) * 64;
         const i32x4 ia = *reinterpret_cast<const i32x4 *>(ids + 8 * jgrp);
         const i32x4 ib = *reinterpret_cast<const i32x4 *>(ids + 8 * jgrp + 4);
         const int32_t kid[8] = {ia.x, ia.y, ia.z, ia.w, ib.x, ib.y, ib.z, ib.w};
-        copy_rows(tile, kid, ids[tail_key], ids[lane]);
+        copy_lines(tile, kid, ids[lane]);
+    };
+    auto issue_tail = [&](int tile) {
+        if (!T::kTail || tile >= ntiles) return;
+        copy_tail(tile, id_ring[(tile % kIdSlots) * 64 + tail_key]);
     };
     // Slot ids of tiles 0-2, straight from global memory into registers (so the first copies do
     // not wait on a workgroup barrier, which the score waves reach only after preparing Q).
@@ -521,13 +522,20 @@ __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const MlaSplitAr
             pre_mid[j] = *id_ptr(min(kb + lane, last));
         }
     }
-    // Issue order: ids(3), rows(0), rows(1), rows(2), ids(4), ids(5), then rows(j), ids(j + 3)
-    // for j = 3, 4, ...; ids only in value wave 0, operations for tiles >= ntiles skipped.
-    // Copies retire in issue order.  Rows(j) are read in step j - 1 (the scores of tile j) and
-    // step j + 1 (its values); ids(j) in step j - 3 (the copies of rows(j)).
-    constexpr int NC = T::kCopies;
+    // Schedule (tile j is read by the score waves in step j - 1, and by the value waves in
+    // step j + 1; operations for tiles >= ntiles are skipped, ids only in value wave 0):
+    //   prologue: ids(3), rows(0), rows(1), rows(2), ids(4), ids(5);
+    //   step t:   rows(t + 3) (lines and rope tails; the line slot held tile t - 1, whose values
+    //             this wave has just applied, the tail slot tile t), ids(t + 6).
+    // Copies retire in issue order.  Before the barrier that ends step t, tile t + 2 must have
+    // landed (and with it ids(t + 4)); ids(t + 5) and step t's own issues may be outstanding.
+    constexpr int NC = 8 + (T::kTail ? 1 : 0);
     auto cnt_rows = [&](int j) { return j >= 0 && j < ntiles ? NC : 0; };
     auto cnt_ids = [&](int j) { return id_loader && j >= 0 && j < ntiles ? 1 : 0; };
+    auto issue_rows = [&](int tile) {
+        issue_lines(tile);
+        issue_tail(tile);
+    };
 
     // ---- PV on v_mfma_f32_32x32x16_f16 as O^T = V^T P^T, four MFMAs per 64 keys.  V^T (A
     // operand) of column block cb: transposed read r hands lane (m, h) 8 fp8 bytes, keys
@@ -549,7 +557,11 @@ __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const MlaSplitAr
 #pragma unroll
         for (int r = 0; r < 4; ++r) p_rd[rb][r] = p_slot(32 * rb + n, 2 * h + (r & 1) + 4 * (r >> 1));
 
-    int mc[2] = {kNoMax, kNoMax};   // the running maxima of rows n and 32 + n the accumulators hold
+    // The accumulators of rows n and 32 + n hold sums relative to mc[rb], the largest block
+    // maximum applied so far.  A block whose maximum is larger first rescales them by the exact
+    // power of two 2^(mc - m); one whose maximum is smaller has its fp16 weights scaled by
+    // 2^(m - mc) (exact, or below 2^-24 of the row's largest weights, where they no longer count).
+    int mc[2] = {kNoMax, kNoMax};
     f32x16 oacc[2][4];
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb)
@@ -558,42 +570,64 @@ __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const MlaSplitAr
 #pragma unroll
             for (int i = 0; i < 16; ++i) oacc[rb][cb][i] = 0.f;
 
-    // PV of tile t: the rescale when a row's running maximum moved, then 32 MFMAs.
+    // PV of tile t: every LDS read first (V^T bytes of both blocks, the weights, the block maxima),
+    // so that their latency overlaps; then, block by block, the alignment of maxima, the exact
+    // fp8 -> fp16 conversion of V and 16 MFMAs.
     auto pv = [&](int t) {
         const uint8_t *pbuf = P + (t & 1) * 8192;
         const uint8_t *mlb = ML + (t & 1) * T::kMlBytes;
+        const uint8_t *lb = lds + (t % kLineSlots) * 32768;
+        int2v raw[4][4];   // [cb][r]: MFMA r's V^T bytes of column block cb
 #pragma unroll
-        for (int rb = 0; rb < 2; ++rb) {
-            const int m_new = *reinterpret_cast<const int *>(mlb + (32 * rb + n) * 4);
-            const float alpha = ldexpf(1.f, mc[rb] - m_new);
-            mc[rb] = m_new;
-            if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
+        for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
-                for (int cb = 0; cb < 4; ++cb) oacc[rb][cb] *= alpha;
-            }
-        }
+            for (int r = 0; r < 4; ++r)
+                raw[cb][r] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                    (__attribute__((address_space(3))) int2v *)(lb + v_off[cb][r]));
         f16x8 pw[2][4];
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
             for (int r = 0; r < 4; ++r)
                 pw[rb][r] = __builtin_bit_cast(f16x8, *reinterpret_cast<const u32x4 *>(pbuf + p_rd[rb][r]));
-        const uint8_t *lb = lds + (t % kLineSlots) * 32768;
+        int mblk[2][2];
 #pragma unroll
-        for (int cb = 0; cb < 4; ++cb) {
-            f16x8 vt[4];
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int2v raw = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-                    (__attribute__((address_space(3))) int2v *)(lb + v_off[cb][r]));
-                vt[r] = fp8x8_to_f16x8(uint32_t(raw.x), uint32_t(raw.y));
+            for (int rb = 0; rb < 2; ++rb)
+                mblk[kb][rb] = *reinterpret_cast<const int *>(mlb + 256 * kb + (32 * rb + n) * 4);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb) {
+                const int m = mblk[kb][rb];
+                if (m > mc[rb]) {
+                    const float alpha = ldexpf(1.f, mc[rb] - m);
+                    mc[rb] = m;
+                    if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
+#pragma unroll
+                        for (int cb = 0; cb < 4; ++cb) oacc[rb][cb] *= alpha;
+                    }
+                }
+                const _Float16 ps = static_cast<_Float16>(ldexpf(1.f, m - mc[rb]));
+                if (__builtin_amdgcn_ballot_w64(ps != _Float16(1.f))) {
+#pragma unroll
+                    for (int r = 2 * kb; r < 2 * kb + 2; ++r) pw[rb][r] *= ps;
+                }
             }
-            // the two row blocks alternate, so no MFMA waits on the one just before it
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
+            for (int cb = 0; cb < 4; ++cb) {
+                f16x8 vt[2];
 #pragma unroll
-                for (int rb = 0; rb < 2; ++rb)
-                    oacc[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vt[r], pw[rb][r], oacc[rb][cb], 0, 0, 0);
+                for (int r = 0; r < 2; ++r)
+                    vt[r] = fp8x8_to_f16x8(uint32_t(raw[cb][2 * kb + r].x), uint32_t(raw[cb][2 * kb + r].y));
+                // the two row blocks alternate, so no MFMA waits on the one just before it
+#pragma unroll
+                for (int r = 0; r < 2; ++r)
+#pragma unroll
+                    for (int rb = 0; rb < 2; ++rb)
+                        oacc[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vt[r], pw[rb][2 * kb + r], oacc[rb][cb], 0, 0, 0);
+            }
         }
     };
 
@@ -602,13 +636,16 @@ __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const MlaSplitAr
         issue_ids(3);
 #pragma unroll
         for (int j = 0; j < 3; ++j)
-            if (j < ntiles) copy_rows(j, pre_kid[j], pre_tid[j], pre_mid[j]);
+            if (j < ntiles) {
+                copy_lines(j, pre_kid[j], pre_mid[j]);
+                copy_tail(j, pre_tid[j]);
+            }
         issue_ids(4);
         issue_ids(5);
         // ids(3), rows(0), rows(1) landed; issued after rows(1): rows(2), ids(4), ids(5)
         wait_vmem(cnt_rows(2) + cnt_ids(4) + cnt_ids(5));
         __syncthreads();   // tiles 0 and 1, the ids of tile 3 and the masks of tiles 0-2 landed
-        __syncthreads();   // the score waves read tile 0 (tail slot 0 is refilled in step 0)
+        __syncthreads();   // the score waves read tile 0's rope tails (its slot is refilled in step 0)
         for (int t = 0; t < ntiles; ++t) {
             if (t > 0) pv(t - 1);
             // line slot (t + 3) % 4 held tile t - 1 and tail slot (t + 3) % 3 tile t: every read
@@ -623,6 +660,7 @@ __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const MlaSplitAr
             __syncthreads();   // P(t) published; tile t + 2 landed
         }
         pv(ntiles - 1);
+        __syncthreads();   // the score waves' final states published
     }
 
     // ---- epilogue: lane (n, h) of block cb holds columns m = 8 q + 4 h + 0..3 of row 32 rb + n;
@@ -635,12 +673,17 @@ __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const MlaSplitAr
         // partial row: [row, np] or, with planned slots, [slot, rows_per_req]
         const int64_t prow = a.part_start ? int64_t(rest) * a.rows_per_req + row0 + rl
                                           : row * a.np + part;
-        // the sums of the row over all its tiles, stored with the last tile's maximum
+        // the row's sums: those of the two score waves (one per block of every tile), each
+        // relative to its own maximum, brought to the accumulators' maximum mc
         float lq = 0.f, le = 0.f;
         if (ntiles > 0) {
-            const uint8_t *mlb = ML + ((ntiles - 1) & 1) * T::kMlBytes + rl * 4;
-            lq = *reinterpret_cast<const float *>(mlb + 256);
-            le = *reinterpret_cast<const float *>(mlb + 512);
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                const uint8_t *fin = P + (ntiles & 1) * 8192 + kb * 768 + rl * 4;
+                const float f = ldexpf(1.f, *reinterpret_cast<const int *>(fin) - mc[rb]);
+                lq = fmaf(*reinterpret_cast<const float *>(fin + 256), f, lq);
+                le = fmaf(*reinterpret_cast<const float *>(fin + 512), f, le);
+            }
         }
         const float inv = lq > 0.f ? a.out_scale / lq : 0.f;
         const float lse2 = le > 0.f ? float(mc[rb] - 8) + __log2f(le) : kNegInf;
