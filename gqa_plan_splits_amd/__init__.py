@@ -17,6 +17,8 @@ from ._lib import (  # noqa: F401
     block_k_for,
     decode,
     decode_plan,
+    decode_scratch,
+    SCRATCH_BYTES,
     decode_split,
     decode_workspace_bytes,
     decode_proportional,

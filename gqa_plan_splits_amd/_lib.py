@@ -11,19 +11,20 @@ KIND_MLA_FUSED = 0
 KIND_GQA_PAGED = 1
 FP8_E4M3FN = 0
 FP8_E4M3FNUZ = 1
+SCRATCH_BYTES = 64 << 20   # GQA_SCRATCH_BYTES: the device-side partials of decode_scratch
 
 # Every function include/gqa_splits.h declares.
 _SYMBOLS = ("plan_splits", "plan_sparse_splits", "plan_sparse_splits_measured", "plan_gqa_splits_measured", "block_k_for", "device_sm_count", "decode_plan", "decode_split",
             "splitk_reduce", "splitk_reduce_f32", "merge_ranks", "decode_workspace_bytes", "decode",
             "plan_proportional_device", "decode_proportional_workspace_bytes", "decode_proportional",
-            "fp8_e4m3_to_bf16",
+            "decode_scratch", "fp8_e4m3_to_bf16",
             "status_string", "last_error_detail")
 
 
 class GqaError(RuntimeError):
-    def __init__(self, status: int, where: str):
+    def __init__(self, status: int, where: str, with_detail: bool = False):
         self.status = status
-        detail = last_error_detail() if status == -4 else ""
+        detail = last_error_detail() if (status == -4 or with_detail) else ""
         super().__init__("%s failed: %s (status %d)%s" % (where, status_string(status), status,
                                                           (": " + detail) if detail else ""))
 
@@ -114,6 +115,7 @@ def _load():
     lib.plan_proportional_device.argtypes = [vp, vp, i64, i64, i64, i32, vp, vp, vp]
     lib.decode_proportional_workspace_bytes.argtypes = [pp, i64, i64, ctypes.POINTER(ctypes.c_size_t)]
     lib.decode_proportional.argtypes = [pp, i64, i64, i32, vp, ctypes.c_size_t, vp, vp, vp]
+    lib.decode_scratch.argtypes = [pp, i64, i32, vp, vp, vp]
     lib.fp8_e4m3_to_bf16.argtypes = [vp, i64, vp, vp]
     lib.status_string.argtypes = [i32]
     lib.status_string.restype = ctypes.c_char_p
@@ -351,6 +353,14 @@ def decode(problem: DecodeProblem, out, lse2_out=None, *, np: int = 0, block_k: 
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(_load().decode(ctypes.byref(problem), np, block_k, _ptr(workspace), ws_bytes, _ptr(out),
                           _ptr(lse2_out), _stream(stream)), "decode")
+
+
+def decode_scratch(problem: DecodeProblem, out, lse2_out=None, *, np: int = 0, block_k: int = 0,
+                   stream=None):
+    rc = _load().decode_scratch(ctypes.byref(problem), np, block_k, _ptr(out), _ptr(lse2_out),
+                                _stream(stream))
+    if rc != 0:
+        raise GqaError(rc, "decode_scratch", with_detail=True)
 
 
 def plan_proportional_device(seq_lens, extra_indptr, batch: int, budget: int, cap: int,

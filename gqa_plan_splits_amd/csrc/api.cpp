@@ -26,7 +26,13 @@ int ilog2(int64_t x) {
 }
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-thread_local char g_last_error[160] = "";
+thread_local char g_last_error[200] = "";
+
+}  // namespace
+
+void gqa::set_error_detail(const char *msg) { snprintf(g_last_error, sizeof g_last_error, "%s", msg); }
+
+namespace {
 
 int launch_status(hipError_t err, const char *what) {
     if (err == hipSuccess) return GQA_OK;

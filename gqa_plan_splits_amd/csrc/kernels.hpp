@@ -90,4 +90,7 @@ hipError_t launch_splitk_reduce(const ReduceArgs &a, hipStream_t s);
 hipError_t launch_plan_proportional(const PlanArgs &a, hipStream_t s);
 hipError_t launch_fp8_to_bf16(const uint8_t *in, int64_t n, uint16_t *out, hipStream_t s);
 
+// Sets the text last_error_detail() returns on this thread (host code of the C ABI).
+void set_error_detail(const char *msg);
+
 }  // namespace gqa

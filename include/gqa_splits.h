@@ -26,9 +26,11 @@
  * Conventions (all entry points):
  *   - Row numbering: row r = (b * q_len + t) * H + h for request b, draft position t, query
  *     head h.  Row (b, t, h) attends keys 0 .. seq_lens[b] - q_len + t of request b [MM].
- *   - Ownership: the caller owns every buffer.  The library never allocates device memory;
- *     decode() takes its scratch space as a caller-provided workspace.  Outputs are written in
- *     place.  The only state is the CU count of each device, cached on first query.
+ *   - Ownership: the caller owns every buffer.  The library never calls an allocator: decode()
+ *     takes its scratch space as a caller-provided workspace, and decode_scratch() uses a
+ *     fixed device-side array of the library's code object.  Outputs are written in place.  The
+ *     only other state is the CU count and the scratch address of each device, cached on first
+ *     query.
  *   - Streams: every kernel is enqueued on the caller's stream `s` (a hipStream_t; NULL is the
  *     null stream).  No entry point synchronises the host with the device, so every call can be
  *     captured into a HIP graph.
@@ -320,6 +322,26 @@ int decode_proportional(const gqa_decode_problem *p, int64_t np_or_0, int64_t ca
                         int block_k_or_0, void *workspace, size_t ws_bytes, void *out,
                         float *lse2_out, gqa_stream_t s);
 
+/* Bytes of the device-side scratch array decode_scratch() keeps its partials in (64 MiB per GPU). */
+#define GQA_SCRATCH_BYTES ((size_t)64 << 20)
+
+/* Allocation-free decode, for callers that cannot allocate device memory or pass a workspace
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid allocation): the same
+ * plan, split and reduce as decode(), with the fp32 partials in a device-side array of
+ * GQA_SCRATCH_BYTES that the library's code object holds on every GPU it runs on until the
+ * process ends.  Calls nothing that allocates.  The first call on a device queries that device's
+ * address of the array (hipGetSymbolAddress) and caches it.
+ *   out      [B*q_len, H, d_v] bf16, contiguous (output)
+ *   lse2_out [B*q_len, H] fp32 (output; may be NULL)
+ * The array is shared by every call on a GPU and holds the last call's partials: calls that
+ * overlap on one GPU (other streams, other threads) race and must be serialized by the caller.
+ * Nothing in it needs clearing (every partial a call reads, that call wrote).
+ * Errors: as decode, and WORKSPACE_TOO_SMALL when the partials of the plan exceed
+ * GQA_SCRATCH_BYTES (np == 1 needs none); DEVICE when the array's address cannot be queried.
+ * last_error_detail() then says how many bytes were needed. */
+int decode_scratch(const gqa_decode_problem *p, int64_t np_or_0, int block_k_or_0, void *out,
+                   float *lse2_out, gqa_stream_t s);
+
 /* Utility: decode n OCP e4m3fn bytes to bf16 with the same conversion the MLA split kernel
  * applies to the pool (exact; unit scale).  in, out 16-byte aligned device buffers; out holds
  * n bf16 values.  Lets callers and tests check the device's fp8 decoding byte by byte. */
@@ -328,8 +350,8 @@ int fp8_e4m3_to_bf16(const void *in, int64_t n, void *out, gqa_stream_t s);
 /* Static description of a status code. */
 const char *status_string(int status);
 
-/* Text of the HIP error behind the calling thread's most recent GQA_ERR_LAUNCH_FAILED ("" if
- * none); valid until the thread's next failing call. */
+/* Text behind the calling thread's most recent GQA_ERR_LAUNCH_FAILED (the HIP error) or
+ * decode_scratch failure ("" if none); valid until the thread's next failing call. */
 const char *last_error_detail(void);
 
 #ifdef __cplusplus

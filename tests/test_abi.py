@@ -377,3 +377,23 @@ def test_gqa_measured_planner_properties():
     expect_status(lambda: g.plan_gqa_splits_measured(0, 100, 1, 256), -1)
     expect_status(lambda: g.plan_gqa_splits_measured(1, -1, 1, 256), -1)
     expect_status(lambda: g.plan_gqa_splits_measured(1, 100, 0, 256), -1)
+
+
+def test_decode_scratch_rejects_partials_beyond_the_static_array():
+    # checked on the host before anything touches the device: 4096 rows x 256 partitions of
+    # 512 fp32 values need 2 GiB, beyond GQA_SCRATCH_BYTES
+    prob = g.DecodeProblem()
+    prob.kind, prob.fp8_format = g.KIND_MLA_FUSED, g.FP8_E4M3FN
+    prob.batch, prob.q_len, prob.num_heads, prob.num_kv_heads = 64, 1, 64, 1
+    prob.d_qk, prob.d_rope, prob.d_v, prob.page_size, prob.max_num_keys = 576, 64, 512, 1, 300
+    prob.q = prob.q_pe = prob.kv = prob.kv_indices = prob.kv_indptr = prob.seq_lens = FAKE
+    prob.q_stride_tok, prob.q_stride_head = 64 * 512, 512
+    prob.q_pe_stride_tok, prob.q_pe_stride_head = 64 * 64, 64
+    prob.kv_stride_row = 576
+    prob.scale, prob.kv_scale = 576 ** -0.5, 1 / 32
+    assert g.decode_workspace_bytes(prob, 256) > g.SCRATCH_BYTES
+    with pytest.raises(g.GqaError) as e:
+        g.decode_scratch(prob, FAKE, FAKE, np=256, block_k=32)
+    assert e.value.status == -3 and "static scratch holds" in str(e.value)
+    # a plan that fits goes past this check (and would need the device)
+    assert g.decode_workspace_bytes(prob, 2) <= g.SCRATCH_BYTES
