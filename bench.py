@@ -44,6 +44,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle sample")
     ap.add_argument("--table-steps", type=int, default=20)
+    ap.add_argument("--oracle-seconds", type=float, default=1.0,
+                    help="target CPU time of each workload's oracle sample in the per-workload table")
     ap.add_argument("--settle-ms", type=float, default=150.0,
                     help="untimed run of each workload's step before its warmup, so clocks settle")
     ap.add_argument("--block-k", type=int, default=0,
@@ -119,7 +121,7 @@ class Case:
 
     def proportional_step(self):
         # the same budget of np partitions per request, planned on the device in proportion to
-        # the lengths (at most 4 np per request)
+        # the lengths (at most 256 partitions per request: cap 0)
         import torch
         if not hasattr(self, "ws_prop"):
             n = self.g.decode_proportional_workspace_bytes(self.p, self.np)
@@ -197,6 +199,100 @@ def measured_counters(workload):
     busy = float(vals["mfma_busy_cycles"]) / (
         float(vals["grbm_gui_active"]) / float(vals["xcds"]) * float(vals["simds"]))
     return {"traffic": int(fetch + write), "mfma_busy": round(busy, 4)}
+
+
+def cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo), and the logical CPUs this process may use."""
+    name = platform.processor() or platform.machine()
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    name = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return name
+
+
+def oracle_sample(case, target_s, n_threads=0):
+    """The oracle on a bounded sample of this workload's rows (doubling the sample until it takes
+    about target_s / 2), extrapolated to the whole call; also the sampled rows' parity of the GPU
+    output against it."""
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    import oracle
+    from gpu_util import compare, oracle_gqa, oracle_mla, sample_rows
+    inp = case.inp
+    H = inp.H if case.is_mla else inp.Hq
+    total = case.rows
+    threads = n_threads or oracle.default_threads()
+    n = min(total, max(threads, 4))
+    while True:
+        rows = sample_rows(inp.B, inp.q_len, H, n, seed=n) if n < total else list(range(total))
+        t0 = time.perf_counter()
+        ref_o, ref_l = (oracle_mla if case.is_mla else oracle_gqa)(inp, rows, n_threads=threads)
+        dt = time.perf_counter() - t0
+        if dt * 2.2 > target_s or n >= total:
+            break
+        n = min(total, n * 2)
+    max_abs, rel, lse_err = compare(case.out[rows], case.lse[rows], ref_o, ref_l, inp.name + " oracle sample")
+    return {"s_per_call": round(dt * total / len(rows), 4), "rows": len(rows), "of_rows": total,
+            "threads": threads, "sample_s": round(dt, 3),
+            "parity": {"max_abs": max_abs, "rel": rel, "lse2_rel": lse_err}}
+
+
+def planner_ns_per_call(reps=20000):
+    """Host planner and tile rule through the C ABI (ctypes call included), ns per call."""
+    import gqa_plan_splits_amd as g
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        g.plan_splits(16, 131072, 64, 256, 1)
+    t_plan = (time.perf_counter() - t0) / reps
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        g.block_k_for(512, 256)
+    t_bk = (time.perf_counter() - t0) / reps
+    return {"plan_splits_ns": round(t_plan * 1e9, 1), "block_k_for_ns": round(t_bk * 1e9, 1),
+            "note": "ctypes call from Python included"}
+
+
+def ceilings(stream, case):
+    """Streaming-read and row-gather ceilings of this GPU with the split kernels' copy instruction
+    (the library's bw_stream_read and bw_gather_rows): a 2 GiB contiguous read, and a gather of
+    the headline workload's own shuffled slot list over its pool, in the MLA kernel's copy
+    pattern.  Median of 5 timed launches after 2 untimed ones, HIP events on the stream."""
+    import torch
+    import gqa_plan_splits_amd as g
+    inp = case.inp
+    buf = torch.ones(2 << 30, dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+
+    def timed(fn):
+        for _ in range(2):
+            fn()
+        ts = sorted(time_events(fn, 1, stream) for _ in range(5))
+        return ts[2]
+    ms_stream = timed(lambda: g.bw_stream_read(buf, buf.numel(), 1024, stream=stream))
+    del buf
+    torch.cuda.empty_cache()
+    n = (inp.kv_indices.numel() // 64) * 64
+    row_bytes = inp.pool.shape[1]
+    ms_gather = timed(lambda: g.bw_gather_rows(inp.pool, row_bytes, inp.kv_indices, n, 256, stream=stream))
+    stream_gbs = (2 << 30) / (ms_stream * 1e-3) / 1e9
+    gather_gbs = n * row_bytes / (ms_gather * 1e-3) / 1e9
+    return {"stream_read_gbs": round(stream_gbs, 1), "stream_read_pct_peak": round(100 * stream_gbs / HBM_PEAK_GBS, 1),
+            "gather_rows_gbs": round(gather_gbs, 1), "gather_rows_pct_peak": round(100 * gather_gbs / HBM_PEAK_GBS, 1),
+            "gather_rows": n, "row_bytes": row_bytes,
+            "method": "bw_stream_read (2 GiB, 1024 CTAs) and bw_gather_rows (the headline's slot list, 256 CTAs); "
+                      "global_load_lds_dwordx4 nt into LDS; median of 5 launches, HIP events"}
+
+
+def mla_flops(inp):
+    """Algorithmic flops of one MLA decode: per (row, visible key) 2 * (d_qk + d_v) (QK^T and PV)."""
+    lens = inp.seq_lens.tolist()
+    q, H = inp.q_len, inp.H
+    keys = sum(sum(max(0, L - q + t + 1) for t in range(q)) for L in lens)
+    return keys * H * 2 * (inp.d_qk + inp.d_v)
 
 
 def settle(fn, ms):
@@ -376,14 +472,17 @@ def wave_sweep(stream, steps):
 
 
 def branch_sweep(stream, steps):
-    """The planner's other branches on this library's kernels: MLA with 32 and 128 heads, and
+    """The planner's other branches on this library's kernels: MLA with 16 heads (the page's
+    two-wave exception), 32, 64 (two requests of 65536 keys) and 128 heads, and
     GQA with one kv head (16 query heads) and with 4 query heads per kv head, each timed at every
     power-of-two partition count up to 256 (graph-replayed decode calls) beside the planner's
     choice."""
     import torch
     import gqa_plan_splits_amd as g
     import workloads as w
-    cases = [("mla_h32_b4_s65536", "mla", 4, 32, 1, 65536), ("mla_h32_b16_s16384", "mla", 16, 32, 1, 16384),
+    cases = [("mla_h16_b4_s65536", "mla", 4, 16, 1, 65536), ("mla_h16_b16_s16384", "mla", 16, 16, 1, 16384),
+             ("mla_h64_b2_s65536", "mla", 2, 64, 1, 65536),
+             ("mla_h32_b4_s65536", "mla", 4, 32, 1, 65536), ("mla_h32_b16_s16384", "mla", 16, 32, 1, 16384),
              ("mla_h128_b4_s65536", "mla", 4, 128, 1, 65536), ("mla_h128_b16_s16384", "mla", 16, 128, 1, 16384),
              ("gqa_hq16_hkv1_b8_s32768", "gqa", 8, 16, 1, 32768), ("gqa_hq16_hkv1_b64_s8192", "gqa", 64, 16, 1, 8192),
              ("gqa_hq32_hkv8_b8_s32768", "gqa", 8, 32, 8, 32768), ("gqa_hq32_hkv8_b64_s8192", "gqa", 64, 32, 8, 8192)]
@@ -422,10 +521,10 @@ def branch_sweep(stream, steps):
         best = min(times, key=times.get)
         res[name] = {"us_by_np": {str(k): round(v, 2) for k, v in times.items()}, "best_np": best,
                      "planner_np": planner, "planner_vs_best": round(times[planner] / times[best], 3)}
-        if kind == "gqa":   # the MI355X-measured GQA variant (a power of two, or the planner's np)
-            m = g.plan_gqa_splits_measured(B, S, Hkv)
-            if m in times:
-                res[name].update(measured_np=m, measured_vs_best=round(times[m] / times[best], 3))
+        # the MI355X-measured variants (a power of two, or the planner's np)
+        m = g.plan_gqa_splits_measured(B, S, Hkv) if kind == "gqa" else g.plan_mla_splits_measured(B, S, H)
+        if m in times:
+            res[name].update(measured_np=m, measured_vs_best=round(times[m] / times[best], 3))
         print("# branch %s %s" % (name, json.dumps(res[name])), file=sys.stderr, flush=True)
         del inp, p, out, lse
         torch.cuda.empty_cache()
@@ -567,7 +666,7 @@ def cpu_baseline(case, target_s):
         "sample": "%d of %d output rows of %s (fp64 unsplit attention, %d threads, %.2f s); "
                   "value = KV bytes / (sample time x rows / sampled rows)"
                   % (len(rows), total_rows, inp.name, cores, dt),
-        "cpu_model": platform.processor() or platform.machine(),
+        "cpu_model": cpu_model(),
         "parity": {"max_abs": max_abs, "rel": rel, "lse2_rel": lse_err, "rows": len(rows)},
     }
 
@@ -649,6 +748,12 @@ def main():
             "us_per_call_proportional": round(ms_prop * 1e3, 2) if ms_prop else None,
             "proportional_vs_equal": round(ms_prop / ms_eq, 3) if ms_prop else None,
         }
+        if not args.headline_only and not args.no_cpu_baseline:
+            entry["oracle"] = oracle_sample(case, args.oracle_seconds)
+            if name == "mla_tiny_b1_h16_s4096_np1":   # the tiny call on one host thread
+                entry["oracle_single_thread"] = oracle_sample(case, 60.0, n_threads=1)
+        if case.is_mla and inp.q_len == 4:
+            entry["mfma_tflops"] = round(mla_flops(inp) / (ms_split * 1e-3) / 1e12, 1)
         table[name] = entry
         print("# %-36s %s" % (name, json.dumps(entry)), file=sys.stderr, flush=True)
         if is_head:
@@ -662,7 +767,8 @@ def main():
         sys.exit(2)
     case, ms, ms_split, steps = headline
     alg = case.split_algorithmic_bytes()
-    achieved = alg / (ms_split * 1e-3) / 1e9
+    kv = case.kv_bytes()
+    achieved = kv / (ms_split * 1e-3) / 1e9
     counters = measured_counters(args.workload)
     inp = case.inp
     result = {
@@ -676,7 +782,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "fp8e4m3 KV decoded exactly: bf16 QK^T and fp16 PV MFMA, fp32 accumulate" if case.is_mla
+                 else "bf16 QK^T and PV MFMA, fp32 accumulate",
         "data": "synthetic (seeded N(0,1) bf16 queries, fp8 e4m3fn KV = N(0,1)*32, shuffled slots)",
         "config": {
             "workload": args.workload,
@@ -698,12 +805,29 @@ def main():
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": counters["traffic"] if counters else None,
             "mfma_busy": counters["mfma_busy"] if counters else None,
-            "algorithmic_bytes": alg,
+            "algorithmic_bytes": kv,
+            "algorithmic_bytes_what": "KV payload: every key's row once (576 B per key)",
+            "bytes_with_ids_q_partials": alg,
             "avg_launch_us": round(ms_split * 1e3, 2),
+            "timer": "HIP events on the launch stream around the split-only launches of the timed "
+                     "interleaved rounds (average per launch)",
         },
         "per_config": table,
     }
+    q4 = table.get("mla_h64_b16_s131072_q4")
+    if q4 and "mfma_tflops" in q4:
+        result["roofline_q4"] = {
+            "kernel": "mla_split_kernel", "workload": "mla_h64_b16_s131072_q4", "bound": "mfma",
+            "achieved": q4["mfma_tflops"], "peak": 2500.0, "unit": "TFLOP/s",
+            "frac": round(q4["mfma_tflops"] / 2500.0, 4), "avg_launch_us": q4["split_us"],
+            "flops_what": "per (row, visible key) 2 x (576 + 512): QK^T on bf16 MFMA and PV on fp16 MFMA, "
+                          "both at the 2.5 PFLOP/s dense bf16/fp16 peak"}
     if not args.headline_only:
+        result["ceilings"] = ceilings(stream, case)
+        result["ceilings"]["headline_split_pct_of_gather"] = round(
+            100 * achieved / result["ceilings"]["gather_rows_gbs"], 1)
+        print("# ceilings %s" % json.dumps(result["ceilings"]), file=sys.stderr, flush=True)
+        result["planner_ns"] = planner_ns_per_call()
         result["dcp"] = dcp_line(stream, args.table_steps)
         print("# dcp %s" % json.dumps(result["dcp"]), file=sys.stderr, flush=True)
         result["planner_waves"] = wave_sweep(stream, args.table_steps)

@@ -15,6 +15,8 @@ from ._lib import (  # noqa: F401
     FP8_E4M3FN,
     FP8_E4M3FNUZ,
     block_k_for,
+    bw_gather_rows,
+    bw_stream_read,
     decode,
     decode_plan,
     decode_scratch,
@@ -33,6 +35,7 @@ from ._lib import (  # noqa: F401
     merge_ranks,
     mla_problem,
     plan_gqa_splits_measured,
+    plan_mla_splits_measured,
     plan_sparse_splits,
     plan_sparse_splits_measured,
     plan_splits,

@@ -14,10 +14,10 @@ FP8_E4M3FNUZ = 1
 SCRATCH_BYTES = 64 << 20   # GQA_SCRATCH_BYTES: the device-side partials of decode_scratch
 
 # Every function include/gqa_splits.h declares.
-_SYMBOLS = ("plan_splits", "plan_sparse_splits", "plan_sparse_splits_measured", "plan_gqa_splits_measured", "block_k_for", "device_sm_count", "decode_plan", "decode_split",
+_SYMBOLS = ("plan_splits", "plan_sparse_splits", "plan_sparse_splits_measured", "plan_gqa_splits_measured", "plan_mla_splits_measured", "block_k_for", "device_sm_count", "decode_plan", "decode_split",
             "splitk_reduce", "splitk_reduce_f32", "merge_ranks", "decode_workspace_bytes", "decode",
             "plan_proportional_device", "decode_proportional_workspace_bytes", "decode_proportional",
-            "decode_scratch", "fp8_e4m3_to_bf16",
+            "decode_scratch", "fp8_e4m3_to_bf16", "bw_stream_read", "bw_gather_rows",
             "status_string", "last_error_detail")
 
 
@@ -104,6 +104,7 @@ def _load():
                                        ctypes.POINTER(i64)]
     lib.plan_sparse_splits_measured.argtypes = [i64, i64, i64, i64, i64, i64, i64, ctypes.POINTER(i64)]
     lib.plan_gqa_splits_measured.argtypes = [i64, i64, i64, i64, ctypes.POINTER(i64)]
+    lib.plan_mla_splits_measured.argtypes = [i64, i64, i64, i64, ctypes.POINTER(i64)]
     lib.device_sm_count.argtypes = [ctypes.POINTER(i64)]
     lib.decode_plan.argtypes = [pp, i64, i32, i64, ctypes.POINTER(i64), ctypes.POINTER(i32)]
     lib.decode_split.argtypes = [pp, i64, i32, vp, vp, vp]
@@ -117,6 +118,8 @@ def _load():
     lib.decode_proportional.argtypes = [pp, i64, i64, i32, vp, ctypes.c_size_t, vp, vp, vp]
     lib.decode_scratch.argtypes = [pp, i64, i32, vp, vp, vp]
     lib.fp8_e4m3_to_bf16.argtypes = [vp, i64, vp, vp]
+    lib.bw_stream_read.argtypes = [vp, ctypes.c_size_t, i64, vp]
+    lib.bw_gather_rows.argtypes = [vp, i64, vp, i64, i64, vp]
     lib.status_string.argtypes = [i32]
     lib.status_string.restype = ctypes.c_char_p
     lib.last_error_detail.argtypes = []
@@ -186,6 +189,14 @@ def plan_gqa_splits_measured(batch_size: int, max_num_keys: int, num_kv_heads: i
     out = ctypes.c_int64(0)
     _check(_load().plan_gqa_splits_measured(batch_size, max_num_keys, num_kv_heads, sm_count,
                                             ctypes.byref(out)), "plan_gqa_splits_measured")
+    return out.value
+
+
+def plan_mla_splits_measured(batch_size: int, max_num_keys: int, rows_per_request: int,
+                             sm_count: int = 0) -> int:
+    out = ctypes.c_int64(0)
+    _check(_load().plan_mla_splits_measured(batch_size, max_num_keys, rows_per_request, sm_count,
+                                            ctypes.byref(out)), "plan_mla_splits_measured")
     return out.value
 
 
@@ -361,6 +372,15 @@ def decode_scratch(problem: DecodeProblem, out, lse2_out=None, *, np: int = 0, b
                                 _stream(stream))
     if rc != 0:
         raise GqaError(rc, "decode_scratch", with_detail=True)
+
+
+def bw_stream_read(src, nbytes: int, ctas: int, stream=None):
+    _check(_load().bw_stream_read(_ptr(src), nbytes, ctas, _stream(stream)), "bw_stream_read")
+
+
+def bw_gather_rows(pool, row_bytes: int, idx, n: int, ctas: int, stream=None):
+    _check(_load().bw_gather_rows(_ptr(pool), row_bytes, _ptr(idx), n, ctas, _stream(stream)),
+           "bw_gather_rows")
 
 
 def plan_proportional_device(seq_lens, extra_indptr, batch: int, budget: int, cap: int,

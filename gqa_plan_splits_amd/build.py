@@ -13,7 +13,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libgqa_splits.so")
-SOURCES = ["plan.cpp", "api.cpp", "mla_split.hip", "gqa_split.hip", "splitk_reduce.hip", "plan_device.hip", "scratch.hip"]
+SOURCES = ["plan.cpp", "api.cpp", "mla_split.hip", "gqa_split.hip", "splitk_reduce.hip", "plan_device.hip", "scratch.hip", "ceiling.hip"]
 HEADERS = ["kernels.hpp", "device_common.hpp"]
 ARCH = "gfx950"
 

@@ -248,3 +248,23 @@ extern "C" int plan_gqa_splits_measured(int64_t batch_size, int64_t max_num_keys
     *np_out = std::max(base, fill);
     return GQA_OK;
 }
+
+extern "C" int plan_mla_splits_measured(int64_t batch_size, int64_t max_num_keys,
+                                        int64_t rows_per_request, int64_t sm_count, int64_t *np_out) {
+    if (!np_out || batch_size < 1 || max_num_keys < 0 || rows_per_request < 1)
+        return GQA_ERR_INVALID_ARGUMENT;
+    if (sm_count <= 0) {
+        const int rc = device_sm_count(&sm_count);
+        if (rc != GQA_OK) return rc;
+    }
+    // this library's MLA split kernel runs one CTA of 64 query rows per CU, each hiding its own
+    // read latency: one wave of those CTAs fills the chip, and a partition keeps at least four
+    // 64-key tiles
+    constexpr int64_t kRowsPerCta = 64, kMinKeys = 256, kMax = 256;
+    const int64_t ctas = batch_size * ((rows_per_request + kRowsPerCta - 1) / kRowsPerCta);
+    const int64_t key_cap = std::max<int64_t>(1, std::min(kMax, max_num_keys / kMinKeys));
+    int64_t np = 1;
+    while (np * 2 <= key_cap && ctas * np * 2 <= sm_count) np *= 2;
+    *np_out = np;
+    return GQA_OK;
+}

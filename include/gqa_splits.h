@@ -200,6 +200,18 @@ int plan_sparse_splits(int64_t num_tokens, int64_t num_heads, int64_t topk, int6
 int plan_gqa_splits_measured(int64_t batch_size, int64_t max_num_keys, int64_t num_kv_heads,
                              int64_t sm_count, int64_t *np_out);
 
+/* The partition count this library's MLA split kernel measured best on MI355X (a tuning for this
+ * kernel, not a rule of the pages; plan_splits stays [MAX]'s rule): the largest power of two np
+ * <= 256 with batch_size * ceil(rows_per_request / 64) * np <= sm_count -- one wave of the
+ * kernel's 64-row CTAs, of which one runs per CU and hides its own read latency -- and at least
+ * 256 keys (four 64-key tiles) per partition; 1 when neither allows 2.  rows_per_request is
+ * q_len * H.  Where [MAX]'s EXCEPTION paragraph (MLA with <= 16 heads) asks for two waves,
+ * this keeps one: a second wave of this kernel's CTAs only adds their prologues and epilogues.
+ * sm_count <= 0 queries the current device.  Checked by the benchmark's planner-branch sweep.
+ * Errors: INVALID_ARGUMENT (NULL output, a size below its bound), DEVICE. */
+int plan_mla_splits_measured(int64_t batch_size, int64_t max_num_keys, int64_t rows_per_request,
+                             int64_t sm_count, int64_t *np_out);
+
 /* The sparse planner's decision with thresholds measured on MI355X for this library's MLA
  * kernel rather than the page's (which were measured for a Blackwell kernel): the largest power
  * of two (<= max_splits) that keeps num_tokens * ceil(num_heads / rows_per_cta) * splits within
@@ -346,6 +358,27 @@ int decode_scratch(const gqa_decode_problem *p, int64_t np_or_0, int block_k_or_
  * applies to the pool (exact; unit scale).  in, out 16-byte aligned device buffers; out holds
  * n bf16 values.  Lets callers and tests check the device's fp8 decoding byte by byte. */
 int fp8_e4m3_to_bf16(const void *in, int64_t n, void *out, gqa_stream_t s);
+
+/* ---------------------------------------------------------------------------------------- */
+/* Measurement: data-movement ceilings of this GPU (for the benchmark's roofline)            */
+/* ---------------------------------------------------------------------------------------- */
+
+/* Reads `bytes` contiguous bytes of src into LDS with the copy instruction the split kernels use
+ * (global_load_lds_dwordx4, non-temporal), discarding them: the streaming-read ceiling.  ctas
+ * workgroups of 4 waves each read bytes / ctas contiguous bytes.  src 16-byte aligned device
+ * memory; bytes a multiple of ctas * 4096.  Enqueued on s.  Errors: INVALID_ARGUMENT (NULL src,
+ * ctas < 1), UNSUPPORTED (alignment, sizes), LAUNCH_FAILED. */
+int bw_stream_read(const void *src, size_t bytes, int64_t ctas, gqa_stream_t s);
+
+/* Gathers the n rows pool[idx[i] * row_bytes ..] (row_bytes 576 or 512) into LDS with the MLA split
+ * kernel's copy pattern and instruction (per 64 rows: four lines of 128 bytes, 8 rows per copy,
+ * and for 576-byte rows the 64-byte rope tails, 16 rows per copy), discarding them: the ceiling of
+ * that kernel's gather [MM, MLA decode: page_size 1 slot lists].  ctas workgroups of 4 waves take
+ * 64-row groups in turn.  pool and idx 16-byte aligned device memory; every idx[i] a pool row
+ * (not checked); n a multiple of 64.  Enqueued on s.  Errors: INVALID_ARGUMENT, UNSUPPORTED,
+ * LAUNCH_FAILED. */
+int bw_gather_rows(const void *pool, int64_t row_bytes, const int32_t *idx, int64_t n, int64_t ctas,
+                   gqa_stream_t s);
 
 /* Static description of a status code. */
 const char *status_string(int status);

@@ -397,3 +397,41 @@ def test_decode_scratch_rejects_partials_beyond_the_static_array():
     assert e.value.status == -3 and "static scratch holds" in str(e.value)
     # a plan that fits goes past this check (and would need the device)
     assert g.decode_workspace_bytes(prob, 2) <= g.SCRATCH_BYTES
+
+
+def test_mla_measured_planner_properties():
+    for B in (1, 2, 3, 8, 16, 64, 300):
+        for S in (0, 100, 255, 256, 4096, 16384, 131072, 1 << 20):
+            for rows in (1, 16, 64, 65, 128, 256):
+                for sm in (80, 256):
+                    n = g.plan_mla_splits_measured(B, S, rows, sm)
+                    ctas = B * -(-rows // 64)
+                    assert 1 <= n <= 256 and n & (n - 1) == 0
+                    if n > 1:
+                        assert ctas * n <= sm and n * 256 <= S
+                    # the largest such power of two
+                    assert 2 * n > 256 or ctas * 2 * n > sm or 2 * n * 256 > S
+    # the two-wave exception of the pages' planner (MLA, 16 heads) becomes one wave of CTAs
+    assert g.plan_splits(4, 65536, 16, 256, True) == 128
+    assert g.plan_mla_splits_measured(4, 65536, 16, 256) == 64
+    expect_status(lambda: g.plan_mla_splits_measured(0, 100, 64, 256), -1)
+    expect_status(lambda: g.plan_mla_splits_measured(1, -1, 64, 256), -1)
+    expect_status(lambda: g.plan_mla_splits_measured(1, 100, 0, 256), -1)
+
+
+def test_ceiling_argument_rejections():
+    expect_status(lambda: g.bw_stream_read(FAKE, 4096 * 3, 2), -2)      # not a multiple of ctas * 4 KiB
+    expect_status(lambda: g.bw_stream_read(FAKE + 4, 4096, 1), -2)      # misaligned
+    expect_status(lambda: g.bw_stream_read(FAKE, 4096, 0), -1)
+    expect_status(lambda: g.bw_gather_rows(FAKE, 300, FAKE, 64, 1), -2)  # row width
+    expect_status(lambda: g.bw_gather_rows(FAKE, 576, FAKE, 65, 1), -2)  # not 64-row groups
+    expect_status(lambda: g.bw_gather_rows(FAKE, 576, FAKE, -64, 1), -1)
+
+
+@pytest.mark.parametrize("B,S,rows,best", [(4, 65536, 16, 64), (16, 16384, 16, 16), (2, 65536, 64, 128),
+                                           (4, 65536, 32, 64), (16, 16384, 32, 16), (4, 65536, 128, 32),
+                                           (16, 16384, 128, 8), (16, 131072, 64, 16), (8, 131072, 64, 32)])
+def test_mla_measured_planner_hits_the_measured_best(B, S, rows, best):
+    # the best partition counts of the planner-branch sweep on MI355X (256 CUs), graph-replayed
+    # decode calls at every power-of-two np; the last two rows are the long-context workloads
+    assert g.plan_mla_splits_measured(B, S, rows, 256) == best
