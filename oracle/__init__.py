@@ -81,6 +81,10 @@ def _load():
                                           _vp, _vp, _vp, _dbl, _dbl, _int, _vp, _i64, _vp, _vp,
                                           _int]
         lib.oracle_mla_decode_two_caches.restype = _int
+        lib.oracle_mla_decode_bf16.restype = _int
+        lib.oracle_mla_decode_bf16.argtypes = [_i64, _i64, _i64, _i64, _i64, _i64, _vp, _vp, _vp, _i64,
+                                               _vp, _vp, _vp, ctypes.c_double, ctypes.c_double, _vp,
+                                               _i64, _vp, _vp, _int]
         lib.oracle_mla_decode_two_caches.argtypes = [_i64, _i64, _i64, _i64, _i64, _vp, _vp, _vp,
                                                      _i64, _vp, _vp, _vp, _vp, _i64, _vp, _vp,
                                                      _dbl, _dbl, _vp, _i64, _vp, _vp, _int]
@@ -196,7 +200,7 @@ def mla_decode(q_lat, q_pe, pool, kv_indices, kv_indptr, seq_lens, *, B, q_len, 
     """fp64 unsplit attention for absorbed MLA decode.
 
     q_lat: uint16 bf16 bits [B*q_len, H, d_lat]; q_pe: [B*q_len, H, d_rope] or None;
-    pool: uint8 [N, d_lat + d_rope].  With pool2 (q_len 1): query b also attends the second
+    pool: uint8 fp8 bytes [N, d_lat + d_rope], or uint16 bf16 bits (the bf16-cache variant).  With pool2 (q_len 1): query b also attends the second
     cache's rows kv2_indices[kv2_indptr[b]:kv2_indptr[b+1]], in the same softmax.
     Returns (o [n_rows, d_v] float64, lse2 [n_rows])."""
     q_lat = _c(q_lat, np.uint16)
@@ -206,7 +210,8 @@ def mla_decode(q_lat, q_pe, pool, kv_indices, kv_indptr, seq_lens, *, B, q_len, 
         d_rope = q_pe.shape[-1]
     else:
         d_rope = 0
-    pool = _c(pool, np.uint8)
+    kv_bf16 = np.asarray(pool).dtype == np.uint16
+    pool = _c(pool, np.uint16 if kv_bf16 else np.uint8)
     assert pool.shape[-1] == d_lat + d_rope, (pool.shape, d_lat, d_rope)
     kv_indices = _c(kv_indices, np.int32)
     kv_indptr = _c(kv_indptr, np.int32)
@@ -214,7 +219,14 @@ def mla_decode(q_lat, q_pe, pool, kv_indices, kv_indptr, seq_lens, *, B, q_len, 
     rows_a, n_rows = _rows_arg(rows, B * q_len * H)
     o = np.empty((n_rows, d_v), dtype=np.float64)
     lse2 = np.empty((n_rows,), dtype=np.float64)
-    if pool2 is None:
+    if kv_bf16:
+        assert pool2 is None and not fnuz
+        rc = _load().oracle_mla_decode_bf16(B, q_len, H, d_lat, d_rope, d_v, _ptr(q_lat), _ptr(q_pe),
+                                            _ptr(pool), pool.shape[0], _ptr(kv_indices),
+                                            _ptr(kv_indptr), _ptr(seq_lens), float(scale),
+                                            float(kv_scale), _ptr(rows_a), n_rows, _ptr(o), _ptr(lse2),
+                                            int(n_threads))
+    elif pool2 is None:
         rc = _load().oracle_mla_decode(B, q_len, H, d_lat, d_rope, d_v, _ptr(q_lat), _ptr(q_pe),
                                        _ptr(pool), pool.shape[0], _ptr(kv_indices), _ptr(kv_indptr),
                                        _ptr(seq_lens), float(scale), float(kv_scale), int(bool(fnuz)),

@@ -17,6 +17,9 @@
  *  - Skipped keys: AITER issue "[Perf] pa_decode_sparse ...", section "Measurements" (the
  *    has_invalid flag of the top-k index lists): a negative slot id in an MLA index list is a
  *    key that is not attended.
+ *  - bf16 cache: AITER issue "[Perf] pa_decode_sparse ...", closing paragraph (an offer to
+ *    re-measure on a bf16 cache).  Read as the same fused rows stored as bf16 instead of fp8,
+ *    dequantized by the same per-tensor scale (1 for a plain bf16 cache).
  *  - Second cache: FlashInfer API page "cake_sparse_mla_sm120_dsv4_nvfp4_plan_splits", Parameters
  *    (extra_topk: candidate slots per token in a second cache).  Read as a second pool of rows of
  *    the same format and scale whose candidates a query attends together with its main-cache
@@ -235,6 +238,7 @@ typedef struct {
     const uint8_t *pool2;            /* a second cache, or NULL */
     const int32_t *kv2_indices, *kv2_indptr;
     const double *fp8_table; /* 256 decoded values */
+    int kv_bf16;             /* the pool holds bf16 rows (2 bytes per element) instead of fp8 */
     /* GQA */
     int64_t Hkv, D, page_size;
     const uint16_t *q, *k_cache, *v_cache;
@@ -266,7 +270,13 @@ static const uint8_t *mla_row(const attn_job *j, int64_t b, int64_t k) {
         slot = j->kv2_indices[j->kv2_indptr[b] + (k - j->seq_lens[b])];
         pool = j->pool2;
     }
-    return slot < 0 ? NULL : pool + slot * dqk;
+    return slot < 0 ? NULL : pool + slot * dqk * (j->kv_bf16 ? 2 : 1);
+}
+
+/* Element d of a pool row, dequantized: e4m3 by table, or bf16, times kv_scale. */
+static double mla_elem(const attn_job *j, const uint8_t *row, int64_t d) {
+    const double x = j->kv_bf16 ? oracle_bf16_value(((const uint16_t *)row)[d]) : j->fp8_table[row[d]];
+    return x * j->kv_scale;
 }
 
 /* Scores s[0..L) of one MLA row against its keys. */
@@ -283,13 +293,13 @@ static void mla_scores(const attn_job *j, int64_t r, int64_t b, int64_t L, doubl
             continue;
         }
         double dot = 0.0;
-        for (int64_t d = 0; d < dqk; ++d) dot += qv[d] * (j->fp8_table[row[d]] * j->kv_scale);
+        for (int64_t d = 0; d < dqk; ++d) dot += qv[d] * mla_elem(j, row, d);
         s[k] = j->scale * dot;
     }
 }
 
 static double mla_value(const attn_job *j, int64_t b, int64_t k, int64_t d) {
-    return j->fp8_table[mla_row(j, b, k)[d]] * j->kv_scale;
+    return mla_elem(j, mla_row(j, b, k), d);
 }
 
 static const uint16_t *gqa_row(const attn_job *j, const uint16_t *cache, int64_t b, int64_t k,
@@ -427,7 +437,7 @@ static int mla_decode(int64_t B, int64_t q_len, int64_t H, int64_t d_lat, int64_
                       const int32_t *kv_indptr, const int32_t *seq_lens,
                       const uint8_t *pool2, int64_t pool2_rows, const int32_t *kv2_indices,
                       const int32_t *kv2_indptr, double scale,
-                      double kv_scale, int fnuz, const int64_t *rows, int64_t n_rows,
+                      double kv_scale, int fnuz, int kv_bf16, const int64_t *rows, int64_t n_rows,
                       double *o_out, double *lse2_out, int n_threads) {
     if (B <= 0 || q_len <= 0 || H <= 0 || d_lat <= 0 || d_rope < 0 || d_v <= 0) return -1;
     if (pool2) {
@@ -464,6 +474,7 @@ static int mla_decode(int64_t B, int64_t q_len, int64_t H, int64_t d_lat, int64_
     proto.pool = pool; proto.kv_indices = kv_indices; proto.kv_scale = kv_scale;
     proto.pool2 = pool2; proto.kv2_indices = kv2_indices; proto.kv2_indptr = kv2_indptr;
     proto.fp8_table = table;
+    proto.kv_bf16 = kv_bf16;
     if (n_rows == 0) return 0;
     return run_jobs(&proto, n_threads);
 }
@@ -475,8 +486,19 @@ int oracle_mla_decode(int64_t B, int64_t q_len, int64_t H, int64_t d_lat, int64_
                       double kv_scale, int fnuz, const int64_t *rows, int64_t n_rows,
                       double *o_out, double *lse2_out, int n_threads) {
     return mla_decode(B, q_len, H, d_lat, d_rope, d_v, q_lat, q_pe, pool, pool_rows, kv_indices,
-                      kv_indptr, seq_lens, NULL, 0, NULL, NULL, scale, kv_scale, fnuz, rows,
+                      kv_indptr, seq_lens, NULL, 0, NULL, NULL, scale, kv_scale, fnuz, 0, rows,
                       n_rows, o_out, lse2_out, n_threads);
+}
+
+int oracle_mla_decode_bf16(int64_t B, int64_t q_len, int64_t H, int64_t d_lat, int64_t d_rope,
+                           int64_t d_v, const uint16_t *q_lat, const uint16_t *q_pe,
+                           const uint16_t *pool, int64_t pool_rows, const int32_t *kv_indices,
+                           const int32_t *kv_indptr, const int32_t *seq_lens, double scale,
+                           double kv_scale, const int64_t *rows, int64_t n_rows, double *o_out,
+                           double *lse2_out, int n_threads) {
+    return mla_decode(B, q_len, H, d_lat, d_rope, d_v, q_lat, q_pe, (const uint8_t *)pool, pool_rows,
+                      kv_indices, kv_indptr, seq_lens, NULL, 0, NULL, NULL, scale, kv_scale, 0, 1,
+                      rows, n_rows, o_out, lse2_out, n_threads);
 }
 
 int oracle_mla_decode_two_caches(int64_t B, int64_t H, int64_t d_lat, int64_t d_rope,
@@ -491,7 +513,7 @@ int oracle_mla_decode_two_caches(int64_t B, int64_t H, int64_t d_lat, int64_t d_
     if (!pool2) return -1;
     return mla_decode(B, 1, H, d_lat, d_rope, d_v, q_lat, q_pe, pool, pool_rows, kv_indices,
                       kv_indptr, seq_lens, pool2, pool2_rows, kv2_indices, kv2_indptr, scale,
-                      kv_scale, 0, rows, n_rows, o_out, lse2_out, n_threads);
+                      kv_scale, 0, 0, rows, n_rows, o_out, lse2_out, n_threads);
 }
 
 int oracle_gqa_decode(int64_t B, int64_t q_len, int64_t Hq, int64_t Hkv, int64_t D,

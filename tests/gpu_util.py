@@ -26,6 +26,14 @@ def bits16(t):
     return t.contiguous().cpu().view(torch.int16).numpy().view(np.uint16)
 
 
+def pool_np(pool):
+    """A pool tensor as numpy: uint8 fp8 bytes, or uint16 bits of bf16 rows."""
+    pool = pool.contiguous().cpu()
+    if pool.dtype == torch.bfloat16:
+        return pool.view(torch.int16).numpy().view(np.uint16)
+    return pool.numpy()
+
+
 def mla_problem(inp):
     return g.mla_problem(inp.q_lat, inp.q_pe, inp.pool, inp.kv_indices, inp.kv_indptr, inp.seq_lens,
                          batch=inp.B, q_len=inp.q_len, num_heads=inp.H,
@@ -62,7 +70,7 @@ def oracle_mla(inp, rows=None, n_threads=0):
         if inp.pool2 is not None:
             second = dict(pool2=inp.pool2.cpu().numpy(), kv2_indices=inp.kv2_indices.cpu().numpy(),
                           kv2_indptr=inp.kv2_indptr.cpu().numpy())
-        return oracle.mla_decode(bits16(inp.q_lat), bits16(inp.q_pe), inp.pool.cpu().numpy(),
+        return oracle.mla_decode(bits16(inp.q_lat), bits16(inp.q_pe), pool_np(inp.pool),
                                  inp.kv_indices.cpu().numpy(), inp.kv_indptr.cpu().numpy(),
                                  inp.seq_lens.cpu().numpy(), B=inp.B, q_len=q_len, H=H,
                                  d_v=inp.d_v, scale=inp.scale, kv_scale=inp.kv_scale,
@@ -85,14 +93,14 @@ def oracle_mla(inp, rows=None, n_threads=0):
         idx.append(new_idx)
         new_indptr.append(new_indptr[-1] + (e - a))
         new_lens.append(e - a)
-    pool = torch.cat(pools) if pools else torch.zeros((1, inp.d_qk), dtype=torch.uint8)
+    pool = torch.cat(pools) if pools else torch.zeros((1, inp.d_qk), dtype=inp.pool.dtype)
     if pool.shape[0] == 0:
-        pool = torch.zeros((1, inp.d_qk), dtype=torch.uint8)
+        pool = torch.zeros((1, inp.d_qk), dtype=inp.pool.dtype)
     ql = torch.cat([inp.q_lat[b * q_len:(b + 1) * q_len].cpu() for b in reqs])
     qp = torch.cat([inp.q_pe[b * q_len:(b + 1) * q_len].cpu() for b in reqs])
     pos = {b: i for i, b in enumerate(reqs)}
     sub_rows = [pos[r // (q_len * H)] * q_len * H + r % (q_len * H) for r in rows]
-    return oracle.mla_decode(bits16(ql), bits16(qp), pool.numpy(), torch.cat(idx).numpy(),
+    return oracle.mla_decode(bits16(ql), bits16(qp), pool_np(pool), torch.cat(idx).numpy(),
                              np.array(new_indptr, dtype=np.int32), np.array(new_lens, dtype=np.int32),
                              B=len(reqs), q_len=q_len, H=H, d_v=inp.d_v, scale=inp.scale,
                              kv_scale=inp.kv_scale, rows=sub_rows, n_threads=n_threads)

@@ -484,3 +484,108 @@ def test_second_cache_rejections():
                           inp.kv_indptr.numpy(), inp.seq_lens.numpy(), B=inp.B, q_len=1, H=inp.H,
                           d_v=inp.d_v, scale=inp.scale, kv_scale=inp.kv_scale, pool2=u8(inp.pool2),
                           kv2_indices=bad.numpy(), kv2_indptr=inp.kv2_indptr.numpy())
+
+
+# --- bf16 cache: the same fused rows stored as bf16 (AITER issue "[Perf] pa_decode_sparse ...",
+# closing paragraph, read as a bf16 copy of the cache dequantized by the same scale) -------------
+
+def bf16_mla(seed=31, B=2, q_len=2, H=3, lens=(9, 4), d_qk=40, d_rope=8, d_v=32, pool_rows=24):
+    return workloads.mla_inputs(B=B, q_len=q_len, H=H, seq_lens=list(lens), pool_rows=pool_rows,
+                                d_qk=d_qk, d_rope=d_rope, d_v=d_v, seed=seed, kv_dtype="bf16")
+
+
+def run_mla_bf16(inp, rows=None, kv_scale=None):
+    return oracle.mla_decode(bits16(inp.q_lat), bits16(inp.q_pe), bits16(inp.pool),
+                             inp.kv_indices.numpy(), inp.kv_indptr.numpy(), inp.seq_lens.numpy(),
+                             B=inp.B, q_len=inp.q_len, H=inp.H, d_v=inp.d_v, scale=inp.scale,
+                             kv_scale=inp.kv_scale if kv_scale is None else kv_scale, rows=rows)
+
+
+def torch_mla_reference_bf16(inp, kv_scale):
+    """Textbook attention in torch CPU float64 over bf16 rows decoded by torch."""
+    q = torch.cat([inp.q_lat, inp.q_pe], dim=-1).to(torch.float64)
+    pool = inp.pool.to(torch.float64) * kv_scale
+    outs, lses = [], []
+    for b in range(inp.B):
+        S = int(inp.seq_lens[b])
+        idx = inp.kv_indices[int(inp.kv_indptr[b]):int(inp.kv_indptr[b]) + S].long()
+        K = pool[idx]
+        for t in range(inp.q_len):
+            L = max(0, S - inp.q_len + t + 1)
+            if L == 0:
+                outs.append(torch.zeros(inp.H, inp.d_v, dtype=torch.float64))
+                lses.append(torch.full((inp.H,), -math.inf, dtype=torch.float64))
+                continue
+            s = inp.scale * (q[b * inp.q_len + t] @ K[:L].T)
+            outs.append(torch.softmax(s, dim=-1) @ K[:L, :inp.d_v])
+            lses.append(torch.logsumexp(s, dim=-1) / LN2)
+    return torch.cat(outs).numpy(), torch.cat(lses).numpy()
+
+
+@pytest.mark.parametrize("shape,kv_scale", [
+    (dict(), 1.0),
+    (dict(), 0.375),
+    (dict(B=2, q_len=1, H=16, lens=(64, 33), d_qk=576, d_rope=64, d_v=512, pool_rows=128), 1.0),
+    (dict(B=3, q_len=4, H=2, lens=(9, 2, 0), d_qk=512, d_rope=64, d_v=448, pool_rows=16), 1.0),
+])
+def test_bf16_cache_matches_torch_textbook(shape, kv_scale):
+    inp = bf16_mla(**shape)
+    assert inp.pool.dtype == torch.bfloat16 and inp.kv_scale == 1.0
+    o, lse2 = run_mla_bf16(inp, kv_scale=kv_scale)
+    ref_o, ref_lse = torch_mla_reference_bf16(inp, kv_scale)
+    np.testing.assert_allclose(o, ref_o, rtol=1e-12, atol=1e-13)
+    fin = np.isfinite(ref_lse)
+    assert np.array_equal(fin, np.isfinite(lse2))
+    np.testing.assert_allclose(lse2[fin], ref_lse[fin], rtol=1e-12, atol=1e-12)
+
+
+def test_bf16_cache_holding_fp8_values_equals_fp8_cache():
+    """Every e4m3 value is a bf16 value: a bf16 pool holding the fp8 pool's decoded values (times
+    the scale, a power of two here) must reproduce the fp8 result bit for bit."""
+    inp = small_mla(seed=12, B=2, q_len=2, H=3, lens=(11, 3), pool_rows=20)
+    o8, l8 = run_mla(inp)
+    vals = inp.pool.view(torch.float8_e4m3fn).to(torch.float32) * inp.kv_scale
+    b16 = vals.to(torch.bfloat16)
+    assert torch.equal(b16.to(torch.float32), vals)          # the conversion is exact
+    o16, l16 = oracle.mla_decode(bits16(inp.q_lat), bits16(inp.q_pe), bits16(b16),
+                                 inp.kv_indices.numpy(), inp.kv_indptr.numpy(), inp.seq_lens.numpy(),
+                                 B=inp.B, q_len=inp.q_len, H=inp.H, d_v=inp.d_v, scale=inp.scale,
+                                 kv_scale=1.0)
+    assert np.array_equal(o8, o16) and np.array_equal(l8, l16)
+
+
+def test_bf16_cache_single_key_closed_form():
+    inp = bf16_mla(seed=33, B=1, q_len=1, H=2, lens=(1,), pool_rows=3)
+    o, l = run_mla_bf16(inp)
+    k = inp.pool[int(inp.kv_indices[0])].to(torch.float64)
+    s = inp.scale * (torch.cat([inp.q_lat, inp.q_pe], -1).to(torch.float64)[0] @ k)
+    for h in range(2):
+        assert np.array_equal(o[h], k[:inp.d_v].numpy())
+        assert l[h] == pytest.approx(float(s[h]) / LN2, rel=1e-14, abs=1e-14)
+
+
+def test_bf16_cache_row_stride_uses_two_bytes():
+    """A wrong row stride (one byte per element) would read row k's second half as row 2k+1:
+    attending only the last pool row must return that row's values."""
+    inp = bf16_mla(seed=34, B=1, q_len=1, H=1, lens=(1,), pool_rows=9)
+    inp.kv_indices[0] = 8
+    o, _ = run_mla_bf16(inp)
+    assert np.array_equal(o[0], inp.pool[8, :inp.d_v].to(torch.float64).numpy())
+
+
+def test_bf16_cache_skipped_keys_equal_their_removal():
+    inp = bf16_mla(seed=35, B=1, q_len=1, H=3, lens=(12,), pool_rows=12)
+    o_full, l_full = run_mla_bf16(inp)
+    keep = [0, 1, 2, 5, 6, 7, 8, 9, 10, 11]
+    skipped = inp.kv_indices.clone()
+    skipped[3], skipped[4] = -1, -1
+    o_s, l_s = oracle.mla_decode(bits16(inp.q_lat), bits16(inp.q_pe), bits16(inp.pool), skipped.numpy(),
+                                 inp.kv_indptr.numpy(), inp.seq_lens.numpy(), B=1, q_len=1, H=3,
+                                 d_v=inp.d_v, scale=inp.scale, kv_scale=1.0)
+    sub = inp.kv_indices[keep]
+    o_r, l_r = oracle.mla_decode(bits16(inp.q_lat), bits16(inp.q_pe), bits16(inp.pool), sub.numpy(),
+                                 np.array([0, len(keep)], np.int32), np.array([len(keep)], np.int32),
+                                 B=1, q_len=1, H=3, d_v=inp.d_v, scale=inp.scale, kv_scale=1.0)
+    np.testing.assert_allclose(o_s, o_r, rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(l_s, l_r, rtol=1e-13, atol=1e-13)
+    assert not np.allclose(o_s, o_full)

@@ -59,6 +59,16 @@ def _fp8_pool(rows, width, seed, device, chunk_rows=1 << 20):
     return out
 
 
+def _bf16_pool(rows, width, seed, device, chunk_rows=1 << 20):
+    """[rows, width] bf16 values N(0,1) (the bf16-cache variant: no quantization, kv_scale 1)."""
+    out = torch.empty((rows, width), dtype=torch.bfloat16, device=device)
+    g = _gen(device, seed)
+    for r0 in range(0, rows, chunk_rows):
+        r1 = min(rows, r0 + chunk_rows)
+        out[r0:r1] = torch.randn((r1 - r0, width), generator=g, device=device, dtype=torch.float32)
+    return out
+
+
 @dataclasses.dataclass
 class MlaInputs:
     B: int
@@ -69,7 +79,7 @@ class MlaInputs:
     d_v: int
     q_lat: torch.Tensor        # bf16 [B*q_len, H, d_qk - d_rope] (may be a strided view)
     q_pe: torch.Tensor         # bf16 [B*q_len, H, d_rope] (may be a strided view)
-    pool: torch.Tensor         # uint8 [N, d_qk] fp8 e4m3fn bytes
+    pool: torch.Tensor         # uint8 [N, d_qk] fp8 e4m3fn bytes, or bf16 [N, d_qk] (bf16 cache)
     kv_indices: torch.Tensor   # int32 [sum of keys]
     kv_indptr: torch.Tensor    # int32 [B+1]
     seq_lens: torch.Tensor     # int32 [B]
@@ -88,12 +98,17 @@ class MlaInputs:
         return self.B * self.q_len * self.H
 
     @property
+    def kv_bf16(self) -> bool:
+        return self.pool.dtype == torch.bfloat16
+
+    @property
     def kv_bytes(self) -> int:
-        """KV payload bytes one decode reads: every key of every request once (576 or 512 B)."""
+        """KV payload bytes one decode reads: every key of every request once (576 or 512
+        elements of 1 byte, or 2 bytes for a bf16 cache)."""
         n = int(self.seq_lens.sum().item())
         if self.kv2_indices is not None:
             n += int(self.kv2_indices.numel())
-        return n * self.d_qk
+        return n * self.d_qk * self.pool.element_size()
 
 
 @dataclasses.dataclass
@@ -126,11 +141,13 @@ class GqaInputs:
 
 def mla_inputs(*, B: int, q_len: int, H: int, seq_lens: Sequence[int], pool_rows: Optional[int] = None,
                d_qk: int = 576, d_rope: int = 64, d_v: int = 512, seed: int = 0,
-               device="cpu", shuffle: bool = True, fused_q: bool = False, name: str = "") -> MlaInputs:
+               device="cpu", shuffle: bool = True, fused_q: bool = False, name: str = "",
+               kv_dtype: str = "fp8") -> MlaInputs:
     """Absorbed-MLA decode inputs; request b owns keys kv_indices[kv_indptr[b]:kv_indptr[b+1]].
 
     fused_q=True draws one q [B*q_len, H, d_qk] and exposes q_lat / q_pe as views of it (the
-    sparse top-k workload's single 512-wide query)."""
+    sparse top-k workload's single 512-wide query).  kv_dtype="bf16": the pool holds bf16
+    N(0,1) rows with kv_scale 1 (the bf16-cache variant)."""
     lens = [int(x) for x in seq_lens]
     assert len(lens) == B
     total = sum(lens)
@@ -142,7 +159,7 @@ def mla_inputs(*, B: int, q_len: int, H: int, seq_lens: Sequence[int], pool_rows
     else:
         q_lat = _randn((B * q_len, H, d_lat), seed + 1, device, torch.bfloat16)
         q_pe = _randn((B * q_len, H, d_rope), seed + 2, device, torch.bfloat16)
-    pool = _fp8_pool(N, d_qk, seed + 3, device)
+    pool = _bf16_pool(N, d_qk, seed + 3, device) if kv_dtype == "bf16" else _fp8_pool(N, d_qk, seed + 3, device)
     if shuffle:
         if total <= N:
             idx = torch.randperm(N, generator=_gen(device, seed + 4), device=device)[:total]
@@ -159,13 +176,14 @@ def mla_inputs(*, B: int, q_len: int, H: int, seq_lens: Sequence[int], pool_rows
     return MlaInputs(B=B, q_len=q_len, H=H, d_qk=d_qk, d_rope=d_rope, d_v=d_v, q_lat=q_lat,
                      q_pe=q_pe, pool=pool, kv_indices=kv_indices, kv_indptr=kv_indptr,
                      seq_lens=sl, max_num_keys=max(lens) if lens else 0,
-                     scale=float(d_qk) ** -0.5, name=name)
+                     scale=float(d_qk) ** -0.5, kv_scale=1.0 if kv_dtype == "bf16" else KV_SCALE,
+                     name=name)
 
 
 def sparse_mla_inputs(*, num_queries: int, topk: int = 2048, cache_rows: int = 262144, H: int = 64,
                       seed: int = 4000, device="cpu", name: str = "", invalid_frac: float = 0.0,
                       all_invalid: Sequence[int] = (), extra_topk: int = 0,
-                      extra_rows: int = 65536) -> MlaInputs:
+                      extra_rows: int = 65536, kv_dtype: str = "fp8") -> MlaInputs:
     """Sparse top-k MLA decode: each query is its own request whose keys are `topk` cache rows
     drawn without replacement; rows are 512 fp8 bytes (448 NoPE + 64 RoPE), value = NoPE part.
     invalid_frac: that fraction of the index entries (seeded positions) is -1, a skipped key;
@@ -196,6 +214,7 @@ def sparse_mla_inputs(*, num_queries: int, topk: int = 2048, cache_rows: int = 2
     return MlaInputs(B=nq, q_len=1, H=H, d_qk=512, d_rope=64, d_v=448, q_lat=q[..., :448],
                      q_pe=q[..., 448:], pool=pool, kv_indices=kv_indices, kv_indptr=kv_indptr,
                      seq_lens=sl, max_num_keys=topk + extra_topk, scale=512.0 ** -0.5, name=name,
+                     kv_scale=1.0 if kv_dtype == "bf16" else KV_SCALE,
                      pool2=pool2, kv2_indices=kv2_indices, kv2_indptr=kv2_indptr)
 
 
@@ -293,9 +312,17 @@ def gqa_paged(device="cpu"):
 SPARSE_QUERY_COUNTS = (24, 32, 34, 64, 128, 256)
 
 
-def sparse_topk(num_queries: int, device="cpu"):
-    return sparse_mla_inputs(num_queries=num_queries, seed=4000, device=device,
-                             name="sparse_mla_h64_topk2048_nq%d" % num_queries)
+def sparse_topk(num_queries: int, device="cpu", kv_dtype: str = "fp8"):
+    tag = "" if kv_dtype == "fp8" else "_bf16"
+    return sparse_mla_inputs(num_queries=num_queries, seed=4000, device=device, kv_dtype=kv_dtype,
+                             name="sparse_mla_h64_topk2048_nq%d%s" % (num_queries, tag))
+
+
+def mla_long_bf16(B: int, device="cpu"):
+    """The H=64 long-context workload over a bf16 cache (131072 keys per request, 1152-byte
+    rows, kv_scale 1)."""
+    return mla_inputs(B=B, q_len=1, H=64, seq_lens=[131072] * B, pool_rows=B * 131072, seed=2200,
+                      device=device, kv_dtype="bf16", name="mla_h64_b%d_s131072_bf16" % B)
 
 
 # --------------------------------------------------------------------------------------------
