@@ -74,6 +74,12 @@ def make_workloads():
     ]
     for nq in w.SPARSE_QUERY_COUNTS:
         items.append(("sparse_mla_h64_topk2048_nq%d" % nq, (lambda n: lambda d: w.sparse_topk(n, d))(nq), 0))
+    # the same rows stored as bf16 (twice the bytes per key)
+    items += [
+        ("mla_h64_b16_s131072_q1_bf16", lambda d: w.mla_long_bf16(16, 1, d), 0),
+        ("mla_h64_b8_s131072_q4_bf16", lambda d: w.mla_long_bf16(8, 4, d), 0),
+        ("sparse_mla_h64_topk2048_nq256_bf16", lambda d: w.sparse_topk(256, d, kv_dtype="bf16"), 0),
+    ]
     return items
 
 
@@ -744,6 +750,7 @@ def main():
             "split_us": round(ms_split * 1e3, 2),
             "reduce_us": round(ms_red * 1e3, 2),
             "np": case.np, "block_k": case.bk, "kv_bytes": case.kv_bytes(),
+            "kv_dtype": ("bf16" if inp.kv_bf16 else "fp8_e4m3fn") if case.is_mla else "bf16",
             # decode_proportional with the same budget, timed against decode in one interleave
             "us_per_call_proportional": round(ms_prop * 1e3, 2) if ms_prop else None,
             "proportional_vs_equal": round(ms_prop / ms_eq, 3) if ms_prop else None,

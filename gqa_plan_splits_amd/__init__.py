@@ -14,6 +14,7 @@ from ._lib import (  # noqa: F401
     KIND_MLA_FUSED,
     FP8_E4M3FN,
     FP8_E4M3FNUZ,
+    KV_BF16,
     block_k_for,
     bw_gather_rows,
     bw_stream_read,

@@ -11,6 +11,7 @@ KIND_MLA_FUSED = 0
 KIND_GQA_PAGED = 1
 FP8_E4M3FN = 0
 FP8_E4M3FNUZ = 1
+KV_BF16 = 2
 SCRATCH_BYTES = 64 << 20   # GQA_SCRATCH_BYTES: the device-side partials of decode_scratch
 
 # Every function include/gqa_splits.h declares.
@@ -254,16 +255,20 @@ def _strides(t):
 
 
 def mla_problem(q_lat, q_pe, pool, kv_indices, kv_indptr, seq_lens, *, batch, q_len, num_heads,
-                max_num_keys, scale, kv_scale, d_v=None, fp8_format=FP8_E4M3FN, glen=None,
+                max_num_keys, scale, kv_scale, d_v=None, fp8_format=None, glen=None,
                 cp_rank=0, cp_world=1, pool2=None, kv2_indices=None, kv2_indptr=None) -> DecodeProblem:
     """Absorbed-MLA (or sparse top-k) problem: q_lat [B*q_len, H, d_lat], q_pe [.., H, d_rope]
-    bf16 views; pool [N, d_qk] fp8 bytes (uint8 or float8); int32 index tensors.  With glen
+    bf16 views; pool [N, d_qk] fp8 bytes (uint8 or float8), or bf16 (format KV_BF16, the default
+    for a bf16 pool); int32 index tensors.  With glen
     (int32 [B] global lengths), the call is rank cp_rank of cp_world decode-context-parallel
     ranks: seq_lens and the index lists hold that rank's positions.  With pool2 (sparse rows,
     q_len 1; the pool's row stride), request b also attends the second-cache rows
     kv2_indices[kv2_indptr[b]:kv2_indptr[b+1]]; max_num_keys covers both lists."""
     p = DecodeProblem()
     p.kind = KIND_MLA_FUSED
+    if fp8_format is None:
+        import torch
+        fp8_format = KV_BF16 if pool.dtype == torch.bfloat16 else FP8_E4M3FN
     p.fp8_format = fp8_format
     p.batch, p.q_len, p.num_heads, p.num_kv_heads = batch, q_len, num_heads, 1
     p.d_rope = q_pe.shape[-1]

@@ -12,7 +12,6 @@
 namespace {
 
 constexpr int kMaxPartitions = 256;
-constexpr int kMlaRowsPerCta = 32;
 constexpr int kGqaHeadDim = 128;
 constexpr int kGqaMaxRowsPerCta = 16;
 constexpr float kLog2e = 1.4426950408889634f;
@@ -43,7 +42,7 @@ int launch_status(hipError_t err, const char *what) {
 struct Derived {
     int64_t rows;           // B * q_len * H
     int64_t rows_per_req;   // q_len * H
-    int64_t cta_rows;       // MLA: 32-row blocks per request; GQA: kv heads
+    int64_t cta_rows;       // CTAs per request and partition: MLA, the kernel's row blocks; GQA, kv heads
     int64_t hpg;            // heads_per_group the planner sees
     bool is_mla;
 };
@@ -61,7 +60,8 @@ int check_problem(const gqa_decode_problem *p, Derived *d) {
     if (p->q_stride_tok % 8 || p->q_stride_head % 8 || !aligned16(p->q)) return GQA_ERR_UNSUPPORTED;
 
     if (p->kind == GQA_KIND_MLA_FUSED) {
-        if (p->fp8_format != GQA_FP8_E4M3FN && p->fp8_format != GQA_FP8_E4M3FNUZ)
+        if (p->fp8_format != GQA_FP8_E4M3FN && p->fp8_format != GQA_FP8_E4M3FNUZ &&
+            p->fp8_format != GQA_KV_BF16)
             return GQA_ERR_INVALID_ARGUMENT;
         if (!p->kv || !p->q_pe || p->num_kv_heads != 1) return GQA_ERR_INVALID_ARGUMENT;
         if (!(p->kv_scale > 0.f) || !std::isfinite(p->kv_scale)) return GQA_ERR_INVALID_ARGUMENT;
@@ -71,7 +71,8 @@ int check_problem(const gqa_decode_problem *p, Derived *d) {
         const bool sparse = p->d_qk == 512 && p->d_rope == 64 && p->d_v == 448;
         if (!wide && !sparse) return GQA_ERR_UNSUPPORTED;
         if (p->page_size != 1) return GQA_ERR_UNSUPPORTED;
-        if (p->kv_stride_row < p->d_qk || p->kv_stride_row % 16 || !aligned16(p->kv))
+        const int64_t elem = p->fp8_format == GQA_KV_BF16 ? 2 : 1;
+        if (p->kv_stride_row < p->d_qk * elem || p->kv_stride_row % 16 || !aligned16(p->kv))
             return GQA_ERR_UNSUPPORTED;
         if (p->q_pe_stride_tok % 8 || p->q_pe_stride_head % 8 || !aligned16(p->q_pe))
             return GQA_ERR_UNSUPPORTED;
@@ -85,13 +86,15 @@ int check_problem(const gqa_decode_problem *p, Derived *d) {
         // a second cache: q_len 1 without context parallelism, rows of the pool's format
         if (p->kv2 || p->kv2_indices || p->kv2_indptr) {
             if (!p->kv2 || !p->kv2_indices || !p->kv2_indptr) return GQA_ERR_INVALID_ARGUMENT;
-            if (p->q_len != 1 || p->cp_world > 1 || p->glen || !sparse) return GQA_ERR_UNSUPPORTED;
+            if (p->q_len != 1 || p->cp_world > 1 || p->glen || !sparse || p->fp8_format == GQA_KV_BF16)
+                return GQA_ERR_UNSUPPORTED;
             // the kernel addresses both caches with the pool's row stride
             if (p->kv2_stride_row != 0 && p->kv2_stride_row != p->kv_stride_row) return GQA_ERR_UNSUPPORTED;
             if (!aligned16(p->kv2)) return GQA_ERR_UNSUPPORTED;
         }
         d->is_mla = true;
-        d->cta_rows = (rows_per_req + kMlaRowsPerCta - 1) / kMlaRowsPerCta;
+        // the tile rule counts the CTAs the launch has: the kernel's own row blocks
+        d->cta_rows = (rows_per_req + gqa::mla_rows_per_cta() - 1) / gqa::mla_rows_per_cta();
         d->hpg = rows_per_req;
     } else if (p->kind == GQA_KIND_GQA_PAGED) {
         if (!p->k_cache || !p->v_cache || p->num_kv_heads < 1) return GQA_ERR_INVALID_ARGUMENT;
@@ -148,9 +151,7 @@ int launch_split(const gqa_decode_problem *p, const Derived &d, int64_t np, int 
     const bool direct = out != nullptr;
     const int64_t grid_parts = part_start ? slots : p->batch * np;
     if (d.is_mla) {
-        // the kernel's own row blocks (the planner's 32-row CTA count only sizes the split)
-        const int64_t rpc = gqa::mla_rows_per_cta();
-        const int64_t row_blocks = (d.rows_per_req + rpc - 1) / rpc;
+        const int64_t row_blocks = d.cta_rows;
         const int64_t total = grid_parts * row_blocks;
         if (total > (int64_t(1) << 30)) return GQA_ERR_UNSUPPORTED;
         gqa::MlaSplitArgs a;
@@ -189,7 +190,8 @@ int launch_split(const gqa_decode_problem *p, const Derived &d, int64_t np, int 
         a.part_lse2 = part_lse2;
         a.out = static_cast<uint16_t *>(out);
         a.lse2_out = lse2_out;
-        const hipError_t err = gqa::launch_mla_split(a, int(p->d_qk), int(p->d_v), direct, s);
+        const hipError_t err = gqa::launch_mla_split(a, int(p->d_qk), int(p->d_v),
+                                                     p->fp8_format == GQA_KV_BF16, direct, s);
         return launch_status(err, "mla split");
     } else {
         const int64_t total = grid_parts * d.cta_rows;

@@ -14,10 +14,10 @@ struct MlaSplitArgs {
     int64_t q_st_tok, q_st_head;
     const uint16_t *q_pe;         // bf16 [tokens, H, 64]
     int64_t qpe_st_tok, qpe_st_head;
-    const uint8_t *kv;            // fp8 rows
+    const uint8_t *kv;            // fp8 rows, or bf16 rows (kv_bf16)
     int64_t kv_stride;            // bytes between rows
     const int32_t *kv_indices, *kv_indptr, *seq_lens;
-    const uint8_t *kv2;           // second cache (fp8 rows of the pool's format), or null
+    const uint8_t *kv2;           // second cache (rows of the pool's format), or null
     int64_t kv2_stride;
     const int32_t *kv2_indices, *kv2_indptr;   // request b's second-cache rows, after its pool keys
     const int32_t *glen;          // global lengths under context parallelism (cp_world > 1)
@@ -30,7 +30,7 @@ struct MlaSplitArgs {
     const int32_t *part_start, *part_chunk;
     int32_t batch;
     float score_scale;            // scale * kv_scale * log2(e): scores in base-2 units
-    float out_scale;              // kv_scale: the raw fp8 values are accumulated unscaled
+    float out_scale;              // kv_scale: the stored values are accumulated unscaled
     float *part_o;                // [rows, np, DV]
     float *part_lse2;             // [rows, np]
     uint16_t *out;                // bf16 [rows, DV] when np == 1 (direct mode)
@@ -83,7 +83,7 @@ struct PlanArgs {
 // Launchers: return hipSuccess or the launch error.  All enqueue on `s` only.
 // Query rows one MLA split CTA covers (row_blocks = ceil(rows per request / this)).
 int mla_rows_per_cta();
-hipError_t launch_mla_split(const MlaSplitArgs &a, int d_qk, int d_v, bool direct, hipStream_t s);
+hipError_t launch_mla_split(const MlaSplitArgs &a, int d_qk, int d_v, bool kv_bf16, bool direct, hipStream_t s);
 // (with a.kv2 set: the second-cache variant of the same kernel)
 hipError_t launch_gqa_split(const GqaSplitArgs &a, bool direct, hipStream_t s);
 hipError_t launch_splitk_reduce(const ReduceArgs &a, hipStream_t s);

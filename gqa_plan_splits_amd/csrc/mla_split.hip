@@ -1,8 +1,10 @@
 // mla_split.hip -- split kernel of absorbed MLA decode for gfx950.
 //
 // What it computes (moonmath-amd README, "MLA decode"; Modular MAX planner page, MLA-style
-// bullet): every key row of the pool is one fused fp8 e4m3 row that serves as K (all DQK bytes)
-// and as V (its first DV bytes), dequantized with one per-tensor kv_scale.  A CTA owns up to 64
+// bullet): every key row of the pool is one fused row that serves as K (all DQK elements) and as
+// V (its first DV elements), dequantized with one per-tensor kv_scale; rows are fp8 e4m3, or bf16
+// (the bf16 cache the AITER issue "[Perf] pa_decode_sparse" offers to re-measure on, in its
+// closing paragraph).  A CTA owns up to 64
 // query rows of one request and walks one partition of that request's keys, writing the
 // partition's softmax-weighted mean of values and the base-2 log-sum-exp of its scores.  Under
 // decode context parallelism (same README section) the call holds one rank's share of each
@@ -21,29 +23,36 @@
 // are stored as fp16 (11 significant bits); PV multiplies them by V decoded exactly to fp16 on
 // the fp16 MFMA.  The output is normalized by the sum of the stored weights, so a dominant key
 // carries no rounding of its own weight into it; the LSE comes from the sum of the exact ones.
+// bf16 rows go to the bf16 MFMA as stored, and their value part is converted to fp16 (exact for
+// magnitudes in fp16's normal range; the library requires stored values below 65520).
 //
-// Work split (512 threads = 8 waves, one CTA per CU; waves w and w + 4 share SIMD w):
-//   - Score waves 0-3: wave w computes S^T = K Q^T for query rows 16 w .. 16 w + 15 against the 64
-//     keys of a tile on v_mfma_f32_16x16x32_bf16, one accumulator per 16-key block, then the
-//     rows' online softmax.  It keeps each row's running maximum and both sums, and hands the
-//     value waves P(t) (64 rows x 64 keys, fp16) and the rows' maxima and sums through LDS.
-//   - Value waves 4-7: wave 4 + v accumulates output columns 128 v .. +127 (line v of the key rows)
-//     for all 64 rows on v_mfma_f32_32x32x16_f16: V^T comes from the fp8 tile through
-//     ds_read_b64_tr_b8 (decoded to fp16), P^T from LDS; when a row's maximum moved, its
-//     accumulators are first scaled by the exact power of two 2^(m_old - m_new).  The value
-//     waves also move the data: wave 4 + v copies line v
-//     of every key of a tile (and a quarter of the 64-byte rope tails of 576-byte rows) straight
-//     from HBM into LDS with global_load_lds_dwordx4, two tiles ahead, after loading the tile's
-//     slot ids the same way two tiles before that.  The copies are issued from inline assembly and
-//     waited for with explicit vmcnt counts (the compiler would drain every copy in flight before
-//     each LDS read).
-//   - One barrier per tile, and the score waves run one tile ahead: in step t a score wave issues
-//     the MFMAs of tile t + 1 and, between them, computes the softmax of tile t, while the value
-//     waves apply tile t - 1.  So on each SIMD the matrix core stays busy with one role's MFMAs
-//     while the vector ALU runs the other role's softmax and bookkeeping.
+// Work split (512 threads = 8 waves, one CTA per CU; waves w and w + 4 share SIMD w & 3, and
+// waves 0-3 sit on four different SIMDs):
+//   - Score waves 0, 4 (query rows 0-31) and 1, 5 (rows 32-63) hold their rows' queries in
+//     registers and compute S^T = K Q^T on v_mfma_f32_32x32x16_bf16 for 32 keys at a time; the
+//     two waves of a SIMD take alternate 32-key blocks (fp8: the two halves of each 64-key tile;
+//     bf16: alternate 32-key tiles) and each keeps its own online softmax of those blocks.  They
+//     hand the value waves each block's weights P (fp16) and integer maximum through LDS, and
+//     their final sums at the end.
+//   - Value waves 2, 6 and 3, 7 (SIMDs 2 and 3) accumulate output columns 128 v .. 128 v + 127
+//     (v = 0..3) of all 64 rows on v_mfma_f32_32x32x16_f16: V^T comes from the tile in LDS through
+//     transposed reads (ds_read_b64_tr_b8 for fp8, ds_read_b64_tr_b16 for bf16) and is converted
+//     to fp16, P^T from LDS; when a block's maximum is above the accumulators', they are first
+//     scaled by the exact power of two 2^(m_old - m_new).  The value waves also move the data:
+//     wave v copies its columns of every key of a tile (and a quarter of the rope tails of
+//     576-wide rows) straight from HBM into LDS with global_load_lds_dwordx4, three tiles ahead,
+//     after loading the tile's slot ids the same way three tiles before that.  The copies are
+//     issued from inline assembly and waited for with explicit vmcnt counts (the compiler would
+//     drain every copy in flight before each LDS read).
+//   - One barrier per tile.  The score waves run one tile ahead of the value waves: in step t
+//     they compute the softmax of tile t and the scores of tile t + 1 (fp8: each wave both,
+//     interleaved; bf16: the owner of tile t its softmax while the other wave of its SIMD runs
+//     the MFMAs of tile t + 1), while the value waves apply tile t - 1.  On each SIMD the matrix
+//     core is kept busy by one wave while the vector ALU runs the other's softmax and
+//     bookkeeping.
 //
-// LDS (160 KiB): a four-slot ring of the key rows' first 512 bytes and a three-slot ring of the
-// 64-byte rope tails of 576-byte rows.  Line j (bytes 128 j .. 128 j + 127 of the rows) of a
+// LDS (160 KiB): a four-slot ring of the key rows' first 512 elements and a three-slot ring of the
+// 64-element rope tails of 576-wide rows (fp8 layout below; bf16 rows at swz16).  Line j (bytes 128 j .. 128 j + 127 of the rows) of a
 // slot's 64 keys fills 8 KiB at j * 8192, tile position P at P * 128, its 16-byte chunks permuted
 // by an XOR with swz_line(P) (bits 2, 1 and 3 of P); a tail slot holds position P at P * 64,
 // chunks permuted with bit 2 of P.  A copy instruction writes 1 KiB of consecutive 16-byte slots,
@@ -74,16 +83,17 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kBM = 64;            // query rows per CTA
-constexpr int kBK = 64;            // keys per tile
 constexpr int kThreads = 512;
 constexpr int kLineSlots = 4;      // ring of the rows' first 512 bytes
 constexpr int kTailSlots = 3;      // ring of the 64-byte rope tails (576-byte rows)
 constexpr int kIdSlots = 4;        // ring of slot-id lists
 constexpr int kNoMax = -(1 << 20); // integer maximum of a block with no visible key
 
-template <int DQK>
+// KV16: bf16 rows (1152 or 1024 bytes) in tiles of 32 keys, so that a tile's bytes (36 KiB for
+// 576-wide rows) and the ring match those of 64 fp8 keys.
+template <int DQK, bool KV16>
 struct MlaLayout {
-    static constexpr int kSteps = DQK / 64;                 // 64-byte contraction steps per row
+    static constexpr int kBK = KV16 ? 32 : 64;              // keys per tile
     static constexpr bool kTail = DQK == 576;               // rope tails in their own ring
     static constexpr int kTailOff = kLineSlots * 32768;
     static constexpr int kPOff = kTailOff + (kTail ? kTailSlots * 4096 : 0);
@@ -107,6 +117,19 @@ __device__ __forceinline__ int tail_off(int pos, int c) { return pos * 64 + ((c 
 // Slot-list index (0..63, relative to the tile) of the key at tile position pos.
 __device__ __forceinline__ int key_of_pos(int pos) { return 8 * (pos & 7) + (pos >> 3); }
 
+// bf16 rows: a line slot holds the 128-byte lines j = 0..7 (elements 64 j .. 64 j + 63) of a
+// tile's 32 keys, line j at j * 4096, tile position P at P * 128; a tail slot holds the 128-byte
+// rope tails (elements 512 .. 575) the same way.  Chunks are permuted by an XOR with swz16(P)
+// (bits 2, 3 and 1 of P): the score reads (16 lanes with one chunk index, keys of both parities
+// of bits 1-3) and the transposed value reads (keys P .. P + 3, four chunks of one 64-byte half
+// each; P and P + 2 land in opposite halves) touch distinct slots of a bank row.  Positions
+// 8 i .. 8 i + 7 hold keys i, 4 + i, .., 28 + i of the tile.
+__device__ __forceinline__ int swz16(int pos) { return ((pos >> 2) & 1) | ((pos >> 2) & 2) | ((pos << 1) & 4); }
+__device__ __forceinline__ int line_off16(int line, int pos, int c) {
+    return line * 4096 + pos * 128 + ((c ^ swz16(pos)) << 4);
+}
+__device__ __forceinline__ int key_of_pos16(int pos) { return 4 * (pos & 7) + (pos >> 3); }
+
 // P rows of a tile: 128 bytes per query row (64 fp16 weights in tile-position order), the
 // 16-byte slot q (weights 8 q .. 8 q + 7) stored at slot q ^ ((row >> 1) & 7).  The value waves'
 // reads of one slot by 16 rows whose bits 1-3 differ (with either bit 0) then touch 16 distinct
@@ -121,6 +144,18 @@ __device__ __forceinline__ f16x2 pack_f16x2(float a, float b) {
     r.x = static_cast<_Float16>(a);
     r.y = static_cast<_Float16>(b);
     return r;
+}
+// Eight bf16 values (two transposed reads of four) to fp16: exact for magnitudes in fp16's
+// normal range (every 8-bit significand fits in fp16's 11), rounded to nearest even below it (an
+// error under 2^-25), infinite above 65504.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ f16x8 bf16x8_to_f16x8(s16x4 a, s16x4 b) {
+    const u32x2 wa = __builtin_bit_cast(u32x2, a), wb = __builtin_bit_cast(u32x2, b);
+    const f16x2 p0 = pack_f16x2(__uint_as_float(wa.x << 16), __uint_as_float(wa.x & 0xffff0000u));
+    const f16x2 p1 = pack_f16x2(__uint_as_float(wa.y << 16), __uint_as_float(wa.y & 0xffff0000u));
+    const f16x2 p2 = pack_f16x2(__uint_as_float(wb.x << 16), __uint_as_float(wb.x & 0xffff0000u));
+    const f16x2 p3 = pack_f16x2(__uint_as_float(wb.y << 16), __uint_as_float(wb.y & 0xffff0000u));
+    return f16x8{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
 }
 // Eight OCP e4m3fn bytes to fp16, exactly (every e4m3fn value is an fp16 value).
 __device__ __forceinline__ f16x8 fp8x8_to_f16x8(uint32_t lo, uint32_t hi) {
@@ -183,10 +218,11 @@ __device__ __forceinline__ float rows4_sum(float x) {
 
 // EXTRA: a second cache (the sparse planner page's extra_topk): request b's keys are its
 // seq_lens[b] pool keys and then its second-cache rows; a key's list position picks the cache.
-template <int DQK, int DV, bool DIRECT, bool EXTRA>
+template <int DQK, int DV, bool DIRECT, bool EXTRA, bool KV16>
 __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const MlaSplitArgs a) {
-    using T = MlaLayout<DQK>;
+    using T = MlaLayout<DQK, KV16>;
     constexpr int DLAT = DQK - 64;
+    constexpr int kBK = T::kBK;
     __shared__ __attribute__((aligned(1024))) uint8_t lds[T::kLdsBytes];
 
     const int logical = xcd_logical_block(blockIdx.x, a.total_ctas);
@@ -255,8 +291,10 @@ __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const MlaSplitAr
         const int kb = wave >> 2;               // this wave's block of every tile
         const int srow = 32 * (wave & 1) + n;   // row within the CTA
         const bool row_ok = srow < nrows;
-        constexpr int NL = DQK / 128;           // full 128-byte lines per row
-        constexpr int NQ = 8 * NL + (T::kTail ? 4 : 0);   // MFMAs per 32-key block
+        constexpr int NL = DQK / 128;           // full 128-byte lines per fp8 row
+        // MFMAs per 32-key block: fp8, 8 per 128-byte line and 4 for the rope tail; bf16, 4 per
+        // 64 elements
+        constexpr int NQ = KV16 ? 4 * (DQK / 64) : 8 * NL + (T::kTail ? 4 : 0);
         int p_end;                              // keys visible to this row
         const float c_row = a.score_scale;      // base-2 score per unit of the raw product
         bf16x8 qv[NQ];                          // B operands: this lane's query dims per MFMA
@@ -271,27 +309,38 @@ __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const MlaSplitAr
             auto piece = [&](int d) {
                 return as_bf16x8(row_ok ? load_q8<DLAT>(ql, qp, d) : u32x4{0u, 0u, 0u, 0u});
             };
+            if constexpr (KV16) {
 #pragma unroll
-            for (int L = 0; L < NL; ++L)
+                for (int L = 0; L < DQK / 64; ++L)
 #pragma unroll
-                for (int j = 0; j < 8; ++j) qv[8 * L + j] = piece(128 * L + 64 * h + 8 * j);
-            if constexpr (T::kTail) {
+                    for (int j = 0; j < 4; ++j) qv[4 * L + j] = piece(64 * L + 32 * h + 8 * j);
+            } else {
 #pragma unroll
-                for (int j = 0; j < 4; ++j) qv[8 * NL + j] = piece(512 + 32 * h + 8 * j);
+                for (int L = 0; L < NL; ++L)
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) qv[8 * L + j] = piece(128 * L + 64 * h + 8 * j);
+                if constexpr (T::kTail) {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) qv[8 * NL + j] = piece(512 + 32 * h + 8 * j);
+                }
             }
         }
 
         // LDS offsets of this lane's K operand within tile t's slots: key at position 32 kb + n,
         // chunks 4 h .. 4 h + 3 of each line (line L adds 8192 bytes), rope-tail chunks 2 h and
         // 2 h + 1.
+        // (bf16 rows: key at position n of the 32-key tile, chunks 4 h .. 4 h + 3 of each line
+        // and of the rope tail, each chunk 8 dims of one MFMA.)
         int k_off[4], k_tail[2];
 #pragma unroll
-        for (int c = 0; c < 4; ++c) k_off[c] = line_off(0, 32 * kb + n, 4 * h + c);
+        for (int c = 0; c < 4; ++c) k_off[c] = KV16 ? line_off16(0, n, 4 * h + c) : line_off(0, 32 * kb + n, 4 * h + c);
 #pragma unroll
         for (int c = 0; c < 2; ++c) k_tail[c] = T::kTailOff + tail_off(32 * kb + n, 2 * h + c);
-        // Slot-list index of this lane's score (j, i), relative to the tile:
-        // key_of_pos(32 kb + 8 j + 4 h + i) = 32 h + 8 i + 4 kb + j.
-        const int kidx = 32 * h + 4 * kb;
+        // Slot-list index of this lane's score (j, i), relative to the tile: fp8,
+        // key_of_pos(32 kb + 8 j + 4 h + i) = 32 h + 8 i + 4 kb + j; bf16,
+        // key_of_pos16(8 j + 4 h + i) = 16 h + 4 i + j.
+        const int kidx = KV16 ? 16 * h : 32 * h + 4 * kb;
+        constexpr int kIStride = KV16 ? 4 : 8;
 
         // K operand reads, their exact conversion to bf16 and the MFMAs of this wave's block of
         // tile t, in one accumulator chain (the matrix core forwards an accumulator to the next
@@ -317,6 +366,27 @@ __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const MlaSplitAr
         auto zero16 = [](f32x16 &x) {
 #pragma unroll
             for (int i = 0; i < 16; ++i) x[i] = 0.f;
+        };
+        // bf16 rows: the scores of tile t, the stored K chunks straight into the bf16 MFMA, in two
+        // accumulator chains (alternate 64-element lines) summed at the end.
+        auto qk16 = [&](int t, f32x16 &acc) {
+            f32x16 acc2;
+            zero16(acc);
+            zero16(acc2);
+#pragma unroll
+            for (int L = 0; L < DQK / 64; ++L) {
+                const uint8_t *lb = L < 8 ? lds + (t % kLineSlots) * 32768 + 4096 * L
+                                          : lds + T::kTailOff + (t % kTailSlots) * 4096;
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const u32x4 k16 = *reinterpret_cast<const u32x4 *>(lb + k_off[c]);
+                    if (L & 1)
+                        acc2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(k16), qv[4 * L + c], acc2, 0, 0, 0);
+                    else
+                        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(k16), qv[4 * L + c], acc, 0, 0, 0);
+                }
+            }
+            acc += acc2;
         };
 
         // Online softmax over this wave's blocks, in base 2 with an integer running maximum m
@@ -345,7 +415,7 @@ __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const MlaSplitAr
                 for (int j = 0; j < 4; ++j)
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
-                        if (((bad >> (8 * i + j)) & 1) || 8 * i + j >= thr) sc[4 * j + i] = kNegInf;
+                        if (((bad >> (kIStride * i + j)) & 1) || kIStride * i + j >= thr) sc[4 * j + i] = kNegInf;
             }
             float mx = sc[0];
 #pragma unroll
@@ -372,7 +442,7 @@ __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const MlaSplitAr
                 const f16x2 h01 = pack_f16x2(p0, p1), h23 = pack_f16x2(p2, p3);
                 sf.esum += (p0 + p1) + (p2 + p3);
                 sf.qsum += (float(h01.x) + float(h01.y)) + (float(h23.x) + float(h23.y));
-                *reinterpret_cast<u32x2 *>(pb + p_slot(srow, 4 * kb + j) + 8 * h) =
+                *reinterpret_cast<u32x2 *>(pb + p_slot(srow, (KV16 ? 0 : 4 * kb) + j) + 8 * h) =
                     u32x2{__builtin_bit_cast(uint32_t, h01), __builtin_bit_cast(uint32_t, h23)};
             }
         };
@@ -411,6 +481,40 @@ __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const MlaSplitAr
 
         using yes = std::integral_constant<bool, true>;
         using no = std::integral_constant<bool, false>;
+        // tiles with keys past some row's window or the partition end, or with skipped keys (mask
+        // published when the tile's copies were issued), take the masked variant
+        auto masked_tile = [&](int t) {
+            return t >= n_full || __builtin_amdgcn_readfirstlane(uint32_t(bad_ring[t % kIdSlots] != 0));
+        };
+        if constexpr (KV16) {
+            // bf16 rows: the two score waves of a SIMD take alternate tiles (wave kb the tiles
+            // t = kb mod 2) and alternate between two kinds of step: in step t the owner of tile t
+            // runs its softmax (P(t) and the block maximum to LDS) while the other wave computes
+            // the scores of tile t + 1 on the matrix core.
+            if (ntiles > 0) {
+                __syncthreads();   // tiles 0 and 1 landed
+                f32x16 sc;
+                if (kb == 0) qk16(0, sc);
+                __syncthreads();   // tile 0's rope tails read: step 0's copies may refill their slot
+                for (int t = 0; t < ntiles; ++t) {
+                    if ((t & 1) == kb) {
+                        Soft sf = masked_tile(t) ? sm0(t, sc, yes{}) : sm0(t, sc, no{});
+                        sm12(t, 0, sc, sf);
+                        sm12(t, 2, sc, sf);
+                        sm3(t, sf);
+                    } else if (t + 1 < ntiles) {
+                        qk16(t + 1, sc);
+                    }
+                    __syncthreads();   // P(t) published; tile t + 2 landed
+                }
+                uint8_t *fin = P + (ntiles & 1) * 8192 + kb * 768 + srow * 4;
+                *reinterpret_cast<int *>(fin) = m_run;
+                *reinterpret_cast<float *>(fin + 256) = lq_run;
+                *reinterpret_cast<float *>(fin + 512) = le_run;
+                __syncthreads();   // final states published
+            }
+            return;
+        }
         if (ntiles > 0) {
             __syncthreads();   // tiles 0 and 1 landed
             f32x16 sa, sb;
@@ -419,11 +523,6 @@ __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const MlaSplitAr
 #pragma unroll
             for (int L = 0; L < NL; ++L) qk_line(0, L, sa);
             __syncthreads();   // tile 0's rope tails read: step 0's copies may refill their slot
-            // tiles with keys past some row's window or the partition end, or with skipped keys
-            // (mask published when the tile's copies were issued), take the masked variant
-            auto masked_tile = [&](int t) {
-                return t >= n_full || __builtin_amdgcn_readfirstlane(uint32_t(bad_ring[t % kIdSlots] != 0));
-            };
             int t = 0;
             for (; t + 1 < ntiles; t += 2) {
                 if (masked_tile(t)) step(t, sa, sb, yes{}); else step(t, sa, sb, no{});
@@ -450,10 +549,13 @@ __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const MlaSplitAr
     // slot-list key 8 (L >> 3) + i at position 8 i + (L >> 3), chunk position L & 7, i.e. global
     // chunk (L & 7) ^ swz_line(position).  The tail copy writes positions 16 v .. 16 v + 15.
     // Value wave 0 also loads every tile's slot ids into the shared id ring.
+    // (bf16 rows: instruction i writes positions 8 (i & 3) .. + 7 of line 2 v + (i >> 2), lane L
+    // key 4 (L >> 3) + (i & 3); the tail copy positions 8 v .. 8 v + 7.)
     const int jgrp = lane >> 3;
-    const int tail_pos = 16 * v + (lane >> 2);
-    const int tail_chunk = 512 + 16 * ((lane & 3) ^ swz_tail(tail_pos));
-    const int tail_key = key_of_pos(tail_pos);
+    const int tail_pos = KV16 ? 8 * v + jgrp : 16 * v + (lane >> 2);
+    const int tail_chunk = KV16 ? 1024 + 16 * ((lane & 7) ^ swz16(tail_pos))
+                                : 512 + 16 * ((lane & 3) ^ swz_tail(tail_pos));
+    const int tail_key = KV16 ? key_of_pos16(tail_pos) : key_of_pos(tail_pos);
     const uint64_t kv_stride = uint64_t(a.kv_stride);
     const bool id_loader = v == 0;
 
@@ -474,17 +576,30 @@ __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const MlaSplitAr
         if (EXTRA && min(k0 + tile * kBK + idx, k1 - 1) >= S1) p += kv2_delta;
         return p;
     };
+    // (kid: the ids of the lane's line keys 8 jgrp + i; bf16 rows, 4 jgrp + i for i < 4.  mid:
+    // the id of the key numbered by the lane, or 0 past the tile's keys.)
     auto copy_lines = [&](int tile, const int32_t (&kid)[8], int32_t mid) {
-        const uint32_t lslot = lds_addr + (tile % kLineSlots) * 32768 + v * 8192;
         if (id_loader) {
             // every lane stores the same mask (no branch)
             const uint64_t bad = __builtin_amdgcn_ballot_w64(mid < 0);
             bad_ring[tile % kIdSlots] = bad;
         }
+        if constexpr (KV16) {
+            const uint32_t lslot = lds_addr + (tile % kLineSlots) * 32768 + v * 8192;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int gc = (lane & 7) ^ swz_line(8 * i + jgrp);
-            copy16(row_of(tile, 8 * jgrp + i, kid[i]) + 128 * v + 16 * gc, lslot + 1024 * i);
+            for (int i = 0; i < 8; ++i) {
+                const int line = 2 * v + (i >> 2), gi = i & 3;
+                const int gc = (lane & 7) ^ swz16(8 * gi + jgrp);
+                copy16(row_of(tile, 4 * jgrp + gi, kid[gi]) + 128 * line + 16 * gc,
+                       lslot + 4096 * (i >> 2) + 1024 * gi);
+            }
+        } else {
+            const uint32_t lslot = lds_addr + (tile % kLineSlots) * 32768 + v * 8192;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int gc = (lane & 7) ^ swz_line(8 * i + jgrp);
+                copy16(row_of(tile, 8 * jgrp + i, kid[i]) + 128 * v + 16 * gc, lslot + 1024 * i);
+            }
         }
     };
     auto copy_tail = [&](int tile, int32_t tid) {
@@ -496,10 +611,16 @@ __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const MlaSplitAr
     auto issue_lines = [&](int tile) {
         if (tile >= ntiles) return;
         const int32_t *ids = id_ring + (tile % kIdSlots) * 64;
-        const i32x4 ia = *reinterpret_cast<const i32x4 *>(ids + 8 * jgrp);
-        const i32x4 ib = *reinterpret_cast<const i32x4 *>(ids + 8 * jgrp + 4);
-        const int32_t kid[8] = {ia.x, ia.y, ia.z, ia.w, ib.x, ib.y, ib.z, ib.w};
-        copy_lines(tile, kid, ids[lane]);
+        if constexpr (KV16) {
+            const i32x4 ia = *reinterpret_cast<const i32x4 *>(ids + 4 * jgrp);
+            const int32_t kid[8] = {ia.x, ia.y, ia.z, ia.w, 0, 0, 0, 0};
+            copy_lines(tile, kid, lane < kBK ? ids[lane] : 0);
+        } else {
+            const i32x4 ia = *reinterpret_cast<const i32x4 *>(ids + 8 * jgrp);
+            const i32x4 ib = *reinterpret_cast<const i32x4 *>(ids + 8 * jgrp + 4);
+            const int32_t kid[8] = {ia.x, ia.y, ia.z, ia.w, ib.x, ib.y, ib.z, ib.w};
+            copy_lines(tile, kid, ids[lane]);
+        }
     };
     auto issue_tail = [&](int tile) {
         if (!T::kTail || tile >= ntiles) return;
@@ -516,10 +637,15 @@ __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const MlaSplitAr
         for (int i = 0; i < 8; ++i) pre_kid[j][i] = 0;
         pre_tid[j] = pre_mid[j] = 0;
         if (j < ntiles) {
+            if constexpr (KV16) {
 #pragma unroll
-            for (int i = 0; i < 8; ++i) pre_kid[j][i] = *id_ptr(min(kb + 8 * jgrp + i, last));
+                for (int i = 0; i < 4; ++i) pre_kid[j][i] = *id_ptr(min(kb + 4 * jgrp + i, last));
+            } else {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) pre_kid[j][i] = *id_ptr(min(kb + 8 * jgrp + i, last));
+            }
             pre_tid[j] = *id_ptr(min(kb + tail_key, last));
-            pre_mid[j] = *id_ptr(min(kb + lane, last));
+            if (!KV16 || lane < kBK) pre_mid[j] = *id_ptr(min(kb + lane, last));
         }
     }
     // Schedule (tile j is read by the score waves in step j - 1, and by the value waves in
@@ -556,6 +682,27 @@ __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const MlaSplitAr
     for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
         for (int r = 0; r < 4; ++r) p_rd[rb][r] = p_slot(32 * rb + n, 2 * h + (r & 1) + 4 * (r >> 1));
+    // bf16 rows, two MFMAs per 32 keys.  V^T of column block cb (columns 128 v + 32 cb + 0..31,
+    // line 2 v + (cb >> 1)): transposed read u of MFMA r (ds_read_b64_tr_b16) hands lane (m, h)
+    // the bf16 values of keys 16 r + 8 h + 4 u + 0..3 of column m (a 16-lane group reads 4 keys x
+    // 16 columns: lane s points at key s >> 2, columns 4 (s & 3) .. + 3 of its group's 16); the
+    // two reads, converted to fp16, are the k slots 8 h .. 8 h + 7 of MFMA r.  P^T of MFMA r for
+    // row 32 rb + n: P slot 2 r + h of the row.
+    const int s16 = lane & 15, g16 = (lane >> 4) & 1;
+    int v_off16[4][2][2];
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+        for (int r = 0; r < 2; ++r)
+#pragma unroll
+            for (int u = 0; u < 2; ++u)
+                v_off16[cb][r][u] = line_off16(2 * v + (cb >> 1), 16 * r + 8 * h + 4 * u + (s16 >> 2),
+                                               4 * (cb & 1) + 2 * g16 + ((s16 & 3) >> 1)) + 8 * (s16 & 1);
+    int p_rd16[2][2];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int r = 0; r < 2; ++r) p_rd16[rb][r] = p_slot(32 * rb + n, 2 * r + h);
 
     // The accumulators of rows n and 32 + n hold sums relative to mc[rb], the largest block
     // maximum applied so far.  A block whose maximum is larger first rescales them by the exact
@@ -631,6 +778,62 @@ __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const MlaSplitAr
         }
     };
 
+    // PV of a bf16 tile t: its one block of weights (score wave t & 1), as in pv.
+    auto pv16 = [&](int t) {
+        const uint8_t *pbuf = P + (t & 1) * 8192;
+        const uint8_t *mlb = ML + (t & 1) * T::kMlBytes + 256 * (t & 1);
+        const uint8_t *lb = lds + (t % kLineSlots) * 32768;
+        s16x4 raw[4][2][2];
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+            for (int r = 0; r < 2; ++r)
+#pragma unroll
+                for (int u = 0; u < 2; ++u)
+                    raw[cb][r][u] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (__attribute__((address_space(3))) s16x4 *)(lb + v_off16[cb][r][u]));
+        f16x8 pw[2][2];
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+            for (int r = 0; r < 2; ++r)
+                pw[rb][r] = __builtin_bit_cast(f16x8, *reinterpret_cast<const u32x4 *>(pbuf + p_rd16[rb][r]));
+        int mblk[2];
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) mblk[rb] = *reinterpret_cast<const int *>(mlb + (32 * rb + n) * 4);
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+            const int m = mblk[rb];
+            if (m > mc[rb]) {
+                const float alpha = ldexpf(1.f, mc[rb] - m);
+                mc[rb] = m;
+                if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
+#pragma unroll
+                    for (int cb = 0; cb < 4; ++cb) oacc[rb][cb] *= alpha;
+                }
+            }
+            const _Float16 ps = static_cast<_Float16>(ldexpf(1.f, m - mc[rb]));
+            if (__builtin_amdgcn_ballot_w64(ps != _Float16(1.f))) {
+#pragma unroll
+                for (int r = 0; r < 2; ++r) pw[rb][r] *= ps;
+            }
+        }
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb) {
+            f16x8 vt[2];
+#pragma unroll
+            for (int r = 0; r < 2; ++r) vt[r] = bf16x8_to_f16x8(raw[cb][r][0], raw[cb][r][1]);
+#pragma unroll
+            for (int r = 0; r < 2; ++r)
+#pragma unroll
+                for (int rb = 0; rb < 2; ++rb)
+                    oacc[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vt[r], pw[rb][r], oacc[rb][cb], 0, 0, 0);
+        }
+    };
+    auto pv_tile = [&](int t) {
+        if constexpr (KV16) pv16(t); else pv(t);
+    };
+
     if (ntiles > 0) {
         wait_vmem(0);   // the slot ids of tiles 0-2 are in registers
         issue_ids(3);
@@ -647,7 +850,7 @@ __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const MlaSplitAr
         __syncthreads();   // tiles 0 and 1, the ids of tile 3 and the masks of tiles 0-2 landed
         __syncthreads();   // the score waves read tile 0's rope tails (its slot is refilled in step 0)
         for (int t = 0; t < ntiles; ++t) {
-            if (t > 0) pv(t - 1);
+            if (t > 0) pv_tile(t - 1);
             // line slot (t + 3) % 4 held tile t - 1 and tail slot (t + 3) % 3 tile t: every read
             // of them is done (the score waves' before the previous barrier, this wave's own
             // line just above)
@@ -659,12 +862,12 @@ __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const MlaSplitAr
             wait_vmem(cnt_ids(t + 5) + cnt_rows(t + 3) + cnt_ids(t + 6));
             __syncthreads();   // P(t) published; tile t + 2 landed
         }
-        pv(ntiles - 1);
+        pv_tile(ntiles - 1);
         __syncthreads();   // the score waves' final states published
     }
 
     // ---- epilogue: lane (n, h) of block cb holds columns m = 8 q + 4 h + 0..3 of row 32 rb + n;
-    // m < 16 lie in chunk cb of line v, the others in chunk cb ^ 4.
+    // fp8, m < 16 lie in chunk cb of line v, the others in chunk cb ^ 4; bf16, column 32 cb + m.
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
         const int rl = 32 * rb + n;
@@ -691,7 +894,8 @@ __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const MlaSplitAr
         for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const int col = 128 * v + 16 * (q < 2 ? cb : (cb ^ 4)) + 8 * (q & 1) + 4 * h;
+                const int col = KV16 ? 128 * v + 32 * cb + 8 * q + 4 * h
+                                     : 128 * v + 16 * (q < 2 ? cb : (cb ^ 4)) + 8 * (q & 1) + 4 * h;
                 if (col >= DV) continue;
                 const float v0 = oacc[rb][cb][4 * q] * inv, v1 = oacc[rb][cb][4 * q + 1] * inv;
                 const float v2 = oacc[rb][cb][4 * q + 2] * inv, v3 = oacc[rb][cb][4 * q + 3] * inv;
@@ -713,28 +917,34 @@ __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const MlaSplitAr
     }
 }
 
-template <int DQK, int DV, bool EXTRA>
+template <int DQK, int DV, bool EXTRA, bool KV16>
 hipError_t launch_shape(const MlaSplitArgs &a, bool direct, hipStream_t s) {
     const dim3 grid(xcd_grid_size(a.total_ctas)), block(kThreads);
     if (direct)
-        hipLaunchKernelGGL((mla_split_kernel<DQK, DV, true, EXTRA>), grid, block, 0, s, a);
+        hipLaunchKernelGGL((mla_split_kernel<DQK, DV, true, EXTRA, KV16>), grid, block, 0, s, a);
     else
-        hipLaunchKernelGGL((mla_split_kernel<DQK, DV, false, EXTRA>), grid, block, 0, s, a);
+        hipLaunchKernelGGL((mla_split_kernel<DQK, DV, false, EXTRA, KV16>), grid, block, 0, s, a);
     return hipGetLastError();
+}
+
+template <bool KV16>
+hipError_t launch_format(const MlaSplitArgs &a, int d_qk, int d_v, bool direct, hipStream_t s) {
+    const bool extra = a.kv2 != nullptr;
+    if (d_qk == 576 && d_v == 512)   // (the second cache is a sparse top-k feature: 512-wide rows)
+        return extra ? hipErrorInvalidValue : launch_shape<576, 512, false, KV16>(a, direct, s);
+    if (d_qk == 512 && d_v == 448)
+        return extra ? launch_shape<512, 448, true, KV16>(a, direct, s)
+                     : launch_shape<512, 448, false, KV16>(a, direct, s);
+    return hipErrorInvalidValue;
 }
 
 }  // namespace
 
 int mla_rows_per_cta() { return kBM; }
 
-hipError_t launch_mla_split(const MlaSplitArgs &a, int d_qk, int d_v, bool direct, hipStream_t s) {
+hipError_t launch_mla_split(const MlaSplitArgs &a, int d_qk, int d_v, bool kv_bf16, bool direct, hipStream_t s) {
     if (a.block_k != 32 && a.block_k != 64) return hipErrorInvalidValue;
-    const bool extra = a.kv2 != nullptr;
-    if (d_qk == 576 && d_v == 512)   // (the second cache is a sparse top-k feature: 512-byte rows)
-        return extra ? hipErrorInvalidValue : launch_shape<576, 512, false>(a, direct, s);
-    if (d_qk == 512 && d_v == 448)
-        return extra ? launch_shape<512, 448, true>(a, direct, s) : launch_shape<512, 448, false>(a, direct, s);
-    return hipErrorInvalidValue;
+    return kv_bf16 ? launch_format<true>(a, d_qk, d_v, direct, s) : launch_format<false>(a, d_qk, d_v, direct, s);
 }
 
 }  // namespace gqa

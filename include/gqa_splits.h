@@ -64,22 +64,28 @@ typedef enum gqa_status {
 } gqa_status;
 
 typedef enum gqa_kind {
-    /* Absorbed MLA [MM]: one fused fp8 row per token, K = the whole row, V = its first d_v
-     * bytes; page_size 1.  Sparse top-k decode [AITER] is this kind with one request per query
+    /* Absorbed MLA [MM]: one fused row per token (fp8, or bf16 with GQA_KV_BF16), K = the
+     * whole row, V = its first d_v elements; page_size 1.  Sparse top-k decode [AITER] is this kind with one request per query
      * whose kv_indices row holds that query's top-k slots. */
     GQA_KIND_MLA_FUSED = 0,
     /* Grouped-query / multi-head decode over bf16 K and V pages [MM, forward_paged]. */
     GQA_KIND_GQA_PAGED = 1
 } gqa_kind;
 
+/* Element format of the MLA pool (and of a second cache). */
 typedef enum gqa_fp8_format {
     GQA_FP8_E4M3FN = 0,    /* OCP e4m3fn: gfx950's native fp8 */
-    GQA_FP8_E4M3FNUZ = 1   /* e4m3fnuz (the gfx942 encoding used by [MM]) */
+    GQA_FP8_E4M3FNUZ = 1,  /* e4m3fnuz (the gfx942 encoding used by [MM]) */
+    /* bf16 rows (2 bytes per element), the same fused rows and the same per-tensor kv_scale
+     * (1 for a plain bf16 cache) [AITER, closing paragraph: the bf16-cache measurement].  The
+     * value part is multiplied in fp16: stored values must lie within fp16's range (|v| < 65520);
+     * below 2^-14 they are rounded to fp16's subnormal step (an error under 2^-25). */
+    GQA_KV_BF16 = 2
 } gqa_fp8_format;
 
 typedef struct gqa_decode_problem {
     int32_t kind;          /* gqa_kind */
-    int32_t fp8_format;    /* gqa_fp8_format (MLA only) */
+    int32_t fp8_format;    /* gqa_fp8_format: the MLA pool's element format (MLA only) */
 
     int64_t batch;         /* B: requests, >= 1 */
     int64_t q_len;         /* queries per request, >= 1 (1: decode; > 1: draft window) */
@@ -99,8 +105,8 @@ typedef struct gqa_decode_problem {
     const void *q_pe;
     int64_t q_pe_stride_tok, q_pe_stride_head;
 
-    /* MLA pool: fp8 bytes [N, d_qk]; row stride kv_stride_row bytes (a multiple of 16,
-     * >= d_qk; pointer 16-byte aligned). */
+    /* MLA pool: [N, d_qk] elements of fp8_format (fp8 bytes or bf16); row stride kv_stride_row
+     * bytes (a multiple of 16, >= d_qk elements; pointer 16-byte aligned). */
     const void *kv;
     int64_t kv_stride_row;
 
@@ -118,7 +124,7 @@ typedef struct gqa_decode_problem {
     const int32_t *seq_lens;
 
     float scale;           /* softmax scale applied to q . k */
-    float kv_scale;        /* MLA: per-tensor dequantization scale of the fp8 pool; GQA: 1 */
+    float kv_scale;        /* MLA: per-tensor dequantization scale of the pool; GQA: 1 */
 
     /* Decode context parallelism [MM, MLA decode] (MLA with d_qk 576 only; cp_world 0 or 1 and
      * glen NULL: off).  The keys of each request are dealt over cp_world ranks by position
@@ -133,14 +139,14 @@ typedef struct gqa_decode_problem {
 
     /* A second cache [FI, Parameters: extra_topk, candidate slots per token in a second cache]
      * (sparse MLA rows, d_qk 512, with q_len 1 and no context parallelism; kv2 NULL: off).
-     * kv2: fp8 rows of the pool's format [N2, d_qk] at the pool's row stride (kv2_stride_row 0
+     * kv2: rows of the pool's format [N2, d_qk] at the pool's row stride (kv2_stride_row 0
      * or equal to kv_stride_row; pointer 16-byte aligned), dequantized with kv_scale.  Request b
      * attends its seq_lens[b] pool keys and then the second-cache rows
      * kv2_indices[kv2_indptr[b] .. kv2_indptr[b + 1]) (negative: skipped), all in one softmax;
      * partitions cut the concatenated list.  kv2_indptr: int32 [B + 1].  max_num_keys must cover
      * seq_lens[b] plus the request's second-cache count.  Errors: kv2 without both index lists
-     * (or the reverse) GQA_ERR_INVALID_ARGUMENT; with the GQA kind, wide rows, q_len > 1,
-     * context parallelism or another row stride GQA_ERR_UNSUPPORTED. */
+     * (or the reverse) GQA_ERR_INVALID_ARGUMENT; with the GQA kind, wide rows, a bf16 pool,
+     * q_len > 1, context parallelism or another row stride GQA_ERR_UNSUPPORTED. */
     const void *kv2;
     int64_t kv2_stride_row;
     const int32_t *kv2_indices;
@@ -231,8 +237,10 @@ int device_sm_count(int64_t *sm_out);
  * and the tile size (block_k_or_0, or the tile rule's choice when 0), for the device with
  * sm_count CUs (<= 0: the current device).  The planner sees heads_per_group = q_len * H for
  * MLA (the query rows packed per request) and num_kv_heads for GQA; the tile rule sees the
- * split kernel's CTA count, B * np * ceil(q_len * H / 32) for MLA and B * np * num_kv_heads
- * for GQA. */
+ * CTA count of the split launch, B * np * ceil(q_len * H / 64) for MLA (the kernel's CTAs run 64
+ * query rows) and B * np * num_kv_heads for GQA.  The split kernels' key tiles are fixed (MLA:
+ * 64 fp8 or 32 bf16 keys; GQA: 16 tokens), so block_k sets the partitions' granularity: partition
+ * lengths are rounded up to it. */
 int decode_plan(const gqa_decode_problem *p, int64_t np_or_0, int block_k_or_0, int64_t sm_count,
                 int64_t *np_out, int *block_k_out);
 
@@ -303,8 +311,8 @@ int decode(const gqa_decode_problem *p, int64_t np_or_0, int block_k_or_0, void 
  * partitions of chunk_b keys as that needs.  c is the smallest multiple of block_k for which
  * the sum of n_b is at most budget; if none is (budget below the number of non-empty requests),
  * c is the longest L_b rounded up to block_k.  Partition j of request b covers its keys
- * [j * chunk_b, (j + 1) * chunk_b).  A negative L_b counts as 0, and one above 2^31 - 1 as
- * 2^31 - 1.
+ * [j * chunk_b, (j + 1) * chunk_b).  A negative L_b counts as 0, and one above 2^31 - 64 as
+ * 2^31 - 64 (so that every chunk_b fits an int32).
  *   seq_lens [batch], extra_indptr [batch + 1] or NULL: int32 device (inputs)
  *   part_start [batch + 1] int32 device (output): exclusive prefix sum of n_b
  *   part_chunk [batch] int32 device (output): chunk_b

@@ -68,7 +68,7 @@ def oracle_mla(inp, rows=None, n_threads=0):
     if rows is None:
         second = {}
         if inp.pool2 is not None:
-            second = dict(pool2=inp.pool2.cpu().numpy(), kv2_indices=inp.kv2_indices.cpu().numpy(),
+            second = dict(pool2=pool_np(inp.pool2), kv2_indices=inp.kv2_indices.cpu().numpy(),
                           kv2_indptr=inp.kv2_indptr.cpu().numpy())
         return oracle.mla_decode(bits16(inp.q_lat), bits16(inp.q_pe), pool_np(inp.pool),
                                  inp.kv_indices.cpu().numpy(), inp.kv_indptr.cpu().numpy(),

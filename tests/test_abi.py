@@ -157,10 +157,11 @@ def gqa_fake(B=32, Hq=64, Hkv=8, page=16, q_len=1, max_keys=32768):
 def test_decode_plan_mla_matches_oracle(B, q_len, H, keys):
     p = mla_fake(B=B, q_len=q_len, H=H, max_keys=keys)
     np_, bk = g.decode_plan(p, 0, 0, 256)
-    # the planner sees the query rows packed per request; the tile rule sees the split CTAs
+    # the planner sees the query rows packed per request; the tile rule sees the CTAs the split
+    # launches (64 query rows each)
     want_np = oracle.plan_splits(B, keys, q_len * H, 256, True)
     assert np_ == want_np
-    assert bk == oracle.block_k(B * want_np * -(-(q_len * H) // 32), 256)
+    assert bk == oracle.block_k(B * want_np * -(-(q_len * H) // 64), 256)
 
 
 def test_decode_plan_gqa_matches_oracle():
@@ -284,6 +285,24 @@ def test_second_cache_rejections():
     p = gqa_fake()
     p.kv2, p.kv2_indices, p.kv2_indptr = FAKE, FAKE, FAKE
     expect_status(lambda: g.decode_split(p, 4, 32, FAKE, FAKE), -2)
+
+
+def test_bf16_pool_checks():
+    # a bf16 pool: rows of 2 bytes per element (stride >= 2 d_qk), no second cache
+    p = mla_fake()
+    p.fp8_format = g.KV_BF16
+    p.kv_stride_row = 576
+    expect_status(lambda: g.decode_split(p, 4, 32, FAKE, FAKE), -2)
+    p.kv_stride_row = 1152
+    assert g.decode_plan(p, 4, 32, 256) == (4, 32)
+    p = mla_fake(d_qk=512, d_v=448, max_keys=4096)
+    p.fp8_format, p.kv_stride_row = g.KV_BF16, 1024
+    assert g.decode_plan(p, 0, 0, 256)[0] >= 1
+    p.kv2, p.kv2_indices, p.kv2_indptr = FAKE, FAKE, FAKE
+    expect_status(lambda: g.decode_split(p, 4, 32, FAKE, FAKE), -2)
+    p = mla_fake()
+    p.fp8_format = 3
+    expect_status(lambda: g.decode_split(p, 4, 32, FAKE, FAKE), -1)
 
 
 def test_proportional_plan_argument_rejections():

@@ -1,13 +1,12 @@
 """GPU parity of the MLA split kernel at wide dynamic range, against the fp64 CPU oracle.
 
-The kernel multiplies fp8 operands on the block-scaled fp8 MFMA: a bf16 query row is scaled by
-a power of two that puts its largest element in [128, 256) and split into an e4m3 hi part and an
-e4m3 lo remainder; the softmax weights p * 2^8 of a key tile (relative to the tile's integer
-maximum) are split the same way.  Both splits are exact for elements within about 2^-9 of their
-row (or tile) maximum and keep an absolute error of at most 2^-10 of the scaled unit below it.
-These cases drive the regimes where that matters: scores spread over tens of octaves within and
-across tiles, query rows whose elements span 20 octaves, pool bytes at the largest e4m3
-magnitudes and in the subnormal range, and one dominant key per tile.
+The kernel multiplies the bf16 query by the stored fp8 K decoded exactly to bf16 (exact
+products, fp32 sums), stores the softmax weights 2^(score - m + 8) relative to an integer
+running maximum m as fp16, and multiplies them by V decoded exactly to fp16 (fp32 sums); the
+output is normalized by the sum of the stored weights and the LSE comes from the exact ones.
+The cases drive the regimes where rounding could show: scores spread over tens of octaves
+within and across tiles, query rows whose elements span 20 octaves, pool bytes at the largest
+e4m3 magnitudes and in the subnormal range, and one dominant key per tile.
 
 Bars (the oracle is unsplit fp64 softmax attention over the same stored bytes, the comparison
 the moonmath-amd README's "Numerics" paragraph describes: an fp32-or-better reference over the

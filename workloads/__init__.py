@@ -12,6 +12,8 @@ Shapes follow the workloads the pages describe:
 * sparse top-k MLA decode (AITER issue on pa_decode_sparse, "Measurements"): 64 heads, rows of
   512 fp8 bytes (448 NoPE + 64 RoPE) in a 262144-token cache, 2048 indices per query drawn
   without replacement;
+* the bf16 cache (the AITER issue's closing paragraph): the same fused rows stored as bf16 values
+  N(0,1) with kv_scale 1;
 * grouped-query decode over bf16 pages (moonmath-amd README, gfx950 "forward_paged"): caches
   ``[pages, 16, kv_heads, 128]``, ``kv_indptr`` counting pages per sequence and
   ``kv_page_indices`` a random placement of pages in the pool.
@@ -188,10 +190,15 @@ def sparse_mla_inputs(*, num_queries: int, topk: int = 2048, cache_rows: int = 2
     drawn without replacement; rows are 512 fp8 bytes (448 NoPE + 64 RoPE), value = NoPE part.
     invalid_frac: that fraction of the index entries (seeded positions) is -1, a skipped key;
     all_invalid: queries whose whole list is -1.  extra_topk > 0: a second cache of extra_rows
-    rows of the same format, from which each query draws extra_topk more candidates."""
+    rows of the same format, from which each query draws extra_topk more candidates.
+    kv_dtype="bf16": a bf16 cache of N(0,1) rows with kv_scale 1 (no second cache)."""
+    assert kv_dtype in ("fp8", "bf16") and not (kv_dtype == "bf16" and extra_topk)
     nq = num_queries
     q = _randn((nq, H, 512), seed + 1, device, torch.bfloat16)
-    pool = _fp8_pool(cache_rows, 512, seed + 3, device)
+    if kv_dtype == "bf16":
+        pool = _bf16_pool(cache_rows, 512, seed + 3, device)
+    else:
+        pool = _fp8_pool(cache_rows, 512, seed + 3, device)
     g = _gen(device, seed + 4)
     rows = []
     for _ in range(nq):
@@ -318,11 +325,12 @@ def sparse_topk(num_queries: int, device="cpu", kv_dtype: str = "fp8"):
                              name="sparse_mla_h64_topk2048_nq%d%s" % (num_queries, tag))
 
 
-def mla_long_bf16(B: int, device="cpu"):
+def mla_long_bf16(B: int, q_len: int = 1, device="cpu"):
     """The H=64 long-context workload over a bf16 cache (131072 keys per request, 1152-byte
     rows, kv_scale 1)."""
-    return mla_inputs(B=B, q_len=1, H=64, seq_lens=[131072] * B, pool_rows=B * 131072, seed=2200,
-                      device=device, kv_dtype="bf16", name="mla_h64_b%d_s131072_bf16" % B)
+    return mla_inputs(B=B, q_len=q_len, H=64, seq_lens=[131072] * B, pool_rows=B * 131072,
+                      seed=2200, device=device, kv_dtype="bf16",
+                      name="mla_h64_b%d_s131072_q%d_bf16" % (B, q_len))
 
 
 # --------------------------------------------------------------------------------------------
@@ -375,6 +383,23 @@ def extreme_pool(inp: MlaInputs, frac_large: float = 0.1, frac_subnormal: float 
     return dataclasses.replace(inp, pool=pool.to(inp.pool.device))
 
 
+def extreme_bf16_pool(inp: MlaInputs, frac_large: float = 0.1, frac_small: float = 0.1,
+                      seed: int = 0) -> MlaInputs:
+    """A copy of a bf16 pool in which a seeded fraction of the elements is replaced by large
+    magnitudes (log-uniform in [8, 16), the top of the fp8 cache's dequantized range) and another
+    by tiny ones (log-uniform in [2^-24, 2^-14), fp16's subnormal range), both signs."""
+    g = _gen("cpu", seed)
+    pool = inp.pool.cpu().float().clone()
+    r = torch.rand(pool.shape, generator=g)
+    sgn = torch.where(torch.rand(pool.shape, generator=g) < 0.5, -1.0, 1.0)
+    u = torch.rand(pool.shape, generator=g)
+    large = sgn * torch.exp2(3.0 + u)
+    small = sgn * torch.exp2(-24.0 + 10.0 * u)
+    pool = torch.where(r < frac_large, large, pool)
+    pool = torch.where(r >= 1.0 - frac_small, small, pool)
+    return dataclasses.replace(inp, pool=pool.to(torch.bfloat16).to(inp.pool.device))
+
+
 def dominant_keys(inp: MlaInputs, seed: int = 0, noise: float = 0.05, block: int = 64) -> MlaInputs:
     """Queries that share one direction u (per-head noise of relative size `noise`), and in every
     run of `block` consecutive positions of each request's slot list one key whose pool row is u
@@ -401,7 +426,10 @@ def dominant_keys(inp: MlaInputs, seed: int = 0, noise: float = 0.05, block: int
             if slot < 0:
                 continue
             amp = 100.0 + 340.0 * float(torch.rand((1,), generator=g))
-            pool[slot] = fp8_e4m3fn_bytes((unit * amp).float())
+            if pool.dtype == torch.bfloat16:   # the same stored magnitude after the kv scale
+                pool[slot] = (unit * amp * KV_SCALE).to(torch.bfloat16)
+            else:
+                pool[slot] = fp8_e4m3fn_bytes((unit * amp).float())
     return dataclasses.replace(inp, q_lat=q[..., :d_lat].contiguous().to(dev),
                                q_pe=q[..., d_lat:].contiguous().to(dev), pool=pool.to(dev))
 
