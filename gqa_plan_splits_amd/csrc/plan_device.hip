@@ -12,16 +12,18 @@ constexpr int kPlanThreads = 256;
 constexpr int kPlanWaves = kPlanThreads / 64;
 constexpr int kPlanCached = 8192;   // requests whose key counts the search reads from LDS
 
-// Keys of request b (negative counts as none), held to 2^31 - 1 so that the search below runs
-// in 32-bit arithmetic.
+// Keys of request b (negative counts as none), held to kMaxKeys = 2^31 - 64, a multiple of
+// block_k: every chunk below is then a multiple of block_k of at most kMaxKeys, so it fits an
+// int32 and n + c - 1 fits 32 bits.
+constexpr int64_t kMaxKeys = (int64_t(1) << 31) - 64;
 __device__ __forceinline__ uint32_t keys_in_memory(const PlanArgs &a, int b) {
     int64_t n = a.seq_lens[b];
     if (a.extra_indptr) n += int64_t(a.extra_indptr[b + 1]) - a.extra_indptr[b];
-    return uint32_t(min(max(n, int64_t(0)), int64_t(INT32_MAX)));
+    return uint32_t(min(max(n, int64_t(0)), kMaxKeys));
 }
 
-// Slots of a request with n keys under the common chunk c, and the chunk it uses (n, c < 2^31,
-// so n + c - 1 fits 32 bits).
+// Slots of a request with n keys under the common chunk c, and the chunk it uses (n, c <=
+// kMaxKeys, so n + c - 1 fits 32 bits, and the chunk stays at most kMaxKeys).
 __device__ __forceinline__ void slots_of(const PlanArgs &a, uint32_t n, uint32_t c, int *slots,
                                          int *chunk) {
     uint32_t k = (n + c - 1) / c;

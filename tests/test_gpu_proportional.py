@@ -37,7 +37,12 @@ PLAN_CASES = [
     ("wide batch", None, 600 * 2, 8, 32, None),          # 600 requests: three scan rounds
     ("second cache", [100, 2048, 0, 7], 16, 16, 64, [0, 64, 64, 1000, 1001]),
     ("past the LDS cache", "big", 9000 * 2, 16, 32, None),   # 9000 requests: counts read from memory
+    # key counts at the int32 edge (held to 2^31 - 64, so that every chunk fits an int32): with
+    # cap 1 each request's chunk is its whole length rounded up to block_k
+    ("near 2^31", [2 ** 31 - 1, 2 ** 31 - 40, 5, 0], 3, 1, 64, None),
+    ("near 2^31 with a second cache", [2 ** 31 - 100, 7], 2, 1, 32, [0, 200, 201]),
 ]
+MAX_KEYS = 2 ** 31 - 64
 
 
 @pytest.mark.parametrize("name,lens,budget,cap,bk,extra", PLAN_CASES, ids=[c[0] for c in PLAN_CASES])
@@ -56,7 +61,7 @@ def test_plan_tables_match_oracle(name, lens, budget, cap, bk, extra):
     g.plan_proportional_device(seq, ext, B, budget, cap, bk, start, chunk)
     torch.cuda.synchronize()
     keys = list(lens) if extra is None else [lens[b] + extra[b + 1] - extra[b] for b in range(B)]
-    ref_start, ref_chunk = oracle.proportional_plan(keys, budget, cap, bk)
+    ref_start, ref_chunk = oracle.proportional_plan([min(k, MAX_KEYS) for k in keys], budget, cap, bk)
     assert start.cpu().tolist() == ref_start
     assert chunk.cpu().tolist() == ref_chunk
 
