@@ -441,7 +441,10 @@ __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const MlaSplitAr
                 const float p3 = fast_exp2(fmaf(sc[4 * j + 3], c_row, sf.bias));
                 const f16x2 h01 = pack_f16x2(p0, p1), h23 = pack_f16x2(p2, p3);
                 sf.esum += (p0 + p1) + (p2 + p3);
-                sf.qsum += (float(h01.x) + float(h01.y)) + (float(h23.x) + float(h23.y));
+                // the stored weights' sum: v_dot2_f32_f16 against (1, 1) adds two fp16 values
+                // to an fp32 sum (exact products)
+                sf.qsum = __builtin_amdgcn_fdot2(h01, f16x2{1.0f16, 1.0f16}, sf.qsum, false);
+                sf.qsum = __builtin_amdgcn_fdot2(h23, f16x2{1.0f16, 1.0f16}, sf.qsum, false);
                 *reinterpret_cast<u32x2 *>(pb + p_slot(srow, (KV16 ? 0 : 4 * kb) + j) + 8 * h) =
                     u32x2{__builtin_bit_cast(uint32_t, h01), __builtin_bit_cast(uint32_t, h23)};
             }
