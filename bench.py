@@ -162,9 +162,12 @@ class Case:
 
 # Counter summaries under profiles/, per timed workload: the file and the sources its kernel is
 # compiled from (hashed in this order).
+MLA_SOURCES = ("mla_split.hip", "device_common.hpp", "kernels.hpp")
 COUNTER_PROFILES = {
-    "mla_h64_b16_s131072_q1": ("mla_split_b16_s131072_counters.txt",
-                               ("mla_split.hip", "device_common.hpp", "kernels.hpp")),
+    "mla_h64_b16_s131072_q1": ("mla_split_b16_s131072_counters.txt", MLA_SOURCES),
+    "mla_h64_b16_s131072_q4": ("mla_split_b16_s131072_q4_counters.txt", MLA_SOURCES),
+    "sparse_mla_h64_topk2048_nq256": ("mla_split_sparse_nq256_counters.txt", MLA_SOURCES),
+    "mla_h64_b16_s131072_q1_bf16": ("mla_split_b16_s131072_bf16_counters.txt", MLA_SOURCES),
     "gqa_b32_hq64_hkv8_d128_p16": ("gqa_split_b32_hq64_hkv8_counters.txt",
                                    ("gqa_split.hip", "device_common.hpp", "kernels.hpp")),
 }
@@ -789,15 +792,18 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8e4m3 KV decoded exactly: bf16 QK^T and fp16 PV MFMA, fp32 accumulate" if case.is_mla
-                 else "bf16 QK^T and PV MFMA, fp32 accumulate",
-        "data": "synthetic (seeded N(0,1) bf16 queries, fp8 e4m3fn KV = N(0,1)*32, shuffled slots)",
+        "dtype": ("bf16 KV: bf16 QK^T and fp16 PV MFMA, fp32 accumulate" if case.is_mla and inp.kv_bf16
+                  else "fp8e4m3 KV decoded exactly: bf16 QK^T and fp16 PV MFMA, fp32 accumulate" if case.is_mla
+                  else "bf16 QK^T and PV MFMA, fp32 accumulate"),
+        "data": ("synthetic (seeded N(0,1) bf16 queries, bf16 KV = N(0,1), shuffled slots)" if case.is_mla and inp.kv_bf16
+                 else "synthetic (seeded N(0,1) bf16 queries, fp8 e4m3fn KV = N(0,1)*32, shuffled slots)" if case.is_mla
+                 else "synthetic (seeded N(0,1) bf16 queries and K/V pages, random page placement)"),
         "config": {
             "workload": args.workload,
             "batch": inp.B, "q_len": inp.q_len,
             "heads": inp.H if case.is_mla else inp.Hq,
             "seq_len": int(inp.max_num_keys),
-            "kv_dtype": "fp8_e4m3fn" if case.is_mla else "bf16",
+            "kv_dtype": ("bf16" if inp.kv_bf16 else "fp8_e4m3fn") if case.is_mla else "bf16",
             "np": case.np, "block_k": case.bk, "sm_count": sm,
             "us_per_call": round(ms * 1e3, 2),
             "pct_hbm_peak": round(100 * case.kv_bytes() / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
@@ -813,7 +819,8 @@ def main():
             "traffic": counters["traffic"] if counters else None,
             "mfma_busy": counters["mfma_busy"] if counters else None,
             "algorithmic_bytes": kv,
-            "algorithmic_bytes_what": "KV payload: every key's row once (576 B per key)",
+            "algorithmic_bytes_what": ("KV payload: every key's row once (%d B per key)" % (inp.d_qk * inp.pool.element_size())
+                                       if case.is_mla else "KV payload: every token's K and V rows once per kv head (512 B)"),
             "bytes_with_ids_q_partials": alg,
             "avg_launch_us": round(ms_split * 1e3, 2),
             "timer": "HIP events on the launch stream around the split-only launches of the timed "
