@@ -248,7 +248,9 @@ int decode_plan(const gqa_decode_problem *p, int64_t np_or_0, int block_k_or_0, 
 /* Split, reduce, decode                                                                    */
 /* ---------------------------------------------------------------------------------------- */
 
-/* Split kernel: request b's keys are cut into np contiguous partitions of
+/* Split kernel [MM, MLA decode: the op "splits a batch's KV by request length" and returns a
+ * base-2 LSE; gfx950 forward_paged for the paged GQA kind] [MAX, Args: np partitions per
+ * request]: request b's keys are cut into np contiguous partitions of
  * ceil(seq_lens[b] / np) keys rounded up to block_k (trailing partitions may be empty).  For
  * every row r and partition i it writes
  *   partial_o   [rows, np, d_v] fp32: softmax-weighted mean of the partition's values,
@@ -290,11 +292,15 @@ int merge_ranks(int64_t world, int64_t rows, int64_t d_v, const float *parts, co
 
 /* Workspace decode() needs for np partitions (np = 0: the planner's choice on the current
  * device): the fp32 partials, 256-byte aligned; 0 when np == 1 (the split kernel then writes
- * the final output itself). */
+ * the final output itself).  The partials are fp32 as the reducer's inputs [MAX, AMD reducer
+ * constraint] and [MM, Numerics: "the fp32 partial merge"].  Errors: those of decode_split's
+ * checks, INVALID_ARGUMENT for a NULL bytes. */
 int decode_workspace_bytes(const gqa_decode_problem *p, int64_t np, size_t *bytes);
 
-/* Whole decode: plan (np_or_0 == 0 / block_k_or_0 == 0 use the planner / tile rule on the
- * current device), split, and reduce.
+/* Whole decode [MM, MLA decode usage: one call with outputs written in place on the caller's
+ * stream; Numerics: deterministic, the split a function of the inputs]: plan (np_or_0 == 0 /
+ * block_k_or_0 == 0 use the planner [MAX] / tile rule [AITER] on the current device), split,
+ * and reduce.
  *   out      [B*q_len, H, d_v] bf16, contiguous (output)
  *   lse2_out [B*q_len, H] fp32 (output; may be NULL)
  * Errors: as decode_split, plus WORKSPACE_TOO_SMALL when ws_bytes is below
@@ -388,7 +394,9 @@ int bw_stream_read(const void *src, size_t bytes, int64_t ctas, gqa_stream_t s);
 int bw_gather_rows(const void *pool, int64_t row_bytes, const int32_t *idx, int64_t n, int64_t ctas,
                    gqa_stream_t s);
 
-/* Static description of a status code. */
+/* Static description of a status code (the error classes of the constraints lists [MM, MLA
+ * decode and gfx950 constraints]: shapes outside them are UNSUPPORTED); never NULL, "unknown
+ * status" for a value outside gqa_status. */
 const char *status_string(int status);
 
 /* Text behind the calling thread's most recent GQA_ERR_LAUNCH_FAILED (the HIP error) or
