@@ -495,10 +495,10 @@ __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const MlaSplitAr
             // runs its softmax (P(t) and the block maximum to LDS) while the other wave computes
             // the scores of tile t + 1 on the matrix core.
             if (ntiles > 0) {
-                __syncthreads();   // tiles 0 and 1 landed
+                __syncthreads();   // tile 0 landed
                 f32x16 sc;
                 if (kb == 0) qk16(0, sc);
-                __syncthreads();   // tile 0's rope tails read: step 0's copies may refill their slot
+                __syncthreads();   // tile 1 landed; tile 0's rope tails read (step 0 refills their slot)
                 for (int t = 0; t < ntiles; ++t) {
                     if ((t & 1) == kb) {
                         Soft sf = masked_tile(t) ? sm0(t, sc, yes{}) : sm0(t, sc, no{});
@@ -519,13 +519,13 @@ __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const MlaSplitAr
             return;
         }
         if (ntiles > 0) {
-            __syncthreads();   // tiles 0 and 1 landed
+            __syncthreads();   // tile 0 landed
             f32x16 sa, sb;
             zero16(sa);
             if constexpr (T::kTail) qk_tail(0, sa);
 #pragma unroll
             for (int L = 0; L < NL; ++L) qk_line(0, L, sa);
-            __syncthreads();   // tile 0's rope tails read: step 0's copies may refill their slot
+            __syncthreads();   // tile 1 landed; tile 0's rope tails read (step 0 refills their slot)
             int t = 0;
             for (; t + 1 < ntiles; t += 2) {
                 if (masked_tile(t)) step(t, sa, sb, yes{}); else step(t, sa, sb, no{});
@@ -658,6 +658,8 @@ __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const MlaSplitAr
     //             this wave has just applied, the tail slot tile t), ids(t + 6).
     // Copies retire in issue order.  Before the barrier that ends step t, tile t + 2 must have
     // landed (and with it ids(t + 4)); ids(t + 5) and step t's own issues may be outstanding.
+    // The prologue's two barriers wait for tile 0 (whose scores the score waves compute between
+    // them) and then tile 1.
     constexpr int NC = 8 + (T::kTail ? 1 : 0);
     auto cnt_rows = [&](int j) { return j >= 0 && j < ntiles ? NC : 0; };
     auto cnt_ids = [&](int j) { return id_loader && j >= 0 && j < ntiles ? 1 : 0; };
@@ -848,10 +850,12 @@ __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const MlaSplitAr
             }
         issue_ids(4);
         issue_ids(5);
-        // ids(3), rows(0), rows(1) landed; issued after rows(1): rows(2), ids(4), ids(5)
+        // ids(3) and rows(0) landed; issued after rows(0): rows(1), rows(2), ids(4), ids(5)
+        wait_vmem(cnt_rows(1) + cnt_rows(2) + cnt_ids(4) + cnt_ids(5));
+        __syncthreads();   // tile 0, the ids of tile 3 and the masks of tiles 0-2 landed
         wait_vmem(cnt_rows(2) + cnt_ids(4) + cnt_ids(5));
-        __syncthreads();   // tiles 0 and 1, the ids of tile 3 and the masks of tiles 0-2 landed
-        __syncthreads();   // the score waves read tile 0's rope tails (its slot is refilled in step 0)
+        __syncthreads();   // tile 1 landed; the score waves read tile 0 (its tail slot is refilled
+                           // in step 0)
         for (int t = 0; t < ntiles; ++t) {
             if (t > 0) pv_tile(t - 1);
             // line slot (t + 3) % 4 held tile t - 1 and tail slot (t + 3) % 3 tile t: every read

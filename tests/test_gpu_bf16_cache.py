@@ -178,3 +178,53 @@ def test_bf16_full_size_sampled(name, make, d_v):
     compare(out[rows], lse[rows], ref_o, ref_l, "bf16 " + name)
     del inp, out, lse
     torch.cuda.empty_cache()
+
+
+def test_bf16_other_entry_points():
+    # the bf16 instance through decode_proportional (slot-major partials placed by the device
+    # plan) and decode_scratch (partials in the static array), and 96 heads (a half row block)
+    from test_gpu_proportional import run_prop
+    from test_zz_no_alloc import scratch_decode
+    lens = [9000, 0, 33, 1, 2500]
+    inp = workloads.mla_inputs(B=5, q_len=1, H=96, seq_lens=lens, pool_rows=12000, seed=231,
+                               device=DEV, kv_dtype="bf16")
+    torch.cuda.synchronize()
+    p = mla_problem(inp)
+    ref_o, ref_l = oracle_mla(inp)
+    log("bf16 proportional")
+    out, lse = run_prop(p, 512, 8, 0, 32)
+    torch.cuda.synchronize()
+    compare(out, lse, ref_o, ref_l, "bf16 proportional")
+    log("bf16 scratch")
+    d_o, d_l = run_decode(p, 512, 8, 32)
+    s_o, s_l = scratch_decode(p, 512, 8, 32)
+    torch.cuda.synchronize()
+    assert torch.equal(s_o, d_o) and torch.equal(s_l, d_l)
+    compare(s_o, s_l, ref_o, ref_l, "bf16 scratch")
+
+
+def test_bf16_graph_replay_matches_eager():
+    inp = workloads.mla_inputs(B=2, q_len=1, H=64, seq_lens=[3000, 700], pool_rows=4000, seed=241,
+                               device=DEV, kv_dtype="bf16")
+    torch.cuda.synchronize()
+    p = mla_problem(inp)
+    np_, bk = 8, 32
+    out = torch.empty((p.rows, 512), dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty((p.rows,), dtype=torch.float32, device=DEV)
+    ws = torch.empty((g.decode_workspace_bytes(p, np_) // 4 + 64,), dtype=torch.float32, device=DEV)
+    s = torch.cuda.Stream()
+    torch.cuda.synchronize()   # the inputs, built on the default stream, exist before `s` reads them
+    with torch.cuda.stream(s):
+        g.decode(p, out, lse, np=np_, block_k=bk, workspace=ws, stream=s)
+    torch.cuda.synchronize()
+    eager_o, eager_l = out.clone(), lse.clone()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=s):
+        g.decode(p, out, lse, np=np_, block_k=bk, workspace=ws, stream=s)
+    for _ in range(3):
+        out.zero_()
+        lse.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager_o) and torch.equal(lse, eager_l)
