@@ -440,8 +440,9 @@ def dcp_line(stream, steps, world=8):
 
 def wave_sweep(stream, steps):
     """The planner's one-wave / two-wave choice for MLA with 16 heads (the page's exception,
-    where the two-wave count is the planner's), timed at both counts: batch 4 over 32K-128K
-    keys and batches 8 and 16 at short context."""
+    where the two-wave count is the planner's), timed at both counts and at the count of
+    plan_mla_splits_measured (this kernel's own CTAs, one wave): batch 4 over 32K-128K keys and
+    batches 8 and 16 at short context."""
     import torch
     import gqa_plan_splits_amd as g
     import workloads as w
@@ -460,7 +461,8 @@ def wave_sweep(stream, steps):
         pages = -(-S // 256)
         counts = {"one_wave": max(1, min(sm // ctas, pages, 256)),
                   "two_wave": max(1, min(2 * sm // ctas, pages, 256)),
-                  "planner": g.decode_plan(p)[0]}
+                  "planner": g.decode_plan(p)[0],
+                  "measured": g.plan_mla_splits_measured(B, S, 16, sm)}
         row = {}
         for name, n in counts.items():
             bk = g.block_k_for(B * n, sm)
@@ -474,6 +476,8 @@ def wave_sweep(stream, steps):
             ms = time_graph(fn, steps, stream) or time_events(fn, steps, stream)
             row[name] = {"np": n, "us_per_call": round(ms * 1e3, 2)}
         row["two_wave_speedup"] = round(row["one_wave"]["us_per_call"] / row["two_wave"]["us_per_call"], 3)
+        best = min(row[k]["us_per_call"] for k in counts)
+        row["measured_vs_best"] = round(row["measured"]["us_per_call"] / best, 3)
         res["mla_h16_b%d_s%d" % (B, S)] = row
         del inp, p
         torch.cuda.empty_cache()

@@ -287,7 +287,9 @@ __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const MlaSplitAr
         // two score waves of a SIMD run the same rows on alternate blocks, so each keeps its own
         // online softmax; the value waves align the two, and merge their sums at the end.
         // In the MFMA output layout lane (n, h) holds row n's scores of block positions
-        // 8 j + 4 h + i (j, i = 0..3).
+        // 8 j + 4 h + i (j, i = 0..3).  bf16 rows: block kb is every other 32-key tile (t = kb
+        // mod 2), and lane (n, h) reads elements 32 h .. 32 h + 31 of each 64-element line, one
+        // 16-byte chunk (8 dims) per MFMA, the rope tail as a ninth line.
         const int kb = wave >> 2;               // this wave's block of every tile
         const int srow = 32 * (wave & 1) + n;   // row within the CTA
         const bool row_ok = srow < nrows;
