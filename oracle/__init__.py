@@ -88,6 +88,8 @@ def _load():
         lib.oracle_mla_decode_two_caches.argtypes = [_i64, _i64, _i64, _i64, _i64, _vp, _vp, _vp,
                                                      _i64, _vp, _vp, _vp, _vp, _i64, _vp, _vp,
                                                      _dbl, _dbl, _vp, _i64, _vp, _vp, _int]
+        lib.oracle_mla_decode_two_caches_bf16.restype = _int
+        lib.oracle_mla_decode_two_caches_bf16.argtypes = lib.oracle_mla_decode_two_caches.argtypes
         lib.oracle_gqa_decode.restype = _int
         lib.oracle_gqa_decode.argtypes = [_i64, _i64, _i64, _i64, _i64, _i64, _vp, _vp, _vp, _i64,
                                           _vp, _vp, _vp, _dbl, _vp, _i64, _vp, _vp, _int]
@@ -200,7 +202,8 @@ def mla_decode(q_lat, q_pe, pool, kv_indices, kv_indptr, seq_lens, *, B, q_len, 
     """fp64 unsplit attention for absorbed MLA decode.
 
     q_lat: uint16 bf16 bits [B*q_len, H, d_lat]; q_pe: [B*q_len, H, d_rope] or None;
-    pool: uint8 fp8 bytes [N, d_lat + d_rope], or uint16 bf16 bits (the bf16-cache variant).  With pool2 (q_len 1): query b also attends the second
+    pool: uint8 fp8 bytes [N, d_lat + d_rope], or uint16 bf16 bits (the bf16-cache variant; pool2
+    then holds bf16 bits too).  With pool2 (q_len 1): query b also attends the second
     cache's rows kv2_indices[kv2_indptr[b]:kv2_indptr[b+1]], in the same softmax.
     Returns (o [n_rows, d_v] float64, lse2 [n_rows])."""
     q_lat = _c(q_lat, np.uint16)
@@ -219,8 +222,19 @@ def mla_decode(q_lat, q_pe, pool, kv_indices, kv_indptr, seq_lens, *, B, q_len, 
     rows_a, n_rows = _rows_arg(rows, B * q_len * H)
     o = np.empty((n_rows, d_v), dtype=np.float64)
     lse2 = np.empty((n_rows,), dtype=np.float64)
-    if kv_bf16:
-        assert pool2 is None and not fnuz
+    if kv_bf16 and pool2 is not None:
+        assert q_len == 1 and not fnuz
+        pool2 = _c(pool2, np.uint16)
+        assert pool2.shape[-1] == d_lat + d_rope, (pool2.shape, d_lat, d_rope)
+        kv2_indices = _c(kv2_indices, np.int32)
+        kv2_indptr = _c(kv2_indptr, np.int32)
+        rc = _load().oracle_mla_decode_two_caches_bf16(
+            B, H, d_lat, d_rope, d_v, _ptr(q_lat), _ptr(q_pe), _ptr(pool), pool.shape[0],
+            _ptr(kv_indices), _ptr(kv_indptr), _ptr(seq_lens), _ptr(pool2), pool2.shape[0],
+            _ptr(kv2_indices), _ptr(kv2_indptr), float(scale), float(kv_scale), _ptr(rows_a),
+            n_rows, _ptr(o), _ptr(lse2), int(n_threads))
+    elif kv_bf16:
+        assert not fnuz
         rc = _load().oracle_mla_decode_bf16(B, q_len, H, d_lat, d_rope, d_v, _ptr(q_lat), _ptr(q_pe),
                                             _ptr(pool), pool.shape[0], _ptr(kv_indices),
                                             _ptr(kv_indptr), _ptr(seq_lens), float(scale),

@@ -516,6 +516,23 @@ int oracle_mla_decode_two_caches(int64_t B, int64_t H, int64_t d_lat, int64_t d_
                       kv_scale, 0, 0, rows, n_rows, o_out, lse2_out, n_threads);
 }
 
+/* The second cache over a bf16 pool: both caches hold bf16 rows of the same width and scale. */
+int oracle_mla_decode_two_caches_bf16(int64_t B, int64_t H, int64_t d_lat, int64_t d_rope,
+                                      int64_t d_v, const uint16_t *q_lat, const uint16_t *q_pe,
+                                      const uint16_t *pool, int64_t pool_rows,
+                                      const int32_t *kv_indices, const int32_t *kv_indptr,
+                                      const int32_t *seq_lens, const uint16_t *pool2,
+                                      int64_t pool2_rows, const int32_t *kv2_indices,
+                                      const int32_t *kv2_indptr, double scale, double kv_scale,
+                                      const int64_t *rows, int64_t n_rows, double *o_out,
+                                      double *lse2_out, int n_threads) {
+    if (!pool2) return -1;
+    return mla_decode(B, 1, H, d_lat, d_rope, d_v, q_lat, q_pe, (const uint8_t *)pool, pool_rows,
+                      kv_indices, kv_indptr, seq_lens, (const uint8_t *)pool2, pool2_rows,
+                      kv2_indices, kv2_indptr, scale, kv_scale, 0, 1, rows, n_rows, o_out,
+                      lse2_out, n_threads);
+}
+
 int oracle_gqa_decode(int64_t B, int64_t q_len, int64_t Hq, int64_t Hkv, int64_t D,
                       int64_t page_size, const uint16_t *q, const uint16_t *k_cache,
                       const uint16_t *v_cache, int64_t num_pages,

@@ -91,6 +91,15 @@ int oracle_mla_decode_two_caches(int64_t B, int64_t H, int64_t d_lat, int64_t d_
                                  const int32_t *kv2_indptr, double scale, double kv_scale,
                                  const int64_t *rows, int64_t n_rows, double *o_out,
                                  double *lse2_out, int n_threads);
+int oracle_mla_decode_two_caches_bf16(int64_t B, int64_t H, int64_t d_lat, int64_t d_rope,
+                                      int64_t d_v, const uint16_t *q_lat, const uint16_t *q_pe,
+                                      const uint16_t *pool, int64_t pool_rows,
+                                      const int32_t *kv_indices, const int32_t *kv_indptr,
+                                      const int32_t *seq_lens, const uint16_t *pool2,
+                                      int64_t pool2_rows, const int32_t *kv2_indices,
+                                      const int32_t *kv2_indptr, double scale, double kv_scale,
+                                      const int64_t *rows, int64_t n_rows, double *o_out,
+                                      double *lse2_out, int n_threads);
 
 /* Unsplit softmax attention of grouped-query decode over bf16 K/V pages.
  *   q        [B*q_len, Hq, D] bf16 bits

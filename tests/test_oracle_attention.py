@@ -589,3 +589,58 @@ def test_bf16_cache_skipped_keys_equal_their_removal():
     np.testing.assert_allclose(o_s, o_r, rtol=1e-13, atol=1e-14)
     np.testing.assert_allclose(l_s, l_r, rtol=1e-13, atol=1e-13)
     assert not np.allclose(o_s, o_full)
+
+
+def bf16_two_cache_case(seed=41, lens=(9, 0, 30), extra=(5, 7, 0)):
+    inp = workloads.mla_inputs(B=len(lens), q_len=1, H=3, seq_lens=list(lens), pool_rows=48,
+                               d_qk=512, d_rope=64, d_v=448, seed=seed, kv_dtype="bf16")
+    return workloads.with_second_cache(inp, pool2_rows=20, extra_lens=list(extra), seed=seed + 50)
+
+
+def run_mla2_bf16(inp):
+    return oracle.mla_decode(bits16(inp.q_lat), bits16(inp.q_pe), bits16(inp.pool),
+                             inp.kv_indices.numpy(), inp.kv_indptr.numpy(), inp.seq_lens.numpy(),
+                             B=inp.B, q_len=1, H=inp.H, d_v=inp.d_v, scale=inp.scale,
+                             kv_scale=inp.kv_scale, pool2=bits16(inp.pool2),
+                             kv2_indices=inp.kv2_indices.numpy(), kv2_indptr=inp.kv2_indptr.numpy())
+
+
+def test_bf16_two_caches_match_torch_textbook():
+    inp = bf16_two_cache_case()
+    assert inp.pool2.dtype == torch.bfloat16
+    q = torch.cat([inp.q_lat, inp.q_pe], dim=-1).to(torch.float64)
+    pool, pool2 = inp.pool.to(torch.float64), inp.pool2.to(torch.float64)
+    outs, lses = [], []
+    for b in range(inp.B):
+        i1 = inp.kv_indices[int(inp.kv_indptr[b]):int(inp.kv_indptr[b]) + int(inp.seq_lens[b])].long()
+        i2 = inp.kv2_indices[int(inp.kv2_indptr[b]):int(inp.kv2_indptr[b + 1])].long()
+        K = torch.cat([pool[i1], pool2[i2]])
+        if K.shape[0] == 0:
+            outs.append(torch.zeros(inp.H, inp.d_v, dtype=torch.float64))
+            lses.append(torch.full((inp.H,), -math.inf, dtype=torch.float64))
+            continue
+        s = inp.scale * (q[b] @ K.T)
+        outs.append(torch.softmax(s, dim=-1) @ K[:, :inp.d_v])
+        lses.append(torch.logsumexp(s, dim=-1) / LN2)
+    o, l = run_mla2_bf16(inp)
+    np.testing.assert_allclose(o, torch.cat(outs).numpy(), rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(l, torch.cat(lses).numpy(), rtol=1e-12, atol=1e-12)
+
+
+def test_bf16_two_caches_equal_one_merged_pool():
+    inp = bf16_two_cache_case(lens=(9, 3, 30), extra=(5, 7, 2))
+    n1 = inp.pool.shape[0]
+    merged = torch.cat([inp.pool, inp.pool2])
+    idx, indptr, lens = [], [0], []
+    for b in range(inp.B):
+        a = inp.kv_indices[int(inp.kv_indptr[b]):int(inp.kv_indptr[b]) + int(inp.seq_lens[b])]
+        e = inp.kv2_indices[int(inp.kv2_indptr[b]):int(inp.kv2_indptr[b + 1])] + n1
+        idx.append(torch.cat([a, e]))
+        lens.append(len(a) + len(e))
+        indptr.append(indptr[-1] + lens[-1])
+    o2, l2 = run_mla2_bf16(inp)
+    o1, l1 = oracle.mla_decode(bits16(inp.q_lat), bits16(inp.q_pe), bits16(merged),
+                               torch.cat(idx).numpy(), np.array(indptr, np.int32),
+                               np.array(lens, np.int32), B=inp.B, q_len=1, H=inp.H, d_v=inp.d_v,
+                               scale=inp.scale, kv_scale=inp.kv_scale)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)

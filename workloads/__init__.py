@@ -227,12 +227,16 @@ def sparse_mla_inputs(*, num_queries: int, topk: int = 2048, cache_rows: int = 2
 
 def with_second_cache(inp: MlaInputs, *, pool2_rows: int, extra_lens: Sequence[int], seed: int,
                       skip: Sequence[int] = ()) -> MlaInputs:
-    """The same q_len-1 requests with a second cache of pool2_rows rows (the pool's format) from
+    """The same q_len-1 requests with a second cache of pool2_rows rows (the pool's format: fp8
+    N(0,1)*32 bytes, or bf16 N(0,1) for a bf16 pool) from
     which request b draws extra_lens[b] candidates (with replacement allowed across requests);
     `skip` lists flat positions of the second-cache list set to -1 (skipped keys)."""
     assert inp.q_len == 1 and len(extra_lens) == inp.B
     device = inp.pool.device
-    pool2 = _fp8_pool(pool2_rows, inp.d_qk, seed, device)
+    if inp.pool.dtype == torch.bfloat16:
+        pool2 = _bf16_pool(pool2_rows, inp.d_qk, seed, device)
+    else:
+        pool2 = _fp8_pool(pool2_rows, inp.d_qk, seed, device)
     g = _gen("cpu", seed + 1)
     idx = torch.cat([torch.randperm(pool2_rows, generator=g)[:n] for n in extra_lens]).to(torch.int32)
     for k in skip:
