@@ -86,8 +86,7 @@ int check_problem(const gqa_decode_problem *p, Derived *d) {
         // a second cache: q_len 1 without context parallelism, rows of the pool's format
         if (p->kv2 || p->kv2_indices || p->kv2_indptr) {
             if (!p->kv2 || !p->kv2_indices || !p->kv2_indptr) return GQA_ERR_INVALID_ARGUMENT;
-            if (p->q_len != 1 || p->cp_world > 1 || p->glen || !sparse || p->fp8_format == GQA_KV_BF16)
-                return GQA_ERR_UNSUPPORTED;
+            if (p->q_len != 1 || p->cp_world > 1 || p->glen || !sparse) return GQA_ERR_UNSUPPORTED;
             // the kernel addresses both caches with the pool's row stride
             if (p->kv2_stride_row != 0 && p->kv2_stride_row != p->kv_stride_row) return GQA_ERR_UNSUPPORTED;
             if (!aligned16(p->kv2)) return GQA_ERR_UNSUPPORTED;

@@ -79,7 +79,8 @@ typedef enum gqa_fp8_format {
     /* bf16 rows (2 bytes per element), the same fused rows and the same per-tensor kv_scale
      * (1 for a plain bf16 cache) [AITER, closing paragraph: the bf16-cache measurement].  The
      * value part is multiplied in fp16: stored values must lie within fp16's range (|v| < 65520);
-     * below 2^-14 they are rounded to fp16's subnormal step (an error under 2^-25). */
+     * below 2^-14 they are rounded to fp16's subnormal step (an error under 2^-25).  A second
+     * cache then holds bf16 rows too. */
     GQA_KV_BF16 = 2
 } gqa_fp8_format;
 
@@ -145,8 +146,8 @@ typedef struct gqa_decode_problem {
      * kv2_indices[kv2_indptr[b] .. kv2_indptr[b + 1]) (negative: skipped), all in one softmax;
      * partitions cut the concatenated list.  kv2_indptr: int32 [B + 1].  max_num_keys must cover
      * seq_lens[b] plus the request's second-cache count.  Errors: kv2 without both index lists
-     * (or the reverse) GQA_ERR_INVALID_ARGUMENT; with the GQA kind, wide rows, a bf16 pool,
-     * q_len > 1, context parallelism or another row stride GQA_ERR_UNSUPPORTED. */
+     * (or the reverse) GQA_ERR_INVALID_ARGUMENT; with the GQA kind, wide rows, q_len > 1,
+     * context parallelism or another row stride GQA_ERR_UNSUPPORTED. */
     const void *kv2;
     int64_t kv2_stride_row;
     const int32_t *kv2_indices;

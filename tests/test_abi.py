@@ -288,7 +288,7 @@ def test_second_cache_rejections():
 
 
 def test_bf16_pool_checks():
-    # a bf16 pool: rows of 2 bytes per element (stride >= 2 d_qk), no second cache
+    # a bf16 pool: rows of 2 bytes per element (stride >= 2 d_qk); a second cache at its stride
     p = mla_fake()
     p.fp8_format = g.KV_BF16
     p.kv_stride_row = 576
@@ -298,7 +298,9 @@ def test_bf16_pool_checks():
     p = mla_fake(d_qk=512, d_v=448, max_keys=4096)
     p.fp8_format, p.kv_stride_row = g.KV_BF16, 1024
     assert g.decode_plan(p, 0, 0, 256)[0] >= 1
-    p.kv2, p.kv2_indices, p.kv2_indptr = FAKE, FAKE, FAKE
+    p.kv2, p.kv2_indices, p.kv2_indptr = FAKE, FAKE, FAKE   # a second bf16 cache
+    assert g.decode_workspace_bytes(p, 4) > 0
+    p.kv2_stride_row = 512   # not the pool's stride
     expect_status(lambda: g.decode_split(p, 4, 32, FAKE, FAKE), -2)
     p = mla_fake()
     p.fp8_format = 3

@@ -228,3 +228,34 @@ def test_bf16_graph_replay_matches_eager():
         graph.replay()
         torch.cuda.synchronize()
         assert torch.equal(out, eager_o) and torch.equal(lse, eager_l)
+
+
+@pytest.mark.parametrize("np_,bk", [(1, 64), (3, 32), (0, 0)])
+def test_bf16_second_cache(np_, bk):
+    # ragged second-cache counts over a bf16 pool: none, fewer than a tile, tiles that straddle
+    # the two caches, a whole list skipped, an extra list longer than the main one
+    base = workloads.sparse_mla_inputs(num_queries=8, topk=200, cache_rows=4096, seed=4700,
+                                       invalid_frac=0.1, device=DEV, kv_dtype="bf16")
+    extra = [0, 7, 64, 100, 33, 1, 300, 129]
+    skip = list(range(7, 7 + 64)) + [200, 201, 500]
+    inp = workloads.with_second_cache(base, pool2_rows=2048, extra_lens=extra, seed=4710, skip=skip)
+    torch.cuda.synchronize()
+    assert inp.pool2.dtype == torch.bfloat16
+    log("bf16 second cache np=%d bk=%d" % (np_, bk))
+    out, lse = run_decode(mla_problem(inp), 448, np_, bk)
+    torch.cuda.synchronize()
+    ref_o, ref_l = oracle_mla(inp)
+    compare(out, lse, ref_o, ref_l, "bf16 second cache np=%d bk=%d" % (np_, bk))
+
+
+def test_bf16_second_cache_full_size():
+    inp = workloads.sparse_mla_inputs(num_queries=32, seed=4800, extra_topk=512, device=DEV,
+                                      kv_dtype="bf16")
+    torch.cuda.synchronize()
+    p = mla_problem(inp)
+    np_, bk = g.decode_plan(p)
+    log("bf16 second cache full size np=%d bk=%d" % (np_, bk))
+    out, lse = run_decode(p, 448, np_, bk)
+    torch.cuda.synchronize()
+    ref_o, ref_l = oracle_mla(inp, n_threads=8)
+    compare(out, lse, ref_o, ref_l, "bf16 second cache full size")

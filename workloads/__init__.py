@@ -191,8 +191,8 @@ def sparse_mla_inputs(*, num_queries: int, topk: int = 2048, cache_rows: int = 2
     invalid_frac: that fraction of the index entries (seeded positions) is -1, a skipped key;
     all_invalid: queries whose whole list is -1.  extra_topk > 0: a second cache of extra_rows
     rows of the same format, from which each query draws extra_topk more candidates.
-    kv_dtype="bf16": a bf16 cache of N(0,1) rows with kv_scale 1 (no second cache)."""
-    assert kv_dtype in ("fp8", "bf16") and not (kv_dtype == "bf16" and extra_topk)
+    kv_dtype="bf16": bf16 caches of N(0,1) rows with kv_scale 1."""
+    assert kv_dtype in ("fp8", "bf16")
     nq = num_queries
     q = _randn((nq, H, 512), seed + 1, device, torch.bfloat16)
     if kv_dtype == "bf16":
@@ -213,7 +213,7 @@ def sparse_mla_inputs(*, num_queries: int, topk: int = 2048, cache_rows: int = 2
     sl = torch.full((nq,), topk, dtype=torch.int32, device=device)
     pool2 = kv2_indices = kv2_indptr = None
     if extra_topk > 0:
-        pool2 = _fp8_pool(extra_rows, 512, seed + 7, device)
+        pool2 = (_bf16_pool if kv_dtype == "bf16" else _fp8_pool)(extra_rows, 512, seed + 7, device)
         g2 = _gen(device, seed + 8)
         kv2_indices = torch.cat([torch.randperm(extra_rows, generator=g2, device=device)[:extra_topk]
                                  for _ in range(nq)]).to(torch.int32)
