@@ -259,3 +259,31 @@ def test_bf16_second_cache_full_size():
     torch.cuda.synchronize()
     ref_o, ref_l = oracle_mla(inp, n_threads=8)
     compare(out, lse, ref_o, ref_l, "bf16 second cache full size")
+
+
+@pytest.mark.parametrize("kv", ["fp8", "bf16"])
+@pytest.mark.parametrize("shape", ["one_head", "q_len16", "padded_rows"])
+def test_mla_edge_shapes(kv, shape):
+    # one query head (a 64-row block with one row), a 16-position draft window over 8 heads (two
+    # row blocks per request), and a pool whose rows are padded (row stride 640 B for fp8 rows,
+    # 1280 B for bf16 rows: a stride other than the row width)
+    H, q_len, lens = {"one_head": (1, 1, [700, 5, 1]),
+                      "q_len16": (8, 16, [900, 10, 300]),
+                      "padded_rows": (64, 2, [1500, 66])}[shape]
+    inp = workloads.mla_inputs(B=len(lens), q_len=q_len, H=H, seq_lens=lens, pool_rows=sum(lens) + 50,
+                               seed=251, device=DEV, kv_dtype=kv)
+    if shape == "padded_rows":
+        width = inp.pool.shape[1]
+        pad = torch.zeros((inp.pool.shape[0], width + 64), dtype=inp.pool.dtype, device=DEV)
+        pad[:, :width] = inp.pool
+        import dataclasses
+        inp = dataclasses.replace(inp, pool=pad[:, :width])
+        assert inp.pool.stride(0) == width + 64
+    torch.cuda.synchronize()
+    p = mla_problem(inp)
+    ref_o, ref_l = oracle_mla(inp)
+    for np_, bk in ((1, 64), (0, 0)):
+        log("edge %s %s np=%d" % (kv, shape, np_))
+        out, lse = run_decode(p, 512, np_, bk)
+        torch.cuda.synchronize()
+        compare(out, lse, ref_o, ref_l, "edge %s %s np=%d" % (kv, shape, np_))
