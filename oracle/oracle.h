@@ -68,11 +68,6 @@ int oracle_mla_decode(int64_t B, int64_t q_len, int64_t H, int64_t d_lat, int64_
                       double kv_scale, int fnuz, const int64_t *rows, int64_t n_rows,
                       double *o_out, double *lse2_out, int n_threads);
 
-/* oracle_mla_decode with a second cache (sparse top-k with extra candidates, q_len = 1): query b
- * attends its seq_lens[b] main-cache keys (pool rows kv_indices[kv_indptr[b] + j]) and then every
- * second-cache key, pool2 row kv2_indices[kv2_indptr[b] + j] for j < kv2_indptr[b + 1] -
- * kv2_indptr[b] (negative entries skipped), in one softmax; pool2 has the pool's row width and
- * dequantization scale.  Returns 0, or -1 on an invalid argument. */
 /* The same over a pool of bf16 rows ([pool_rows, d_lat + d_rope] bf16 bits), dequantized by
  * kv_scale (the bf16-cache variant). */
 int oracle_mla_decode_bf16(int64_t B, int64_t q_len, int64_t H, int64_t d_lat, int64_t d_rope,
@@ -82,6 +77,11 @@ int oracle_mla_decode_bf16(int64_t B, int64_t q_len, int64_t H, int64_t d_lat, i
                            double kv_scale, const int64_t *rows, int64_t n_rows, double *o_out,
                            double *lse2_out, int n_threads);
 
+/* oracle_mla_decode with a second cache (sparse top-k with extra candidates, q_len = 1): query b
+ * attends its seq_lens[b] main-cache keys (pool rows kv_indices[kv_indptr[b] + j]) and then every
+ * second-cache key, pool2 row kv2_indices[kv2_indptr[b] + j] for j < kv2_indptr[b + 1] -
+ * kv2_indptr[b] (negative entries skipped), in one softmax; pool2 has the pool's row width and
+ * dequantization scale.  Returns 0, or -1 on an invalid argument. */
 int oracle_mla_decode_two_caches(int64_t B, int64_t H, int64_t d_lat, int64_t d_rope,
                                  int64_t d_v, const uint16_t *q_lat, const uint16_t *q_pe,
                                  const uint8_t *pool, int64_t pool_rows,
@@ -91,6 +91,7 @@ int oracle_mla_decode_two_caches(int64_t B, int64_t H, int64_t d_lat, int64_t d_
                                  const int32_t *kv2_indptr, double scale, double kv_scale,
                                  const int64_t *rows, int64_t n_rows, double *o_out,
                                  double *lse2_out, int n_threads);
+/* The same with both caches holding bf16 rows. */
 int oracle_mla_decode_two_caches_bf16(int64_t B, int64_t H, int64_t d_lat, int64_t d_rope,
                                       int64_t d_v, const uint16_t *q_lat, const uint16_t *q_pe,
                                       const uint16_t *pool, int64_t pool_rows,
