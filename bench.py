@@ -68,6 +68,7 @@ def make_workloads():
         ("mla_h64_b8_s131072_q4", lambda d: w.mla_long(8, 4, d), 0),
         ("mla_h64_b16_s131072_q4", lambda d: w.mla_long(16, 4, d), 0),
         ("gqa_b32_hq64_hkv8_d128_p16", lambda d: w.gqa_paged(d), 0),
+        ("gqa_b32_hq64_hkv1_d128_p16", lambda d: w.gqa_mqa(d), 0),
         # not one of the quoted configurations: a skewed batch, where the equal split leaves the
         # long request's few partitions to carry most of the keys
         ("mla_h64_b32_skewed_1x131072_31x2048", lambda d: w.mla_skewed(d), 0),

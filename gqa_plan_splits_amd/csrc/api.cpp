@@ -13,7 +13,7 @@ namespace {
 
 constexpr int kMaxPartitions = 256;
 constexpr int kGqaHeadDim = 128;
-constexpr int kGqaMaxRowsPerCta = 16;
+constexpr int kGqaMaxRowsPerCta = 64;
 constexpr float kLog2e = 1.4426950408889634f;
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }

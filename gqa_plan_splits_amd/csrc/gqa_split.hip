@@ -4,16 +4,20 @@
 // [pages, page_size, kv_heads, 128], kv_indptr counting pages per sequence, kv_page_indices;
 // Modular MAX planner page, MHA-style bullet: one CTA per (kv head, request) per partition):
 // for one kv head of one request and one partition of its tokens, the query rows of that head
-// group (q_len x group <= 16 of them) attend the partition's tokens; the CTA writes each row's
+// group (q_len x group <= 64 of them) attend the partition's tokens; the CTA writes each row's
 // softmax-weighted mean of values and the base-2 log-sum-exp of its scores.
 //
-// Layout of the work: one wave per CTA and no barriers.  This path reads 8 flop per byte, so it
-// only has to keep HBM busy: the wave streams its tokens in tiles of 16 through a ring of three
-// LDS slots, two tiles in flight, each tile's K and V rows (256 bytes per token) copied straight
-// from HBM into LDS with global_load_lds_dwordx4.  The small ring (24 KiB) lets six CTAs share a
-// CU; on MI355X more waves with shallower rings move more bytes than fewer with deeper ones.  The copies are issued from inline assembly and
-// waited for with explicit vmcnt counts (the compiler would drain every copy before each LDS
-// read); page ids come through scalar loads, which count on a different counter.
+// Layout of the work: one wave per 16 query rows.  Up to 16 rows per kv head the CTA is one wave
+// and has no barriers; 17 to 64 rows take W = 2 or 4 waves, wave w holding rows 16 w .. 16 w + 15,
+// all reading the same K and V tiles from LDS, with one barrier per tile.  At 16 rows this path
+// reads 8 flop per byte, so it only has to keep HBM busy: the CTA streams its tokens in tiles of
+// 16 through a ring of three LDS slots, each tile's K and V rows (256 bytes per token) copied
+// straight from HBM into LDS with global_load_lds_dwordx4 (the W waves share the copies); tile
+// t + 2 is issued before tile t is computed.  The small ring (24 KiB) lets six one-wave CTAs
+// share a CU; on MI355X more waves with shallower rings move more bytes than fewer with deeper
+// ones.  The copies are issued from inline assembly and waited for with explicit vmcnt counts
+// (the compiler would drain every copy before each LDS read); page ids come through scalar
+// loads, which count on a different counter.
 //   - QK^T on v_mfma_f32_16x16x32_bf16 as S^T = K Q^T: the query rows are the 16 B-operand
 //     columns (unused columns are zero); lane (row, g) then holds the scores of tokens 4g..4g+3.
 //   - PV on v_mfma_f32_16x16x16_bf16 as O^T = V^T P^T: those four probabilities are exactly the
@@ -52,12 +56,13 @@ __device__ __forceinline__ int vpos(int t, int c) { return t * kRowBytes + ((c ^
 __device__ __forceinline__ void copy16(const void *g, uint32_t m0) {
     asm volatile("global_load_lds_dwordx4 %0, off nt" ::"v"(g), "{m0}"(m0) : "memory");
 }
-// s_waitcnt vmcnt(n) for a wave-uniform n in {0, 8, 16}: the copies of `later` younger tiles
-// (8 copy instructions each) may still be in flight.
+// s_waitcnt vmcnt(n) for a wave-uniform n: the copies of `later` younger tiles (2 C copy
+// instructions each, C copy steps per block and wave) may still be in flight.
+template <int C>
 __device__ __forceinline__ void wait_tiles(int later) {
     static_assert(kSlots == 3, "wait_tiles covers up to two younger tiles");
-    if (later >= 2) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
-    else if (later == 1) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    if (later >= 2) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(4 * C) : "memory");
+    else if (later == 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * C) : "memory");
     else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 __device__ __forceinline__ float rows4_max(float x) {
@@ -88,13 +93,14 @@ __device__ __forceinline__ int request_by_length(const int32_t *seq_lens, int ba
     return __builtin_amdgcn_readfirstlane(int(__builtin_ctzll(m)));
 }
 
-template <bool DIRECT>
-__global__ void __launch_bounds__(64) gqa_split_kernel(const GqaSplitArgs a) {
+template <bool DIRECT, int W>
+__global__ void __launch_bounds__(64 * W) gqa_split_kernel(const GqaSplitArgs a) {
     __shared__ __attribute__((aligned(1024))) uint8_t lds[kSlots * kSlotBytes];
 
     const int logical = blockIdx.x;
     if (logical >= a.total_ctas) return;
-    const int lane = threadIdx.x, g = lane >> 4, col = lane & 15;
+    const int lane = W > 1 ? threadIdx.x & 63 : threadIdx.x, g = lane >> 4, col = lane & 15;
+    const int wv = W > 1 ? __builtin_amdgcn_readfirstlane(int(threadIdx.x) >> 6) : 0;
     const int kvh = logical % a.Hkv;
     const int rest = logical / a.Hkv;
     // np equal partitions per request (longest requests first), or the planned
@@ -117,13 +123,14 @@ __global__ void __launch_bounds__(64) gqa_split_kernel(const GqaSplitArgs a) {
     const int kfull = min(k1, max(0, S - a.q_len + 1));   // tokens every row sees
     const int ntiles = k1 > k0 ? (k1 - k0 + kTile - 1) / kTile : 0;
 
-    // Query row in MFMA column `col`.
-    const bool row_ok = col < rows_cta;
-    const int t = row_ok ? col / a.group : 0;
-    const int head = kvh * a.group + (row_ok ? col - t * a.group : 0);
+    // Query row 16 wv + col of the group in MFMA column `col` of this wave.
+    const int r = 16 * wv + col;
+    const bool row_ok = r < rows_cta;
+    const int t = row_ok ? r / a.group : 0;
+    const int head = kvh * a.group + (row_ok ? r - t * a.group : 0);
     const int row_end = row_ok ? min(max(0, S - a.q_len + t + 1), k1) : k0;
 
-    bf16x8 qf[4];  // B operand: row col, d = 32 s + 8 g .. +7
+    bf16x8 qf[4];  // B operand: row 16 wv + col, d = 32 s + 8 g .. +7
     {
         const uint16_t *q = a.q + (int64_t(b) * a.q_len + t) * a.q_st_tok + int64_t(head) * a.q_st_head;
 #pragma unroll
@@ -133,7 +140,8 @@ __global__ void __launch_bounds__(64) gqa_split_kernel(const GqaSplitArgs a) {
     }
 
     // ---- copies.  Copy i of a block moves tokens 4i..4i+3: lane L carries token 4i + L/16 and
-    // lands on chunk position L % 16 of its row, i.e. global chunk (L % 16) ^ swz(token).
+    // lands on chunk position L % 16 of its row, i.e. global chunk (L % 16) ^ swz(token).  Wave wv
+    // issues copies 4 wv / W .. 4 (wv + 1) / W - 1 of each block.
     const uint32_t lds_addr = uint32_t(reinterpret_cast<uintptr_t>(lds));
     const int64_t row_stride = int64_t(a.Hkv) * kRowBytes;       // bytes between tokens of a page
     const uint8_t *const kbase = reinterpret_cast<const uint8_t *>(a.k_cache) + int64_t(kvh) * kRowBytes;
@@ -148,12 +156,14 @@ __global__ void __launch_bounds__(64) gqa_split_kernel(const GqaSplitArgs a) {
         const int last = min(tb + kTile, k1) - 1;
         return Pages{pids[tb >> a.page_shift], pids[last >> a.page_shift]};
     };
+    constexpr int kCopies = 4 / W;   // copy steps per block and wave
     auto issue_tile = [&](int tile, Pages pg) {
         const int tb = k0 + tile * kTile;
         const int first_page_end = ((tb >> a.page_shift) + 1) << a.page_shift;
         const uint32_t m0 = lds_addr + (tile % kSlots) * kSlotBytes;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int c = 0; c < kCopies; ++c) {
+            const int i = kCopies * wv + c;
             const int tl = 4 * i + (lane >> 4);
             const int tok = min(tb + tl, k1 - 1);
             const int page = tok < first_page_end ? pg.p0 : pg.p1;
@@ -185,14 +195,34 @@ __global__ void __launch_bounds__(64) gqa_split_kernel(const GqaSplitArgs a) {
             if (j < ntiles) issue_tile(j, tile_pages(j));
         if (kSlots - 1 < ntiles) next_pages = tile_pages(kSlots - 1);
     }
+    // The queries are used from here on: the compiler waits for their loads (vmcnt(0), which
+    // also covers the first two tiles' copies) once, here.  Without this use it would put that
+    // wait at the first score of every tile, draining the copies of the tiles ahead each time,
+    // which the multi-wave CTAs cannot afford.
+    asm volatile("" ::"v"(qf[0]), "v"(qf[1]), "v"(qf[2]), "v"(qf[3]));
 
     for (int it = 0; it < ntiles; ++it) {
-        // slot (it + 2) % 3 held tile it - 1, whose reads all finished last iteration
-        if (it + kSlots - 1 < ntiles) {
-            issue_tile(it + kSlots - 1, next_pages);
-            if (it + kSlots < ntiles) next_pages = tile_pages(it + kSlots);
+        if (W == 1) {
+            // slot (it + 2) % 3 held tile it - 1, whose reads all finished last iteration.  The
+            // wave then waits for all its copies, tile it + 2's included: with six one-wave CTAs
+            // per CU the other waves' copies keep HBM busy meanwhile, and on the 32-request paged
+            // batch this ran 389 us per launch against 398 us when tiles it + 1 and it + 2 stay
+            // in flight (measured on MI355X in one process).
+            if (it + kSlots - 1 < ntiles) {
+                issue_tile(it + kSlots - 1, next_pages);
+                if (it + kSlots < ntiles) next_pages = tile_pages(it + kSlots);
+            }
+            wait_tiles<kCopies>(0);
+        } else {
+            // this wave's copies of tile it have landed; after the barrier so have every wave's,
+            // and every wave is done reading tile it - 1, whose slot then takes tile it + 2
+            wait_tiles<kCopies>(min(kSlots - 2, ntiles - 1 - it));
+            __syncthreads();
+            if (it + kSlots - 1 < ntiles) {
+                issue_tile(it + kSlots - 1, next_pages);
+                if (it + kSlots < ntiles) next_pages = tile_pages(it + kSlots);
+            }
         }
-        wait_tiles(min(kSlots - 1, ntiles - 1 - it));
         const uint8_t *kt = lds + (it % kSlots) * kSlotBytes;
         const uint8_t *vt = kt + kTile * kRowBytes;
 
@@ -202,7 +232,7 @@ __global__ void __launch_bounds__(64) gqa_split_kernel(const GqaSplitArgs a) {
             sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
                 as_bf16x8(*reinterpret_cast<const u32x4 *>(kt + k_off[s])), qf[s], sacc, 0, 0, 0);
 
-        // Online softmax in base 2; lane (col, g) holds tokens tb + 4 g + i of row col.
+        // Online softmax in base 2; lane (col, g) holds tokens tb + 4 g + i of row 16 wv + col.
         const int tb = k0 + it * kTile;
         float sv[4];
         const bool masked = tb + kTile > kfull;
@@ -233,7 +263,7 @@ __global__ void __launch_bounds__(64) gqa_split_kernel(const GqaSplitArgs a) {
         }
     }
 
-    // Lane (col, g) of block j holds value columns 16 j + 4 g .. + 3 of row col.
+    // Lane (col, g) of block j holds value columns 16 j + 4 g .. + 3 of row 16 wv + col.
     if (!row_ok) return;
     const int64_t row = (int64_t(b) * a.q_len + t) * a.Hq + head;
     const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
@@ -257,16 +287,25 @@ __global__ void __launch_bounds__(64) gqa_split_kernel(const GqaSplitArgs a) {
     }
 }
 
+template <int W>
+hipError_t launch_rows(const GqaSplitArgs &a, bool direct, hipStream_t s) {
+    const dim3 grid(a.total_ctas), block(64 * W);
+    if (direct)
+        hipLaunchKernelGGL((gqa_split_kernel<true, W>), grid, block, 0, s, a);
+    else
+        hipLaunchKernelGGL((gqa_split_kernel<false, W>), grid, block, 0, s, a);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_gqa_split(const GqaSplitArgs &a, bool direct, hipStream_t s) {
     if (a.block_k % kTile) return hipErrorInvalidValue;
-    const dim3 grid(a.total_ctas), block(64);
-    if (direct)
-        hipLaunchKernelGGL((gqa_split_kernel<true>), grid, block, 0, s, a);
-    else
-        hipLaunchKernelGGL((gqa_split_kernel<false>), grid, block, 0, s, a);
-    return hipGetLastError();
+    const int rows = a.q_len * a.group;
+    if (rows <= 16) return launch_rows<1>(a, direct, s);
+    if (rows <= 32) return launch_rows<2>(a, direct, s);
+    if (rows <= 64) return launch_rows<4>(a, direct, s);
+    return hipErrorInvalidValue;
 }
 
 }  // namespace gqa

@@ -258,7 +258,7 @@ int decode_plan(const gqa_decode_problem *p, int64_t np_or_0, int block_k_or_0, 
  *   partial_lse2[rows, np]      fp32: log2 of the sum of e^score over the partition's keys,
  * with (0, -inf) for a partition the row sees no key of.  np in 1..256, block_k 32 or 64.
  * Errors: INVALID_ARGUMENT, UNSUPPORTED (shapes outside the table at the top of the problem
- * struct, fnuz fp8, group or q_len * group above 16 for GQA), LAUNCH_FAILED. */
+ * struct, fnuz fp8, q_len * group above 64 for GQA), LAUNCH_FAILED. */
 int decode_split(const gqa_decode_problem *p, int64_t np, int block_k, float *partial_o,
                  float *partial_lse2, gqa_stream_t s);
 

@@ -203,13 +203,22 @@ def test_mla_rejections(field, value, status):
 @pytest.mark.parametrize("field,value,status", [
     ("num_kv_heads", 0, -1), ("num_kv_heads", 7, -1), ("k_cache", 0, -1), ("v_cache", 0, -1),
     ("d_qk", 64, -2), ("d_rope", 64, -2), ("page_size", 12, -2), ("page_size", 4, -2),
-    ("num_kv_heads", 2, -2),  # 32 query rows per kv head: above the 16-row tile
+    ("q_len", 9, -2),  # 9 x 8 = 72 query rows per kv head: above the four 16-row blocks
 ])
 def test_gqa_rejections(field, value, status):
     p = gqa_fake()
     setattr(p, field, value)
     expect_status(lambda: g.decode_plan(p, 4, 32, 256), status)
     expect_status(lambda: g.decode_split(p, 4, 32, FAKE, FAKE), status)
+
+
+@pytest.mark.parametrize("Hq,Hkv,q_len", [(64, 1, 1), (32, 1, 2), (16, 1, 4), (64, 8, 8), (24, 1, 1)])
+def test_gqa_row_blocks_accepted(Hq, Hkv, q_len):
+    # up to 64 query rows per kv head (four blocks of 16) plan like any other GQA problem
+    p = gqa_fake(Hq=Hq, Hkv=Hkv, q_len=q_len)
+    np_, bk = g.decode_plan(p, 0, 0, 256)
+    assert np_ == oracle.plan_splits(32, 32768, Hkv, 256, False)
+    assert bk == oracle.block_k(32 * np_ * Hkv, 256)
 
 
 def test_split_argument_rejections():

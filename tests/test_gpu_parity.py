@@ -476,6 +476,62 @@ def test_gqa_ragged_all_rows(Hq, Hkv, q_len, np_, bk):
     compare(out, lse, ref_o, ref_l, "gqa ragged")
 
 
+# More than 16 query rows per kv head: the CTA runs 2 or 4 blocks of 16 rows over each tile.
+# Shapes: 64 heads on one kv head (MQA), 24 rows (a half-empty second block), 30 rows where a
+# draft position straddles two blocks, 51 rows (a last block of 3), 64 rows from q_len 8 x 8.
+@pytest.mark.parametrize("Hq,Hkv,q_len", [(64, 1, 1), (24, 1, 1), (20, 2, 3), (17, 1, 3),
+                                          (64, 8, 8), (32, 1, 2)])
+@pytest.mark.parametrize("np_,bk", [(1, 32), (3, 64), (32, 32), (0, 0)])
+def test_gqa_row_blocks_all_rows(Hq, Hkv, q_len, np_, bk):
+    lens = [700, 33, 1, 0, 1600, 16]
+    inp = workloads.gqa_inputs(B=6, Hq=Hq, Hkv=Hkv, D=128, page_size=16, seq_lens=lens,
+                               num_pages=300, q_len=q_len, seed=33, device=DEV)
+    log("gqa row blocks Hq=%d Hkv=%d q_len=%d np=%d bk=%d" % (Hq, Hkv, q_len, np_, bk))
+    out, lse = run_decode(gqa_problem(inp), 128, np_, bk)
+    torch.cuda.synchronize()
+    ref_o, ref_l = oracle_gqa(inp)
+    compare(out, lse, ref_o, ref_l, "gqa row blocks")
+
+
+def test_gqa_row_blocks_other_entry_points():
+    # the scratch and proportional entry points launch the same kernel with other partial layouts
+    lens = [9000, 31, 0, 2500, 700]
+    inp = workloads.gqa_inputs(B=5, Hq=48, Hkv=1, D=128, page_size=32, seq_lens=lens,
+                               num_pages=420, q_len=1, seed=35, device=DEV)
+    p = gqa_problem(inp)
+    ref_o, ref_l = oracle_gqa(inp)
+    log("gqa row blocks scratch")
+    out = torch.empty((p.rows, 128), dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty((p.rows,), dtype=torch.float32, device=DEV)
+    g.decode_scratch(p, out, lse, np=6, block_k=32)
+    torch.cuda.synchronize()
+    compare(out, lse, ref_o, ref_l, "gqa row blocks scratch")
+    log("gqa row blocks proportional")
+    nbytes = g.decode_proportional_workspace_bytes(p, 12, 0)
+    ws = torch.empty((nbytes // 4 + 64,), dtype=torch.float32, device=DEV)
+    g.decode_proportional(p, out, lse, np=12, cap=0, block_k=32, workspace=ws)
+    torch.cuda.synchronize()
+    compare(out, lse, ref_o, ref_l, "gqa row blocks proportional")
+
+
+def test_gqa_mqa_full_size_sampled():
+    # 64 query heads over one kv head, 32 requests of 32768 tokens, planner launch
+    lens = [32768] * 32
+    inp = workloads.gqa_inputs(B=32, Hq=64, Hkv=1, D=128, page_size=16, seq_lens=lens,
+                               num_pages=32 * 2048, seed=37, device=DEV)
+    p = gqa_problem(inp)
+    np_, bk = g.decode_plan(p)
+    log("gqa mqa full planner np=%d bk=%d" % (np_, bk))
+    out, lse = run_decode(p, 128)
+    torch.cuda.synchronize()
+    rows = sample_rows(inp.B, 1, inp.Hq, 48, seed=124)
+    ref_o, ref_l = oracle_gqa(inp, rows)
+    compare(out[rows], lse[rows], ref_o, ref_l, "gqa mqa full")
+    o2, l2 = run_decode(p, 128)
+    torch.cuda.synchronize()
+    assert torch.equal(out, o2) and torch.equal(lse, l2)
+
+
 @pytest.mark.parametrize("page_size", [8, 32, 64])
 def test_gqa_page_sizes(page_size):
     lens = [333, 64, 1000]

@@ -320,6 +320,14 @@ def gqa_paged(device="cpu"):
                       seed=3000, device=device, name="gqa_b32_hq64_hkv8_d128_p16")
 
 
+def gqa_mqa(device="cpu"):
+    """The paged GQA batch (same lengths and pool) with all 64 query heads on one kv head: the
+    split CTA then carries 64 query rows."""
+    lens = uniform_lengths(32, 1024, 32768, GQA_LEN_SEED)
+    return gqa_inputs(B=32, Hq=64, Hkv=1, D=128, page_size=16, seq_lens=lens, num_pages=131072,
+                      seed=3000, device=device, name="gqa_b32_hq64_hkv1_d128_p16")
+
+
 SPARSE_QUERY_COUNTS = (24, 32, 34, 64, 128, 256)
 
 
