@@ -13,8 +13,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libgqa_splits.so")
-SOURCES = ["plan.cpp", "api.cpp", "mla_split.hip", "gqa_split.hip", "splitk_reduce.hip", "plan_device.hip", "scratch.hip", "ceiling.hip"]
-HEADERS = ["kernels.hpp", "device_common.hpp"]
+SOURCES = ["plan.cpp", "api.cpp", "mla_split.hip", "mla_wide.hip", "gqa_split.hip", "splitk_reduce.hip", "plan_device.hip", "scratch.hip", "ceiling.hip"]
+HEADERS = ["kernels.hpp", "device_common.hpp", "mla_common.hpp"]
 ARCH = "gfx950"
 
 # -packed-fp32-ops: hipcc must not emit packed fp32 arithmetic (v_pk_*_f32) on its own.

@@ -85,6 +85,9 @@ struct PlanArgs {
 int mla_rows_per_cta();
 hipError_t launch_mla_split(const MlaSplitArgs &a, int d_qk, int d_v, bool kv_bf16, bool direct, hipStream_t s);
 // (with a.kv2 set: the second-cache variant of the same kernel)
+// The four-wave MLA split kernel (fp8 rows, one cache): same arguments and results as
+// launch_mla_split.
+hipError_t launch_mla_wide(const MlaSplitArgs &a, int d_qk, int d_v, bool direct, hipStream_t s);
 hipError_t launch_gqa_split(const GqaSplitArgs &a, bool direct, hipStream_t s);
 hipError_t launch_splitk_reduce(const ReduceArgs &a, hipStream_t s);
 hipError_t launch_plan_proportional(const PlanArgs &a, hipStream_t s);
