@@ -163,15 +163,26 @@ class Case:
 
 # Counter summaries under profiles/, per timed workload: the file and the sources its kernel is
 # compiled from (hashed in this order).
-MLA_SOURCES = ("mla_split.hip", "device_common.hpp", "kernels.hpp")
+MLA_SOURCES = ("mla_split.hip", "mla_common.hpp", "device_common.hpp", "kernels.hpp")
+WIDE_SOURCES = ("mla_wide.hip", "mla_common.hpp", "device_common.hpp", "kernels.hpp")
 COUNTER_PROFILES = {
     "mla_h64_b16_s131072_q1": ("mla_split_b16_s131072_counters.txt", MLA_SOURCES),
     "mla_h64_b16_s131072_q4": ("mla_split_b16_s131072_q4_counters.txt", MLA_SOURCES),
-    "sparse_mla_h64_topk2048_nq256": ("mla_split_sparse_nq256_counters.txt", MLA_SOURCES),
+    "sparse_mla_h64_topk2048_nq256": ("mla_wide_sparse_nq256_counters.txt", WIDE_SOURCES),
     "mla_h64_b16_s131072_q1_bf16": ("mla_split_b16_s131072_bf16_counters.txt", MLA_SOURCES),
     "gqa_b32_hq64_hkv8_d128_p16": ("gqa_split_b32_hq64_hkv8_counters.txt",
                                    ("gqa_split.hip", "device_common.hpp", "kernels.hpp")),
 }
+
+
+def split_kernel_name(inp):
+    """The split kernel a workload's decode launches: 512-byte fp8 rows of one cache (the sparse
+    top-k layout) run on mla_wide_kernel, other MLA rows on mla_split_kernel."""
+    if not hasattr(inp, "pool"):
+        return "gqa_split_kernel"
+    if inp.d_qk == 512 and not inp.kv_bf16 and inp.pool2 is None:
+        return "mla_wide_kernel"
+    return "mla_split_kernel"
 
 
 def source_sha256(names):
@@ -815,7 +826,7 @@ def main():
             "parallelism": "single GPU",
         },
         "roofline": {
-            "kernel": "mla_split_kernel" if case.is_mla else "gqa_split_kernel",
+            "kernel": split_kernel_name(inp),
             "bound": "hbm",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS,
