@@ -193,7 +193,9 @@ int launch_split(const gqa_decode_problem *p, const Derived &d, int64_t np, int 
                                                      p->fp8_format == GQA_KV_BF16, direct, s);
         return launch_status(err, "mla split");
     } else {
-        const int64_t total = grid_parts * d.cta_rows;
+        // one CTA per kv head, or one per pair of kv heads
+        const int hc = gqa::gqa_heads_per_cta(int(p->num_kv_heads), int(d.rows_per_req / p->num_kv_heads));
+        const int64_t total = grid_parts * (hc ? p->num_kv_heads / hc : d.cta_rows);
         if (total > (int64_t(1) << 30)) return GQA_ERR_UNSUPPORTED;
         gqa::GqaSplitArgs a;
         a.q = static_cast<const uint16_t *>(p->q);

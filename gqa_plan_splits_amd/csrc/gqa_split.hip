@@ -9,7 +9,9 @@
 //
 // Layout of the work: one wave per 16 query rows.  Up to 16 rows per kv head the CTA is one wave
 // and has no barriers; 17 to 64 rows take W = 2 or 4 waves, wave w holding rows 16 w .. 16 w + 15,
-// all reading the same K and V tiles from LDS, with one barrier per tile.  At 16 rows this path
+// all reading the same K and V tiles from LDS, with one barrier per tile.  With an even number of
+// kv heads and up to 16 rows per head, gqa_pair_kernel below runs instead: one CTA per two kv
+// heads, one wave each, copying both heads' rows of a token as one 512-byte run.  At 16 rows this path
 // reads 8 flop per byte, so it only has to keep HBM busy: the CTA streams its tokens in tiles of
 // 16 through a ring of three LDS slots, each tile's K and V rows (256 bytes per token) copied
 // straight from HBM into LDS with global_load_lds_dwordx4 (the W waves share the copies); tile
@@ -51,6 +53,12 @@ __device__ __forceinline__ int swz(int t) {
 // Byte offset, inside a K or V block, of 16-byte chunk c of tile token t.
 __device__ __forceinline__ int vpos(int t, int c) { return t * kRowBytes + ((c ^ swz(t)) << 4); }
 
+// The fp32 partial rows (the reducer reads each once) are stored non-temporal.  Each store
+// instruction covers 64 bytes of 8 or 16 rows; with ordinary stores they cost 12 to 14 % of a
+// split's time on MI355X at 1.5 % of its bytes, marked non-temporal about half of that.  (The
+// 4-byte log-sum-exp stores are faster left ordinary.)
+__device__ __forceinline__ void store_partial(f32x4 *p, f32x4 v) { __builtin_nontemporal_store(v, p); }
+
 // Direct HBM -> LDS copy of 16 bytes per lane (lane L -> m0 + 16 L), non-temporal: each page is
 // read once, and the streaming hint raises gfx950's read bandwidth.
 __device__ __forceinline__ void copy16(const void *g, uint32_t m0) {
@@ -91,6 +99,50 @@ __device__ __forceinline__ int request_by_length(const int32_t *seq_lens, int ba
     // ranks are a permutation of 0 .. batch - 1, so exactly one lane matches r < batch
     const uint64_t m = __builtin_amdgcn_ballot_w64(lane < batch && rank == r);
     return __builtin_amdgcn_readfirstlane(int(__builtin_ctzll(m)));
+}
+
+// One 16-token tile for one wave's 16 query rows (lane (col, g): row col, tokens 4 g .. 4 g + 3):
+// S^T = K Q^T, the online softmax in base 2 (masking tokens at or past row_end when the tile
+// reaches past kfull, the tokens every row sees), then O^T += V^T P^T.  k_off: this lane's score
+// operand offsets in the K block kt; voff(j): its transposed read of value block j in vt.
+template <typename VOff>
+__device__ __forceinline__ void tile_math(const uint8_t *kt, const uint8_t *vt, const int (&k_off)[4], VOff voff,
+                                          const bf16x8 (&qf)[4], float score_scale, int tb, int kfull,
+                                          int row_end, int g, float &m_run, float &l_run, f32x4 (&oacc)[8]) {
+    f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            as_bf16x8(*reinterpret_cast<const u32x4 *>(kt + k_off[s])), qf[s], sacc, 0, 0, 0);
+
+    // Online softmax in base 2; lane (col, g) holds tokens tb + 4 g + i of its row.
+    float sv[4];
+    const bool masked = tb + kTile > kfull;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        sv[i] = sacc[i] * score_scale;
+        if (masked && tb + 4 * g + i >= row_end) sv[i] = kNegInf;
+    }
+    const float mx = rows4_max(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])));
+    const float m_new = fmaxf(m_run, mx);
+    const float m_use = m_new == kNegInf ? 0.f : m_new;
+    const float alpha = fast_exp2(m_run - m_use);
+    float p[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) p[i] = fast_exp2(sv[i] - m_use);
+    l_run = l_run * alpha + rows4_sum((p[0] + p[1]) + (p[2] + p[3]));
+    m_run = m_new;
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) oacc[j] *= alpha;
+    }
+    const s16x4 pb = __builtin_bit_cast(s16x4, u32x2{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])});
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const s16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4 *)(vt + voff(j)));
+        oacc[j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb, oacc[j], 0, 0, 0);
+    }
 }
 
 template <bool DIRECT, int W>
@@ -226,41 +278,8 @@ __global__ void __launch_bounds__(64 * W) gqa_split_kernel(const GqaSplitArgs a)
         const uint8_t *kt = lds + (it % kSlots) * kSlotBytes;
         const uint8_t *vt = kt + kTile * kRowBytes;
 
-        f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s = 0; s < 4; ++s)
-            sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                as_bf16x8(*reinterpret_cast<const u32x4 *>(kt + k_off[s])), qf[s], sacc, 0, 0, 0);
-
-        // Online softmax in base 2; lane (col, g) holds tokens tb + 4 g + i of row 16 wv + col.
-        const int tb = k0 + it * kTile;
-        float sv[4];
-        const bool masked = tb + kTile > kfull;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            sv[i] = sacc[i] * a.score_scale;
-            if (masked && tb + 4 * g + i >= row_end) sv[i] = kNegInf;
-        }
-        const float mx = rows4_max(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])));
-        const float m_new = fmaxf(m_run, mx);
-        const float m_use = m_new == kNegInf ? 0.f : m_new;
-        const float alpha = fast_exp2(m_run - m_use);
-        float p[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) p[i] = fast_exp2(sv[i] - m_use);
-        l_run = l_run * alpha + rows4_sum((p[0] + p[1]) + (p[2] + p[3]));
-        m_run = m_new;
-        if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
-#pragma unroll
-            for (int j = 0; j < 8; ++j) oacc[j] *= alpha;
-        }
-        const s16x4 pb = __builtin_bit_cast(s16x4, u32x2{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])});
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const s16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) s16x4 *)(vt + vpos(v_tok, 2 * j + v_c) + v_b));
-            oacc[j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb, oacc[j], 0, 0, 0);
-        }
+        tile_math(kt, vt, k_off, [&](int j) { return vpos(v_tok, 2 * j + v_c) + v_b; }, qf, a.score_scale,
+                  k0 + it * kTile, kfull, row_end, g, m_run, l_run, oacc);
     }
 
     // Lane (col, g) of block j holds value columns 16 j + 4 g .. + 3 of row 16 wv + col.
@@ -282,9 +301,161 @@ __global__ void __launch_bounds__(64 * W) gqa_split_kernel(const GqaSplitArgs a)
                                           : row * a.np + part;
         float *o = a.part_o + prow * kD + 4 * g;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) *reinterpret_cast<f32x4 *>(o + 16 * j) = oacc[j] * inv;
+        for (int j = 0; j < 8; ++j) store_partial(reinterpret_cast<f32x4 *>(o + 16 * j), oacc[j] * inv);
         if (g == 0) a.part_lse2[prow] = lse2;
     }
+}
+
+// ---- kv-head-pair variant, for an even number of kv heads and at most 16 query rows per head
+// group.  A CTA serves HC = 2 consecutive kv heads of one (request, partition): wave w takes kv
+// head h0 + w and its head group's query rows, as a one-wave CTA of gqa_split_kernel would.  A
+// tile's 16 tokens of K (and of V) for those heads are 16 runs of HC x 256 contiguous bytes, and
+// the CTA copies them as such: instruction i of thread tid moves the j-th 16-byte chunk,
+// j = 64 HC i + tid, i.e. token j / (16 HC), head (j / 16) % HC, chunk position j % 16 (holding
+// global chunk (j % 16) ^ swz(token)).  Measured on MI355X (32 requests, 8 kv heads, partial
+// rows stored non-temporal): 2, 4 and 8 heads per CTA (8 = whole pages) within 3 % of each
+// other, 2 the fastest and 2 % ahead of one-head CTAs; rings of 3 slots slower than 2.  The ring
+// has two slots of HC x 16 KiB; each step waits for this wave's copies of tile t, then a barrier
+// (every copy landed, every wave done with tile t - 1), then the copies of tile t + 1 into tile
+// t - 1's slot, then tile t's math.
+constexpr int kPairSlots = 2;
+
+template <bool DIRECT, int HC>
+__global__ void __launch_bounds__(64 * HC) gqa_pair_kernel(const GqaSplitArgs a) {
+    constexpr int kRow = HC * kRowBytes;            // one token's rows of the CTA's heads
+    constexpr int kHalf = kTile * kRow;             // K (or V) part of a slot
+    constexpr int SLOTS = kPairSlots;
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[SLOTS * 2 * kHalf];
+
+    const int logical = blockIdx.x;
+    if (logical >= a.total_ctas) return;
+    const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, col = lane & 15;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int hgroups = a.Hkv / HC;
+    const int h0 = (logical % hgroups) * HC;
+    const int kvh = h0 + w;
+    const int rest = logical / hgroups;
+    const int b = a.part_start ? request_of_slot(a.part_start, a.batch, rest)
+                               : request_by_length(a.seq_lens, a.batch, rest / a.np, lane);
+    if (b >= a.batch) return;
+    const int part = a.part_start ? rest - a.part_start[b] : rest % a.np;
+    const int rows_cta = a.q_len * a.group;
+    const int page_mask = (1 << a.page_shift) - 1;
+
+    const int S = a.seq_lens[b];
+    const int pbase = a.kv_indptr[b];
+    const int chunk = a.part_start ? a.part_chunk[b]
+                                   : ((S + a.np - 1) / a.np + a.block_k - 1) / a.block_k * a.block_k;
+    const int k0 = part * chunk;
+    const int k1 = min(max(0, S - a.q_len + (rows_cta - 1) / a.group + 1), k0 + chunk);
+    const int kfull = min(k1, max(0, S - a.q_len + 1));
+    const int ntiles = k1 > k0 ? (k1 - k0 + kTile - 1) / kTile : 0;
+
+    // query row col of kv head kvh's group
+    const bool row_ok = col < rows_cta;
+    const int t = row_ok ? col / a.group : 0;
+    const int head = kvh * a.group + (row_ok ? col - t * a.group : 0);
+    const int row_end = row_ok ? min(max(0, S - a.q_len + t + 1), k1) : k0;
+    bf16x8 qf[4];
+    {
+        const uint16_t *q = a.q + (int64_t(b) * a.q_len + t) * a.q_st_tok + int64_t(head) * a.q_st_head;
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+            qf[s] = as_bf16x8(row_ok ? *reinterpret_cast<const u32x4 *>(q + 32 * s + 8 * g)
+                                     : u32x4{0u, 0u, 0u, 0u});
+    }
+
+    const uint32_t lds_addr = uint32_t(reinterpret_cast<uintptr_t>(lds));
+    const int64_t row_stride = int64_t(a.Hkv) * kRowBytes;       // bytes between tokens of a page
+    const uint8_t *const kbase = reinterpret_cast<const uint8_t *>(a.k_cache) + int64_t(h0) * kRowBytes;
+    const uint8_t *const vbase = reinterpret_cast<const uint8_t *>(a.v_cache) + int64_t(h0) * kRowBytes;
+    typedef const __attribute__((address_space(4))) int32_t *const_ids;
+    const const_ids pids = (const_ids)(uintptr_t)(a.page_indices + pbase);
+    struct Pages { int p0, p1; };
+    auto tile_pages = [&](int tile) -> Pages {
+        const int tb = k0 + tile * kTile;
+        const int last = min(tb + kTile, k1) - 1;
+        return Pages{pids[tb >> a.page_shift], pids[last >> a.page_shift]};
+    };
+    auto issue_tile = [&](int tile, Pages pg) {
+        const int tb = k0 + tile * kTile;
+        const int first_page_end = ((tb >> a.page_shift) + 1) << a.page_shift;
+        const uint32_t m0 = lds_addr + (tile % SLOTS) * 2 * kHalf;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int j = 64 * HC * i + tid;
+            const int tl = j / (16 * HC), hh = (j >> 4) % HC;
+            const int tok = min(tb + tl, k1 - 1);
+            const int page = tok < first_page_end ? pg.p0 : pg.p1;
+            const int64_t slot = (int64_t(page) << a.page_shift) | (tok & page_mask);
+            const int64_t off = slot * row_stride + hh * kRowBytes + (((j & 15) ^ swz(tl)) << 4);
+            copy16(kbase + off, m0 + 1024 * (HC * i + w));
+            copy16(vbase + off, m0 + kHalf + 1024 * (HC * i + w));
+        }
+    };
+
+    // this wave's reads: token tk's row of its head at tk * kRow + w * 256, chunks permuted
+    auto posp = [&](int tk, int c) { return tk * kRow + w * kRowBytes + ((c ^ swz(tk)) << 4); };
+    int k_off[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) k_off[s] = posp(col, 4 * s + g);
+    const int v_tok = 4 * g + (col >> 2);
+    const int v_c = (col & 3) >> 1, v_b = 8 * (col & 1);
+
+    float m_run = kNegInf, l_run = 0.f;
+    f32x4 oacc[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) oacc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // tile 0 in flight before the loop; page ids one tile ahead of their copies
+    static_assert(SLOTS == 2, "one tile in flight during the math");
+    Pages next_pages{0, 0};
+    if (ntiles > 0) issue_tile(0, tile_pages(0));
+    if (1 < ntiles) next_pages = tile_pages(1);
+    // (the queries are used here, so the compiler's wait for their loads is not inside the loop)
+    asm volatile("" ::"v"(qf[0]), "v"(qf[1]), "v"(qf[2]), "v"(qf[3]));
+
+    for (int it = 0; it < ntiles; ++it) {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's copies of tile it
+        __syncthreads();   // tile it landed (every wave's copies); tile it - 1 read by every wave
+        if (it + 1 < ntiles) {
+            issue_tile(it + 1, next_pages);
+            if (it + 2 < ntiles) next_pages = tile_pages(it + 2);
+        }
+        const uint8_t *kt = lds + (it % SLOTS) * 2 * kHalf;
+        tile_math(kt, kt + kHalf, k_off, [&](int j) { return posp(v_tok, 2 * j + v_c) + v_b; }, qf,
+                  a.score_scale, k0 + it * kTile, kfull, row_end, g, m_run, l_run, oacc);
+    }
+
+    if (!row_ok) return;
+    const int64_t row = (int64_t(b) * a.q_len + t) * a.Hq + head;
+    const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+    const float lse2 = l_run > 0.f ? m_run + __log2f(l_run) : kNegInf;
+    if (DIRECT) {
+        uint16_t *o = a.out + row * kD + 4 * g;
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            *reinterpret_cast<uint2 *>(o + 16 * j) =
+                make_uint2(pack_bf16x2(oacc[j][0] * inv, oacc[j][1] * inv),
+                           pack_bf16x2(oacc[j][2] * inv, oacc[j][3] * inv));
+        if (g == 0 && a.lse2_out) a.lse2_out[row] = lse2;
+    } else {
+        const int64_t prow = a.part_start ? (int64_t(rest) * a.q_len + t) * a.Hq + head
+                                          : row * a.np + part;
+        float *o = a.part_o + prow * kD + 4 * g;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) store_partial(reinterpret_cast<f32x4 *>(o + 16 * j), oacc[j] * inv);
+        if (g == 0) a.part_lse2[prow] = lse2;
+    }
+}
+
+hipError_t launch_pair(const GqaSplitArgs &a, bool direct, hipStream_t s) {
+    const dim3 grid(a.total_ctas), block(64 * 2);
+    if (direct)
+        hipLaunchKernelGGL((gqa_pair_kernel<true, 2>), grid, block, 0, s, a);
+    else
+        hipLaunchKernelGGL((gqa_pair_kernel<false, 2>), grid, block, 0, s, a);
+    return hipGetLastError();
 }
 
 template <int W>
@@ -299,9 +470,14 @@ hipError_t launch_rows(const GqaSplitArgs &a, bool direct, hipStream_t s) {
 
 }  // namespace
 
+int gqa_heads_per_cta(int num_kv_heads, int rows_per_group) {
+    return num_kv_heads % 2 == 0 && rows_per_group <= 16 ? 2 : 0;
+}
+
 hipError_t launch_gqa_split(const GqaSplitArgs &a, bool direct, hipStream_t s) {
     if (a.block_k % kTile) return hipErrorInvalidValue;
     const int rows = a.q_len * a.group;
+    if (gqa_heads_per_cta(a.Hkv, rows) == 2) return launch_pair(a, direct, s);
     if (rows <= 16) return launch_rows<1>(a, direct, s);
     if (rows <= 32) return launch_rows<2>(a, direct, s);
     if (rows <= 64) return launch_rows<4>(a, direct, s);

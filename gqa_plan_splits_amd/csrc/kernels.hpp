@@ -88,6 +88,11 @@ hipError_t launch_mla_split(const MlaSplitArgs &a, int d_qk, int d_v, bool kv_bf
 // The four-wave MLA split kernel (fp8 rows, one cache): same arguments and results as
 // launch_mla_split.
 hipError_t launch_mla_wide(const MlaSplitArgs &a, int d_qk, int d_v, bool direct, hipStream_t s);
+// Kv heads per CTA of the GQA split when its kv-head-pair kernel runs (an even number of kv
+// heads, at most 16 query rows per head group: 2, the CTA copying both heads' rows of a token as
+// one run), or 0 when the one-head kernel runs (one CTA per request, partition and kv head).  The
+// launch has num_kv_heads / that many CTAs per request and partition.
+int gqa_heads_per_cta(int num_kv_heads, int rows_per_group);
 hipError_t launch_gqa_split(const GqaSplitArgs &a, bool direct, hipStream_t s);
 hipError_t launch_splitk_reduce(const ReduceArgs &a, hipStream_t s);
 hipError_t launch_plan_proportional(const PlanArgs &a, hipStream_t s);

@@ -532,6 +532,45 @@ def test_gqa_mqa_full_size_sampled():
     assert torch.equal(out, o2) and torch.equal(lse, l2)
 
 
+# An even number of kv heads with up to 16 query rows per head group: a CTA serves a pair of kv
+# heads and copies both heads' rows of each token as one run.  Shapes: 16 and 24 kv heads (8 and
+# 12 CTAs per request and partition, the last pair at heads 14-15 and 22-23), 16 rows from
+# q_len 2 x 8, 15 rows from q_len 5 x 3, pages of 8 tokens (each tile on two pages) and of 64.
+@pytest.mark.parametrize("Hq,Hkv,q_len,page_size", [(32, 16, 1, 16), (48, 24, 2, 16), (64, 8, 2, 8),
+                                                    (12, 4, 5, 64), (4, 2, 1, 8), (128, 16, 1, 32)])
+@pytest.mark.parametrize("np_,bk", [(1, 32), (5, 64), (32, 32), (0, 0)])
+def test_gqa_kv_head_pairs(Hq, Hkv, q_len, page_size, np_, bk):
+    lens = [700, 33, 1, 0, 1600, 16]
+    pages = sum(-(-L // page_size) for L in lens)
+    inp = workloads.gqa_inputs(B=6, Hq=Hq, Hkv=Hkv, D=128, page_size=page_size, seq_lens=lens,
+                               num_pages=pages + 9, q_len=q_len, seed=39, device=DEV)
+    log("gqa head pairs Hq=%d Hkv=%d q_len=%d page=%d np=%d bk=%d" % (Hq, Hkv, q_len, page_size, np_, bk))
+    out, lse = run_decode(gqa_problem(inp), 128, np_, bk)
+    torch.cuda.synchronize()
+    ref_o, ref_l = oracle_gqa(inp)
+    compare(out, lse, ref_o, ref_l, "gqa head pairs")
+
+
+def test_gqa_kv_head_pairs_other_entry_points():
+    lens = [9000, 31, 0, 2500, 700]
+    inp = workloads.gqa_inputs(B=5, Hq=64, Hkv=16, D=128, page_size=32, seq_lens=lens,
+                               num_pages=420, q_len=1, seed=43, device=DEV)
+    p = gqa_problem(inp)
+    ref_o, ref_l = oracle_gqa(inp)
+    log("gqa head pairs scratch")
+    out = torch.empty((p.rows, 128), dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty((p.rows,), dtype=torch.float32, device=DEV)
+    g.decode_scratch(p, out, lse, np=6, block_k=32)
+    torch.cuda.synchronize()
+    compare(out, lse, ref_o, ref_l, "gqa head pairs scratch")
+    log("gqa head pairs proportional")
+    nbytes = g.decode_proportional_workspace_bytes(p, 12, 0)
+    ws = torch.empty((nbytes // 4 + 64,), dtype=torch.float32, device=DEV)
+    g.decode_proportional(p, out, lse, np=12, cap=0, block_k=32, workspace=ws)
+    torch.cuda.synchronize()
+    compare(out, lse, ref_o, ref_l, "gqa head pairs proportional")
+
+
 @pytest.mark.parametrize("page_size", [8, 32, 64])
 def test_gqa_page_sizes(page_size):
     lens = [333, 64, 1000]
