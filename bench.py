@@ -170,16 +170,19 @@ COUNTER_PROFILES = {
     "mla_h64_b16_s131072_q4": ("mla_split_b16_s131072_q4_counters.txt", MLA_SOURCES),
     "sparse_mla_h64_topk2048_nq256": ("mla_wide_sparse_nq256_counters.txt", WIDE_SOURCES),
     "mla_h64_b16_s131072_q1_bf16": ("mla_split_b16_s131072_bf16_counters.txt", MLA_SOURCES),
-    "gqa_b32_hq64_hkv8_d128_p16": ("gqa_split_b32_hq64_hkv8_counters.txt",
+    "gqa_b32_hq64_hkv8_d128_p16": ("gqa_pair_b32_hq64_hkv8_counters.txt",
                                    ("gqa_split.hip", "device_common.hpp", "kernels.hpp")),
 }
 
 
 def split_kernel_name(inp):
     """The split kernel a workload's decode launches: 512-byte fp8 rows of one cache (the sparse
-    top-k layout) run on mla_wide_kernel, other MLA rows on mla_split_kernel."""
+    top-k layout) run on mla_wide_kernel, other MLA rows on mla_split_kernel; GQA with an even
+    number of kv heads and at most 16 query rows per head group on gqa_pair_kernel, other GQA
+    shapes on gqa_split_kernel."""
     if not hasattr(inp, "pool"):
-        return "gqa_split_kernel"
+        rows = inp.q_len * (inp.Hq // inp.Hkv)
+        return "gqa_pair_kernel" if inp.Hkv % 2 == 0 and rows <= 16 else "gqa_split_kernel"
     if inp.d_qk == 512 and not inp.kv_bf16 and inp.pool2 is None:
         return "mla_wide_kernel"
     return "mla_split_kernel"
