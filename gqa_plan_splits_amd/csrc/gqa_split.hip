@@ -136,12 +136,21 @@ __device__ __forceinline__ void tile_math(const uint8_t *kt, const uint8_t *vt, 
 #pragma unroll
         for (int j = 0; j < 8; ++j) oacc[j] *= alpha;
     }
-    const s16x4 pb = __builtin_bit_cast(s16x4, u32x2{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])});
+    // The weights go to the bf16 MFMA as two parts, p = hi + lo (hi = p rounded to bf16, lo = the
+    // remainder rounded to bf16), so each carries a relative error of at most 2^-17 instead of
+    // bf16's 2^-9 (which, with values of magnitude 16, alone moves the output by 0.03).  Both
+    // parts go through one v_mfma_f32_16x16x32_bf16: the lane's k slots 8 g .. 8 g + 3 take V's
+    // tokens 4 g .. 4 g + 3 against hi, slots 8 g + 4 .. 8 g + 7 the same tokens against lo.
+    const uint32_t h01 = pack_bf16x2(p[0], p[1]), h23 = pack_bf16x2(p[2], p[3]);
+    const uint32_t l01 = pack_bf16x2(p[0] - bf16_lo(h01), p[1] - bf16_hi(h01));
+    const uint32_t l23 = pack_bf16x2(p[2] - bf16_lo(h23), p[3] - bf16_hi(h23));
+    const bf16x8 pb = as_bf16x8(u32x4{h01, h23, l01, l23});
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-        const s16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) s16x4 *)(vt + voff(j)));
-        oacc[j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb, oacc[j], 0, 0, 0);
+        const u32x2 va = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4 *)(vt + voff(j))));
+        oacc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(u32x4{va[0], va[1], va[0], va[1]}), pb,
+                                                          oacc[j], 0, 0, 0);
     }
 }
 

@@ -350,6 +350,26 @@ def mla_long_bf16(B: int, q_len: int = 1, device="cpu"):
 # MlaInputs with the same requests and slot lists; only values change.
 # --------------------------------------------------------------------------------------------
 
+def gqa_scaled(inp: GqaInputs, q_mul: float = 1.0, v_mul: float = 1.0) -> GqaInputs:
+    """Queries and values multiplied by powers of two (exact in bf16): larger queries spread the
+    scores over more octaves, larger values raise the output's magnitude."""
+    return dataclasses.replace(inp, q=(inp.q.float() * q_mul).to(torch.bfloat16),
+                               v_cache=(inp.v_cache.float() * v_mul).to(torch.bfloat16))
+
+
+def gqa_dominant_keys(inp: GqaInputs, mul: float = 8.0, every: int = 16, seed: int = 0) -> GqaInputs:
+    """K rows of one seeded token slot in every `every` slots of each page multiplied by `mul`
+    (all kv heads), so that about one key per 16-token tile dominates its rows' softmax."""
+    g = _gen("cpu", seed)
+    k = inp.k_cache.clone()
+    ps = inp.page_size
+    for start in range(0, ps, every):
+        width = min(every, ps - start)
+        pick = start + int(torch.randint(0, width, (1,), generator=g))
+        k[:, pick] = (k[:, pick].float() * mul).to(torch.bfloat16)
+    return dataclasses.replace(inp, k_cache=k)
+
+
 def scaled_queries(inp: MlaInputs, mul: float) -> MlaInputs:
     """q_lat and q_pe multiplied by `mul` (a power of two keeps the bf16 values exact), so that
     scores spread over many octaves within and across key tiles."""
