@@ -43,7 +43,9 @@ def parse():
                     help="only the planner-branch sweep (MLA 32/128 heads, GQA one kv head)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle sample")
-    ap.add_argument("--table-steps", type=int, default=20)
+    ap.add_argument("--table-steps", type=int, default=50)
+    ap.add_argument("--sweep-steps", type=int, default=20,
+                    help="timed calls per point of the planner sweeps")
     ap.add_argument("--oracle-seconds", type=float, default=1.0,
                     help="target CPU time of each workload's oracle sample in the per-workload table")
     ap.add_argument("--settle-ms", type=float, default=150.0,
@@ -723,13 +725,13 @@ def main():
     stream = torch.cuda.Stream()
     sm = g.device_sm_count()
     if args.sparse_sweep:
-        print(json.dumps({"sparse_planner": sparse_sweep(stream, args.table_steps)}), flush=True)
+        print(json.dumps({"sparse_planner": sparse_sweep(stream, args.sweep_steps)}), flush=True)
         return
     if args.proportional_sweep:
-        print(json.dumps({"proportional": proportional_sweep(stream, args.table_steps)}), flush=True)
+        print(json.dumps({"proportional": proportional_sweep(stream, args.sweep_steps)}), flush=True)
         return
     if args.branch_sweep:
-        print(json.dumps({"planner_branches": branch_sweep(stream, args.table_steps)}), flush=True)
+        print(json.dumps({"planner_branches": branch_sweep(stream, args.sweep_steps)}), flush=True)
         return
     flush = torch.empty((512 << 20) // 4, dtype=torch.float32, device="cuda")
 
@@ -861,13 +863,13 @@ def main():
             100 * achieved / result["ceilings"]["gather_rows_gbs"], 1)
         print("# ceilings %s" % json.dumps(result["ceilings"]), file=sys.stderr, flush=True)
         result["planner_ns"] = planner_ns_per_call()
-        result["dcp"] = dcp_line(stream, args.table_steps)
+        result["dcp"] = dcp_line(stream, args.sweep_steps)
         print("# dcp %s" % json.dumps(result["dcp"]), file=sys.stderr, flush=True)
-        result["planner_waves"] = wave_sweep(stream, args.table_steps)
+        result["planner_waves"] = wave_sweep(stream, args.sweep_steps)
         print("# planner_waves %s" % json.dumps(result["planner_waves"]), file=sys.stderr, flush=True)
-        result["sparse_planner"] = sparse_sweep(stream, args.table_steps)
+        result["sparse_planner"] = sparse_sweep(stream, args.sweep_steps)
         print("# sparse_planner %s" % json.dumps(result["sparse_planner"]), file=sys.stderr, flush=True)
-        result["planner_branches"] = branch_sweep(stream, args.table_steps)
+        result["planner_branches"] = branch_sweep(stream, args.sweep_steps)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)
     print(json.dumps(result), flush=True)
