@@ -857,6 +857,19 @@ def main():
             "frac": round(q4["mfma_tflops"] / 2500.0, 4), "avg_launch_us": q4["split_us"],
             "flops_what": "per (row, visible key) 2 x (576 + 512): QK^T on bf16 MFMA and PV on fp16 MFMA, "
                           "both at the 2.5 PFLOP/s dense bf16/fp16 peak"}
+    gq = table.get("gqa_b32_hq64_hkv8_d128_p16")
+    if gq and args.workload != "gqa_b32_hq64_hkv8_d128_p16":
+        # the paged GQA workload's split kernel against the HBM peak (its table row's split-only time)
+        gq_counters = measured_counters("gqa_b32_hq64_hkv8_d128_p16")
+        gq_gbs = gq["kv_bytes"] / (gq["split_us"] * 1e-6) / 1e9
+        result["roofline_gqa"] = {
+            "kernel": "gqa_pair_kernel", "workload": "gqa_b32_hq64_hkv8_d128_p16", "bound": "hbm",
+            "achieved": round(gq_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(gq_gbs / HBM_PEAK_GBS, 4), "avg_launch_us": gq["split_us"],
+            "traffic": gq_counters["traffic"] if gq_counters else None,
+            "mfma_busy": gq_counters["mfma_busy"] if gq_counters else None,
+            "bytes_what": "KV payload: every token's K and V rows once per kv head (512 B)",
+            "timer": "HIP events around the table row's split-only launches (50 per row)"}
     if not args.headline_only:
         result["ceilings"] = ceilings(stream, case)
         result["ceilings"]["headline_split_pct_of_gather"] = round(
