@@ -8,10 +8,11 @@
 // softmax-weighted mean of values and the base-2 log-sum-exp of its scores.
 //
 // Layout of the work: one wave per 16 query rows.  Up to 16 rows per kv head the CTA is one wave
-// and has no barriers; 17 to 64 rows take W = 2 or 4 waves, wave w holding rows 16 w .. 16 w + 15,
-// all reading the same K and V tiles from LDS, with one barrier per tile.  With an even number of
+// and has no barriers; 17 to 32 rows take W = 2 waves, wave w holding rows 16 w .. 16 w + 15,
+// both reading the same K and V tiles from LDS, with one barrier per tile.  With an even number of
 // kv heads and up to 16 rows per head, gqa_pair_kernel below runs instead: one CTA per two kv
-// heads, one wave each, copying both heads' rows of a token as one 512-byte run.  At 16 rows this path
+// heads, one wave each, copying both heads' rows of a token as one 512-byte run; 33 to 64 rows
+// run on gqa_rows32_kernel (two waves of 32 rows, 32-token tiles).  At 16 rows this path
 // reads 8 flop per byte, so it only has to keep HBM busy: the CTA streams its tokens in tiles of
 // 16 through a ring of three LDS slots, each tile's K and V rows (256 bytes per token) copied
 // straight from HBM into LDS with global_load_lds_dwordx4 (the W waves share the copies); tile
@@ -467,6 +468,255 @@ hipError_t launch_pair(const GqaSplitArgs &a, bool direct, hipStream_t s) {
     return hipGetLastError();
 }
 
+// ---- 32-row variant, for 33 to 64 query rows per kv head (MQA, wide groups, draft windows).
+// One CTA per (request, partition, kv head), two waves of 32 query rows, 32-token tiles on
+// v_mfma_f32_32x32x16_bf16: per token and row it issues fewer instructions than 16-row waves
+// (each K operand serves 32 rows, half the MFMAs, row reductions over 16 scores per lane).
+// Measured on MI355X against four 16-row waves (64 query heads on one kv head, 32 requests of
+// 1024 to 32768 tokens): 105 against 118 us at np = 16, 78 against 89-95 us at np = 64; q_len 8
+// over 8 kv heads, 503-506 against 579-593 us.  A ring of 3 slots (3 CTAs per CU instead of 5)
+// was slower, and so was one 32-row wave for 17 to 32 rows against two 16-row waves (451 against
+// 431 us on q_len 4 over 8 kv heads), which keep that range.
+//   - QK^T as S^T = K Q^T: MFMA s (0..7) covers dims 16 s .. 16 s + 15, lane (m, h) reading dims
+//     16 s + 8 h .. + 7 of token m; lane (n, h) of the result holds row n's scores of tokens
+//     8 j + 4 h + i (j, i = 0..3).
+//   - PV as O^T = V^T P^T in K steps j = 0..3 of 16 slots: the lane's slots 8 h .. 8 h + 3 take
+//     tokens 8 j + 4 h + 0..3 against the weights' bf16 hi parts, slots 8 h + 4 .. 8 h + 7 the same
+//     tokens against the lo parts; ds_read_b64_tr_b16 hands lane (m, h) those 4 tokens of value
+//     dim 32 mb + m (M block mb = 0..3).
+//   - LDS: token t's 256-byte row at t * 256 in a 32-token K (then V) block, 16-byte chunk c at
+//     position c ^ f(t), f(t) = ((t & 3) << 2) | ((t >> 2) & 3).  Score reads (one chunk of the 16
+//     tokens a 16-lane read cycle serves) and transposed value reads (4 tokens x 4 chunks per
+//     32-lane cycle) then touch distinct 16-byte (8-byte) slots of a bank row.
+constexpr int kTile32 = 32;
+constexpr int kHalf32 = kTile32 * kRowBytes;   // K (or V) block of a slot
+constexpr int kSlots32 = 2;                    // LDS ring (32 KiB)
+constexpr int kWaves32 = 2;
+__device__ __forceinline__ int swz32(int t) { return ((t & 3) << 2) | ((t >> 2) & 3); }
+
+template <bool DIRECT>
+__global__ void __launch_bounds__(64 * kWaves32) gqa_rows32_kernel(const GqaSplitArgs a) {
+    constexpr int W = kWaves32, SLOTS = kSlots32;
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[SLOTS * 2 * kHalf32];
+    typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+    const int logical = blockIdx.x;
+    if (logical >= a.total_ctas) return;
+    const int lane = threadIdx.x & 63;
+    const int n = lane & 31, h = lane >> 5;
+    const int wv = __builtin_amdgcn_readfirstlane(int(threadIdx.x) >> 6);
+    const int kvh = logical % a.Hkv;
+    const int rest = logical / a.Hkv;
+    const int b = a.part_start ? request_of_slot(a.part_start, a.batch, rest)
+                               : request_by_length(a.seq_lens, a.batch, rest / a.np, lane);
+    if (b >= a.batch) return;
+    const int part = a.part_start ? rest - a.part_start[b] : rest % a.np;
+    const int rows_cta = a.q_len * a.group;
+    const int page_mask = (1 << a.page_shift) - 1;
+
+    const int S = a.seq_lens[b];
+    const int pbase = a.kv_indptr[b];
+    const int chunk = a.part_start ? a.part_chunk[b]
+                                   : ((S + a.np - 1) / a.np + a.block_k - 1) / a.block_k * a.block_k;
+    const int k0 = part * chunk;
+    const int k1 = min(max(0, S - a.q_len + (rows_cta - 1) / a.group + 1), k0 + chunk);
+    const int kfull = min(k1, max(0, S - a.q_len + 1));   // tokens every row sees
+    const int ntiles = k1 > k0 ? (k1 - k0 + kTile32 - 1) / kTile32 : 0;
+
+    // Query row 32 wv + n in MFMA column n of this wave.
+    const int r = 32 * wv + n;
+    const bool row_ok = r < rows_cta;
+    const int t = row_ok ? r / a.group : 0;
+    const int head = kvh * a.group + (row_ok ? r - t * a.group : 0);
+    const int row_end = row_ok ? min(max(0, S - a.q_len + t + 1), k1) : k0;
+
+    bf16x8 qf[8];  // B operand of QK MFMA s: row 32 wv + n, dims 16 s + 8 h .. + 7
+    {
+        const uint16_t *q = a.q + (int64_t(b) * a.q_len + t) * a.q_st_tok + int64_t(head) * a.q_st_head;
+#pragma unroll
+        for (int s = 0; s < 8; ++s)
+            qf[s] = as_bf16x8(row_ok ? *reinterpret_cast<const u32x4 *>(q + 16 * s + 8 * h)
+                                     : u32x4{0u, 0u, 0u, 0u});
+    }
+
+    // ---- copies.  Instruction i (0..7) of a block moves tokens 4 i .. 4 i + 3: lane L carries
+    // token 4 i + L / 16 and lands on chunk position L % 16 of its row, i.e. global chunk
+    // (L % 16) ^ swz32(token).  Pages hold at least 8 tokens, so the 4 tokens of an instruction
+    // share a page, whose id is one scalar load.  Wave wv issues instructions 8 wv / W ..
+    const uint32_t lds_addr = uint32_t(reinterpret_cast<uintptr_t>(lds));
+    const int64_t row_stride = int64_t(a.Hkv) * kRowBytes;
+    const uint8_t *const kbase = reinterpret_cast<const uint8_t *>(a.k_cache) + int64_t(kvh) * kRowBytes;
+    const uint8_t *const vbase = reinterpret_cast<const uint8_t *>(a.v_cache) + int64_t(kvh) * kRowBytes;
+    typedef const __attribute__((address_space(4))) int32_t *const_ids;
+    const const_ids pids = (const_ids)(uintptr_t)(a.page_indices + pbase);
+    constexpr int kIns = 8 / W;   // copy instructions per block and wave
+    struct Pages { int p[kIns]; };
+    auto tile_pages = [&](int tile) -> Pages {
+        const int tb = k0 + tile * kTile32;
+        Pages pg;
+#pragma unroll
+        for (int c = 0; c < kIns; ++c) pg.p[c] = pids[min(tb + 4 * (kIns * wv + c), k1 - 1) >> a.page_shift];
+        return pg;
+    };
+    auto issue_tile = [&](int tile, const Pages &pg) {
+        const int tb = k0 + tile * kTile32;
+        const uint32_t m0 = lds_addr + (tile % SLOTS) * 2 * kHalf32;
+#pragma unroll
+        for (int c = 0; c < kIns; ++c) {
+            const int i = kIns * wv + c;
+            const int tl = 4 * i + (lane >> 4);
+            const int tok = min(tb + tl, k1 - 1);
+            const int64_t slot = (int64_t(pg.p[c]) << a.page_shift) | (tok & page_mask);
+            const int64_t off = slot * row_stride + (((lane & 15) ^ swz32(tl)) << 4);
+            copy16(kbase + off, m0 + i * 1024);
+            copy16(vbase + off, m0 + kHalf32 + i * 1024);
+        }
+    };
+
+    // Loop-invariant LDS offsets.  Score operand of MFMA s: token n, chunk 2 s + h.  Transposed
+    // value read of (M block mb, K step j): in 16-lane group (h, dh = bit 4 of the lane), lane
+    // 4 k + e points at token 8 j + 4 h + k, dims 32 mb + 16 dh + 4 e .. + 3, i.e. chunk
+    // 4 mb + 2 dh + e / 2, byte 8 (e % 2).
+    const int dh = (lane >> 4) & 1, vk = (lane & 15) >> 2, ve = lane & 3;
+    auto kpos = [&](int s) { return n * kRowBytes + (((2 * s + h) ^ swz32(n)) << 4); };
+    auto vposj = [&](int mb, int j) {
+        const int tk = 8 * j + 4 * h + vk;
+        return tk * kRowBytes + (((4 * mb + 2 * dh + (ve >> 1)) ^ swz32(tk)) << 4) + 8 * (ve & 1);
+    };
+
+    float m_run = kNegInf, l_run = 0.f;
+    f32x16 oacc[4];
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[mb][i] = 0.f;
+
+    Pages next_pages;
+    if (ntiles > 0) issue_tile(0, tile_pages(0));
+    if (1 < ntiles) next_pages = tile_pages(1);
+    // (the queries are used here, so the compiler's wait for their loads is not inside the loop)
+    asm volatile("" ::"v"(qf[0]), "v"(qf[1]), "v"(qf[2]), "v"(qf[3]), "v"(qf[4]), "v"(qf[5]), "v"(qf[6]),
+                 "v"(qf[7]));
+
+    static_assert(SLOTS == 2, "one tile in flight during the math");
+    for (int it = 0; it < ntiles; ++it) {
+        // this wave's copies of tile it have landed; after the barrier so have every wave's, and
+        // every wave is done reading tile it - 1, whose slot then takes tile it + 1
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        if (it + 1 < ntiles) {
+            issue_tile(it + 1, next_pages);
+            if (it + 2 < ntiles) next_pages = tile_pages(it + 2);
+        }
+        const uint8_t *kt = lds + (it % SLOTS) * 2 * kHalf32;
+        const uint8_t *vt = kt + kHalf32;
+        const int tb = k0 + it * kTile32;
+
+        f32x16 sacc;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sacc[i] = 0.f;
+#pragma unroll
+        for (int s = 0; s < 8; ++s)
+            sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                as_bf16x8(*reinterpret_cast<const u32x4 *>(kt + kpos(s))), qf[s], sacc, 0, 0, 0);
+
+        // online softmax in base 2; lane (n, h) holds tokens tb + 8 j + 4 h + i of row n
+        float sv[16];
+        const bool masked = tb + kTile32 > kfull;
+        float mx = kNegInf;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                float x = sacc[4 * j + i] * a.score_scale;
+                if (masked && tb + 8 * j + 4 * h + i >= row_end) x = kNegInf;
+                sv[4 * j + i] = x;
+                mx = fmaxf(mx, x);
+            }
+        {
+            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+            mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+        }
+        const float m_new = fmaxf(m_run, mx);
+        const float m_use = m_new == kNegInf ? 0.f : m_new;
+        const float alpha = fast_exp2(m_run - m_use);
+        float psum = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            sv[i] = fast_exp2(sv[i] - m_use);
+            psum += sv[i];
+        }
+        {
+            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(psum), __float_as_uint(psum), false, false);
+            psum = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+        }
+        l_run = l_run * alpha + psum;
+        m_run = m_new;
+        if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
+#pragma unroll
+            for (int mb = 0; mb < 4; ++mb) oacc[mb] *= alpha;
+        }
+        // weights as bf16 hi + lo (relative error at most 2^-17); K step j: {hi, lo} of tokens
+        // 8 j + 4 h + 0..3
+        bf16x8 pb[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float *p = sv + 4 * j;
+            const uint32_t h01 = pack_bf16x2(p[0], p[1]), h23 = pack_bf16x2(p[2], p[3]);
+            const uint32_t l01 = pack_bf16x2(p[0] - bf16_lo(h01), p[1] - bf16_hi(h01));
+            const uint32_t l23 = pack_bf16x2(p[2] - bf16_lo(h23), p[3] - bf16_hi(h23));
+            pb[j] = as_bf16x8(u32x4{h01, h23, l01, l23});
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int mb = 0; mb < 4; ++mb) {
+                const u32x2 va = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (__attribute__((address_space(3))) s16x4 *)(vt + vposj(mb, j))));
+                oacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(u32x4{va[0], va[1], va[0], va[1]}),
+                                                                   pb[j], oacc[mb], 0, 0, 0);
+            }
+    }
+
+    // Lane (n, h) of M block mb holds value dims 32 mb + 8 jj + 4 h + 0..3 (jj = 0..3) of row n.
+    if (!row_ok) return;
+    const int64_t row = (int64_t(b) * a.q_len + t) * a.Hq + head;
+    const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+    const float lse2 = l_run > 0.f ? m_run + __log2f(l_run) : kNegInf;
+    if (DIRECT) {
+        uint16_t *o = a.out + row * kD + 4 * h;
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj)
+                *reinterpret_cast<uint2 *>(o + 32 * mb + 8 * jj) =
+                    make_uint2(pack_bf16x2(oacc[mb][4 * jj] * inv, oacc[mb][4 * jj + 1] * inv),
+                               pack_bf16x2(oacc[mb][4 * jj + 2] * inv, oacc[mb][4 * jj + 3] * inv));
+        if (h == 0 && a.lse2_out) a.lse2_out[row] = lse2;
+    } else {
+        const int64_t prow = a.part_start ? (int64_t(rest) * a.q_len + t) * a.Hq + head
+                                          : row * a.np + part;
+        float *o = a.part_o + prow * kD + 4 * h;
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj)
+                store_partial(reinterpret_cast<f32x4 *>(o + 32 * mb + 8 * jj),
+                              f32x4{oacc[mb][4 * jj] * inv, oacc[mb][4 * jj + 1] * inv,
+                                    oacc[mb][4 * jj + 2] * inv, oacc[mb][4 * jj + 3] * inv});
+        if (h == 0) a.part_lse2[prow] = lse2;
+    }
+}
+
+hipError_t launch_rows32(const GqaSplitArgs &a, bool direct, hipStream_t s) {
+    const dim3 grid(a.total_ctas), block(64 * kWaves32);
+    if (direct)
+        hipLaunchKernelGGL((gqa_rows32_kernel<true>), grid, block, 0, s, a);
+    else
+        hipLaunchKernelGGL((gqa_rows32_kernel<false>), grid, block, 0, s, a);
+    return hipGetLastError();
+}
+
 template <int W>
 hipError_t launch_rows(const GqaSplitArgs &a, bool direct, hipStream_t s) {
     const dim3 grid(a.total_ctas), block(64 * W);
@@ -489,7 +739,8 @@ hipError_t launch_gqa_split(const GqaSplitArgs &a, bool direct, hipStream_t s) {
     if (gqa_heads_per_cta(a.Hkv, rows) == 2) return launch_pair(a, direct, s);
     if (rows <= 16) return launch_rows<1>(a, direct, s);
     if (rows <= 32) return launch_rows<2>(a, direct, s);
-    if (rows <= 64) return launch_rows<4>(a, direct, s);
+    if (a.block_k % kTile32) return hipErrorInvalidValue;
+    if (rows <= 64) return launch_rows32(a, direct, s);
     return hipErrorInvalidValue;
 }
 

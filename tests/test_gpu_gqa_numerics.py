@@ -1,5 +1,6 @@
-"""GPU parity of the GQA split kernels (the kv-head-pair kernel and the one-head kernel with 1, 2
-and 4 waves) at wider dynamic range than N(0,1) data, against the fp64 CPU oracle.
+"""GPU parity of the GQA split kernels (the kv-head-pair kernel, the one-head kernel with one and
+two 16-row waves, and the kernel of two 32-row waves) at wider dynamic range than N(0,1) data,
+against the fp64 CPU oracle.
 
 The kernels multiply bf16 queries by bf16 keys (exact products, fp32 sums), keep an fp32
 running maximum and sum, and hand the weights 2^(score - max) to the PV MFMA rounded to bf16,
@@ -33,8 +34,8 @@ CASES = {
                                                           v_mul=4.0),
 }
 
-# (Hq, Hkv, q_len): kv-head pairs (group 8), one-head CTAs of 1 wave (3 kv heads), 2 waves
-# (24 rows) and 4 waves (64 rows on one kv head)
+# (Hq, Hkv, q_len): kv-head pairs (group 8), one-head CTAs of one 16-row wave (3 kv heads), two
+# 16-row waves (24 rows) and two 32-row waves (64 rows on one kv head)
 SHAPES = [(64, 8, 1), (12, 3, 1), (24, 1, 1), (64, 1, 1)]
 
 

@@ -476,9 +476,11 @@ def test_gqa_ragged_all_rows(Hq, Hkv, q_len, np_, bk):
     compare(out, lse, ref_o, ref_l, "gqa ragged")
 
 
-# More than 16 query rows per kv head: the CTA runs 2 or 4 blocks of 16 rows over each tile.
+# More than 16 query rows per kv head: 17 to 32 rows run 2 waves of 16 rows over each tile, 33 to
+# 64 rows 2 waves of 32 rows.
 # Shapes: 64 heads on one kv head (MQA), 24 rows (a half-empty second block), 30 rows where a
-# draft position straddles two blocks, 51 rows (a last block of 3), 64 rows from q_len 8 x 8.
+# draft position straddles two blocks, 51 rows (the second 32-row wave holds 19), 64 rows from
+# q_len 8 x 8.
 @pytest.mark.parametrize("Hq,Hkv,q_len", [(64, 1, 1), (24, 1, 1), (20, 2, 3), (17, 1, 3),
                                           (64, 8, 8), (32, 1, 2)])
 @pytest.mark.parametrize("np_,bk", [(1, 32), (3, 64), (32, 32), (0, 0)])
@@ -491,6 +493,22 @@ def test_gqa_row_blocks_all_rows(Hq, Hkv, q_len, np_, bk):
     torch.cuda.synchronize()
     ref_o, ref_l = oracle_gqa(inp)
     compare(out, lse, ref_o, ref_l, "gqa row blocks")
+
+
+# 33 to 64 rows run on 32-row waves with 32-token tiles: a tile covers four pages of 8 tokens,
+# two of 16 or part of one of 64; 40 rows leave the second wave's rows 40-63 empty.
+@pytest.mark.parametrize("page_size", [8, 16, 64])
+@pytest.mark.parametrize("np_,bk", [(1, 32), (5, 64), (0, 0)])
+def test_gqa_rows32_page_sizes(page_size, np_, bk):
+    lens = [1333, 64, 0, 31, 2000]
+    pages = sum(-(-L // page_size) for L in lens)
+    inp = workloads.gqa_inputs(B=5, Hq=40, Hkv=1, D=128, page_size=page_size, seq_lens=lens,
+                               num_pages=pages + 11, q_len=1, seed=45, device=DEV)
+    log("gqa 40 rows page=%d np=%d bk=%d" % (page_size, np_, bk))
+    out, lse = run_decode(gqa_problem(inp), 128, np_, bk)
+    torch.cuda.synchronize()
+    ref_o, ref_l = oracle_gqa(inp)
+    compare(out, lse, ref_o, ref_l, "gqa 40 rows page %d" % page_size)
 
 
 def test_gqa_row_blocks_other_entry_points():
