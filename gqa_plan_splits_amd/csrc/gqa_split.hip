@@ -157,7 +157,11 @@ __device__ __forceinline__ void tile_math(const uint8_t *kt, const uint8_t *vt, 
 
 template <bool DIRECT, int W>
 __global__ void __launch_bounds__(64 * W) gqa_split_kernel(const GqaSplitArgs a) {
-    __shared__ __attribute__((aligned(1024))) uint8_t lds[kSlots * kSlotBytes];
+    // Two-wave CTAs reserve 40 KiB (16 KiB beyond the ring, holding nothing), which caps the CU at
+    // four of them (eight waves) instead of six: on MI355X q_len 4 over 8 kv heads (32 rows per
+    // kv head) ran 409-415 us per split against 430 us with six, 421 us with five, and fell to
+    // 567-648 us with three or two.
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[kSlots * kSlotBytes + (W > 1 ? 16384 : 0)];
 
     const int logical = blockIdx.x;
     if (logical >= a.total_ctas) return;
