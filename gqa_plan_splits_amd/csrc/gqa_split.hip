@@ -329,9 +329,9 @@ __global__ void __launch_bounds__(64 * W) gqa_split_kernel(const GqaSplitArgs a)
 // global chunk (j % 16) ^ swz(token)).  Measured on MI355X (32 requests, 8 kv heads, partial
 // rows stored non-temporal): 2, 4 and 8 heads per CTA (8 = whole pages) within 3 % of each
 // other, 2 the fastest and 2 % ahead of one-head CTAs; rings of 3 slots slower than 2.  The ring
-// has two slots of HC x 16 KiB (four CTAs per CU); each step waits for this wave's copies of tile t, then a barrier
-// (every copy landed, every wave done with tile t - 1), then the copies of tile t + 1 into tile
-// t - 1's slot, then tile t's math.
+// has two slots of HC x 16 KiB (four CTAs per CU); each step waits for this wave's copies of
+// tile t, then a barrier (every copy landed, every wave done with tile t - 1), then the copies of
+// tile t + 1 into tile t - 1's slot, then tile t's math.
 constexpr int kPairSlots = 2;
 
 template <bool DIRECT, int HC>
