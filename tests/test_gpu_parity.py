@@ -495,6 +495,31 @@ def test_gqa_row_blocks_all_rows(Hq, Hkv, q_len, np_, bk):
     compare(out, lse, ref_o, ref_l, "gqa row blocks")
 
 
+# The most partitions a call allows (256): most partitions of the short requests are empty and the
+# others hold one tile or a partial one; the pair kernel (16 rows), two 16-row waves (24 rows)
+# and two 32-row waves (48 rows), through decode and through decode_split + splitk_reduce_f32.
+@pytest.mark.parametrize("Hq,Hkv", [(16, 2), (24, 1), (48, 1)])
+def test_gqa_max_partitions(Hq, Hkv):
+    lens = [9000, 100, 0, 33, 2600]
+    pages = sum(-(-L // 16) for L in lens)
+    inp = workloads.gqa_inputs(B=5, Hq=Hq, Hkv=Hkv, D=128, page_size=16, seq_lens=lens,
+                               num_pages=pages + 3, q_len=1, seed=47, device=DEV)
+    p = gqa_problem(inp)
+    ref_o, ref_l = oracle_gqa(inp)
+    log("gqa np=256 Hq=%d Hkv=%d" % (Hq, Hkv))
+    out, lse = run_decode(p, 128, 256, 32)
+    torch.cuda.synchronize()
+    compare(out, lse, ref_o, ref_l, "gqa np=256 decode")
+    po = torch.empty((p.rows, 256, 128), dtype=torch.float32, device=DEV)
+    pl = torch.empty((p.rows, 256), dtype=torch.float32, device=DEV)
+    g.decode_split(p, 256, 32, po, pl)
+    o32 = torch.empty((p.rows, 128), dtype=torch.float32, device=DEV)
+    l32 = torch.empty((p.rows,), dtype=torch.float32, device=DEV)
+    g.splitk_reduce_f32(p.rows, 256, 128, po, pl, o32, l32)
+    torch.cuda.synchronize()
+    compare(o32, l32, ref_o, ref_l, "gqa np=256 split + reduce")
+
+
 # 33 to 64 rows run on 32-row waves with 32-token tiles: a tile covers four pages of 8 tokens,
 # two of 16 or part of one of 64; 40 rows leave the second wave's rows 40-63 empty.
 @pytest.mark.parametrize("page_size", [8, 16, 64])
