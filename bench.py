@@ -304,10 +304,14 @@ def ceilings(stream, case):
     ms_stream = timed(lambda: g.bw_stream_read(buf, buf.numel(), 1024, stream=stream))
     del buf
     torch.cuda.empty_cache()
+    stream_gbs = (2 << 30) / (ms_stream * 1e-3) / 1e9
+    if not case.is_mla:   # a paged GQA headline: no slot list of rows to gather
+        return {"stream_read_gbs": round(stream_gbs, 1), "stream_read_pct_peak": round(100 * stream_gbs / HBM_PEAK_GBS, 1),
+                "method": "bw_stream_read (2 GiB, 1024 CTAs); global_load_lds_dwordx4 nt into LDS; median of 5 "
+                          "launches, HIP events"}
     n = (inp.kv_indices.numel() // 64) * 64
     row_bytes = inp.pool.shape[1]
     ms_gather = timed(lambda: g.bw_gather_rows(inp.pool, row_bytes, inp.kv_indices, n, 256, stream=stream))
-    stream_gbs = (2 << 30) / (ms_stream * 1e-3) / 1e9
     gather_gbs = n * row_bytes / (ms_gather * 1e-3) / 1e9
     return {"stream_read_gbs": round(stream_gbs, 1), "stream_read_pct_peak": round(100 * stream_gbs / HBM_PEAK_GBS, 1),
             "gather_rows_gbs": round(gather_gbs, 1), "gather_rows_pct_peak": round(100 * gather_gbs / HBM_PEAK_GBS, 1),
@@ -816,16 +820,6 @@ def main():
         graph_todo.append((name, case, steps))
         del case, inp
 
-    # HIP graph timings last: a graph capture switches the process to serving several hardware
-    # queues, in which splits of more than about a thousand CTAs measured 4-5 % slower on MI355X
-    # (the paged GQA split: 356 us before the first capture, 375 us after; launches on one stream,
-    # copies to the host and other kernels before it changed nothing).
-    for name, case, steps in graph_todo:
-        ms_graph = time_graph(case.step, steps, stream)
-        table[name]["us_per_call_graph"] = round(ms_graph * 1e3, 2) if ms_graph else None
-        print("# graph %-30s %s" % (name, table[name]["us_per_call_graph"]), file=sys.stderr, flush=True)
-    del graph_todo
-    torch.cuda.empty_cache()
 
     if headline is None:
         print("unknown workload %s" % args.workload, file=sys.stderr)
@@ -906,8 +900,9 @@ def main():
             "timer": "HIP events around the table row's split-only launches (50 per row)"}
     if not args.headline_only:
         result["ceilings"] = ceilings(stream, case)
-        result["ceilings"]["headline_split_pct_of_gather"] = round(
-            100 * achieved / result["ceilings"]["gather_rows_gbs"], 1)
+        if "gather_rows_gbs" in result["ceilings"]:
+            result["ceilings"]["headline_split_pct_of_gather"] = round(
+                100 * achieved / result["ceilings"]["gather_rows_gbs"], 1)
         print("# ceilings %s" % json.dumps(result["ceilings"]), file=sys.stderr, flush=True)
         result["planner_ns"] = planner_ns_per_call()
         result["dcp"] = dcp_line(stream, args.sweep_steps)
@@ -919,6 +914,16 @@ def main():
         result["planner_branches"] = branch_sweep(stream, args.sweep_steps)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)
+    # HIP graph timings last, after every other timing (the sweeps too): a graph capture switches
+    # the process to serving several hardware queues, in which splits of more than about a
+    # thousand CTAs measured 4-5 % slower on MI355X (the paged GQA split: 356 us before the first
+    # capture, 375 us after; launches on one stream, copies to the host and other kernels before
+    # it changed nothing).
+    for name, gcase, gsteps in graph_todo:
+        ms_graph = time_graph(gcase.step, gsteps, stream)
+        table[name]["us_per_call_graph"] = round(ms_graph * 1e3, 2) if ms_graph else None
+        print("# graph %-30s %s" % (name, table[name]["us_per_call_graph"]), file=sys.stderr, flush=True)
+    del graph_todo
     print(json.dumps(result), flush=True)
 
 

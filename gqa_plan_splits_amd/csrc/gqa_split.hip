@@ -329,7 +329,7 @@ __global__ void __launch_bounds__(64 * W) gqa_split_kernel(const GqaSplitArgs a)
 // global chunk (j % 16) ^ swz(token)).  Measured on MI355X (32 requests, 8 kv heads, partial
 // rows stored non-temporal): 2, 4 and 8 heads per CTA (8 = whole pages) within 3 % of each
 // other, 2 the fastest and 2 % ahead of one-head CTAs; rings of 3 slots slower than 2.  The ring
-// has two slots of HC x 16 KiB (four CTAs per CU); each step waits for this wave's copies of
+// has two slots of HC x 16 KiB (five CTAs per CU); each step waits for this wave's copies of
 // tile t, then a barrier (every copy landed, every wave done with tile t - 1), then the copies of
 // tile t + 1 into tile t - 1's slot, then tile t's math.
 constexpr int kPairSlots = 2;
@@ -339,10 +339,7 @@ __global__ void __launch_bounds__(64 * HC) gqa_pair_kernel(const GqaSplitArgs a)
     constexpr int kRow = HC * kRowBytes;            // one token's rows of the CTA's heads
     constexpr int kHalf = kTile * kRow;             // K (or V) part of a slot
     constexpr int SLOTS = kPairSlots;
-    // 8 KiB beyond the ring hold nothing: they cap the CU at four CTAs (eight waves, two per SIMD)
-    // instead of five, which measured 1-2 % faster on MI355X (351-352 against 356-359 us on the
-    // 32-request batch; three CTAs per CU, 353 us)
-    __shared__ __attribute__((aligned(1024))) uint8_t lds[SLOTS * 2 * kHalf + 8192];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[SLOTS * 2 * kHalf];
 
     const int logical = blockIdx.x;
     if (logical >= a.total_ctas) return;
