@@ -614,6 +614,24 @@ def test_gqa_kv_head_pairs_other_entry_points():
     compare(out, lse, ref_o, ref_l, "gqa head pairs proportional")
 
 
+# The one-head kernel with 16-row waves at other page sizes: one wave (3 kv heads, 12 rows each
+# at q_len 4) and two waves (24 rows on one kv head); a tile covers two pages of 8 tokens or part
+# of one of 64.
+@pytest.mark.parametrize("Hq,Hkv,q_len", [(9, 3, 4), (24, 1, 1)])
+@pytest.mark.parametrize("page_size", [8, 64])
+def test_gqa_one_head_page_sizes(Hq, Hkv, q_len, page_size):
+    lens = [1333, 64, 0, 31, 2000]
+    pages = sum(-(-L // page_size) for L in lens)
+    inp = workloads.gqa_inputs(B=5, Hq=Hq, Hkv=Hkv, D=128, page_size=page_size, seq_lens=lens,
+                               num_pages=pages + 11, q_len=q_len, seed=49, device=DEV)
+    ref_o, ref_l = oracle_gqa(inp)
+    for np_, bk in ((1, 32), (6, 64), (0, 0)):
+        log("gqa one head Hq=%d Hkv=%d q_len=%d page=%d np=%d" % (Hq, Hkv, q_len, page_size, np_))
+        out, lse = run_decode(gqa_problem(inp), 128, np_, bk)
+        torch.cuda.synchronize()
+        compare(out, lse, ref_o, ref_l, "gqa one head page %d" % page_size)
+
+
 @pytest.mark.parametrize("page_size", [8, 32, 64])
 def test_gqa_page_sizes(page_size):
     lens = [333, 64, 1000]
