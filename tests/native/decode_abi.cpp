@@ -192,8 +192,10 @@ void mla_case(bool bf16_pool, hipStream_t s) {
     HIP_OK(hipFree(const_cast<int32_t *>(p.seq_lens)));
 }
 
-void gqa_case(hipStream_t s) {
-    const int64_t B = 3, q_len = 1, Hq = 16, Hkv = 2, D = 128, page = 16, num_pages = 80;
+// Hq / Hkv x q_len query rows per kv head: 8 (the kv-head-pair kernel), 12 over 3 kv heads (one
+// 16-row wave per kv head), 24 (two 16-row waves) and 48 (two 32-row waves).
+void gqa_case(hipStream_t s, int64_t Hq, int64_t Hkv, int64_t q_len) {
+    const int64_t B = 3, D = 128, page = 16, num_pages = 80;
     const std::vector<int32_t> lens = {700, 33, 1};
     const int64_t rows = B * q_len * Hq;
     Rng rng{78u};
@@ -236,8 +238,11 @@ void gqa_case(hipStream_t s) {
     p.seq_lens = to_device(lens);
     p.scale = float(scale);
     p.kv_scale = 1.0f;
-    run_and_compare("GQA, bf16 pages", p, 0, rows, D, ref_o, ref_l, s);
-    run_and_compare("GQA, bf16 pages", p, 3, rows, D, ref_o, ref_l, s);
+    char what[96];
+    std::snprintf(what, sizeof what, "GQA, bf16 pages, %lld heads over %lld, q_len %lld", (long long)Hq,
+                  (long long)Hkv, (long long)q_len);
+    run_and_compare(what, p, 0, rows, D, ref_o, ref_l, s);
+    run_and_compare(what, p, 3, rows, D, ref_o, ref_l, s);
     HIP_OK(hipFree(const_cast<void *>(p.q)));
     HIP_OK(hipFree(const_cast<void *>(p.k_cache)));
     HIP_OK(hipFree(const_cast<void *>(p.v_cache)));
@@ -259,7 +264,10 @@ int main() {
     HIP_OK(hipStreamCreate(&s));
     mla_case(false, s);
     mla_case(true, s);
-    gqa_case(s);
+    gqa_case(s, 16, 2, 1);
+    gqa_case(s, 12, 3, 3);
+    gqa_case(s, 24, 1, 1);
+    gqa_case(s, 16, 1, 3);
     HIP_OK(hipStreamDestroy(s));
     std::printf("%s (%d failures)\n", g_failures ? "FAILED" : "all cases pass", g_failures);
     return g_failures ? 1 : 0;
