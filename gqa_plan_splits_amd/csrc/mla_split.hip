@@ -26,15 +26,15 @@
 // bf16 rows go to the bf16 MFMA as stored, and their value part is converted to fp16 (exact for
 // magnitudes in fp16's normal range; the library requires stored values below 65520).
 //
-// Work split (512 threads = 8 waves, one CTA per CU; waves w and w + 4 share SIMD w & 3, and
-// waves 0-3 sit on four different SIMDs):
-//   - Score waves 0, 4 (query rows 0-31) and 1, 5 (rows 32-63) hold their rows' queries in
+// Work split (512 threads = 8 waves, one CTA per CU; waves w and w + 4 share SIMD w & 3, so
+// every SIMD runs one score wave and one value wave):
+//   - Score waves 0, 2 (query rows 0-31) and 1, 3 (rows 32-63) hold their rows' queries in
 //     registers and compute S^T = K Q^T on v_mfma_f32_32x32x16_bf16 for 32 keys at a time; the
-//     two waves of a SIMD take alternate 32-key blocks (fp8: the two halves of each 64-key tile;
-//     bf16: alternate 32-key tiles) and each keeps its own online softmax of those blocks.  They
-//     hand the value waves each block's weights P (fp16) and integer maximum through LDS, and
-//     their final sums at the end.
-//   - Value waves 2, 6 and 3, 7 (SIMDs 2 and 3) accumulate output columns 128 v .. 128 v + 127
+//     two waves of the same rows take alternate 32-key blocks (fp8: the two halves of each 64-key
+//     tile; bf16: alternate 32-key tiles) and each keeps its own online softmax of those blocks.
+//     They hand the value waves each block's weights P (fp16) and integer maximum through LDS,
+//     and their final sums at the end.
+//   - Value waves 4-7 accumulate output columns 128 v .. 128 v + 127
 //     (v = 0..3) of all 64 rows on v_mfma_f32_32x32x16_f16: V^T comes from the tile in LDS through
 //     transposed reads (ds_read_b64_tr_b8 for fp8, ds_read_b64_tr_b16 for bf16) and is converted
 //     to fp16, P^T from LDS; when a block's maximum is above the accumulators', they are first
@@ -46,10 +46,11 @@
 //     drain every copy in flight before each LDS read).
 //   - One barrier per tile.  The score waves run one tile ahead of the value waves: in step t
 //     they compute the softmax of tile t and the scores of tile t + 1 (fp8: each wave both,
-//     interleaved; bf16: the owner of tile t its softmax while the other wave of its SIMD runs
-//     the MFMAs of tile t + 1), while the value waves apply tile t - 1.  On each SIMD the matrix
-//     core is kept busy by one wave while the vector ALU runs the other's softmax and
-//     bookkeeping.
+//     interleaved; bf16: the owner of tile t its softmax while the other wave of its rows runs
+//     the MFMAs of tile t + 1), while the value waves apply tile t - 1.  The value waves run at a
+//     raised issue priority (s_setprio 1): their copies and PV MFMAs go out as soon as they are
+//     ready, and the score wave of the SIMD, whose softmax and K conversions are most of the
+//     CTA's vector work, fills the remaining issue slots.
 //
 // LDS (160 KiB): a four-slot ring of the key rows' first 512 elements and a three-slot ring of the
 // 64-element rope tails of 576-wide rows (fp8 layout below; bf16 rows at swz16).  Line j (bytes 128 j .. 128 j + 127 of the rows) of a
@@ -133,25 +134,26 @@ __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const MlaSplitAr
     const int32_t *const id_ring = reinterpret_cast<const int32_t *>(lds + T::kIdOff);
     uint64_t *const bad_ring = reinterpret_cast<uint64_t *>(lds + T::kBadOff);
 
-    // Roles by wave: waves w and w + 4 share a SIMD, and waves 0-3 sit on four different SIMDs.
-    // The score waves 0, 4 (rows 0-31) and 1, 5 (rows 32-63) have two SIMDs to themselves for
-    // their QK^T MFMAs; the value waves 2, 6 and 3, 7 share the other two for PV.
-    if (wave < 2 || wave == 4 || wave == 5) {
+    // Roles by wave: waves w and w + 4 share a SIMD.  Score waves 0-3 (rows 32 (w & 1) ..
+    // + 31, block (w >> 1) of every tile) and value waves 4-7 (columns of line w - 4): one of
+    // each per SIMD, so that the score waves' vector work (K conversions, softmax) spreads over
+    // all four SIMDs.
+    if (wave < 4) {
         // ================================ score wave ================================
-        // Score wave w: query rows 32 (w & 1) .. + 31 against 32-key block kb = w >> 2 of every
+        // Score wave w: query rows 32 (w & 1) .. + 31 against 32-key block kb = w >> 1 of every
         // tile, S^T = K Q^T on v_mfma_f32_32x32x16_bf16.  The stored fp8 K bytes are converted
         // exactly to bf16 in registers, so every product q * k is exact and the sums are fp32.
         // Lane (n, h) reads the 64 bytes 64 h .. 64 h + 63 of each 128-byte line of key n of the
         // block: MFMA j (0..7) of line L takes its bytes 8 j .. 8 j + 7 as k slots 8 h .. 8 h + 7,
         // dims 128 L + 64 h + 8 j + 0..7 (the query operand takes the same dims).  The 64-byte
         // rope tail of 576-byte rows is four more MFMAs over dims 512 + 32 h + 8 j + 0..7.  The
-        // two score waves of a SIMD run the same rows on alternate blocks, so each keeps its own
+        // two score waves of the same rows run alternate blocks, so each keeps its own
         // online softmax; the value waves align the two, and merge their sums at the end.
         // In the MFMA output layout lane (n, h) holds row n's scores of block positions
         // 8 j + 4 h + i (j, i = 0..3).  bf16 rows: block kb is every other 32-key tile (t = kb
         // mod 2), and lane (n, h) reads elements 32 h .. 32 h + 31 of each 64-element line, one
         // 16-byte chunk (8 dims) per MFMA, the rope tail as a ninth line.
-        const int kb = wave >> 2;               // this wave's block of every tile
+        const int kb = wave >> 1;               // this wave's block of every tile
         const int srow = 32 * (wave & 1) + n;   // row within the CTA
         const bool row_ok = srow < nrows;
         constexpr int NL = DQK / 128;           // full 128-byte lines per fp8 row
@@ -353,7 +355,7 @@ __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const MlaSplitAr
             return t >= n_full || __builtin_amdgcn_readfirstlane(uint32_t(bad_ring[t % kIdSlots] != 0));
         };
         if constexpr (KV16) {
-            // bf16 rows: the two score waves of a SIMD take alternate tiles (wave kb the tiles
+            // bf16 rows: the two score waves of the same rows take alternate tiles (wave kb the tiles
             // t = kb mod 2) and alternate between two kinds of step: in step t the owner of tile t
             // runs its softmax (P(t) and the block maximum to LDS) while the other wave computes
             // the scores of tile t + 1 on the matrix core.
@@ -410,7 +412,9 @@ __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const MlaSplitAr
     }
 
     // ================================ value wave ================================
-    const int v = (wave & 1) + ((wave >> 1) & 2);   // waves 2, 3, 6, 7 -> 0, 1, 2, 3: line v
+    const int v = wave - 4;   // line v
+    // raised issue priority on the SIMD it shares with a score wave
+    __builtin_amdgcn_s_setprio(1);
     // ---- copies.  Instruction i writes tile positions 8 i .. 8 i + 7 of line v: lane L carries
     // slot-list key 8 (L >> 3) + i at position 8 i + (L >> 3), chunk position L & 7, i.e. global
     // chunk (L & 7) ^ swz_line(position).  The tail copy writes positions 16 v .. 16 v + 15.
