@@ -207,25 +207,32 @@ __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const MlaSplitAr
         const int kidx = KV16 ? 16 * h : 32 * h + 4 * kb;
         constexpr int kIStride = KV16 ? 4 : 8;
 
-        // K operand reads, their exact conversion to bf16 and the MFMAs of this wave's block of
-        // tile t, in one accumulator chain (the matrix core forwards an accumulator to the next
-        // MFMA of the same kind): line L (8 MFMAs), and the rope tail (4 MFMAs).
-        auto qk_line = [&](int t, int L, f32x16 &acc) {
+        // K operand reads (line L of tile t: 4 chunks; the rope tail: 2), and their exact
+        // conversion to bf16 with the MFMAs of this wave's block, in one accumulator chain (the
+        // matrix core forwards an accumulator to the next MFMA of the same kind): line L (8
+        // MFMAs), and the rope tail (4 MFMAs).  The reads are issued a stage before their MFMAs.
+        auto k_load = [&](int t, int L, u32x4 (&kr)[4]) {
             const uint8_t *lb = lds + (t % kLineSlots) * 32768 + 8192 * L;
 #pragma unroll
+            for (int c = 0; c < 4; ++c) kr[c] = *reinterpret_cast<const u32x4 *>(lb + k_off[c]);
+        };
+        auto qk_regs = [&](int L, const u32x4 (&kr)[4], f32x16 &acc) {
+#pragma unroll
             for (int c = 0; c < 4; ++c) {
-                const u32x4 k16 = *reinterpret_cast<const u32x4 *>(lb + k_off[c]);
-                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fp8x8_to_bf16x8(k16.x, k16.y), qv[8 * L + 2 * c], acc, 0, 0, 0);
-                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fp8x8_to_bf16x8(k16.z, k16.w), qv[8 * L + 2 * c + 1], acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fp8x8_to_bf16x8(kr[c].x, kr[c].y), qv[8 * L + 2 * c], acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fp8x8_to_bf16x8(kr[c].z, kr[c].w), qv[8 * L + 2 * c + 1], acc, 0, 0, 0);
             }
         };
-        auto qk_tail = [&](int t, f32x16 &acc) {
+        auto tail_load = [&](int t, u32x4 (&kr)[2]) {
             const uint8_t *tlb = lds + (t % kTailSlots) * 4096;
 #pragma unroll
+            for (int c = 0; c < 2; ++c) kr[c] = *reinterpret_cast<const u32x4 *>(tlb + k_tail[c]);
+        };
+        auto tail_regs = [&](const u32x4 (&kr)[2], f32x16 &acc) {
+#pragma unroll
             for (int c = 0; c < 2; ++c) {
-                const u32x4 k16 = *reinterpret_cast<const u32x4 *>(tlb + k_tail[c]);
-                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fp8x8_to_bf16x8(k16.x, k16.y), qv[8 * NL + 2 * c], acc, 0, 0, 0);
-                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fp8x8_to_bf16x8(k16.z, k16.w), qv[8 * NL + 2 * c + 1], acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fp8x8_to_bf16x8(kr[c].x, kr[c].y), qv[8 * NL + 2 * c], acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fp8x8_to_bf16x8(kr[c].z, kr[c].w), qv[8 * NL + 2 * c + 1], acc, 0, 0, 0);
             }
         };
         auto zero16 = [](f32x16 &x) {
@@ -328,22 +335,30 @@ __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const MlaSplitAr
 
         // Step t: the softmax of tile t (whose scores `cur` holds) in four stages, each beside the
         // MFMAs of one line of tile t + 1's scores (the last tile again at the end; those scores
-        // are then unused), which accumulate in `nxt`.
+        // are then unused), which accumulate in `nxt`.  Each line's K bytes are read during the
+        // stage before (line 0 and the rope tail before the first stage's softmax work), so the
+        // LDS latency is not waited out in front of the MFMAs.
         auto step = [&](int t, f32x16 &cur, f32x16 &nxt, auto masked) {
             const int tq = min(t + 1, ntiles - 1);
+            u32x4 ka[4], kb2[4], kt[2];
             zero16(nxt);
-            if constexpr (T::kTail) qk_tail(tq, nxt);
+            k_load(tq, 0, ka);
+            if constexpr (T::kTail) tail_load(tq, kt);
             Soft sf = sm0(t, cur, masked);
-            qk_line(tq, 0, nxt);
+            k_load(tq, 1, kb2);
+            if constexpr (T::kTail) tail_regs(kt, nxt);
+            qk_regs(0, ka, nxt);
             GQA_SB;
             sm12(t, 0, cur, sf);
-            qk_line(tq, 1, nxt);
+            k_load(tq, 2, ka);
+            qk_regs(1, kb2, nxt);
             GQA_SB;
             sm12(t, 2, cur, sf);
-            qk_line(tq, 2, nxt);
+            k_load(tq, 3, kb2);
+            qk_regs(2, ka, nxt);
             GQA_SB;
             sm3(t, sf);
-            qk_line(tq, 3, nxt);
+            qk_regs(3, kb2, nxt);
             __syncthreads();   // P(t) published; tile t + 2 landed
         };
 
@@ -387,9 +402,17 @@ __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const MlaSplitAr
             __syncthreads();   // tile 0 landed
             f32x16 sa, sb;
             zero16(sa);
-            if constexpr (T::kTail) qk_tail(0, sa);
+            if constexpr (T::kTail) {
+                u32x4 kt[2];
+                tail_load(0, kt);
+                tail_regs(kt, sa);
+            }
 #pragma unroll
-            for (int L = 0; L < NL; ++L) qk_line(0, L, sa);
+            for (int L = 0; L < NL; ++L) {
+                u32x4 kr[4];
+                k_load(0, L, kr);
+                qk_regs(L, kr, sa);
+            }
             __syncthreads();   // tile 1 landed; tile 0's rope tails read (step 0 refills their slot)
             int t = 0;
             for (; t + 1 < ntiles; t += 2) {
@@ -592,17 +615,25 @@ __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const MlaSplitAr
     // PV of tile t: every LDS read first (V^T bytes of both blocks, the weights, the block maxima),
     // so that their latency overlaps; then, block by block, the alignment of maxima, the exact
     // fp8 -> fp16 conversion of V and 16 MFMAs.
-    auto pv = [&](int t) {
-        const uint8_t *pbuf = P + (t & 1) * 8192;
-        const uint8_t *mlb = ML + (t & 1) * T::kMlBytes;
+    int2v raw[4][4];   // [cb][r]: MFMA r's V^T bytes of column block cb
+    auto read_vt = [&](int t) {
         const uint8_t *lb = lds + (t % kLineSlots) * 32768;
-        int2v raw[4][4];   // [cb][r]: MFMA r's V^T bytes of column block cb
 #pragma unroll
         for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
             for (int r = 0; r < 4; ++r)
                 raw[cb][r] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
                     (__attribute__((address_space(3))) int2v *)(lb + v_off[cb][r]));
+    };
+    // 576-byte rows: the V^T bytes of tile t are read at the end of step t, after the copies are
+    // issued, so their latency passes during the wait for the barrier instead of in front of
+    // the PV MFMAs of step t + 1 (512-byte rows read them in pv: holding them across the
+    // barrier there costs spills).
+    constexpr bool kVtAhead = T::kTail;
+    auto pv = [&](int t) {
+        if constexpr (!kVtAhead) read_vt(t);
+        const uint8_t *pbuf = P + (t & 1) * 8192;
+        const uint8_t *mlb = ML + (t & 1) * T::kMlBytes;
         f16x8 pw[2][4];
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb)
@@ -731,6 +762,8 @@ __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const MlaSplitAr
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
             issue_rows(t + 3);
             issue_ids(t + 6);
+            // tile t's line slot is refilled only in step t + 1, after its PV
+            if constexpr (!KV16 && kVtAhead) read_vt(t);
             // rows(t + 2) and ids(t + 4) landed: everything issued before ids(t + 5) (value wave
             // 0) or before rows(t + 3) (the others)
             wait_vmem(cnt_ids(t + 5) + cnt_rows(t + 3) + cnt_ids(t + 6));
