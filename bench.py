@@ -289,7 +289,9 @@ def ceilings(stream, case):
     """Streaming-read and row-gather ceilings of this GPU with the split kernels' copy instruction
     (the library's bw_stream_read and bw_gather_rows): a 2 GiB contiguous read, and a gather of
     the headline workload's own shuffled slot list over its pool, in the MLA kernel's copy
-    pattern.  Median of 5 timed launches after 2 untimed ones, HIP events on the stream."""
+    pattern (128-byte lines of 8 rows per copy instruction) and with whole-row requests (512
+    bytes of 2 rows per instruction).  Median of 5 timed launches after 2 untimed ones, HIP
+    events on the stream."""
     import torch
     import gqa_plan_splits_amd as g
     inp = case.inp
@@ -313,10 +315,13 @@ def ceilings(stream, case):
     row_bytes = inp.pool.shape[1]
     ms_gather = timed(lambda: g.bw_gather_rows(inp.pool, row_bytes, inp.kv_indices, n, 256, stream=stream))
     gather_gbs = n * row_bytes / (ms_gather * 1e-3) / 1e9
+    ms_whole = timed(lambda: g.bw_gather_whole_rows(inp.pool, row_bytes, inp.kv_indices, n, 256, stream=stream))
+    whole_gbs = n * row_bytes / (ms_whole * 1e-3) / 1e9
     return {"stream_read_gbs": round(stream_gbs, 1), "stream_read_pct_peak": round(100 * stream_gbs / HBM_PEAK_GBS, 1),
             "gather_rows_gbs": round(gather_gbs, 1), "gather_rows_pct_peak": round(100 * gather_gbs / HBM_PEAK_GBS, 1),
+            "gather_whole_rows_gbs": round(whole_gbs, 1), "gather_whole_rows_pct_peak": round(100 * whole_gbs / HBM_PEAK_GBS, 1),
             "gather_rows": n, "row_bytes": row_bytes,
-            "method": "bw_stream_read (2 GiB, 1024 CTAs) and bw_gather_rows (the headline's slot list, 256 CTAs); "
+            "method": "bw_stream_read (2 GiB, 1024 CTAs), bw_gather_rows and bw_gather_whole_rows (the headline's slot list, 256 CTAs); "
                       "global_load_lds_dwordx4 nt into LDS; median of 5 launches, HIP events"}
 
 

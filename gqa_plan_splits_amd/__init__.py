@@ -17,6 +17,7 @@ from ._lib import (  # noqa: F401
     KV_BF16,
     block_k_for,
     bw_gather_rows,
+    bw_gather_whole_rows,
     bw_stream_read,
     decode,
     decode_plan,

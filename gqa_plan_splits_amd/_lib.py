@@ -18,7 +18,7 @@ SCRATCH_BYTES = 64 << 20   # GQA_SCRATCH_BYTES: the device-side partials of deco
 _SYMBOLS = ("plan_splits", "plan_sparse_splits", "plan_sparse_splits_measured", "plan_gqa_splits_measured", "plan_mla_splits_measured", "block_k_for", "device_sm_count", "decode_plan", "decode_split",
             "splitk_reduce", "splitk_reduce_f32", "merge_ranks", "decode_workspace_bytes", "decode",
             "plan_proportional_device", "decode_proportional_workspace_bytes", "decode_proportional",
-            "decode_scratch", "fp8_e4m3_to_bf16", "bw_stream_read", "bw_gather_rows",
+            "decode_scratch", "fp8_e4m3_to_bf16", "bw_stream_read", "bw_gather_rows", "bw_gather_whole_rows",
             "status_string", "last_error_detail")
 
 
@@ -121,6 +121,7 @@ def _load():
     lib.fp8_e4m3_to_bf16.argtypes = [vp, i64, vp, vp]
     lib.bw_stream_read.argtypes = [vp, ctypes.c_size_t, i64, vp]
     lib.bw_gather_rows.argtypes = [vp, i64, vp, i64, i64, vp]
+    lib.bw_gather_whole_rows.argtypes = [vp, i64, vp, i64, i64, vp]
     lib.status_string.argtypes = [i32]
     lib.status_string.restype = ctypes.c_char_p
     lib.last_error_detail.argtypes = []
@@ -386,6 +387,11 @@ def bw_stream_read(src, nbytes: int, ctas: int, stream=None):
 def bw_gather_rows(pool, row_bytes: int, idx, n: int, ctas: int, stream=None):
     _check(_load().bw_gather_rows(_ptr(pool), row_bytes, _ptr(idx), n, ctas, _stream(stream)),
            "bw_gather_rows")
+
+
+def bw_gather_whole_rows(pool, row_bytes: int, idx, n: int, ctas: int, stream=None):
+    _check(_load().bw_gather_whole_rows(_ptr(pool), row_bytes, _ptr(idx), n, ctas, _stream(stream)),
+           "bw_gather_whole_rows")
 
 
 def plan_proportional_device(seq_lens, extra_indptr, batch: int, budget: int, cap: int,

@@ -3,6 +3,8 @@
 //   - as a plain stream of contiguous bytes, and
 //   - as a gather of rows at listed slots, in the MLA split kernel's own copy pattern (each copy
 //     instruction moves one 128-byte line of 8 rows; 64-byte rope tails 16 rows at a time),
+//   - and as the same gather with each copy instruction moving the first 512 bytes of two rows
+//     (whole-row requests; the rope tails as before),
 // with no arithmetic.  The bytes land in LDS and are overwritten; nothing is written to memory.
 #include <hip/hip_runtime.h>
 
@@ -43,7 +45,8 @@ __global__ void __launch_bounds__(kStreamThreads) stream_read_kernel(const uint8
 // Rows of row_bytes (576 or 512) at the slots idx[0 .. n) (n a multiple of 64).  Wave w of CTA c
 // takes the 64-row groups g = 4 c + w, 4 c + w + 4 * grid, ...; per group it issues the MLA split
 // kernel's copies of one tile: for each line v (0..3), 8 instructions of 8 rows x 128 bytes (lane
-// L: row 8 (L >> 3) + i, 16 bytes at 128 v + 16 (L & 7)), and for 576-byte rows four instructions
+// L: row 8 (L >> 3) + i, 16 bytes at 128 v + 16 (L & 7)); WHOLE: 32 instructions of 2 rows x 512
+// bytes (lane L: row 2 i + (L >> 5), 16 bytes at 16 (L & 31)); and for 576-byte rows four instructions
 // of 16 rope tails.  The group's slot ids come two groups ahead into a 4-slot LDS ring
 // (global_load_lds_dword), waited for with explicit counts like the copies; all copies of a wave
 // land in one 33 KiB area, overwritten (the bytes are not used).
@@ -54,6 +57,7 @@ __device__ __forceinline__ void copy4_nt(const int32_t *g, uint32_t m0) {
     asm volatile("global_load_lds_dword %0, off nt" ::"v"(g), "{m0}"(m0) : "memory");
 }
 
+template <bool WHOLE>
 __global__ void __launch_bounds__(kGatherThreads) gather_rows_kernel(const uint8_t *pool, int64_t row_bytes,
                                                                      const int32_t *idx, int64_t n) {
     __shared__ __attribute__((aligned(1024))) uint8_t lds[4 * kGatherArea + 4 * 4 * 256];
@@ -85,12 +89,18 @@ __global__ void __launch_bounds__(kGatherThreads) gather_rows_kernel(const uint8
         const i32x4 ia = *reinterpret_cast<const i32x4 *>(ids + 8 * jgrp);
         const i32x4 ib = *reinterpret_cast<const i32x4 *>(ids + 8 * jgrp + 4);
         const int32_t kid[8] = {ia.x, ia.y, ia.z, ia.w, ib.x, ib.y, ib.z, ib.w};
+        if constexpr (WHOLE) {
 #pragma unroll
-        for (int v = 0; v < 4; ++v)
+            for (int i = 0; i < 32; ++i)
+                copy16_nt(pool + int64_t(ids[2 * i + (lane >> 5)]) * row_bytes + 16 * (lane & 31), area + i * 1024);
+        } else {
 #pragma unroll
-            for (int i = 0; i < 8; ++i)
-                copy16_nt(pool + int64_t(kid[i]) * row_bytes + 128 * v + 16 * (lane & 7),
-                          area + (8 * v + i) * 1024);
+            for (int v = 0; v < 4; ++v)
+#pragma unroll
+                for (int i = 0; i < 8; ++i)
+                    copy16_nt(pool + int64_t(kid[i]) * row_bytes + 128 * v + 16 * (lane & 7),
+                              area + (8 * v + i) * 1024);
+        }
         if (tail) {
 #pragma unroll
             for (int v = 0; v < 4; ++v)
@@ -122,20 +132,37 @@ extern "C" int bw_stream_read(const void *src, size_t bytes, int64_t ctas, gqa_s
     return GQA_OK;
 }
 
-extern "C" int bw_gather_rows(const void *pool, int64_t row_bytes, const int32_t *idx, int64_t n,
-                              int64_t ctas, gqa_stream_t s) {
+namespace {
+int gather_rows(bool whole, const void *pool, int64_t row_bytes, const int32_t *idx, int64_t n, int64_t ctas,
+                gqa_stream_t s) {
     if (!pool || !idx || n < 0 || ctas < 1) return GQA_ERR_INVALID_ARGUMENT;
     if ((row_bytes != 576 && row_bytes != 512) || (reinterpret_cast<uintptr_t>(pool) & 15u) ||
         (reinterpret_cast<uintptr_t>(idx) & 15u) || n % 64 || ctas > (int64_t(1) << 20))
         return GQA_ERR_UNSUPPORTED;
     if (n == 0) return GQA_OK;
-    hipLaunchKernelGGL(gqa::gather_rows_kernel, dim3(unsigned(ctas)), dim3(gqa::kGatherThreads), 0,
-                       reinterpret_cast<hipStream_t>(s), static_cast<const uint8_t *>(pool), row_bytes,
-                       idx, n);
+    if (whole)
+        hipLaunchKernelGGL(gqa::gather_rows_kernel<true>, dim3(unsigned(ctas)), dim3(gqa::kGatherThreads), 0,
+                           reinterpret_cast<hipStream_t>(s), static_cast<const uint8_t *>(pool), row_bytes,
+                           idx, n);
+    else
+        hipLaunchKernelGGL(gqa::gather_rows_kernel<false>, dim3(unsigned(ctas)), dim3(gqa::kGatherThreads), 0,
+                           reinterpret_cast<hipStream_t>(s), static_cast<const uint8_t *>(pool), row_bytes,
+                           idx, n);
     const hipError_t err = hipGetLastError();
     if (err != hipSuccess) {
         gqa::set_error_detail(hipGetErrorString(err));
         return GQA_ERR_LAUNCH_FAILED;
     }
     return GQA_OK;
+}
+}  // namespace
+
+extern "C" int bw_gather_rows(const void *pool, int64_t row_bytes, const int32_t *idx, int64_t n,
+                              int64_t ctas, gqa_stream_t s) {
+    return gather_rows(false, pool, row_bytes, idx, n, ctas, s);
+}
+
+extern "C" int bw_gather_whole_rows(const void *pool, int64_t row_bytes, const int32_t *idx, int64_t n,
+                                    int64_t ctas, gqa_stream_t s) {
+    return gather_rows(true, pool, row_bytes, idx, n, ctas, s);
 }

@@ -395,6 +395,13 @@ int bw_stream_read(const void *src, size_t bytes, int64_t ctas, gqa_stream_t s);
 int bw_gather_rows(const void *pool, int64_t row_bytes, const int32_t *idx, int64_t n, int64_t ctas,
                    gqa_stream_t s);
 
+/* As bw_gather_rows, with whole-row requests: each copy instruction moves the first 512 bytes of
+ * two rows (32 lanes per row), the rope tails of 576-byte rows as there.  The same rows, bytes,
+ * arguments and errors; the gather ceiling of a copy pattern that keeps each row's bytes in one
+ * request [MM, MLA decode: page_size 1 slot lists]. */
+int bw_gather_whole_rows(const void *pool, int64_t row_bytes, const int32_t *idx, int64_t n,
+                         int64_t ctas, gqa_stream_t s);
+
 /* Static description of a status code (the error classes of the constraints lists [MM, MLA
  * decode and gfx950 constraints]: shapes outside them are UNSUPPORTED); never NULL, "unknown
  * status" for a value outside gqa_status. */

@@ -456,6 +456,9 @@ def test_ceiling_argument_rejections():
     expect_status(lambda: g.bw_gather_rows(FAKE, 300, FAKE, 64, 1), -2)  # row width
     expect_status(lambda: g.bw_gather_rows(FAKE, 576, FAKE, 65, 1), -2)  # not 64-row groups
     expect_status(lambda: g.bw_gather_rows(FAKE, 576, FAKE, -64, 1), -1)
+    expect_status(lambda: g.bw_gather_whole_rows(FAKE, 300, FAKE, 64, 1), -2)
+    expect_status(lambda: g.bw_gather_whole_rows(FAKE, 576, FAKE, 65, 1), -2)
+    expect_status(lambda: g.bw_gather_whole_rows(FAKE, 576, FAKE, -64, 1), -1)
 
 
 @pytest.mark.parametrize("B,S,rows,best", [(4, 65536, 16, 64), (16, 16384, 16, 16), (2, 65536, 64, 128),

@@ -15,10 +15,11 @@ def test_stream_read_runs():
     torch.cuda.synchronize()
 
 
+@pytest.mark.parametrize("whole", [False, True])
 @pytest.mark.parametrize("row_bytes", [576, 512])
-def test_gather_rows_runs(row_bytes):
+def test_gather_rows_runs(row_bytes, whole):
     pool = torch.zeros((100000, row_bytes), dtype=torch.uint8, device="cuda")
     idx = torch.randperm(100000, device="cuda")[:64 * 1000].to(torch.int32)
     torch.cuda.synchronize()
-    g.bw_gather_rows(pool, row_bytes, idx, idx.numel(), 256)
+    (g.bw_gather_whole_rows if whole else g.bw_gather_rows)(pool, row_bytes, idx, idx.numel(), 256)
     torch.cuda.synchronize()
