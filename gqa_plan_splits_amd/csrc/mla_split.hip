@@ -754,14 +754,24 @@ __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const MlaSplitAr
         wait_vmem(cnt_rows(2) + cnt_ids(4) + cnt_ids(5));
         __syncthreads();   // tile 1 landed; the score waves read tile 0 (its tail slot is refilled
                            // in step 0)
+        // Draft windows (q_len > 1, whose row blocks of a partition read the same keys, mostly
+        // from L2): with the V^T bytes read a step ahead, tile t - 1's slots are free when step t
+        // starts, so its copies go out before the PV (measured faster there, slower at q_len 1).
+        const bool copies_first = !KV16 && kVtAhead && a.q_len > 1;
         for (int t = 0; t < ntiles; ++t) {
+            if (copies_first) {
+                issue_rows(t + 3);
+                issue_ids(t + 6);
+            }
             if (t > 0) pv_tile(t - 1);
             // line slot (t + 3) % 4 held tile t - 1 and tail slot (t + 3) % 3 tile t: every read
             // of them is done (the score waves' before the previous barrier, this wave's own
             // line just above)
-            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-            issue_rows(t + 3);
-            issue_ids(t + 6);
+            if (!copies_first) {
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+                issue_rows(t + 3);
+                issue_ids(t + 6);
+            }
             // tile t's line slot is refilled only in step t + 1, after its PV
             if constexpr (!KV16 && kVtAhead) read_vt(t);
             // rows(t + 2) and ids(t + 4) landed: everything issued before ids(t + 5) (value wave
