@@ -542,10 +542,13 @@ __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const MlaSplitAr
         }
     }
     // Schedule (tile j is read by the score waves in step j - 1, and by the value waves in
-    // step j + 1; operations for tiles >= ntiles are skipped, ids only in value wave 0):
+    // step j + 1 (576-byte fp8 rows: their V^T bytes at the end of step j); operations for
+    // tiles >= ntiles are skipped, ids only in value wave 0):
     //   prologue: ids(3), rows(0), rows(1), rows(2), ids(4), ids(5);
     //   step t:   rows(t + 3) (lines and rope tails; the line slot held tile t - 1, whose values
-    //             this wave has just applied, the tail slot tile t), ids(t + 6).
+    //             this wave has just applied or, V^T read ahead, holds in registers; the tail
+    //             slot tile t), ids(t + 6), after the PV of tile t - 1 (before it for draft
+    //             windows of 576-byte fp8 rows).
     // Copies retire in issue order.  Before the barrier that ends step t, tile t + 2 must have
     // landed (and with it ids(t + 4)); ids(t + 5) and step t's own issues may be outstanding.
     // The prologue's two barriers wait for tile 0 (whose scores the score waves compute between
