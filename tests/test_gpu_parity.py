@@ -113,12 +113,13 @@ def test_mla_tiny_all_rows(np_, bk):
 
 
 @pytest.mark.parametrize("d_qk,d_v", [(576, 512), (512, 448)])
-@pytest.mark.parametrize("q_len", [1, 4])
+@pytest.mark.parametrize("q_len", [1, 3, 4])
 @pytest.mark.parametrize("np_", [1, 3, 8])
 @pytest.mark.parametrize("bk", [32, 64])
 def test_mla_ragged_all_rows(d_qk, d_v, q_len, np_, bk):
     # several tiles per partition, ragged tails, a request shorter than the draft window (rows
-    # that see no key), an empty request, and 40 heads (a partial second 32-row block)
+    # that see no key), an empty request, and 40 heads (a partial second 32-row block; q_len 3:
+    # 120 rows per request, a partial second 64-row block)
     lens = [1000, 37, 2, 0, 2049]
     inp = workloads.mla_inputs(B=5, q_len=q_len, H=40, seq_lens=lens, pool_rows=4000, d_qk=d_qk,
                                d_v=d_v, seed=77, device=DEV, fused_q=(d_qk == 512))
