@@ -21,6 +21,10 @@ constexpr int kLineSlots = 4;      // ring of the rows' first 512 bytes
 constexpr int kTailSlots = 3;      // ring of the 64-byte rope tails (576-byte rows)
 constexpr int kIdSlots = 4;        // ring of slot-id lists
 constexpr int kNoMax = -(1 << 20); // integer maximum of a block with no visible key
+// A row's reference maximum moves only when a block's maximum exceeds it by more than this, so
+// that the running sums and accumulators are rarely rescaled; weights stay below 2^(8 + kLazyMax),
+// inside fp16's range.
+constexpr int kLazyMax = 7;
 
 // KV16: bf16 rows (1152 or 1024 bytes) in tiles of 32 keys, so that a tile's bytes (36 KiB for
 // 576-wide rows) and the ring match those of 64 fp8 keys.

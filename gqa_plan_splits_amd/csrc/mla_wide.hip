@@ -9,7 +9,8 @@
 // the same exact arithmetic (stored fp8 K decoded exactly to bf16 against the bf16 query, fp32
 // sums; weights p = 2^(score - m + 8) stored as fp16 against V decoded exactly to fp16; the
 // output normalized by the sum of the stored weights, the LSE from the sum of the exact ones; m
-// an integer running maximum), the same draft window and skipped keys.  (Decode context
+// an integer reference maximum, at most kLazyMax below the ceiling of the row's largest base-2
+// score so far), the same draft window and skipped keys.  (Decode context
 // parallelism is defined for 576-byte rows only; those never reach this kernel.)
 //
 // Why.  mla_split.hip holds a row's query in one score wave's registers, 32 rows per wave, so
@@ -256,7 +257,9 @@ __global__ void __launch_bounds__(kThreads, 1) mla_wide_kernel(const MlaSplitArg
                 const int rl = 16 * rb + col;
                 const int mt = max(max(ML[rl], ML[64 + rl]), max(ML[128 + rl], ML[192 + rl]));
                 const int m_old = MR[64 * ((t + 1) & 1) + rl];
-                const int m_new = max(m_old, mt);
+                // the reference maximum moves only when the tile's exceeds it by more than
+                // kLazyMax (weights then stay below 2^(8 + kLazyMax)), so rescales are rare
+                const int m_new = mt > m_old + kLazyMax ? mt : m_old;
                 const float alpha = ldexpf(1.f, m_old - m_new);
                 const float bias = float(8 - m_new);
                 const float p0 = fast_exp2(fmaf(sv[rb][0], c_row, bias));
