@@ -227,7 +227,12 @@ def measured_counters(workload):
     # SQ_VALU_MFMA_BUSY_CYCLES is summed over every SIMD; GRBM_GUI_ACTIVE over the XCDs.
     busy = float(vals["mfma_busy_cycles"]) / (
         float(vals["grbm_gui_active"]) / float(vals["xcds"]) * float(vals["simds"]))
-    return {"traffic": int(fetch + write), "mfma_busy": round(busy, 4)}
+    out = {"traffic": int(fetch + write), "mfma_busy": round(busy, 4)}
+    if "valu_active_inst" in vals:
+        # SQ_ACTIVE_INST_VALU counts issue quads (4 cycles) summed over every wave
+        out["valu_busy"] = round(float(vals["valu_active_inst"]) * 4 / (
+            float(vals["valu_grbm_gui_active"]) / float(vals["xcds"]) * float(vals["simds"])), 4)
+    return out
 
 
 def cpu_model():
@@ -872,6 +877,7 @@ def main():
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": counters["traffic"] if counters else None,
             "mfma_busy": counters["mfma_busy"] if counters else None,
+            "valu_busy": counters.get("valu_busy") if counters else None,
             "algorithmic_bytes": kv,
             "algorithmic_bytes_what": ("KV payload: every key's row once (%d B per key)" % (inp.d_qk * inp.pool.element_size())
                                        if case.is_mla else "KV payload: every token's K and V rows once per kv head (512 B)"),
@@ -890,6 +896,9 @@ def main():
             "frac": round(q4["mfma_tflops"] / 2500.0, 4), "avg_launch_us": q4["split_us"],
             "flops_what": "per (row, visible key) 2 x (576 + 512): QK^T on bf16 MFMA and PV on fp16 MFMA, "
                           "both at the 2.5 PFLOP/s dense bf16/fp16 peak"}
+        q4_counters = measured_counters("mla_h64_b16_s131072_q4")
+        if q4_counters:
+            result["roofline_q4"].update({k: q4_counters.get(k) for k in ("traffic", "mfma_busy", "valu_busy")})
     gq = table.get("gqa_b32_hq64_hkv8_d128_p16")
     if gq and args.workload != "gqa_b32_hq64_hkv8_d128_p16":
         # the paged GQA workload's split kernel against the HBM peak (its table row's split-only time)

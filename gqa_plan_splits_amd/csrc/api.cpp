@@ -72,7 +72,9 @@ int check_problem(const gqa_decode_problem *p, Derived *d) {
         if (!wide && !sparse) return GQA_ERR_UNSUPPORTED;
         if (p->page_size != 1) return GQA_ERR_UNSUPPORTED;
         const int64_t elem = p->fp8_format == GQA_KV_BF16 ? 2 : 1;
-        if (p->kv_stride_row < p->d_qk * elem || p->kv_stride_row % 16 || !aligned16(p->kv))
+        // (row strides below 2^32 bytes: the kernels address a row with one 32 x 32-bit product)
+        if (p->kv_stride_row < p->d_qk * elem || p->kv_stride_row % 16 || p->kv_stride_row >= (int64_t(1) << 32) ||
+            !aligned16(p->kv))
             return GQA_ERR_UNSUPPORTED;
         if (p->q_pe_stride_tok % 8 || p->q_pe_stride_head % 8 || !aligned16(p->q_pe))
             return GQA_ERR_UNSUPPORTED;

@@ -459,7 +459,8 @@ __global__ void __launch_bounds__(kThreads, 1) mla_split_kernel(const MlaSplitAr
     const int tail_chunk = KV16 ? 1024 + 16 * ((lane & 7) ^ swz16(tail_pos))
                                 : 512 + 16 * ((lane & 3) ^ swz_tail(tail_pos));
     const int tail_key = KV16 ? key_of_pos16(tail_pos) : key_of_pos(tail_pos);
-    const uint64_t kv_stride = uint64_t(a.kv_stride);
+    // (row strides are below 2^32 bytes: one 32 x 32-bit product per row address)
+    const uint32_t kv_stride = uint32_t(a.kv_stride);
     const bool id_loader = v == 0;
 
     auto issue_ids = [&](int tile) {

@@ -317,7 +317,8 @@ __global__ void __launch_bounds__(kThreads, 1) mla_wide_kernel(const MlaSplitArg
     const int v = wave - 4;
     // ---- copies (as the value waves of mla_split.hip: value wave v copies line v)
     const int jgrp = lane >> 3;
-    const uint64_t kv_stride = uint64_t(a.kv_stride);
+    // (row strides are below 2^32 bytes: one 32 x 32-bit product per row address)
+    const uint32_t kv_stride = uint32_t(a.kv_stride);
     const bool id_loader = v == 0;
     auto issue_ids = [&](int tile) {
         if (id_loader && tile < ntiles)

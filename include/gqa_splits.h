@@ -107,7 +107,7 @@ typedef struct gqa_decode_problem {
     int64_t q_pe_stride_tok, q_pe_stride_head;
 
     /* MLA pool: [N, d_qk] elements of fp8_format (fp8 bytes or bf16); row stride kv_stride_row
-     * bytes (a multiple of 16, >= d_qk elements; pointer 16-byte aligned). */
+     * bytes (a multiple of 16, >= d_qk elements and below 2^32; pointer 16-byte aligned). */
     const void *kv;
     int64_t kv_stride_row;
 

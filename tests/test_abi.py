@@ -189,7 +189,7 @@ def expect_status(fn, status):
     ("num_heads", 129, -2), ("q", 0, -1), ("kv", 0, -1), ("q_pe", 0, -1), ("kv_indices", 0, -1),
     ("kv_indptr", 0, -1), ("seq_lens", 0, -1), ("num_kv_heads", 2, -1), ("kind", 7, -1),
     ("fp8_format", 1, -2), ("fp8_format", 5, -1), ("d_qk", 128, -2), ("d_v", 256, -2),
-    ("page_size", 16, -2), ("kv_stride_row", 500, -2), ("q", FAKE + 8, -2),
+    ("page_size", 16, -2), ("kv_stride_row", 500, -2), ("kv_stride_row", 1 << 32, -2), ("q", FAKE + 8, -2),
     ("q_stride_head", 4, -2), ("scale", 0.0, -1), ("kv_scale", 0.0, -1),
 ])
 def test_mla_rejections(field, value, status):
