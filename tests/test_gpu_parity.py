@@ -3,6 +3,7 @@
 Small shapes compare every output (several tiles, ragged tails, empty rows); the full-size
 workloads compare sampled rows in exactly the launch configuration the benchmark times
 (planner np, tile rule BLOCK_K)."""
+import zlib
 import numpy as np
 import pytest
 import torch
@@ -430,7 +431,8 @@ def test_mla_full_size_sampled(name, make):
     log("mla %s planner np=%d bk=%d" % (name, np_, bk))
     out, lse = run_decode(p, 512)
     torch.cuda.synchronize()
-    rows = sample_rows(inp.B, inp.q_len, inp.H, 24, seed=hash(name) % 1000)
+    # 128 rows (a stable seed per workload: str hashes vary between processes)
+    rows = sample_rows(inp.B, inp.q_len, inp.H, 128, seed=zlib.crc32(name.encode()) % 1000)
     ref_o, ref_l = oracle_mla(inp, rows)
     compare(out[rows], lse[rows], ref_o, ref_l, "mla " + name)
     del inp, out, lse
@@ -447,7 +449,7 @@ def test_sparse_full_size_both_tiles(nq):
     p = mla_problem(inp)
     np_, bk = g.decode_plan(p)
     log("sparse nq=%d planner np=%d bk=%d" % (nq, np_, bk))
-    rows = sample_rows(inp.B, 1, inp.H, 32, seed=nq)
+    rows = sample_rows(inp.B, 1, inp.H, 128, seed=nq)
     ref_o, ref_l = oracle_mla(inp, rows)
     results = {}
     for tile in (32, 64):   # the rule's choice and the other one: same numerics either way
@@ -568,7 +570,7 @@ def test_gqa_mqa_full_size_sampled():
     log("gqa mqa full planner np=%d bk=%d" % (np_, bk))
     out, lse = run_decode(p, 128)
     torch.cuda.synchronize()
-    rows = sample_rows(inp.B, 1, inp.Hq, 48, seed=124)
+    rows = sample_rows(inp.B, 1, inp.Hq, 128, seed=124)
     ref_o, ref_l = oracle_gqa(inp, rows)
     compare(out[rows], lse[rows], ref_o, ref_l, "gqa mqa full")
     o2, l2 = run_decode(p, 128)
