@@ -22,9 +22,11 @@ constexpr int kTailSlots = 3;      // ring of the 64-byte rope tails (576-byte r
 constexpr int kIdSlots = 4;        // ring of slot-id lists
 constexpr int kNoMax = -(1 << 20); // integer maximum of a block with no visible key
 // A row's reference maximum moves only when a block's maximum exceeds it by more than this, so
-// that the running sums and accumulators are rarely rescaled; weights stay below 2^(8 + kLazyMax),
-// inside fp16's range.
-constexpr int kLazyMax = 7;
+// that the running sums and accumulators are rarely rescaled; weights are then at most
+// 2^(8 + kLazyMax).  Kept small: a block whose reference lags the other block's by more than 24
+// loses its fp16 weights in the value waves' alignment, each at most 2^(kLazyMax + 1 - 24) of the
+// row's largest.
+constexpr int kLazyMax = 3;
 
 // KV16: bf16 rows (1152 or 1024 bytes) in tiles of 32 keys, so that a tile's bytes (36 KiB for
 // 576-wide rows) and the ring match those of 64 fp8 keys.

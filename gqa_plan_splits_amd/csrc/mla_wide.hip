@@ -258,7 +258,7 @@ __global__ void __launch_bounds__(kThreads, 1) mla_wide_kernel(const MlaSplitArg
                 const int mt = max(max(ML[rl], ML[64 + rl]), max(ML[128 + rl], ML[192 + rl]));
                 const int m_old = MR[64 * ((t + 1) & 1) + rl];
                 // the reference maximum moves only when the tile's exceeds it by more than
-                // kLazyMax (weights then stay below 2^(8 + kLazyMax)), so rescales are rare
+                // kLazyMax (weights are then at most 2^(8 + kLazyMax)), so rescales are rare
                 const int m_new = mt > m_old + kLazyMax ? mt : m_old;
                 const float alpha = ldexpf(1.f, m_old - m_new);
                 const float bias = float(8 - m_new);
